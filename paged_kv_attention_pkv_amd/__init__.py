@@ -1,0 +1,19 @@
+"""paged_kv_attention_pkv_amd -- attention over a paged KV cache on MI355X (gfx950).
+
+The compute path is the C-ABI library ``libpkv.so`` (hand-written HIP kernels,
+declared in ``include/pkv.h``).  This package is its thin Python binding:
+argument marshalling from torch tensors (device memory and streams) to the C
+entry points, nothing else.  The library is loaded on first use and a missing
+or unloadable library raises immediately; there is no fallback path.
+"""
+from .api import (  # noqa: F401
+    PkvError,
+    append,
+    decode_attn,
+    decode_workspace_bytes,
+    lib_path,
+    prefill_attn,
+    prefill_workspace_bytes,
+    route,
+    validate_host,
+)
