@@ -1,0 +1,238 @@
+/*
+ * pkv.h -- C ABI of libpkv: attention over a paged KV cache on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The KV cache is one pool of fixed-size physical pages per layer for K and
+ * one for V.  Each sequence owns a row of `block_table` that maps its logical
+ * blocks to physical pages; logical token j of sequence b lives in page
+ * block_table[b][j / page_size] at slot j % page_size.  This is the routing
+ * of the flash_attn `block_table` / `cache_seqlens` call described in
+ * mini-infer 06 "True PagedAttention" §1 and of the page table in the
+ * unsloth scripts commit page ("Why this works", item 1).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is a DEVICE pointer unless its comment says
+ *    "host".  All buffers are owned by the caller; the library allocates and
+ *    frees nothing, keeps no state between calls and never reads device
+ *    memory back to the host, so calls never synchronise the stream and are
+ *    safe to capture in a HIP graph.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    work is enqueued on it asynchronously.
+ *  - Only host scalars and pointer nullness are checked.  Device-resident
+ *    metadata (tables, lengths, indptr) is the caller's contract; on the host
+ *    it can be checked with pkv_validate_host / pkv_validate_append_host.
+ *    Violating it is undefined behaviour (out-of-bounds device accesses).
+ *  - Return value: PKV_OK, or an error code; on an error nothing has been
+ *    enqueued except for PKV_ELAUNCH (the launch itself failed).
+ *
+ * Pool layout (pkv_cache_desc)
+ * ----------------------------
+ * Element (page, kv_head, slot, dim) of a pool is at element offset
+ *     page * s_page + kv_head * s_head + slot * s_tok + dim
+ * from the pool base; the dim stride is 1.  The head-major "HND" layout of
+ * the FlashInfer PR #9451 analysis (§1 domain check) is
+ * [num_pages, num_kv_heads, page_size, head_dim] (s_tok = head_dim,
+ * s_head = page_size*head_dim); the flash_attn block tensor
+ * (num_blocks, block_size, num_kv_heads, head_dim) of mini-infer 06 §1 is
+ * "NHD" (s_head = head_dim, s_tok = num_kv_heads*head_dim).  K and V pools
+ * share one descriptor.  Page 0 is reserved: tables never need to route a
+ * live token to it, and unused table entries may hold 0.
+ *
+ * Supported: dtype PKV_BF16 or PKV_F32; page_size 16; head_dim 64, 128 or
+ * 256; a GQA ratio G = num_q_heads / num_kv_heads from 1 to 16 (this covers
+ * the ratios {1, 2, 4, 8, 16} of the FlashInfer PR #9451 analysis, §1, and
+ * the 48/8 = 6 of its D=256 workload); strides multiples of 8 elements and
+ * all pointers 16-byte aligned.  Query head h reads KV head h / G.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+typedef enum pkv_status {
+    PKV_OK = 0,
+    PKV_EINVAL = 1,        /* null pointer, non-positive size, inconsistent sizes */
+    PKV_EUNSUPPORTED = 2,  /* dtype, head_dim, page_size, GQA ratio, stride or alignment */
+    PKV_EWORKSPACE = 3,    /* workspace missing or smaller than the query says */
+    PKV_ELAUNCH = 4,       /* a kernel launch failed (hipGetLastError) */
+    PKV_EDEVICE = 5,       /* no usable HIP device / device query failed */
+    PKV_EVALIDATE = 6      /* pkv_validate_*: a device-data precondition is violated */
+} pkv_status;
+
+typedef enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+typedef struct pkv_cache_desc {
+    int32_t dtype;        /* pkv_dtype of the pools, q, new K/V and out */
+    int32_t num_pages;    /* physical pages per pool, page 0 included */
+    int32_t page_size;    /* tokens per page (16) */
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t reserved;     /* must be 0 */
+    int64_t s_page;       /* element strides of the pool; dim stride is 1 */
+    int64_t s_head;
+    int64_t s_tok;
+} pkv_cache_desc;
+
+/* PKV_ABI_VERSION of the loaded library. */
+int32_t pkv_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char *pkv_status_string(pkv_status status);
+
+/*
+ * pkv_append -- write each step's new K/V into the pool in place.
+ *
+ * The write half of flash_attn_with_kvcache(k=, v=, cache_seqlens, block_table)
+ * in mini-infer 06 §1 (new keys are stored at the current cache length, in the
+ * block the table routes that position to), and the in-graph
+ * `k_cache[addr] = k_val` of the unsloth scripts commit page ("Files").
+ *
+ *   k_new, v_new   [total_new, num_kv_heads, head_dim], dense, dtype of the pool
+ *   block_table    int32 [batch, bt_cols]
+ *   cache_seqlens  int32 [batch]: tokens already cached (pre-append length L_b)
+ *   new_indptr     int32 [batch+1], new_indptr[0] = 0, new_indptr[batch] =
+ *                  total_new: sequence b appends rows new_indptr[b] ..
+ *                  new_indptr[b+1]-1.  NULL means one token per sequence
+ *                  (total_new must equal batch).
+ *   seqlens_out    int32 [batch] or NULL: receives L_b + tokens appended, the
+ *                  attended length for the following attention call.  Must not
+ *                  alias cache_seqlens.
+ * Token t of sequence b goes to logical position L_b + t; its page must be a
+ * real page (1..num_pages-1) and no two appended tokens may share a slot.  The
+ * copy is bit-exact; no other byte of either pool is written.
+ */
+pkv_status pkv_append(const pkv_cache_desc *cache, void *k_cache, void *v_cache,
+                      const void *k_new, const void *v_new, const int32_t *block_table,
+                      int32_t bt_cols, const int32_t *cache_seqlens, const int32_t *new_indptr,
+                      int32_t batch, int32_t total_new, int32_t *seqlens_out, void *stream);
+
+/*
+ * pkv_decode_workspace_bytes -- device workspace pkv_decode_attn needs for
+ * these sizes on the current device (bytes; 0 only for invalid arguments).
+ * Depends on batch, num_q_heads, the descriptor and the device, not on the
+ * lengths, so one workspace can be reused for every step of a batch shape.
+ */
+size_t pkv_decode_workspace_bytes(const pkv_cache_desc *cache, int32_t batch, int32_t num_q_heads,
+                                  int32_t max_kv_len);
+
+/*
+ * pkv_decode_attn -- GQA decode attention, one query token per sequence.
+ *
+ * The attend half of flash_attn_with_kvcache in mini-infer 06 §1 (the
+ * split-KV path it profiles in §6): query b attends the first
+ * cache_seqlens[b] tokens of its row (the token appended in the same step
+ * included), softmax(scale * q k^T) v, without gathering pages.
+ *
+ *   out            [batch, num_q_heads, head_dim], dtype of the pool
+ *   lse            float [batch, num_q_heads] or NULL: natural-log
+ *                  log-sum-exp of the scaled scores (-inf for an empty row)
+ *   q              [batch, num_q_heads, head_dim], dtype of the pool
+ *   cache_seqlens  int32 [batch]: ATTENDED length n_b (after append); 0 gives
+ *                  out = 0 and lse = -inf for that row
+ *   max_kv_len     host upper bound of cache_seqlens (no device read-back is
+ *                  made to find it; mini-infer 06 §5); must satisfy
+ *                  max_kv_len <= bt_cols * page_size
+ *   workspace      device buffer of at least pkv_decode_workspace_bytes(...)
+ * Long rows are split across workers and merged by a log-sum-exp combine;
+ * every row's result depends only on its logical keys, not on which physical
+ * pages hold them.
+ */
+pkv_status pkv_decode_attn(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
+                           int32_t num_q_heads, const void *k_cache, const void *v_cache,
+                           const int32_t *block_table, int32_t bt_cols,
+                           const int32_t *cache_seqlens, int32_t batch, int32_t max_kv_len,
+                           float scale, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Same as pkv_decode_attn with an explicit number of split workers (0 =
+ * automatic).  For tests of split invariance and for tuning; the workspace
+ * must be sized with pkv_decode_workspace_bytes_ex and the same count.
+ */
+size_t pkv_decode_workspace_bytes_ex(const pkv_cache_desc *cache, int32_t batch,
+                                     int32_t num_q_heads, int32_t max_kv_len, int32_t workers);
+pkv_status pkv_decode_attn_ex(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
+                              int32_t num_q_heads, const void *k_cache, const void *v_cache,
+                              const int32_t *block_table, int32_t bt_cols,
+                              const int32_t *cache_seqlens, int32_t batch, int32_t max_kv_len,
+                              float scale, void *workspace, size_t workspace_bytes,
+                              int32_t workers, void *stream);
+
+/*
+ * pkv_prefill_workspace_bytes / pkv_prefill_attn -- causal (chunked) prefill
+ * over the paged pool.
+ *
+ * Request r has q_r = qo_indptr[r+1] - qo_indptr[r] query rows (its newest
+ * tokens, already appended) and kv_lens[r] keys.  With causal != 0 the
+ * causal mask is end-aligned: query row i (0-based) sees keys
+ * 0 .. kv_r - q_r + i, i.e. kv_r - q_r + i + 1 of them (FlashInfer PR #9451
+ * analysis, §1 work bound); causal == 0 lets every row see all kv_r keys.
+ *
+ *   out        [total_q, num_q_heads, head_dim], dtype of the pool
+ *   lse        float [total_q, num_q_heads] or NULL
+ *   q          [total_q, num_q_heads, head_dim]
+ *   kv_lens    int32 [batch]: keys of each request, chunk included
+ *   qo_indptr  int32 [batch+1], device: ragged query offsets, qo_indptr[0] = 0,
+ *              qo_indptr[batch] = total_q, 0 <= q_r (<= kv_r when causal)
+ *   max_q      host upper bound of q_r; max_kv_len host upper bound of kv_r
+ * Only PKV_BF16 is supported by this entry point.
+ */
+size_t pkv_prefill_workspace_bytes(const pkv_cache_desc *cache, int32_t batch,
+                                   int32_t num_q_heads, int32_t total_q, int32_t max_q,
+                                   int32_t max_kv_len);
+pkv_status pkv_prefill_attn(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
+                            int32_t num_q_heads, const void *k_cache, const void *v_cache,
+                            const int32_t *block_table, int32_t bt_cols, const int32_t *kv_lens,
+                            const int32_t *qo_indptr, int32_t batch, int32_t total_q,
+                            int32_t max_q, int32_t max_kv_len, int32_t causal, float scale,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * pkv_route -- debug/test entry point, not on the hot path: the element
+ * offset (kv head 0, dim 0) of every logical token, as the kernels compute it.
+ *   offsets  int64 [batch, max_len]: offsets[b][j] for j < seqlens[b], -1 after
+ */
+pkv_status pkv_route(const pkv_cache_desc *cache, const int32_t *block_table, int32_t bt_cols,
+                     const int32_t *seqlens, int32_t batch, int32_t max_len, int64_t *offsets,
+                     void *stream);
+
+/*
+ * pkv_validate_host -- host-side check of the device-data preconditions of an
+ * attention call, on HOST copies of the metadata (the fail-closed metadata
+ * consistency rules of the FlashInfer PR #9451 analysis, §1).
+ *   block_table  host int32 [batch, bt_cols]; kv_lens host int32 [batch]
+ *   qo_indptr    host int32 [batch+1] or NULL (decode)
+ * Checks: 0 <= kv_r <= max_kv_len <= bt_cols*page_size; every block a row
+ * touches is a page in 1..num_pages-1; with qo_indptr: qo_indptr[0] == 0,
+ * non-decreasing, qo_indptr[batch] == total_q, q_r <= max_q and, when causal,
+ * 0 < q_r <= kv_r.  Returns PKV_OK or PKV_EVALIDATE and writes a message into
+ * msg (host, may be NULL).
+ */
+pkv_status pkv_validate_host(const pkv_cache_desc *cache, const int32_t *block_table,
+                             int32_t bt_cols, const int32_t *kv_lens, const int32_t *qo_indptr,
+                             int32_t batch, int32_t total_q, int32_t max_q, int32_t max_kv_len,
+                             int32_t causal, char *msg, size_t msg_len);
+
+/*
+ * pkv_validate_append_host -- host-side check of pkv_append's preconditions
+ * on HOST copies: every target position routes to a page in
+ * 1..num_pages-1, the table is wide enough, new_indptr is consistent, and no
+ * two appended tokens target the same (page, slot).
+ */
+pkv_status pkv_validate_append_host(const pkv_cache_desc *cache, const int32_t *block_table,
+                                    int32_t bt_cols, const int32_t *cache_seqlens,
+                                    const int32_t *new_indptr, int32_t batch, int32_t total_new,
+                                    char *msg, size_t msg_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -7,7 +7,9 @@ entry points, nothing else.  The library is loaded on first use and a missing
 or unloadable library raises immediately; there is no fallback path.
 """
 from .api import (  # noqa: F401
+    EXPORTED,
     PkvError,
+    cache_desc,
     append,
     decode_attn,
     decode_workspace_bytes,
@@ -15,5 +17,6 @@ from .api import (  # noqa: F401
     prefill_attn,
     prefill_workspace_bytes,
     route,
+    validate_append_host,
     validate_host,
 )

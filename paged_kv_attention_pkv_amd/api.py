@@ -1,0 +1,324 @@
+"""Python binding of libpkv (include/pkv.h): argument marshalling only.
+
+Every function takes torch tensors that already live on the GPU, checks their
+shapes and dtypes against each other, and passes raw device pointers, sizes
+and the current HIP stream to the C entry point of the same name.  All work
+happens in the library's HIP kernels; nothing here computes attention and
+there is no fallback: a missing library, or a non-OK status from the library,
+raises.
+
+Pool tensors are 4-D: ``layout="HND"`` is [num_pages, num_kv_heads,
+page_size, head_dim] and ``layout="NHD"`` is [num_pages, page_size,
+num_kv_heads, head_dim]; any strides with a unit dim stride are accepted and
+K and V must share them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.environ.get("PKV_LIB", os.path.join(_HERE, "libpkv.so"))
+
+PKV_F32, PKV_BF16 = 0, 1
+_STATUS = {
+    0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace missing or too small",
+    4: "kernel launch failed", 5: "no usable HIP device", 6: "device-data precondition violated",
+}
+
+
+class PkvError(RuntimeError):
+    def __init__(self, fn: str, code: int, detail: str = ""):
+        text = _STATUS.get(code, f"status {code}")
+        super().__init__(f"{fn}: {text}" + (f" ({detail})" if detail else ""))
+        self.code = code
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("s_page", ctypes.c_int64),
+        ("s_head", ctypes.c_int64),
+        ("s_tok", ctypes.c_int64),
+    ]
+
+
+_lib = None
+_lock = threading.Lock()
+
+_VP, _I32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+_DP = ctypes.POINTER(_Desc)
+_SIGS = {
+    "pkv_abi_version": ([], ctypes.c_int32),
+    "pkv_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "pkv_append": ([_DP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _VP, _VP], ctypes.c_int),
+    "pkv_decode_workspace_bytes": ([_DP, _I32, _I32, _I32], _SZ),
+    "pkv_decode_workspace_bytes_ex": ([_DP, _I32, _I32, _I32, _I32], _SZ),
+    "pkv_decode_attn": ([_DP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _VP, _I32, _I32, ctypes.c_float,
+                         _VP, _SZ, _VP], ctypes.c_int),
+    "pkv_decode_attn_ex": ([_DP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _VP, _I32, _I32, ctypes.c_float,
+                            _VP, _SZ, _I32, _VP], ctypes.c_int),
+    "pkv_prefill_workspace_bytes": ([_DP, _I32, _I32, _I32, _I32, _I32], _SZ),
+    "pkv_prefill_attn": ([_DP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32,
+                          _I32, ctypes.c_float, _VP, _SZ, _VP], ctypes.c_int),
+    "pkv_route": ([_DP, _VP, _I32, _VP, _I32, _I32, _VP, _VP], ctypes.c_int),
+    "pkv_validate_host": ([_DP, _VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32, _I32, ctypes.c_char_p, _SZ],
+                          ctypes.c_int),
+    "pkv_validate_append_host": ([_DP, _VP, _I32, _VP, _VP, _I32, _I32, ctypes.c_char_p, _SZ], ctypes.c_int),
+}
+EXPORTED = tuple(_SIGS)
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded libpkv (ctypes.CDLL); raises if it is not built."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(_LIB_PATH):
+                    raise RuntimeError(
+                        f"libpkv.so not found at {_LIB_PATH}: build it with "
+                        "`python -m paged_kv_attention_pkv_amd.build` (hipcc, gfx950)")
+                handle = ctypes.CDLL(_LIB_PATH)
+                for name, (args, res) in _SIGS.items():
+                    f = getattr(handle, name)
+                    f.argtypes = args
+                    f.restype = res
+                _lib = handle
+    return _lib
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return PKV_BF16
+    if dt == torch.float32:
+        return PKV_F32
+    raise TypeError(f"unsupported dtype {dt}; libpkv takes bfloat16 or float32")
+
+
+def cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor | None = None, layout: str = "HND") -> _Desc:
+    """pkv_cache_desc of a 4-D pool tensor in the given layout."""
+    if k_cache.dim() != 4:
+        raise ValueError("pool tensors are 4-D")
+    if k_cache.stride(3) != 1:
+        raise ValueError("pool dim stride must be 1")
+    if v_cache is not None and (v_cache.shape != k_cache.shape or v_cache.stride() != k_cache.stride()
+                                or v_cache.dtype != k_cache.dtype):
+        raise ValueError("K and V pools must have the same shape, strides and dtype")
+    n, a, b, d = k_cache.shape
+    s = k_cache.stride()
+    if layout == "HND":
+        hkv, page, s_head, s_tok = a, b, s[1], s[2]
+    elif layout == "NHD":
+        page, hkv, s_tok, s_head = a, b, s[1], s[2]
+    else:
+        raise ValueError(f"layout must be 'HND' or 'NHD', not {layout!r}")
+    return _Desc(_dtype_code(k_cache.dtype), n, page, hkv, d, 0, s[0], s_head, s_tok)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check(fn: str, rc: int, detail: str = "") -> None:
+    if rc != 0:
+        raise PkvError(fn, rc, detail)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, dev=None, ndim=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} must be on {dev}, got {t.device}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# --------------------------------------------------------------------------
+# entry points
+# --------------------------------------------------------------------------
+
+def append(k_cache, v_cache, k_new, v_new, block_table, cache_seqlens, new_indptr=None,
+           seqlens_out=None, layout: str = "HND"):
+    """pkv_append: write k_new/v_new [total_new, Hkv, D] at each sequence's
+    cached length.  Returns seqlens_out (allocated when not given)."""
+    desc = cache_desc(k_cache, v_cache, layout)
+    dev = k_cache.device
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, nm, k_cache.dtype, dev, 3)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
+    batch = cache_seqlens.shape[0]
+    if new_indptr is not None:
+        _need(new_indptr, "new_indptr", torch.int32, dev, 1)
+        if new_indptr.shape[0] != batch + 1:
+            raise ValueError("new_indptr must have batch+1 entries")
+    if block_table.shape[0] != batch:
+        raise ValueError("block_table rows must equal batch")
+    if seqlens_out is None:
+        seqlens_out = torch.empty_like(cache_seqlens)
+    rc = lib().pkv_append(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+                          _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens), _ptr(new_indptr),
+                          batch, k_new.shape[0], _ptr(seqlens_out), _stream(k_cache))
+    _check("pkv_append", rc)
+    return seqlens_out
+
+
+def decode_workspace_bytes(k_cache, batch: int, num_q_heads: int, max_kv_len: int, layout: str = "HND",
+                           workers: int = 0) -> int:
+    desc = cache_desc(k_cache, None, layout)
+    with torch.cuda.device(k_cache.device):
+        n = lib().pkv_decode_workspace_bytes_ex(ctypes.byref(desc), batch, num_q_heads, max_kv_len, workers)
+    if n == 0:
+        raise PkvError("pkv_decode_workspace_bytes", 1, "invalid sizes")
+    return int(n)
+
+
+def decode_attn(q, k_cache, v_cache, block_table, cache_seqlens, max_kv_len: int, scale: float | None = None,
+                out=None, lse=None, workspace=None, layout: str = "HND", workers: int = 0,
+                return_lse: bool = False):
+    """pkv_decode_attn: q [B, Hq, D] against the first cache_seqlens[b] keys
+    of each row.  Returns out (and lse when return_lse or lse is given)."""
+    desc = cache_desc(k_cache, v_cache, layout)
+    dev = k_cache.device
+    _need(q, "q", k_cache.dtype, dev, 3)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
+    batch, hq, d = q.shape
+    if cache_seqlens.shape[0] != batch or block_table.shape[0] != batch:
+        raise ValueError("batch mismatch between q, block_table and cache_seqlens")
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, dev, 3)
+    if lse is None and return_lse:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev, 2)
+    with torch.cuda.device(dev):
+        need = lib().pkv_decode_workspace_bytes_ex(ctypes.byref(desc), batch, hq, max_kv_len, workers)
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        rc = lib().pkv_decode_attn_ex(ctypes.byref(desc), _ptr(out), _ptr(lse), _ptr(q), hq, _ptr(k_cache),
+                                      _ptr(v_cache), _ptr(block_table), block_table.shape[1],
+                                      _ptr(cache_seqlens), batch, int(max_kv_len), float(scale),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      int(workers), _stream(k_cache))
+    _check("pkv_decode_attn", rc)
+    return (out, lse) if lse is not None else out
+
+
+def prefill_workspace_bytes(k_cache, batch, num_q_heads, total_q, max_q, max_kv_len, layout="HND") -> int:
+    desc = cache_desc(k_cache, None, layout)
+    return int(lib().pkv_prefill_workspace_bytes(ctypes.byref(desc), batch, num_q_heads, total_q, max_q,
+                                                 max_kv_len))
+
+
+def prefill_attn(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, max_q: int, max_kv_len: int,
+                 causal: bool = True, scale: float | None = None, out=None, lse=None, workspace=None,
+                 layout: str = "HND", return_lse: bool = False):
+    """pkv_prefill_attn: ragged queries q [total_q, Hq, D] (offsets qo_indptr)
+    against kv_lens[r] keys of each request, end-aligned causal mask."""
+    desc = cache_desc(k_cache, v_cache, layout)
+    dev = k_cache.device
+    _need(q, "q", k_cache.dtype, dev, 3)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(kv_lens, "kv_lens", torch.int32, dev, 1)
+    _need(qo_indptr, "qo_indptr", torch.int32, dev, 1)
+    total_q, hq, d = q.shape
+    batch = kv_lens.shape[0]
+    if qo_indptr.shape[0] != batch + 1 or block_table.shape[0] != batch:
+        raise ValueError("batch mismatch between qo_indptr, block_table and kv_lens")
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, dev, 3)
+    if lse is None and return_lse:
+        lse = torch.empty((total_q, hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev, 2)
+    with torch.cuda.device(dev):
+        need = lib().pkv_prefill_workspace_bytes(ctypes.byref(desc), batch, hq, total_q, max_q, max_kv_len)
+        if workspace is None and need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        rc = lib().pkv_prefill_attn(ctypes.byref(desc), _ptr(out), _ptr(lse), _ptr(q), hq, _ptr(k_cache),
+                                    _ptr(v_cache), _ptr(block_table), block_table.shape[1], _ptr(kv_lens),
+                                    _ptr(qo_indptr), batch, total_q, int(max_q), int(max_kv_len),
+                                    int(bool(causal)), float(scale), _ptr(workspace),
+                                    0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                    _stream(k_cache))
+    _check("pkv_prefill_attn", rc)
+    return (out, lse) if lse is not None else out
+
+
+def route(k_cache, block_table, seqlens, max_len: int, layout: str = "HND"):
+    """pkv_route: int64 [B, max_len] element offsets of every logical token."""
+    desc = cache_desc(k_cache, None, layout)
+    dev = k_cache.device
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seqlens, "seqlens", torch.int32, dev, 1)
+    batch = seqlens.shape[0]
+    offsets = torch.empty((batch, max_len), dtype=torch.int64, device=dev)
+    rc = lib().pkv_route(ctypes.byref(desc), _ptr(block_table), block_table.shape[1], _ptr(seqlens), batch,
+                         max_len, _ptr(offsets), _stream(k_cache))
+    _check("pkv_route", rc)
+    return offsets
+
+
+def validate_host(k_cache, block_table, kv_lens, qo_indptr=None, max_q: int = 0, max_kv_len: int | None = None,
+                  causal: bool = True, layout: str = "HND") -> None:
+    """pkv_validate_host on host copies of the metadata; raises PkvError
+    naming the first violated precondition."""
+    desc = cache_desc(k_cache, None, layout)
+    bt = block_table.detach().to("cpu", torch.int32).contiguous()
+    kl = kv_lens.detach().to("cpu", torch.int32).contiguous()
+    ip = None if qo_indptr is None else qo_indptr.detach().to("cpu", torch.int32).contiguous()
+    batch = kl.shape[0]
+    total_q = int(ip[-1]) if ip is not None else 0
+    if max_kv_len is None:
+        max_kv_len = int(kl.max()) if batch else 0
+    msg = ctypes.create_string_buffer(256)
+    rc = lib().pkv_validate_host(ctypes.byref(desc), _ptr(bt), bt.shape[1], _ptr(kl), _ptr(ip), batch, total_q,
+                                 int(max_q), int(max_kv_len), int(bool(causal)), msg, 256)
+    _check("pkv_validate_host", rc, msg.value.decode())
+
+
+def validate_append_host(k_cache, block_table, cache_seqlens, new_indptr=None, total_new: int | None = None,
+                         layout: str = "HND") -> None:
+    desc = cache_desc(k_cache, None, layout)
+    bt = block_table.detach().to("cpu", torch.int32).contiguous()
+    cs = cache_seqlens.detach().to("cpu", torch.int32).contiguous()
+    ip = None if new_indptr is None else new_indptr.detach().to("cpu", torch.int32).contiguous()
+    batch = cs.shape[0]
+    if total_new is None:
+        total_new = int(ip[-1]) if ip is not None else batch
+    msg = ctypes.create_string_buffer(256)
+    rc = lib().pkv_validate_append_host(ctypes.byref(desc), _ptr(bt), bt.shape[1], _ptr(cs), _ptr(ip), batch,
+                                        int(total_new), msg, 256)
+    _check("pkv_validate_append_host", rc, msg.value.decode())

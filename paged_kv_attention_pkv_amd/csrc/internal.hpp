@@ -1,0 +1,76 @@
+// internal.hpp -- host-side interfaces between the C ABI (pkv_api.hip) and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Pool geometry after the ABI checks (element strides, dim stride 1).
+struct PoolGeom {
+    int dtype;       // 0 = fp32, 1 = bf16
+    int num_pages;
+    int hkv;
+    int head_dim;
+    int64_t s_page, s_head, s_tok;
+    int elem_bytes() const { return dtype == 1 ? 2 : 4; }
+};
+
+hipError_t launch_append(const PoolGeom &g, void *k_cache, void *v_cache, const void *k_new,
+                         const void *v_new, const int32_t *block_table, int bt_cols,
+                         const int32_t *cache_seqlens, const int32_t *new_indptr, int batch,
+                         int total_new, int32_t *seqlens_out, hipStream_t stream);
+
+hipError_t launch_route(const PoolGeom &g, const int32_t *block_table, int bt_cols,
+                        const int32_t *seqlens, int batch, int max_len, int64_t *offsets,
+                        hipStream_t stream);
+
+// Decode: split-K over a flattened (sequence, kv head, page) space.
+struct DecodeArgs {
+    const void *q;
+    void *out;
+    float *lse;
+    const void *k_cache;
+    const void *v_cache;
+    int64_t s_page, s_head, s_tok;
+    const int32_t *block_table;
+    int32_t bt_cols;
+    const int32_t *seqlens;
+    int32_t batch, hq, hkv;
+    int32_t max_kv;     // host bound on seqlens; longer rows are cut to it
+    int32_t num_pages;  // page ids are clamped into 0..num_pages-1
+    float scale_log2;   // softmax scale times log2(e)
+    int32_t workers;    // split workers (one wave each)
+    float *part_o;      // [(workers + batch*hkv) * group * head_dim]
+    float *part_ml;     // [(workers + batch*hkv) * group * 2]
+    int32_t *meta;      // [batch*hkv * 2]: first worker, piece count
+};
+
+// Workers the decode kernel uses on `device` when the caller asks for
+// `requested` (0 = automatic); never more than `max_pages_bound`.
+int decode_workers(int device, const PoolGeom &g, int hq, int64_t max_pages_bound, int requested);
+size_t decode_workspace(const PoolGeom &g, int batch, int hq, int workers);
+hipError_t launch_decode(const PoolGeom &g, DecodeArgs args, int max_kv_len, hipStream_t stream);
+
+// Prefill (bf16, MFMA).
+struct PrefillArgs {
+    const void *q;
+    void *out;
+    float *lse;
+    const void *k_cache;
+    const void *v_cache;
+    int64_t s_page, s_head, s_tok;
+    const int32_t *block_table;
+    int32_t bt_cols;
+    const int32_t *kv_lens;
+    const int32_t *qo_indptr;
+    int32_t batch, hq, hkv, total_q, max_q, max_kv;
+    int32_t causal;
+    float scale_log2;
+};
+size_t prefill_workspace(const PoolGeom &g, int batch, int hq, int total_q, int max_q, int max_kv);
+hipError_t launch_prefill(const PoolGeom &g, const PrefillArgs &args, hipStream_t stream);
+
+}  // namespace pkv

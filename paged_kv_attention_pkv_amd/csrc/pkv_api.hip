@@ -1,0 +1,351 @@
+// pkv_api.hip -- the C ABI declared in include/pkv.h: host-side argument
+// checks, workspace sizing and kernel launches.  No entry point allocates,
+// frees, synchronises or reads device memory.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "internal.hpp"
+#include "pkv.h"
+
+using pkv::PoolGeom;
+
+namespace {
+
+constexpr int kPageSize = 16;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// One KV head's query heads fill at most the 16 columns of an MFMA tile.
+bool supported_group(int g) { return g >= 1 && g <= 16; }
+
+// Checks of the descriptor shared by every entry point.
+pkv_status check_desc(const pkv_cache_desc *c, PoolGeom *out) {
+    if (!c) return PKV_EINVAL;
+    if (c->reserved != 0) return PKV_EINVAL;
+    if (c->num_pages < 1 || c->num_kv_heads < 1 || c->head_dim < 1 || c->page_size < 1)
+        return PKV_EINVAL;
+    if (c->s_page < 0 || c->s_head < 0 || c->s_tok < 0) return PKV_EINVAL;
+    if (c->dtype != PKV_F32 && c->dtype != PKV_BF16) return PKV_EUNSUPPORTED;
+    if (c->page_size != kPageSize) return PKV_EUNSUPPORTED;
+    if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return PKV_EUNSUPPORTED;
+    if (c->s_page % 8 || c->s_head % 8 || c->s_tok % 8) return PKV_EUNSUPPORTED;
+    out->dtype = c->dtype == PKV_BF16 ? 1 : 0;
+    out->num_pages = c->num_pages;
+    out->hkv = c->num_kv_heads;
+    out->head_dim = c->head_dim;
+    out->s_page = c->s_page;
+    out->s_head = c->s_head;
+    out->s_tok = c->s_tok;
+    return PKV_OK;
+}
+
+pkv_status check_heads(const PoolGeom &g, int hq) {
+    if (hq < 1 || hq % g.hkv) return PKV_EINVAL;
+    if (!supported_group(hq / g.hkv)) return PKV_EUNSUPPORTED;
+    return PKV_OK;
+}
+
+pkv_status launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ELAUNCH; }
+
+int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+void set_msg(char *msg, size_t len, const char *fmt, ...) {
+    if (!msg || !len) return;
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(msg, len, fmt, ap);
+    va_end(ap);
+}
+
+int current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    return dev;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char *pkv_status_string(pkv_status s) {
+    switch (s) {
+        case PKV_OK: return "ok";
+        case PKV_EINVAL: return "invalid argument";
+        case PKV_EUNSUPPORTED: return "unsupported dtype, head_dim, page_size, GQA ratio, stride or alignment";
+        case PKV_EWORKSPACE: return "workspace missing or too small";
+        case PKV_ELAUNCH: return "kernel launch failed";
+        case PKV_EDEVICE: return "no usable HIP device";
+        case PKV_EVALIDATE: return "device-data precondition violated";
+    }
+    return "unknown status";
+}
+
+pkv_status pkv_append(const pkv_cache_desc *cache, void *k_cache, void *v_cache, const void *k_new,
+                      const void *v_new, const int32_t *block_table, int32_t bt_cols,
+                      const int32_t *cache_seqlens, const int32_t *new_indptr, int32_t batch,
+                      int32_t total_new, int32_t *seqlens_out, void *stream) {
+    PoolGeom g;
+    pkv_status st = check_desc(cache, &g);
+    if (st) return st;
+    if (batch < 0 || total_new < 0 || bt_cols < 0) return PKV_EINVAL;
+    if (batch == 0) return total_new == 0 ? PKV_OK : PKV_EINVAL;
+    if (!new_indptr && total_new != batch) return PKV_EINVAL;
+    if (!cache_seqlens || (total_new > 0 && (!k_cache || !v_cache || !k_new || !v_new || !block_table ||
+                                              bt_cols < 1)))
+        return PKV_EINVAL;
+    if (seqlens_out && seqlens_out == cache_seqlens) return PKV_EINVAL;
+    if (total_new == 0 && !seqlens_out) return PKV_OK;
+    if (total_new > 0 &&
+        (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new)))
+        return PKV_EUNSUPPORTED;
+    return launch_status(pkv::launch_append(g, k_cache, v_cache, k_new, v_new, block_table, bt_cols,
+                                            cache_seqlens, new_indptr, batch, total_new, seqlens_out,
+                                            (hipStream_t)stream));
+}
+
+size_t pkv_decode_workspace_bytes_ex(const pkv_cache_desc *cache, int32_t batch, int32_t num_q_heads,
+                                     int32_t max_kv_len, int32_t workers) {
+    PoolGeom g;
+    if (check_desc(cache, &g) || check_heads(g, num_q_heads) || batch < 1 || max_kv_len < 0 || workers < 0)
+        return 0;
+    const int64_t bound = (int64_t)batch * g.hkv * ceil_div64(max_kv_len, kPageSize);
+    const int w = pkv::decode_workers(current_device(), g, num_q_heads, bound, workers);
+    if (w < 1) return 0;
+    return pkv::decode_workspace(g, batch, num_q_heads, w);
+}
+
+size_t pkv_decode_workspace_bytes(const pkv_cache_desc *cache, int32_t batch, int32_t num_q_heads,
+                                  int32_t max_kv_len) {
+    return pkv_decode_workspace_bytes_ex(cache, batch, num_q_heads, max_kv_len, 0);
+}
+
+pkv_status pkv_decode_attn_ex(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
+                              int32_t num_q_heads, const void *k_cache, const void *v_cache,
+                              const int32_t *block_table, int32_t bt_cols, const int32_t *cache_seqlens,
+                              int32_t batch, int32_t max_kv_len, float scale, void *workspace,
+                              size_t workspace_bytes, int32_t workers, void *stream) {
+    PoolGeom g;
+    pkv_status st = check_desc(cache, &g);
+    if (st) return st;
+    if ((st = check_heads(g, num_q_heads))) return st;
+    if (batch < 0 || max_kv_len < 0 || bt_cols < 0 || workers < 0) return PKV_EINVAL;
+    if (batch == 0) return PKV_OK;
+    if (!out || !q || !k_cache || !v_cache || !block_table || !cache_seqlens) return PKV_EINVAL;
+    if ((int64_t)max_kv_len > (int64_t)bt_cols * kPageSize) return PKV_EINVAL;
+    if (!isfinite(scale)) return PKV_EINVAL;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PKV_EUNSUPPORTED;
+    const int dev = current_device();
+    if (dev < 0) return PKV_EDEVICE;
+    const int64_t bound = (int64_t)batch * g.hkv * ceil_div64(max_kv_len, kPageSize);
+    const int w = pkv::decode_workers(dev, g, num_q_heads, bound, workers);
+    if (w < 1) return PKV_EDEVICE;
+    const size_t need = pkv::decode_workspace(g, batch, num_q_heads, w);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PKV_EWORKSPACE;
+
+    pkv::DecodeArgs a;
+    a.q = q;
+    a.out = out;
+    a.lse = lse;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.s_page = g.s_page;
+    a.s_head = g.s_head;
+    a.s_tok = g.s_tok;
+    a.block_table = block_table;
+    a.bt_cols = bt_cols;
+    a.seqlens = cache_seqlens;
+    a.batch = batch;
+    a.hq = num_q_heads;
+    a.hkv = g.hkv;
+    a.max_kv = max_kv_len;
+    a.num_pages = g.num_pages;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.workers = w;
+    a.part_o = (float *)workspace;
+    a.part_ml = nullptr;
+    a.meta = nullptr;
+    return launch_status(pkv::launch_decode(g, a, max_kv_len, (hipStream_t)stream));
+}
+
+pkv_status pkv_decode_attn(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
+                           int32_t num_q_heads, const void *k_cache, const void *v_cache,
+                           const int32_t *block_table, int32_t bt_cols, const int32_t *cache_seqlens,
+                           int32_t batch, int32_t max_kv_len, float scale, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    return pkv_decode_attn_ex(cache, out, lse, q, num_q_heads, k_cache, v_cache, block_table, bt_cols,
+                              cache_seqlens, batch, max_kv_len, scale, workspace, workspace_bytes, 0,
+                              stream);
+}
+
+size_t pkv_prefill_workspace_bytes(const pkv_cache_desc *cache, int32_t batch, int32_t num_q_heads,
+                                   int32_t total_q, int32_t max_q, int32_t max_kv_len) {
+    PoolGeom g;
+    if (check_desc(cache, &g) || check_heads(g, num_q_heads) || batch < 1 || total_q < 0 || max_q < 0 ||
+        max_kv_len < 0)
+        return 0;
+    return pkv::prefill_workspace(g, batch, num_q_heads, total_q, max_q, max_kv_len);
+}
+
+pkv_status pkv_prefill_attn(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
+                            int32_t num_q_heads, const void *k_cache, const void *v_cache,
+                            const int32_t *block_table, int32_t bt_cols, const int32_t *kv_lens,
+                            const int32_t *qo_indptr, int32_t batch, int32_t total_q, int32_t max_q,
+                            int32_t max_kv_len, int32_t causal, float scale, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    PoolGeom g;
+    pkv_status st = check_desc(cache, &g);
+    if (st) return st;
+    if ((st = check_heads(g, num_q_heads))) return st;
+    if (g.dtype != 1) return PKV_EUNSUPPORTED;
+    if (batch < 0 || total_q < 0 || max_q < 0 || max_kv_len < 0 || bt_cols < 0) return PKV_EINVAL;
+    if (batch == 0 || total_q == 0) return batch == 0 && total_q != 0 ? PKV_EINVAL : PKV_OK;
+    if (!out || !q || !k_cache || !v_cache || !block_table || !kv_lens || !qo_indptr) return PKV_EINVAL;
+    if ((int64_t)max_kv_len > (int64_t)bt_cols * kPageSize) return PKV_EINVAL;
+    if (!isfinite(scale)) return PKV_EINVAL;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PKV_EUNSUPPORTED;
+    const size_t need = pkv::prefill_workspace(g, batch, num_q_heads, total_q, max_q, max_kv_len);
+    if (need && (!workspace || workspace_bytes < need || !aligned16(workspace))) return PKV_EWORKSPACE;
+    pkv::PrefillArgs a;
+    a.q = q;
+    a.out = out;
+    a.lse = lse;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.s_page = g.s_page;
+    a.s_head = g.s_head;
+    a.s_tok = g.s_tok;
+    a.block_table = block_table;
+    a.bt_cols = bt_cols;
+    a.kv_lens = kv_lens;
+    a.qo_indptr = qo_indptr;
+    a.batch = batch;
+    a.hq = num_q_heads;
+    a.hkv = g.hkv;
+    a.total_q = total_q;
+    a.max_q = max_q;
+    a.max_kv = max_kv_len;
+    a.causal = causal ? 1 : 0;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    return launch_status(pkv::launch_prefill(g, a, (hipStream_t)stream));
+}
+
+pkv_status pkv_route(const pkv_cache_desc *cache, const int32_t *block_table, int32_t bt_cols,
+                     const int32_t *seqlens, int32_t batch, int32_t max_len, int64_t *offsets,
+                     void *stream) {
+    PoolGeom g;
+    pkv_status st = check_desc(cache, &g);
+    if (st) return st;
+    if (batch < 0 || max_len < 0 || bt_cols < 0) return PKV_EINVAL;
+    if (batch == 0 || max_len == 0) return PKV_OK;
+    if (!block_table || !seqlens || !offsets) return PKV_EINVAL;
+    if ((int64_t)max_len > (int64_t)bt_cols * kPageSize) return PKV_EINVAL;
+    return launch_status(
+        pkv::launch_route(g, block_table, bt_cols, seqlens, batch, max_len, offsets, (hipStream_t)stream));
+}
+
+pkv_status pkv_validate_host(const pkv_cache_desc *cache, const int32_t *block_table, int32_t bt_cols,
+                             const int32_t *kv_lens, const int32_t *qo_indptr, int32_t batch,
+                             int32_t total_q, int32_t max_q, int32_t max_kv_len, int32_t causal, char *msg,
+                             size_t msg_len) {
+    PoolGeom g;
+    pkv_status st = check_desc(cache, &g);
+    if (st) return st;
+    if (batch < 0 || bt_cols < 0) return PKV_EINVAL;
+    if (batch > 0 && (!kv_lens || !block_table)) return PKV_EINVAL;
+    if ((int64_t)max_kv_len > (int64_t)bt_cols * kPageSize) {
+        set_msg(msg, msg_len, "max_kv_len %d exceeds bt_cols*page_size %lld", max_kv_len,
+                (long long)bt_cols * kPageSize);
+        return PKV_EVALIDATE;
+    }
+    for (int b = 0; b < batch; ++b) {
+        const int64_t kv = kv_lens[b];
+        if (kv < 0 || kv > max_kv_len) {
+            set_msg(msg, msg_len, "row %d: kv_len %lld outside 0..max_kv_len (%d)", b, (long long)kv, max_kv_len);
+            return PKV_EVALIDATE;
+        }
+        for (int64_t blk = 0; blk < ceil_div64(kv, kPageSize); ++blk) {
+            const int32_t page = block_table[(int64_t)b * bt_cols + blk];
+            if (page < 1 || page >= g.num_pages) {
+                set_msg(msg, msg_len, "row %d block %lld: page %d not in 1..num_pages-1", b, (long long)blk, page);
+                return PKV_EVALIDATE;
+            }
+        }
+    }
+    if (qo_indptr) {
+        if (qo_indptr[0] != 0 || qo_indptr[batch] != total_q) {
+            set_msg(msg, msg_len, "qo_indptr must start at 0 and end at total_q (%d), got %d..%d",
+                    total_q, qo_indptr[0], qo_indptr[batch]);
+            return PKV_EVALIDATE;
+        }
+        for (int b = 0; b < batch; ++b) {
+            const int64_t ql = (int64_t)qo_indptr[b + 1] - qo_indptr[b];
+            if (ql < 0 || ql > max_q || (causal && (ql == 0 || ql > kv_lens[b]))) {
+                set_msg(msg, msg_len, "request %d: q_len %lld invalid for kv_len %d", b, (long long)ql, kv_lens[b]);
+                return PKV_EVALIDATE;
+            }
+        }
+    }
+    if (msg && msg_len) msg[0] = 0;
+    return PKV_OK;
+}
+
+pkv_status pkv_validate_append_host(const pkv_cache_desc *cache, const int32_t *block_table, int32_t bt_cols,
+                                    const int32_t *cache_seqlens, const int32_t *new_indptr, int32_t batch,
+                                    int32_t total_new, char *msg, size_t msg_len) {
+    PoolGeom g;
+    pkv_status st = check_desc(cache, &g);
+    if (st) return st;
+    if (batch < 0 || bt_cols < 0 || total_new < 0) return PKV_EINVAL;
+    if (batch > 0 && (!cache_seqlens || !block_table)) return PKV_EINVAL;
+    if (new_indptr ? (new_indptr[0] != 0 || new_indptr[batch] != total_new) : total_new != batch) {
+        set_msg(msg, msg_len, "new_indptr inconsistent with total_new %d", total_new);
+        return PKV_EVALIDATE;
+    }
+    // (page, slot) targets must be distinct: mark them in a host bitmap
+    const size_t slots = (size_t)g.num_pages * kPageSize;
+    unsigned char *seen = (unsigned char *)calloc((slots + 7) / 8, 1);
+    if (!seen) return PKV_EINVAL;
+    pkv_status res = PKV_OK;
+    for (int b = 0; b < batch && res == PKV_OK; ++b) {
+        const int64_t n_new = new_indptr ? (int64_t)new_indptr[b + 1] - new_indptr[b] : 1;
+        if (n_new < 0 || cache_seqlens[b] < 0) {
+            set_msg(msg, msg_len, "row %d: negative length (%d, %lld)", b, cache_seqlens[b], (long long)n_new);
+            res = PKV_EVALIDATE;
+            break;
+        }
+        for (int64_t t = 0; t < n_new; ++t) {
+            const int64_t pos = (int64_t)cache_seqlens[b] + t;
+            const int64_t blk = pos / kPageSize;
+            if (blk >= bt_cols) {
+                set_msg(msg, msg_len, "row %d: position %lld beyond the table (%d blocks)", b, (long long)pos, bt_cols);
+                res = PKV_EVALIDATE;
+                break;
+            }
+            const int32_t page = block_table[(int64_t)b * bt_cols + blk];
+            if (page < 1 || page >= g.num_pages) {
+                set_msg(msg, msg_len, "row %d position %lld: page %d not in 1..num_pages-1", b, (long long)pos, page);
+                res = PKV_EVALIDATE;
+                break;
+            }
+            const size_t slot = (size_t)page * kPageSize + (size_t)(pos % kPageSize);
+            if (seen[slot >> 3] & (1u << (slot & 7))) {
+                set_msg(msg, msg_len, "row %d position %lld: slot of page %d written twice", b, (long long)pos, page);
+                res = PKV_EVALIDATE;
+                break;
+            }
+            seen[slot >> 3] |= (unsigned char)(1u << (slot & 7));
+        }
+    }
+    free(seen);
+    if (res == PKV_OK && msg && msg_len) msg[0] = 0;
+    return res;
+}
+
+}  // extern "C"

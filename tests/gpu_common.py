@@ -1,0 +1,136 @@
+"""Helpers for the GPU parity tests: run the same seeded inputs through the
+HIP library (device) and the oracle (host) and compare.
+
+Both sides build their own pool from the same dense history: the library
+with pkv_append on the device, the oracle with its own append on the host.
+Pools start NaN-filled, so page 0, free pages and the tail slots of partly
+filled pages all hold NaN that must never leak into a result."""
+from __future__ import annotations
+
+import math
+import os
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_attention_pkv_amd as pkv
+from paged_kv_attention_pkv_amd import workloads as wl
+
+BF16_TOL = (2e-2, 2e-2)   # (atol, rtol) on bf16 outputs
+F32_TOL = (1e-5, 1e-5)    # (atol, rtol) on fp32 outputs
+
+
+def say(*a):
+    """Progress line naming the case, flushed before each GPU step."""
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def opool(spec) -> oracle.Pool:
+    dt = oracle.BF16 if spec.dtype == "bf16" else oracle.F32
+    ctor = oracle.Pool.hnd if spec.layout == "HND" else oracle.Pool.nhd
+    return ctor(dt, spec.num_pages, spec.page_size, spec.hkv, spec.head_dim)
+
+
+def tol(spec):
+    return BF16_TOL if spec.dtype == "bf16" else F32_TOL
+
+
+def compare(gpu, ref, atol, rtol, what):
+    """|gpu - ref| <= atol + rtol |ref| elementwise, gpu widened exactly."""
+    g = gpu.detach().float().cpu().double().numpy() if isinstance(gpu, torch.Tensor) else np.asarray(gpu)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, f"{what}: shape {g.shape} vs {r.shape}"
+    both_inf = np.isinf(g) & np.isinf(r) & (np.sign(g) == np.sign(r))
+    err = np.where(both_inf, 0.0, np.abs(g - r))
+    assert not np.isnan(g).any(), f"{what}: NaN in GPU result"
+    lim = atol + rtol * np.abs(r)
+    bad = ~(err <= lim)
+    rel = err / np.maximum(np.abs(r), 1e-30)
+    stats = f"max abs err {float(np.max(err, initial=0)):.3e}, max rel err {float(np.max(np.where(both_inf, 0, rel), initial=0)):.3e}"
+    if bad.any():
+        i = np.flatnonzero(bad.ravel())[0]
+        raise AssertionError(f"{what}: {int(bad.sum())} elements out of tolerance; first at {i}: "
+                             f"gpu {g.ravel()[i]!r} ref {r.ravel()[i]!r}; {stats}")
+    return stats
+
+
+class DecodeCase:
+    """A decode workload materialised on both sides."""
+
+    def __init__(self, spec: wl.DecodeSpec, device="cuda", gen_device="cpu", oracle_rows=None):
+        self.spec = spec
+        self.dev = torch.device(device)
+        inp = wl.decode_inputs(spec, device=gen_device)
+        self.inp_host = inp.to("cpu")
+        self.inp = inp.to(self.dev)
+        self.rows = None if oracle_rows is None else np.asarray(sorted(oracle_rows), dtype=np.int64)
+
+    # -- device side -------------------------------------------------------
+    def gpu_pools(self):
+        s, i = self.spec, self.inp
+        kc = wl.empty_pool(s, self.dev)
+        vc = wl.empty_pool(s, self.dev)
+        zeros = torch.zeros(s.batch, dtype=torch.int32, device=self.dev)
+        pkv.append(kc, vc, i.k_hist, i.v_hist, i.block_table, zeros, i.hist_indptr, layout=s.layout)
+        lens = pkv.append(kc, vc, i.k_new, i.v_new, i.block_table, i.hist_lens, i.new_indptr, layout=s.layout)
+        return kc, vc, lens
+
+    def gpu_decode(self, kc, vc, lens, workers=0, q=None):
+        s = self.spec
+        max_kv = int(s.hist_lens.max()) + s.n_new if s.batch else 0
+        return pkv.decode_attn(self.inp.q if q is None else q, kc, vc, self.inp.block_table, lens, max_kv,
+                               scale=s.scale, layout=s.layout, workers=workers, return_lse=True)
+
+    # -- oracle side -------------------------------------------------------
+    def oracle_pools(self):
+        """Host pools built by the oracle's append (all rows, or the sampled
+        rows only when oracle_rows was given)."""
+        s, h = self.spec, self.inp_host
+        orc = oracle.load()
+        pool = opool(s)
+        kc = host_bits(wl.empty_pool(s, "cpu")).copy()
+        vc = kc.copy()
+        if self.rows is None:
+            bt = h.block_table
+            hist = h.hist_lens
+            k_hist, v_hist, indptr = h.k_hist, h.v_hist, h.hist_indptr
+            k_new, v_new, new_indptr = h.k_new, h.v_new, h.new_indptr
+        else:
+            rows = self.rows
+            ip = h.hist_indptr.numpy()
+            bt = h.block_table[rows]
+            hist = h.hist_lens[rows]
+            sel = np.concatenate([np.arange(ip[r], ip[r + 1]) for r in rows]) if len(rows) else np.zeros(0, np.int64)
+            k_hist, v_hist = h.k_hist[sel], h.v_hist[sel]
+            indptr = torch.from_numpy(np.concatenate([[0], np.cumsum(hist.numpy())]).astype(np.int32))
+            n = s.n_new
+            sel_new = np.concatenate([np.arange(r * n, (r + 1) * n) for r in rows])
+            k_new, v_new = h.k_new[sel_new], h.v_new[sel_new]
+            new_indptr = None if n == 1 else torch.arange(0, (len(rows) + 1) * n, n, dtype=torch.int32)
+        orc.append(pool, kc, vc, host_bits(k_hist), host_bits(v_hist), bt.numpy(),
+                   np.zeros(bt.shape[0], np.int32), indptr.numpy())
+        lens = orc.append(pool, kc, vc, host_bits(k_new), host_bits(v_new), bt.numpy(), hist.numpy(),
+                          None if new_indptr is None else new_indptr.numpy())
+        return kc, vc, lens, bt
+
+    def oracle_decode(self, kc, vc, lens, bt, q=None, nthreads=None):
+        s = self.spec
+        q = self.inp_host.q if q is None else q
+        if self.rows is not None:
+            q = q[self.rows]
+        return oracle.load().decode(opool(s), host_bits(q), kc, vc, bt.numpy(), lens, s.scale,
+                                    nthreads=nthreads or min(16, os.cpu_count() or 1))
+
+
+def scale_of(d):
+    return float(np.float32(1.0 / math.sqrt(d)))

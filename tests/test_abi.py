@@ -1,0 +1,167 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point the
+header declares, and rejects bad host scalars before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import paged_kv_attention_pkv_amd as pkv
+from paged_kv_attention_pkv_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ELAUNCH, EDEVICE, EVALIDATE = range(7)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_path():
+    names = declared_functions()
+    for required in ("pkv_append", "pkv_decode_attn", "pkv_prefill_attn"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = api.lib()
+    names = declared_functions()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    assert sorted(api.EXPORTED) == names, "binding signatures out of sync with the header"
+    assert lib.pkv_abi_version() == 1
+    for code in range(7):
+        assert lib.pkv_status_string(code)
+
+
+def _desc(**kw):
+    base = dict(dtype=api.PKV_BF16, num_pages=10, page_size=16, num_kv_heads=8, head_dim=128, reserved=0,
+                s_page=8 * 16 * 128, s_head=16 * 128, s_tok=128)
+    base.update(kw)
+    return api._Desc(*[base[f] for f, _ in api._Desc._fields_])
+
+
+FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: every call below fails its host checks
+
+
+def _decode(desc, hq=32, batch=4, max_kv=64, bt_cols=4, out=FAKE, ws=FAKE, ws_bytes=1 << 30, scale=0.1):
+    return api.lib().pkv_decode_attn(ctypes.byref(desc), out, None, FAKE, hq, FAKE, FAKE, FAKE, bt_cols, FAKE,
+                                     batch, max_kv, scale, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), EUNSUPPORTED),
+    (dict(page_size=32), EUNSUPPORTED),
+    (dict(dtype=7), EUNSUPPORTED),
+    (dict(s_tok=127), EUNSUPPORTED),
+    (dict(reserved=1), EINVAL),
+    (dict(num_kv_heads=0), EINVAL),
+    (dict(s_page=-8), EINVAL),
+])
+def test_decode_rejects_descriptor(kw, code):
+    assert _decode(_desc(**kw)) == code
+
+
+def test_decode_rejects_scalars():
+    d = _desc()
+    assert _decode(d, hq=30) == EINVAL            # Hq % Hkv != 0
+    assert _decode(d, hq=8 * 17) == EUNSUPPORTED  # GQA ratio 17 > 16 MFMA columns
+    assert _decode(d, batch=-1) == EINVAL
+    assert _decode(d, batch=0) == OK              # nothing to do
+    assert _decode(d, max_kv=65, bt_cols=4) == EINVAL  # table too narrow for max_kv_len
+    assert _decode(d, out=None) == EINVAL
+    assert _decode(d, out=ctypes.c_void_p((1 << 20) + 2)) == EUNSUPPORTED  # misaligned
+    assert _decode(d, scale=float("nan")) == EINVAL
+
+
+def test_append_rejects_scalars():
+    d = _desc()
+    lib = api.lib()
+    call = lambda **kw: lib.pkv_append(ctypes.byref(kw.get("desc", d)), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       kw.get("bt_cols", 4), kw.get("seqlens", FAKE), kw.get("indptr", None),
+                                       kw.get("batch", 4), kw.get("total", 4), kw.get("out", None), None)
+    assert call(total=5) == EINVAL                   # no indptr => one token per sequence
+    assert call(batch=-1) == EINVAL
+    assert call(batch=0, total=0) == OK
+    assert call(seqlens=None) == EINVAL
+    assert call(out=FAKE) == EINVAL                  # seqlens_out aliases cache_seqlens
+    assert call(desc=_desc(head_dim=32)) == EUNSUPPORTED
+
+
+def test_prefill_rejects_scalars():
+    lib = api.lib()
+    call = lambda desc, **kw: lib.pkv_prefill_attn(
+        ctypes.byref(desc), FAKE, None, FAKE, kw.get("hq", 48), FAKE, FAKE, FAKE, 300, FAKE, FAKE,
+        kw.get("batch", 2), kw.get("total_q", 10), 8, kw.get("max_kv", 4096), 1, 0.0625, FAKE, 1 << 30, None)
+    assert call(_desc(dtype=api.PKV_F32, head_dim=256, s_page=8 * 16 * 256, s_head=16 * 256, s_tok=256)) == EUNSUPPORTED
+    d = _desc(head_dim=256, s_page=8 * 16 * 256, s_head=16 * 256, s_tok=256)
+    assert call(d, hq=44) == EINVAL
+    assert call(d, batch=0, total_q=3) == EINVAL
+    assert call(d, max_kv=300 * 16 + 1) == EINVAL
+
+
+def _cpu_pool(num_pages=10):
+    return torch.empty((num_pages, 2, 16, 64), dtype=torch.bfloat16)
+
+
+def test_validate_host_paths():
+    kc = _cpu_pool()
+    bt = torch.tensor([[1, 2, 0], [3, 4, 5]], dtype=torch.int32)
+    pkv.validate_host(kc, bt, torch.tensor([20, 40], dtype=torch.int32), max_kv_len=48)
+    with pytest.raises(pkv.PkvError, match="page 0"):
+        pkv.validate_host(kc, bt, torch.tensor([40, 40], dtype=torch.int32), max_kv_len=48)
+    with pytest.raises(pkv.PkvError, match="kv_len"):
+        pkv.validate_host(kc, bt, torch.tensor([20, 49], dtype=torch.int32), max_kv_len=48)
+    bad = torch.tensor([[1, 2, 0], [3, 10, 5]], dtype=torch.int32)
+    with pytest.raises(pkv.PkvError, match="page 10"):
+        pkv.validate_host(kc, bad, torch.tensor([20, 40], dtype=torch.int32), max_kv_len=48)
+    kv = torch.tensor([20, 40], dtype=torch.int32)
+    pkv.validate_host(kc, bt, kv, torch.tensor([0, 5, 45], dtype=torch.int32), max_q=40, max_kv_len=48)
+    for ip, pat in (([0, 21, 30], "q_len"), ([1, 5, 30], "qo_indptr"), ([0, 0, 30], "q_len"),
+                    ([0, 5, 4], "q_len")):
+        with pytest.raises(pkv.PkvError, match=pat):
+            pkv.validate_host(kc, bt, kv, torch.tensor(ip, dtype=torch.int32), max_q=64, max_kv_len=48)
+    # non-causal allows an empty request
+    pkv.validate_host(kc, bt, kv, torch.tensor([0, 0, 30], dtype=torch.int32), max_q=64, max_kv_len=48,
+                      causal=False)
+
+
+def test_validate_append_paths():
+    kc = _cpu_pool()
+    bt = torch.tensor([[1, 2, 0], [3, 4, 5]], dtype=torch.int32)
+    pkv.validate_append_host(kc, bt, torch.tensor([16, 40], dtype=torch.int32))
+    with pytest.raises(pkv.PkvError, match="page 0"):
+        pkv.validate_append_host(kc, bt, torch.tensor([32, 40], dtype=torch.int32))
+    with pytest.raises(pkv.PkvError, match="beyond the table"):
+        pkv.validate_append_host(kc, bt, torch.tensor([16, 48], dtype=torch.int32))
+    shared = torch.tensor([[1, 2, 0], [1, 4, 5]], dtype=torch.int32)
+    with pytest.raises(pkv.PkvError, match="written twice"):
+        pkv.validate_append_host(kc, shared, torch.tensor([3, 3], dtype=torch.int32))
+    pkv.validate_append_host(kc, bt, torch.tensor([10, 40], dtype=torch.int32),
+                             torch.tensor([0, 6, 14], dtype=torch.int32))
+    with pytest.raises(pkv.PkvError, match="new_indptr"):
+        pkv.validate_append_host(kc, bt, torch.tensor([10, 40], dtype=torch.int32),
+                                 torch.tensor([0, 6, 14], dtype=torch.int32), total_new=13)
+
+
+def test_workspace_query_rejects_bad_sizes():
+    lib = api.lib()
+    d = _desc()
+    assert lib.pkv_decode_workspace_bytes_ex(ctypes.byref(d), 0, 32, 100, 10) == 0
+    assert lib.pkv_decode_workspace_bytes_ex(ctypes.byref(d), 4, 30, 100, 10) == 0
+    # an explicit worker count needs no device: (workers + B*Hkv) records of G*D fp32 + (m, l) + meta
+    n = lib.pkv_decode_workspace_bytes_ex(ctypes.byref(d), 4, 32, 100, 10)
+    recs = 10 + 4 * 8
+    assert n >= recs * 4 * 128 * 4 + recs * 4 * 2 * 4 + 4 * 8 * 2 * 4
+
+
+def test_binding_refuses_missing_library(monkeypatch):
+    monkeypatch.setattr(api, "_lib", None)
+    monkeypatch.setattr(api, "_LIB_PATH", "/nonexistent/libpkv.so")
+    with pytest.raises(RuntimeError, match="libpkv.so not found"):
+        api.lib()
