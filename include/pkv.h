@@ -118,7 +118,13 @@ pkv_status pkv_append(const pkv_cache_desc *cache, void *k_cache, void *v_cache,
  * pkv_decode_workspace_bytes -- device workspace pkv_decode_attn needs for
  * these sizes on the current device (bytes; 0 only for invalid arguments).
  * Depends on batch, num_q_heads, the descriptor and the device, not on the
- * lengths, so one workspace can be reused for every step of a batch shape.
+ * lengths, so one workspace serves every step of a batch shape.
+ *
+ * The workspace holds the partial results of rows split across workers and
+ * one arrival counter per (sequence, kv head).  It must be zero-filled before
+ * its first use (and again before it is reused for a different batch or
+ * kv-head count); every call leaves it ready for the next one.  Calls that
+ * run concurrently must not share a workspace.
  */
 size_t pkv_decode_workspace_bytes(const pkv_cache_desc *cache, int32_t batch, int32_t num_q_heads,
                                   int32_t max_kv_len);

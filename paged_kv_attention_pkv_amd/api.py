@@ -223,7 +223,8 @@ def decode_attn(q, k_cache, v_cache, block_table, cache_seqlens, max_kv_len: int
     with torch.cuda.device(dev):
         need = lib().pkv_decode_workspace_bytes_ex(ctypes.byref(desc), batch, hq, max_kv_len, workers)
         if workspace is None:
-            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+            # the arrival counters in the workspace must start at zero
+            workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
         rc = lib().pkv_decode_attn_ex(ctypes.byref(desc), _ptr(out), _ptr(lse), _ptr(q), hq, _ptr(k_cache),
                                       _ptr(v_cache), _ptr(block_table), block_table.shape[1],
                                       _ptr(cache_seqlens), batch, int(max_kv_len), float(scale),
@@ -322,3 +323,88 @@ def validate_append_host(k_cache, block_table, cache_seqlens, new_indptr=None, t
     rc = lib().pkv_validate_append_host(ctypes.byref(desc), _ptr(bt), bt.shape[1], _ptr(cs), _ptr(ip), batch,
                                         int(total_new), msg, 256)
     _check("pkv_validate_append_host", rc, msg.value.decode())
+
+
+# --------------------------------------------------------------------------
+# prepared calls: validate once, then launch with stored ctypes arguments
+# --------------------------------------------------------------------------
+
+class PreparedCall:
+    """A library entry point with every argument already marshalled.
+
+    Calling it enqueues the kernels on the current torch stream (so it can be
+    recorded into a HIP graph) and raises on a non-OK status.  The tensors it
+    was prepared from must stay alive and keep their storage."""
+
+    def __init__(self, name: str, args: tuple, keep: tuple):
+        self._fn = getattr(lib(), name)
+        self._name = name
+        self._args = args
+        self._keep = keep  # tensors whose storage the pointers refer to
+        self._dev = keep[0].device
+
+    def __call__(self) -> None:
+        rc = self._fn(*self._args, ctypes.c_void_p(torch.cuda.current_stream(self._dev).cuda_stream))
+        if rc != 0:
+            raise PkvError(self._name, rc)
+
+
+def prepare_append(k_cache, v_cache, k_new, v_new, block_table, cache_seqlens, seqlens_out, new_indptr=None,
+                   layout: str = "HND") -> PreparedCall:
+    desc = cache_desc(k_cache, v_cache, layout)
+    dev = k_cache.device
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, nm, k_cache.dtype, dev, 3)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
+    _need(seqlens_out, "seqlens_out", torch.int32, dev, 1)
+    batch = cache_seqlens.shape[0]
+    args = (ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(block_table),
+            block_table.shape[1], _ptr(cache_seqlens), _ptr(new_indptr), batch, k_new.shape[0], _ptr(seqlens_out))
+    return PreparedCall("pkv_append", args, (k_cache, v_cache, k_new, v_new, block_table, cache_seqlens,
+                                             seqlens_out, new_indptr, desc))
+
+
+def prepare_decode(q, k_cache, v_cache, block_table, cache_seqlens, max_kv_len: int, out, workspace,
+                   lse=None, scale: float | None = None, layout: str = "HND", workers: int = 0) -> PreparedCall:
+    desc = cache_desc(k_cache, v_cache, layout)
+    dev = k_cache.device
+    _need(q, "q", k_cache.dtype, dev, 3)
+    _need(out, "out", q.dtype, dev, 3)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
+    batch, hq, d = q.shape
+    if scale is None:
+        scale = d ** -0.5
+    with torch.cuda.device(dev):
+        need = lib().pkv_decode_workspace_bytes_ex(ctypes.byref(desc), batch, hq, max_kv_len, workers)
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise PkvError("pkv_decode_attn", 3, f"workspace {nbytes} < {need} bytes")
+    args = (ctypes.byref(desc), _ptr(out), _ptr(lse), _ptr(q), hq, _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            block_table.shape[1], _ptr(cache_seqlens), batch, int(max_kv_len), float(scale), _ptr(workspace),
+            nbytes, int(workers))
+    return PreparedCall("pkv_decode_attn_ex", args, (k_cache, v_cache, q, out, block_table, cache_seqlens,
+                                                     workspace, lse, desc))
+
+
+def prepare_prefill(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, max_q: int, max_kv_len: int, out,
+                    workspace=None, lse=None, causal: bool = True, scale: float | None = None,
+                    layout: str = "HND") -> PreparedCall:
+    desc = cache_desc(k_cache, v_cache, layout)
+    dev = k_cache.device
+    _need(q, "q", k_cache.dtype, dev, 3)
+    _need(out, "out", q.dtype, dev, 3)
+    total_q, hq, d = q.shape
+    batch = kv_lens.shape[0]
+    if scale is None:
+        scale = d ** -0.5
+    need = lib().pkv_prefill_workspace_bytes(ctypes.byref(desc), batch, hq, total_q, max_q, max_kv_len)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise PkvError("pkv_prefill_attn", 3, f"workspace {nbytes} < {need} bytes")
+    args = (ctypes.byref(desc), _ptr(out), _ptr(lse), _ptr(q), hq, _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            block_table.shape[1], _ptr(kv_lens), _ptr(qo_indptr), batch, total_q, int(max_q), int(max_kv_len),
+            int(bool(causal)), float(scale), _ptr(workspace), nbytes)
+    return PreparedCall("pkv_prefill_attn", args, (k_cache, v_cache, q, out, block_table, kv_lens, qo_indptr,
+                                                   workspace, lse, desc))

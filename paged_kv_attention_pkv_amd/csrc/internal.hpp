@@ -45,7 +45,7 @@ struct DecodeArgs {
     int32_t workers;    // split workers (one wave each)
     float *part_o;      // [(workers + batch*hkv) * group * head_dim]
     float *part_ml;     // [(workers + batch*hkv) * group * 2]
-    int32_t *meta;      // [batch*hkv * 2]: first worker, piece count
+    int32_t *arrivals;  // [batch*hkv]: pieces finished per split row; zero between calls
 };
 
 // Workers the decode kernel uses on `device` when the caller asks for

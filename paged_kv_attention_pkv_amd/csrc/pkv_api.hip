@@ -32,6 +32,9 @@ pkv_status check_desc(const pkv_cache_desc *c, PoolGeom *out) {
     if (c->page_size != kPageSize) return PKV_EUNSUPPORTED;
     if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return PKV_EUNSUPPORTED;
     if (c->s_page % 8 || c->s_head % 8 || c->s_tok % 8) return PKV_EUNSUPPORTED;
+    // in-page offsets are 32-bit in the kernels
+    if (c->s_tok * (int64_t)c->page_size + c->s_head * (int64_t)c->num_kv_heads > (int64_t)1 << 30)
+        return PKV_EUNSUPPORTED;
     out->dtype = c->dtype == PKV_BF16 ? 1 : 0;
     out->num_pages = c->num_pages;
     out->hkv = c->num_kv_heads;
@@ -169,7 +172,7 @@ pkv_status pkv_decode_attn_ex(const pkv_cache_desc *cache, void *out, float *lse
     a.workers = w;
     a.part_o = (float *)workspace;
     a.part_ml = nullptr;
-    a.meta = nullptr;
+    a.arrivals = nullptr;
     return launch_status(pkv::launch_decode(g, a, max_kv_len, (hipStream_t)stream));
 }
 

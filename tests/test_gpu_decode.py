@@ -221,3 +221,28 @@ def test_long_ragged_full_size_sampled():
     rng = np.random.default_rng(41)
     rows = set(rng.choice(spec.batch, 10, replace=False).tolist()) | {int(n.argmax()), int(n.argmin())}
     _run_parity(spec, gen_device="cuda", oracle_rows=rows, check_pool=False)
+
+
+def test_workspace_reuse_across_calls():
+    """One zeroed workspace serves consecutive calls with other lengths: the
+    split-row arrival counters are left at zero by every call."""
+    say("[decode] workspace reuse")
+    s1 = wl.custom_decode_spec([3000, 5, 700, 1500], hq=32, hkv=8, head_dim=128, dtype="bf16", seed=61)
+    s2 = wl.custom_decode_spec([100, 2900, 0, 1200], hq=32, hkv=8, head_dim=128, dtype="bf16", seed=62,
+                               extra_cols=2)
+    c1, c2 = DecodeCase(s1), DecodeCase(s2)
+    k1, v1, l1 = c1.gpu_pools()
+    k2, v2, l2 = c2.gpu_pools()
+    m1, m2 = 3001, 2901
+    need = max(pkv.decode_workspace_bytes(k1, 4, 32, m1, workers=37),
+               pkv.decode_workspace_bytes(k2, 4, 32, m2, workers=37))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    first = pkv.decode_attn(c1.inp.q, k1, v1, c1.inp.block_table, l1, m1, workspace=ws, workers=37)
+    second = pkv.decode_attn(c2.inp.q, k2, v2, c2.inp.block_table, l2, m2, workspace=ws, workers=37)
+    again = pkv.decode_attn(c1.inp.q, k1, v1, c1.inp.block_table, l1, m1, workspace=ws, workers=37)
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), again.view(torch.int16))
+    for case, out in ((c1, first), (c2, second)):
+        okc, ovc, olens, obt = case.oracle_pools()
+        ro, _ = case.oracle_decode(okc, ovc, olens, obt)
+        compare(out.cpu(), ro, *tol(case.spec), "workspace reuse")
