@@ -67,6 +67,7 @@ struct PrefillArgs {
     const int32_t *kv_lens;
     const int32_t *qo_indptr;
     int32_t batch, hq, hkv, total_q, max_q, max_kv;
+    int32_t num_pages;  // page ids are clamped into 0..num_pages-1
     int32_t causal;
     float scale_log2;
 };

@@ -234,6 +234,7 @@ pkv_status pkv_prefill_attn(const pkv_cache_desc *cache, void *out, float *lse, 
     a.total_q = total_q;
     a.max_q = max_q;
     a.max_kv = max_kv_len;
+    a.num_pages = g.num_pages;
     a.causal = causal ? 1 : 0;
     a.scale_log2 = scale * 1.4426950408889634f;
     return launch_status(pkv::launch_prefill(g, a, (hipStream_t)stream));

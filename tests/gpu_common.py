@@ -134,3 +134,87 @@ class DecodeCase:
 
 def scale_of(d):
     return float(np.float32(1.0 / math.sqrt(d)))
+
+
+class PrefillCase:
+    """A causal prefill workload on both sides.  The device builds its pool
+    with pkv_append (history, then the chunk); the oracle does the same with
+    its own append, optionally for a subset of requests only."""
+
+    def __init__(self, spec: wl.PrefillSpec, device="cuda", gen_device="cpu"):
+        self.spec = spec
+        self.dev = torch.device(device)
+        inp = wl.prefill_inputs(spec, device=gen_device)
+        self.inp = inp.to(self.dev)
+        self.inp_host = inp.to("cpu")
+
+    def gpu_pools(self):
+        s, i = self.spec, self.inp
+        kc = wl.empty_pool(s, self.dev)
+        vc = wl.empty_pool(s, self.dev)
+        zeros = torch.zeros(s.batch, dtype=torch.int32, device=self.dev)
+        pkv.append(kc, vc, i.k_hist, i.v_hist, i.block_table, zeros, i.hist_indptr, layout=s.layout)
+        kv = pkv.append(kc, vc, i.k_new, i.v_new, i.block_table, i.hist_lens, i.qo_indptr, layout=s.layout)
+        return kc, vc, kv
+
+    def gpu_prefill(self, kc, vc, kv, causal=True):
+        s = self.spec
+        return pkv.prefill_attn(self.inp.q, kc, vc, self.inp.block_table, kv, self.inp.qo_indptr,
+                                int(s.q_lens.max()), int(s.kv_lens.max()), causal=causal, scale=s.scale,
+                                layout=s.layout, return_lse=True)
+
+    def oracle_pools(self, requests=None):
+        """Host pools holding the history and chunk of `requests` (all by default)."""
+        s, h = self.spec, self.inp_host
+        reqs = list(range(s.batch)) if requests is None else list(requests)
+        hi = h.hist_indptr.numpy()
+        qi = h.qo_indptr.numpy()
+        hsel = np.concatenate([np.arange(hi[r], hi[r + 1]) for r in reqs]).astype(np.int64)
+        qsel = np.concatenate([np.arange(qi[r], qi[r + 1]) for r in reqs]).astype(np.int64)
+        hist = s.hist_lens[reqs]
+        ql = s.q_lens[reqs]
+        bt = s.block_table[reqs]
+        pool = opool(s)
+        kc = host_bits(wl.empty_pool(s, "cpu")).copy()
+        vc = kc.copy()
+        orc = oracle.load()
+        orc.append(pool, kc, vc, host_bits(h.k_hist[hsel]), host_bits(h.v_hist[hsel]), bt,
+                   np.zeros(len(reqs), np.int32), np.concatenate([[0], np.cumsum(hist)]).astype(np.int32))
+        kv = orc.append(pool, kc, vc, host_bits(h.k_new[qsel]), host_bits(h.v_new[qsel]), bt, hist,
+                        np.concatenate([[0], np.cumsum(ql)]).astype(np.int32))
+        return kc, vc, kv, bt, reqs
+
+    def oracle_rows(self, kc, vc, kv, bt, reqs, first=None, last=None, causal=True, nthreads=None):
+        """Oracle output for each request of `reqs`: all rows (first = last =
+        None), or its first `first` rows -- the chunk of its first `first`
+        tokens over history + first keys -- and its last `last` rows -- the
+        chunk of its last `last` tokens over all its keys."""
+        s, h = self.spec, self.inp_host
+        qi = h.qo_indptr.numpy()
+        orc = oracle.load()
+        nt = nthreads or min(16, os.cpu_count() or 1)
+        q_parts, lens, rows = [], [], []
+        for n, r in enumerate(reqs):
+            q_r, kv_r = int(s.q_lens[r]), int(kv[n])
+            parts = []
+            if first is None and last is None:
+                parts.append((0, q_r, kv_r))
+            else:
+                if first:
+                    m = min(first, q_r)
+                    parts.append((0, m, kv_r - q_r + m))
+                if last:
+                    m = min(last, q_r)
+                    parts.append((q_r - m, q_r, kv_r))
+            for a0, a1, kvp in parts:
+                q_parts.append(h.q[qi[r] + a0: qi[r] + a1])
+                lens.append((a1 - a0, kvp, n))
+                rows.extend(range(qi[r] + a0, qi[r] + a1))
+        qcat = torch.cat(q_parts)
+        ql = np.array([x[0] for x in lens], np.int32)
+        kvl = np.array([x[1] for x in lens], np.int32)
+        btl = bt[[x[2] for x in lens]]
+        out, lse = orc.prefill(opool(s), host_bits(qcat), kc, vc, btl, kvl,
+                               np.concatenate([[0], np.cumsum(ql)]).astype(np.int32), s.scale, causal=causal,
+                               nthreads=nt)
+        return np.asarray(rows, np.int64), out, lse
