@@ -11,19 +11,20 @@
 //
 // Kernel.  One workgroup (4 waves) per (request, tile of 128 query rows,
 // query head); wave w owns query rows 32w .. 32w+31 of the tile.  Keys are
-// walked in tiles of 32 (two pages).  Per key tile, for every wave:
+// walked in tiles of 64 (four pages).  Per 32 keys, for every wave:
 //   S^T[32 key x 32 q]  = K[32 x D] . Q^T[D x 32]        (D/16 MFMA 32x32x16)
 //   O^T[D x 32 q]      += V^T[D x 32 key] . P^T[32 key x 32 q]  (D/16 MFMA)
 // Query rows sit on lanes (lane % 32) so the softmax statistics of a row live
 // in two lanes (lane and lane ^ 32); scores carry the softmax scale folded
 // into log2 units and use exp2.  Q stays in registers for the whole walk.
-// The key tile is staged in LDS twice over: K as [key][dim] and V transposed
-// as [dim][key] (the PV contraction runs over keys), both row-padded against
-// bank conflicts, double-buffered, with the next tile's global loads in
-// flight while the current one is computed.  Keys at or past kv_r (tail
-// slots of the last page, which may hold anything) are written to LDS as
-// zeros, and masked scores get -inf.  Tiles are scheduled longest first
-// (causal rows late in a request see the most keys).
+// K and V tiles are staged in LDS as [key][dim] rows (padded against bank
+// conflicts, double-buffered, next tile's global loads in flight during the
+// current one); the V^T operand comes straight from the [key][dim] rows
+// through gfx950's transposing LDS read.  Keys at or past kv_r (tail slots
+// of the last page, which may hold anything) are written to LDS as zeros
+// and masked scores get -inf; tiles that no row of a wave needs are skipped
+// and tiles no row's limit cuts are not masked.  Tiles are scheduled
+// longest first (causal rows late in a request see the most keys).
 #include <math.h>
 
 #include "common.hpp"
@@ -38,19 +39,22 @@ constexpr float kNegInff = -__builtin_inff();
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kWaves = 4;            // waves per workgroup
-constexpr int kRowsPerWave = 32;     // query rows per wave
+constexpr int kWaves = 4;                   // waves per workgroup
+constexpr int kRowsPerWave = 32;            // query rows per wave
 constexpr int kBM = kWaves * kRowsPerWave;  // query rows per workgroup
-constexpr int kBN = 32;              // keys per tile (two pages)
+constexpr int kBN = 64;                     // keys per tile (four pages)
 constexpr int kThreads = kWaves * kWave;
+// A row's running max is raised only when a tile's scores exceed it by more
+// than this (log2 units); weights relative to a stale max stay below 2^8, so
+// the output (normalised by the same max) is unchanged and the rescale of the
+// accumulators is skipped for most tiles.
+constexpr float kRescaleSlack = 8.f;
 
 template <int D>
 struct Smem {
-    static constexpr int KSTRIDE = D + 8;    // bf16 elements per K row (16 B pad)
-    static constexpr int VSTRIDE = kBN + 4;  // bf16 elements per V^T row (8 B pad)
-    static constexpr int KELEMS = kBN * KSTRIDE;
-    static constexpr int VELEMS = D * VSTRIDE;
-    static constexpr int BUF = KELEMS + VELEMS;  // one stage
+    static constexpr int STRIDE = D + 8;         // bf16 elements per key row (16 B pad)
+    static constexpr int TILE = kBN * STRIDE;    // one of K or V
+    static constexpr int BUF = 2 * TILE;         // K then V, one stage
     static constexpr int BYTES = 2 * BUF * 2;    // two stages of bf16
 };
 
@@ -66,13 +70,14 @@ template <int D>
 __device__ __forceinline__ void load_tile(const PrefillArgs &a, const int32_t *bt, int g, int tile, int kv,
                                           TileRegs<D> &t) {
     const int tid = threadIdx.x;
-    const int blk0 = tile * 2;
+    const int blk0 = tile * (kBN / kPage);
     const int nblk = (kv + kPage - 1) / kPage;
-    int page[2];
-    page[0] = blk0 < nblk ? bt[blk0] : 0;
-    page[1] = blk0 + 1 < nblk ? bt[blk0 + 1] : 0;
+    int page[kBN / kPage];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) page[u] = page[u] < 0 ? 0 : (page[u] >= a.num_pages ? a.num_pages - 1 : page[u]);
+    for (int u = 0; u < kBN / kPage; ++u) {
+        const int p = blk0 + u < nblk ? bt[blk0 + u] : 0;
+        page[u] = p < 0 ? 0 : (p >= a.num_pages ? a.num_pages - 1 : p);
+    }
 #pragma unroll
     for (int i = 0; i < TileRegs<D>::CHUNKS; ++i) {
         const int c = tid + kThreads * i;
@@ -96,20 +101,25 @@ template <int D>
 __device__ __forceinline__ void store_tile(uint16_t *buf, const TileRegs<D> &t) {
     using S = Smem<D>;
     const int tid = threadIdx.x;
-    uint16_t *ks = buf;
-    uint16_t *vt = buf + S::KELEMS;
 #pragma unroll
     for (int i = 0; i < TileRegs<D>::CHUNKS; ++i) {
         const int c = tid + kThreads * i;
         const int key = c / (D / 8);
         const int d8 = c - key * (D / 8);
-        *reinterpret_cast<u32x4 *>(ks + key * S::KSTRIDE + d8 * 8) = t.k[i];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            vt[(d8 * 8 + 2 * w) * S::VSTRIDE + key] = (uint16_t)(t.v[i][w] & 0xffffu);
-            vt[(d8 * 8 + 2 * w + 1) * S::VSTRIDE + key] = (uint16_t)(t.v[i][w] >> 16);
-        }
+        *reinterpret_cast<u32x4 *>(buf + key * S::STRIDE + d8 * 8) = t.k[i];
+        *reinterpret_cast<u32x4 *>(buf + S::TILE + key * S::STRIDE + d8 * 8) = t.v[i];
     }
+}
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Transposing LDS read: in each group of 16 lanes, lane 4a+b names
+// V[key0 + a][dim0 + 4b .. +3] and lane i of the group receives dims
+// dim0 + i at keys key0 .. key0+3 -- one column of V, i.e. a V^T operand.
+__device__ __forceinline__ u32x2 ld_tr(const uint16_t *p) {
+    const lds_bf16x4 *q = (const lds_bf16x4 *)(__attribute__((address_space(3))) const uint16_t *)p;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)q));
 }
 
 template <int D>
@@ -118,6 +128,7 @@ void prefill_kernel(PrefillArgs a, int n_qtiles) {
     using S = Smem<D>;
     constexpr int KS = D / 16;  // k-steps of the QK contraction
     constexpr int DB = D / 32;  // 32-dim blocks of the output
+    constexpr int NS = kBN / 32;  // 32-key score blocks per tile
     extern __shared__ __align__(16) uint16_t smem[];
 
     // grid: (request, tile, head) with tiles reversed (longest first)
@@ -145,13 +156,14 @@ void prefill_kernel(PrefillArgs a, int n_qtiles) {
     const int i_eff = row_ok ? i_row : q_len - 1;
     const int limit = a.causal ? kv - q_len + i_eff : kv - 1;  // last visible key
 
-    // key tiles the workgroup walks, and the last one this wave needs
+    // key tiles the workgroup walks; keys every row of this wave sees; the last it needs
     const int i_last_wg = min(qt * kBM + kBM, q_len) - 1;
     const int last_key_wg = a.causal ? kv - q_len + i_last_wg : kv - 1;
     const int n_tiles = last_key_wg / kBN + 1;
     const int wave_first = qt * kBM + wave * kRowsPerWave;
     const int i_last_wave = min(wave_first + kRowsPerWave, q_len) - 1;
     const int last_key_wave = wave_first >= q_len ? -1 : (a.causal ? kv - q_len + i_last_wave : kv - 1);
+    const int common_keys = wave_first >= q_len ? -1 : (a.causal ? kv - q_len + wave_first : kv - 1);
     if (kv == 0 || (a.causal && kv < q_len)) {
         // no visible key (only reachable without the causal flag): 0 and -inf
         if (row_ok) {
@@ -174,6 +186,10 @@ void prefill_kernel(PrefillArgs a, int n_qtiles) {
     for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
     float m = kNegInff, l = 0.f;
     const float c = a.scale_log2;
+    // lane's place in the transposing reads of V
+    const int grp = lane >> 4;
+    const int tr_key = 4 * half + ((lane & 15) >> 2);
+    const int tr_dim = 16 * (grp & 1) + 4 * (lane & 3);
 
     TileRegs<D> regs;
     load_tile<D>(a, bt, g, 0, kv, regs);
@@ -187,56 +203,74 @@ void prefill_kernel(PrefillArgs a, int n_qtiles) {
 
         if (tile * kBN <= last_key_wave) {
             const uint16_t *ks = cur;
-            const uint16_t *vt = cur + S::KELEMS;
-            // S^T = K . Q^T
-            f32x16 s = f32x16{};
+            const uint16_t *vs = cur + S::TILE;
+            // S^T = K . Q^T, one 32x32 block per 32 keys
+            f32x16 sc[NS];
 #pragma unroll
-            for (int k = 0; k < KS; ++k) {
-                const u32x4 kop = *reinterpret_cast<const u32x4 *>(ks + col * S::KSTRIDE + 16 * k + 8 * half);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kop),
-                                                            __builtin_bit_cast(bf16x8, qop[k]), s, 0, 0, 0);
+            for (int u = 0; u < NS; ++u) {
+                sc[u] = f32x16{};
+#pragma unroll
+                for (int k = 0; k < KS; ++k) {
+                    const u32x4 kop =
+                        *reinterpret_cast<const u32x4 *>(ks + (32 * u + col) * S::STRIDE + 16 * k + 8 * half);
+                    sc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kop),
+                                                                    __builtin_bit_cast(bf16x8, qop[k]), sc[u], 0, 0,
+                                                                    0);
+                }
             }
-            // mask + online softmax; element e is key tile*32 + 8(e/4) + 4half + e%4
-            float x[16];
+            // scores in log2 units; element e of block u is key tile*64 + 32u + 8(e/4) + 4half + e%4
+            float x[NS][16];
+            const bool need_mask = tile * kBN + kBN - 1 > common_keys;
             float mx = kNegInff;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int j = tile * kBN + 8 * (e >> 2) + 4 * half + (e & 3);
-                x[e] = j <= limit ? s[e] * c : kNegInff;
-                mx = fmaxf(mx, x[e]);
-            }
+            for (int u = 0; u < NS; ++u)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    x[u][e] = sc[u][e] * c;
+                    if (need_mask) {
+                        const int j = tile * kBN + 32 * u + 8 * (e >> 2) + 4 * half + (e & 3);
+                        x[u][e] = j <= limit ? x[u][e] : kNegInff;
+                    }
+                    mx = fmaxf(mx, x[u][e]);
+                }
             mx = fmaxf(mx, shfl_xor(mx, 32));
-            const float mn = fmaxf(m, mx);
-            const float alpha = fast_exp2(m - mn);
-            float sum = 0.f;
-            float p[16];
+            const bool raise = mx > m + kRescaleSlack;
+            if (__any(raise)) {
+                const float mn = raise ? mx : m;
+                const float alpha = fast_exp2(m - mn);
+                l *= alpha;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                p[e] = fast_exp2(x[e] - mn);
-                sum += p[e];
+                for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+                m = mn;
             }
-            l = l * alpha + sum;
-            m = mn;
+            float sum = 0.f;
+            u32x4 pop[2 * NS];
 #pragma unroll
-            for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-            // P^T operands for the two 16-key steps
-            u32x4 pop[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-                pop[t] = u32x4{pack_bf16x2(p[8 * t + 0], p[8 * t + 1]), pack_bf16x2(p[8 * t + 2], p[8 * t + 3]),
-                               pack_bf16x2(p[8 * t + 4], p[8 * t + 5]), pack_bf16x2(p[8 * t + 6], p[8 * t + 7])};
-            // O^T += V^T . P^T; V^T operand: dim row 32db + col, keys 16t + 4half .. and 16t + 8 + 4half ..
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const uint16_t *vrow = vt + (32 * db + col) * S::VSTRIDE;
+            for (int u = 0; u < NS; ++u)
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + 16 * t + 4 * half);
-                    const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + 16 * t + 8 + 4 * half);
+                    float p[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        p[e] = fast_exp2(x[u][8 * t + e] - m);
+                        sum += p[e];
+                    }
+                    pop[2 * u + t] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                           pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+                }
+            l += sum;
+            // O^T += V^T . P^T; per 16-key step tt: keys 16tt + 4half .. +3 and 16tt + 8 + 4half .. +3
+#pragma unroll
+            for (int tt = 0; tt < 2 * NS; ++tt) {
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const uint16_t *base = vs + (16 * tt + tr_key) * S::STRIDE + 32 * db + tr_dim;
+                    const u32x2 lo = ld_tr(base);
+                    const u32x2 hi = ld_tr(base + 8 * S::STRIDE);
                     const u32x4 vop = {lo[0], lo[1], hi[0], hi[1]};
                     acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vop),
-                                                                      __builtin_bit_cast(bf16x8, pop[t]), acc[db], 0,
-                                                                      0, 0);
+                                                                      __builtin_bit_cast(bf16x8, pop[tt]), acc[db],
+                                                                      0, 0, 0);
                 }
             }
         }
