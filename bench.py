@@ -56,6 +56,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     p.add_argument("--workers", type=int, default=0, help="decode split workers (0 = library default)")
+    p.add_argument("--separate", action="store_true",
+                   help="decode step as pkv_append + pkv_decode_attn (two launches) instead of the fused "
+                        "pkv_append_decode_attn")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (for HBM counter calibration)")
     return p.parse_args()
@@ -65,15 +68,18 @@ def parse():
 # accounting
 # --------------------------------------------------------------------------
 
-def decode_bytes(spec) -> dict:
+def decode_bytes(spec, fused=False) -> dict:
     """Algorithmic bytes of one decode call: K and V of exactly the attended
-    tokens, q and out, the table entries the rows touch, the lengths."""
+    tokens, q and out, the table entries the rows touch, the lengths; with
+    the append fused in, also the new token's K and V read and written into
+    the pool and the new lengths written."""
     es = 2 if spec.dtype == "bf16" else 4
     n = [int(x) + spec.n_new for x in spec.hist_lens]
     kv = sum(n) * spec.hkv * spec.head_dim * 2 * es
     qo = 2 * spec.batch * spec.hq * spec.head_dim * es
     table = 4 * sum(-(-x // spec.page_size) for x in n) + 4 * spec.batch
-    return {"kv": kv, "q_out": qo, "table": table, "total": kv + qo + table}
+    app = 2 * 2 * spec.batch * spec.hkv * spec.head_dim * es + 4 * spec.batch if fused else 0
+    return {"kv": kv, "q_out": qo, "table": table, "append": app, "total": kv + qo + table + app}
 
 
 def prefill_flops(spec) -> int:
@@ -169,7 +175,8 @@ def bench_decode(args, torch, pkv, wl):
         spec = wl.decode_spec("long_ragged", batch=args.batch or 256)
     dev = torch.device("cuda:0")
     L = args.layers
-    acc = decode_bytes(spec)
+    fused = not args.separate and spec.dtype == "bf16"
+    acc = decode_bytes(spec, fused)
     if args.workload == "long":
         free = torch.cuda.mem_get_info(dev)[0]
         per_layer = 2 * spec.num_pages * spec.hkv * spec.page_size * spec.head_dim * 2
@@ -193,26 +200,32 @@ def bench_decode(args, torch, pkv, wl):
             workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
         pkv.append(kc, vc, inp.k_hist, inp.v_hist, bt, zeros, inp.hist_indptr)
         out = torch.empty_like(inp.q)
-        app = pkv.api.prepare_append(kc, vc, inp.k_new, inp.v_new, bt, hist, lens)
-        dec = pkv.api.prepare_decode(inp.q, kc, vc, bt, lens, max_kv, out, workspace, workers=args.workers)
+        if fused:
+            app = None
+            dec = pkv.api.prepare_append_decode(inp.q, kc, vc, inp.k_new, inp.v_new, bt, hist, max_kv, out,
+                                                workspace, seqlens_out=lens, workers=args.workers)
+        else:
+            app = pkv.api.prepare_append(kc, vc, inp.k_new, inp.v_new, bt, hist, lens)
+            dec = pkv.api.prepare_decode(inp.q, kc, vc, bt, lens, max_kv, out, workspace, workers=args.workers)
         layers.append((app, dec, inp if layer < 2 else None))
         del inp
     torch.cuda.synchronize()
 
     def step():
         for app, dec, _ in layers:
-            app()
+            if app is not None:
+                app()
             dec()
 
     ms, _ = time_steps(torch, step, args.steps, args.warmup, not args.eager)
     step()  # lens is live again for the per-call brackets below
     dec_mean, dec_med = events_per_call(torch, [d for _, d, _ in layers])
-    app_mean, _ = events_per_call(torch, [a for a, _, _ in layers])
+    app_mean = None if fused else events_per_call(torch, [a for a, _, _ in layers])[0]
     kv_bytes_step = acc["kv"] * L
     value = kv_bytes_step / (ms * 1e-3) / 1e9
     achieved = acc["total"] / (dec_mean * 1e-3) / 1e9
     traffic = traffic_from_profile(os.path.join(ROOT, "paged_kv_attention_pkv_amd", "csrc", "decode.hip"),
-                                   f"decode_split_kernel_{spec.name}_pmc.txt")
+                                   f"decode_kernel_{spec.name}_pmc.txt")
     result = {
         "metric": "paged decode attn: KV-read GB/s (% HBM peak) + us/call at B=64, Hq32/Hkv8/D128",
         "value": round(value, 1),
@@ -229,17 +242,20 @@ def bench_decode(args, torch, pkv, wl):
         "config": {"workload": spec.name, "batch": spec.batch, "hq": spec.hq, "hkv": spec.hkv,
                    "head_dim": spec.head_dim, "page_size": spec.page_size, "layers": L,
                    "mean_attended_len": round(float(spec.hist_lens.mean()) + spec.n_new, 1),
-                   "step": "per layer: pkv_append(1 token/seq) + pkv_decode_attn",
+                   "step": ("per layer: pkv_append_decode_attn (append 1 token/seq + attend, one launch)"
+                            if fused else "per layer: pkv_append(1 token/seq) + pkv_decode_attn"),
                    "launch": "eager" if args.eager else "hip graph", "parallelism": "none (1 GPU)"},
         "us_per_call": round(ms * 1e3 / L, 2),
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "decode_us_per_call_events": round(dec_mean * 1e3, 2),
-        "append_us_per_call_events": round(app_mean * 1e3, 2),
-        "roofline": {"bound": "hbm", "kernel": "decode_kernel (one launch per pkv_decode_attn)",
+        "append_us_per_call_events": None if app_mean is None else round(app_mean * 1e3, 2),
+        "roofline": {"bound": "hbm",
+                     "kernel": "decode_bf16_kernel (one launch per pkv_append_decode_attn)" if fused
+                     else "decode kernel (one launch per pkv_decode_attn)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if traffic is None else round(traffic / (dec_mean * 1e-3) / 1e9, 1),
-                     "bytes_per_launch": acc["total"]},
+                     "traffic": None if traffic is None else int(traffic),
+                     "traffic_unit": "HBM bytes per launch", "bytes_per_launch": acc["total"]},
     }
     return result, spec, layers
 
@@ -303,6 +319,8 @@ def bench_prefill(args, torch, pkv, wl):
     ms, _ = time_steps(torch, call, args.steps, args.warmup, not args.eager)
     mean, _ = events_per_call(torch, [call] * 8)
     tfs = flops / (mean * 1e-3) / 1e12
+    traffic = traffic_from_profile(os.path.join(ROOT, "paged_kv_attention_pkv_amd", "csrc", "prefill.hip"),
+                                   f"prefill_kernel_{spec.name}_pmc.txt")
     result = {
         "metric": "paged causal prefill attn: TFLOP/s (% bf16 MFMA peak), D256 Hq48/Hkv8",
         "value": round(flops / (ms * 1e-3) / 1e12, 2),
@@ -316,7 +334,8 @@ def bench_prefill(args, torch, pkv, wl):
         "us_per_call": round(ms * 1e3, 2),
         "roofline": {"bound": "mfma", "kernel": "pkv_prefill_attn", "achieved": round(tfs, 2),
                      "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s", "frac": round(tfs / BF16_MFMA_PEAK_TFS, 4),
-                     "traffic": None, "flops_per_launch": flops},
+                     "traffic": None if traffic is None else int(traffic),
+                     "traffic_unit": "HBM bytes per launch", "flops_per_launch": flops},
     }
     return result, spec, inp
 
@@ -339,20 +358,27 @@ def cpu_baseline_prefill(args, torch, spec, inp):
                np.zeros(spec.batch, np.int32), h.hist_indptr.numpy())
     kv = orc.append(pool, kc, vc, host_bits(h.k_new), host_bits(h.v_new), spec.block_table, spec.hist_lens,
                     h.qo_indptr.numpy())
-    # the last `rows` query rows of request 0 (the longest rows of a causal request)
-    r0 = int(spec.q_lens[0])
-    rows = min(r0, 64)
+    # blocks of 32 consecutive query rows of request 0, from its last row
+    # backwards, each run as a chunked-prefill request over the keys it sees,
+    # until about --cpu-seconds have been spent
+    r0, kvl = int(spec.q_lens[0]), int(kv[0])
     ip = h.qo_indptr.numpy()
-    q = host_bits(h.q[ip[0] + r0 - rows: ip[0] + r0])
-    t0 = time.perf_counter()
-    orc.prefill(pool, q, kc, vc, spec.block_table[:1], kv[:1], np.array([0, rows], np.int32), spec.scale,
-                causal=True, nthreads=threads)
-    spent = time.perf_counter() - t0
-    kvl = int(kv[0])
-    pairs = sum(kvl - rows + i + 1 for i in range(rows))
-    fl = 4 * spec.head_dim * spec.hq * pairs
+    fl, spent, done, blk = 0, 0.0, 0, 32
+    while (spent < args.cpu_seconds or done == 0) and done < r0:
+        rows = min(blk, r0 - done)
+        a1 = r0 - done
+        a0 = a1 - rows
+        q = host_bits(h.q[ip[0] + a0: ip[0] + a1])
+        kv_seen = kvl - r0 + a1
+        t0 = time.perf_counter()
+        orc.prefill(pool, q, kc, vc, spec.block_table[:1], np.array([kv_seen], np.int32),
+                    np.array([0, rows], np.int32), spec.scale, causal=True, nthreads=threads)
+        spent += time.perf_counter() - t0
+        fl += 4 * spec.head_dim * spec.hq * sum(kv_seen - rows + i + 1 for i in range(rows))
+        done += rows
     return {"value": round(fl / spent / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"last {rows} query rows of request 0 ({fl / 1e9:.2f} GFLOP), fp64 oracle, {spent:.1f} s"}
+            "sample": f"last {done} query rows of request 0 in blocks of {blk} ({fl / 1e9:.2f} GFLOP), "
+                      f"fp64 oracle, {spent:.1f} s"}
 
 
 def calibrate_copy(torch):

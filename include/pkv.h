@@ -172,6 +172,48 @@ pkv_status pkv_decode_attn_ex(const pkv_cache_desc *cache, void *out, float *lse
                               int32_t workers, void *stream);
 
 /*
+ * pkv_append_decode_attn -- one decode step in one launch: append each
+ * sequence's new token to the pool and attend it with the cached ones.
+ *
+ * The same result as pkv_append (one token per sequence) followed by
+ * pkv_decode_attn on the lengths it returns: flash_attn_with_kvcache's
+ * in-place write of the new k/v at the row's current length, then attention
+ * over the updated row (mini-infer 06 §1).  Folding the cache write into the
+ * attention call is what the unsloth scripts page does inside its captured
+ * decode step ("Why this works"); here it removes the separate append launch.
+ *
+ *   k_cache, v_cache  the pools (written: one slot per sequence and kv head)
+ *   k_new, v_new      [batch, num_kv_heads, head_dim], dtype of the pool
+ *   cache_seqlens     int32 [batch]: PRE-append length L_b; the new token goes
+ *                     to position L_b and the row attends L_b + 1 keys
+ *   seqlens_out       int32 [batch] or NULL: receives L_b + 1; must not alias
+ *                     cache_seqlens
+ *   max_kv_len        host upper bound of L_b + 1 (<= bt_cols * page_size);
+ *                     a row with L_b + 1 > max_kv_len is cut to max_kv_len
+ *                     keys and its token is not written
+ *   workspace         as for pkv_decode_attn (same size query)
+ * The slot's page must be a real page (1..num_pages-1; otherwise the token
+ * is not written) and no two sequences may share it.  The written bytes are a
+ * bit copy of k_new / v_new.  Only PKV_BF16 is supported.
+ */
+pkv_status pkv_append_decode_attn(const pkv_cache_desc *cache, void *out, float *lse,
+                                  const void *q, int32_t num_q_heads, void *k_cache,
+                                  void *v_cache, const void *k_new, const void *v_new,
+                                  const int32_t *block_table, int32_t bt_cols,
+                                  const int32_t *cache_seqlens, int32_t *seqlens_out,
+                                  int32_t batch, int32_t max_kv_len, float scale,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+/* With an explicit split-worker count, as pkv_decode_attn_ex. */
+pkv_status pkv_append_decode_attn_ex(const pkv_cache_desc *cache, void *out, float *lse,
+                                     const void *q, int32_t num_q_heads, void *k_cache,
+                                     void *v_cache, const void *k_new, const void *v_new,
+                                     const int32_t *block_table, int32_t bt_cols,
+                                     const int32_t *cache_seqlens, int32_t *seqlens_out,
+                                     int32_t batch, int32_t max_kv_len, float scale,
+                                     void *workspace, size_t workspace_bytes, int32_t workers,
+                                     void *stream);
+
+/*
  * pkv_prefill_workspace_bytes / pkv_prefill_attn -- causal (chunked) prefill
  * over the paged pool.
  *

@@ -11,6 +11,7 @@ from .api import (  # noqa: F401
     PkvError,
     cache_desc,
     append,
+    append_decode_attn,
     decode_attn,
     decode_workspace_bytes,
     lib_path,

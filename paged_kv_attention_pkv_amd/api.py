@@ -66,6 +66,10 @@ _SIGS = {
                          _VP, _SZ, _VP], ctypes.c_int),
     "pkv_decode_attn_ex": ([_DP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _VP, _I32, _I32, ctypes.c_float,
                             _VP, _SZ, _I32, _VP], ctypes.c_int),
+    "pkv_append_decode_attn": ([_DP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32,
+                                ctypes.c_float, _VP, _SZ, _VP], ctypes.c_int),
+    "pkv_append_decode_attn_ex": ([_DP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32,
+                                   ctypes.c_float, _VP, _SZ, _I32, _VP], ctypes.c_int),
     "pkv_prefill_workspace_bytes": ([_DP, _I32, _I32, _I32, _I32, _I32], _SZ),
     "pkv_prefill_attn": ([_DP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32,
                           _I32, ctypes.c_float, _VP, _SZ, _VP], ctypes.c_int),
@@ -234,6 +238,47 @@ def decode_attn(q, k_cache, v_cache, block_table, cache_seqlens, max_kv_len: int
     return (out, lse) if lse is not None else out
 
 
+def append_decode_attn(q, k_cache, v_cache, k_new, v_new, block_table, cache_seqlens, max_kv_len: int,
+                       scale: float | None = None, out=None, lse=None, seqlens_out=None, workspace=None,
+                       layout: str = "HND", workers: int = 0, return_lse: bool = False):
+    """pkv_append_decode_attn: append k_new/v_new [B, Hkv, D] at each row's
+    pre-append length cache_seqlens[b], then attend q [B, Hq, D] over the
+    cache_seqlens[b] + 1 keys, in one launch.  Returns (out, seqlens_out) or
+    (out, lse, seqlens_out) when return_lse or lse is given."""
+    desc = cache_desc(k_cache, v_cache, layout)
+    dev = k_cache.device
+    _need(q, "q", k_cache.dtype, dev, 3)
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, nm, k_cache.dtype, dev, 3)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
+    batch, hq, d = q.shape
+    if cache_seqlens.shape[0] != batch or block_table.shape[0] != batch or k_new.shape[0] != batch:
+        raise ValueError("batch mismatch between q, k_new, block_table and cache_seqlens")
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, dev, 3)
+    if seqlens_out is None:
+        seqlens_out = torch.empty_like(cache_seqlens)
+    if lse is None and return_lse:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev, 2)
+    with torch.cuda.device(dev):
+        need = lib().pkv_decode_workspace_bytes_ex(ctypes.byref(desc), batch, hq, max_kv_len, workers)
+        if workspace is None:
+            workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+        rc = lib().pkv_append_decode_attn_ex(
+            ctypes.byref(desc), _ptr(out), _ptr(lse), _ptr(q), hq, _ptr(k_cache), _ptr(v_cache), _ptr(k_new),
+            _ptr(v_new), _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens), _ptr(seqlens_out), batch,
+            int(max_kv_len), float(scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            int(workers), _stream(k_cache))
+    _check("pkv_append_decode_attn", rc)
+    return (out, lse, seqlens_out) if lse is not None else (out, seqlens_out)
+
+
 def prefill_workspace_bytes(k_cache, batch, num_q_heads, total_q, max_q, max_kv_len, layout="HND") -> int:
     desc = cache_desc(k_cache, None, layout)
     return int(lib().pkv_prefill_workspace_bytes(ctypes.byref(desc), batch, num_q_heads, total_q, max_q,
@@ -386,6 +431,32 @@ def prepare_decode(q, k_cache, v_cache, block_table, cache_seqlens, max_kv_len: 
             nbytes, int(workers))
     return PreparedCall("pkv_decode_attn_ex", args, (k_cache, v_cache, q, out, block_table, cache_seqlens,
                                                      workspace, lse, desc))
+
+
+def prepare_append_decode(q, k_cache, v_cache, k_new, v_new, block_table, cache_seqlens, max_kv_len: int, out,
+                          workspace, seqlens_out=None, lse=None, scale: float | None = None, layout: str = "HND",
+                          workers: int = 0) -> PreparedCall:
+    desc = cache_desc(k_cache, v_cache, layout)
+    dev = k_cache.device
+    _need(q, "q", k_cache.dtype, dev, 3)
+    _need(out, "out", q.dtype, dev, 3)
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, nm, k_cache.dtype, dev, 3)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
+    batch, hq, d = q.shape
+    if scale is None:
+        scale = d ** -0.5
+    with torch.cuda.device(dev):
+        need = lib().pkv_decode_workspace_bytes_ex(ctypes.byref(desc), batch, hq, max_kv_len, workers)
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise PkvError("pkv_append_decode_attn", 3, f"workspace {nbytes} < {need} bytes")
+    args = (ctypes.byref(desc), _ptr(out), _ptr(lse), _ptr(q), hq, _ptr(k_cache), _ptr(v_cache), _ptr(k_new),
+            _ptr(v_new), _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens), _ptr(seqlens_out), batch,
+            int(max_kv_len), float(scale), _ptr(workspace), nbytes, int(workers))
+    return PreparedCall("pkv_append_decode_attn_ex", args, (k_cache, v_cache, q, out, k_new, v_new, block_table,
+                                                            cache_seqlens, seqlens_out, workspace, lse, desc))
 
 
 def prepare_prefill(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, max_q: int, max_kv_len: int, out,

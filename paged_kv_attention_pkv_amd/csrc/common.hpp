@@ -48,6 +48,26 @@ __device__ __forceinline__ int64_t wave_incl_scan64(int64_t v) {
     return v;
 }
 
+// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
+// with gfx950's row-swap permutes (VALU, no LDS round trip).  Each swap of a
+// value with itself leaves, per lane, the pair {x[l], x[l^16]} (or l^32).
+__device__ __forceinline__ float rows4_max(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const uint32_t a0 = r[0], a1 = r[1];
+    x = fmaxf(__uint_as_float(a0), __uint_as_float(a1));
+    auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const uint32_t b0 = t[0], b1 = t[1];
+    return fmaxf(__uint_as_float(b0), __uint_as_float(b1));
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const uint32_t a0 = r[0], a1 = r[1];
+    x = __uint_as_float(a0) + __uint_as_float(a1);
+    auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const uint32_t b0 = t[0], b1 = t[1];
+    return __uint_as_float(b0) + __uint_as_float(b1);
+}
+
 // 2^x on the transcendental unit (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

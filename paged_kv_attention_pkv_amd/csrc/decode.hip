@@ -1,25 +1,37 @@
 // decode.hip -- GQA decode attention over the paged KV pool (gfx950).
 //
 // What is computed: for every sequence b and query head h, softmax attention
-// of q[b,h] over the first cache_seqlens[b] keys of its block_table row,
-// reading KV head h / G (G = Hq / Hkv) -- the attend half of
-// flash_attn_with_kvcache in mini-infer 06 "True PagedAttention" §1, run by a
-// split-KV kernel in its profile (§6).
+// of q[b,h] over the first n_b keys of its block_table row, reading KV head
+// h / G (G = Hq / Hkv) -- the attend half of flash_attn_with_kvcache in
+// mini-infer 06 "True PagedAttention" §1, run there by a split-KV kernel
+// (§6).  Optionally (bf16) the step's new token is appended in the same
+// launch: the cache lengths are then the pre-append lengths L, each row
+// attends L+1 keys, and the token at position L comes from k_new / v_new and
+// is written into its page slot -- the in-place write of §1 folded into the
+// attention call, as the unsloth scripts page does inside its captured
+// decode step ("Why this works").
 //
 // Work decomposition ("stream-K" over pages), one kernel launch.  The pages
 // of all (sequence, kv head) segments are laid end to end, sequence-major,
 // and cut into `workers` equal ranges, one per wavefront.  A wave walks its
-// range, which may start and end inside a segment; every maximal run of one
-// segment is a "piece".  A piece that covers a whole segment writes the
-// final output.  Otherwise it writes an unnormalised (o, m, l) record to the
-// workspace and counts itself in the segment's arrival counter; the piece
-// that arrives last merges every record of the segment, in piece order (so
-// the result does not depend on which piece came last), writes the output
-// and resets the counter to zero for the next call.  Equal page counts per
-// wave keep every CU busy to the end for any mix of lengths.  Rows with no
-// keys are written (0, lse = -inf) by the waves in a round-robin.
+// range as one stream of page pairs that crosses segment boundaries without
+// draining: the next pair's loads are always in flight while the current one
+// is computed.  Every maximal run of one segment inside a range is a
+// "piece".  A piece that covers a whole segment writes the final output;
+// otherwise it writes an unnormalised (o, m, l) record to the workspace.
+// After its range, a wave counts each of its (at most two) split pieces in
+// the segment's arrival counter; the piece that arrives last merges every
+// record of the segment in piece order (so the result does not depend on
+// which piece came last), writes the output and resets the counter to zero
+// for the next call.  Equal page counts per wave keep every CU busy to the
+// end for any mix of lengths.  Rows with no keys are written (0, lse = -inf)
+// by the waves in a round-robin.
 //
-// Per page pair, one wave (bf16 path):
+// A wave first stages the physical page ids of its range in LDS (one
+// coalesced pass over the block table), so no table read ever sits in front
+// of a page load.
+//
+// Per page pair, one wave (bf16):
 //   S^T[16 tok x 16]  = K[16 tok x D] . Q^T[D x 16]        (D/32 MFMA 16x16x32 per page)
 //   O^T[D x 16]      += V^T[D x 32 tok] . P^T[32 tok x 16]  (D/16 MFMA 16x16x32)
 // The 16 MFMA columns are the query heads of one KV head (G <= 16 of them;
@@ -30,21 +42,17 @@
 // V^T operand; the PV token order inside a page pair is chosen so that the
 // P^T operand is exactly the S^T accumulator layout.  No data crosses lanes
 // except the row max / row sum of the online softmax (fp32, exp2 with the
-// softmax scale folded into log2 units).  Masked tokens (past the row length,
-// stale or NaN-poisoned slots) get score -inf and V = 0.  The next page
-// pair's K/V loads are issued before the current pair is computed (two
-// register buffers), and the row's block-table entries are read 64 at a time
-// into one register, so no table read sits in front of a page load.
+// softmax scale folded into log2 units), done with row-swap permutes.
+// Masked tokens (past the row length, stale or NaN-poisoned slots) get score
+// -inf and V = 0.  The query rows travel with each pair's loads (they hit in
+// cache after the first pair of a segment), so the register buffers of a
+// pair are self-contained.
 #include <math.h>
 
 #include "common.hpp"
 #include "internal.hpp"
 
-// Tuning knobs (compile time): prefetch the next page pair into a second
-// register buffer; resident waves per SIMD the bf16 kernel is register-capped to.
-#ifndef PKV_DECODE_PREFETCH
-#define PKV_DECODE_PREFETCH 1
-#endif
+// Resident waves per SIMD the bf16 kernel is register-capped to (head_dim <= 128).
 #ifndef PKV_DECODE_WAVES_PER_EU
 #define PKV_DECODE_WAVES_PER_EU 1
 #endif
@@ -55,20 +63,66 @@ namespace {
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
+constexpr int kStage = 2048;  // page ids of its range a wave keeps in LDS at a time
 
 // ---------------------------------------------------------------------------
-// rows, pages, workers
+// rows, segments, workers
 // ---------------------------------------------------------------------------
 
-// Attended length of row b, cut to the host bound so that every table read
-// stays inside the row (max_kv <= bt_cols * 16 is checked on the host).
-__device__ __forceinline__ int row_len(const DecodeArgs &a, int b) {
-    const int n = a.seqlens[b];
-    return n < 0 ? 0 : (n > a.max_kv ? a.max_kv : n);
+// Attended length for a raw cache length (cut to the host bound, so that
+// every table read stays inside the row: max_kv <= bt_cols * 16 is checked
+// on the host).  In fused-append mode the raw length is the pre-append one.
+__device__ __forceinline__ int attended(const DecodeArgs &a, int raw) {
+    if (raw < 0) return 0;
+    if (a.k_new) return raw >= a.max_kv ? a.max_kv : raw + 1;
+    return raw > a.max_kv ? a.max_kv : raw;
 }
+
+// Fused mode: the row's last attended key is the new token (not cut away).
+__device__ __forceinline__ int fresh_token(const DecodeArgs &a, int raw) {
+    return a.k_new && raw >= 0 && raw < a.max_kv;
+}
+
+__device__ __forceinline__ int raw_len(const DecodeArgs &a, int b) { return b < a.batch ? a.seqlens[b] : -1; }
 
 __device__ __forceinline__ int clamp_page(const DecodeArgs &a, int p) {
     return p < 0 ? 0 : (p >= a.num_pages ? a.num_pages - 1 : p);
+}
+
+// Raw lengths of 64 consecutive rows, one per lane (rows past the batch: -1).
+struct RowLens {
+    int base, raw;
+    __device__ __forceinline__ int get(const DecodeArgs &a, int b) {
+        if (b < base || b >= base + kWave) {
+            base = b & ~(kWave - 1);
+            raw = raw_len(a, base + lane_id());
+        }
+        return __builtin_amdgcn_readlane(raw, b - base);
+    }
+};
+
+// One (sequence, kv head) segment of the flat page space.
+struct Seg {
+    int b, g, n, np, fresh;  // row, kv head, attended length, pages, new-token flag
+    int64_t f;               // flat index of its page 0
+};
+
+__device__ __forceinline__ void seg_row(const DecodeArgs &a, Seg &s, int raw) {
+    s.n = attended(a, raw);
+    s.np = ceil_div(s.n, kPage);
+    s.fresh = fresh_token(a, raw);
+}
+
+// The next non-empty segment (the caller knows one exists).
+__device__ __forceinline__ void seg_next(const DecodeArgs &a, Seg &s, RowLens &rl) {
+    s.f += s.np;
+    if (++s.g == a.hkv) {
+        s.g = 0;
+        do {
+            ++s.b;
+            seg_row(a, s, rl.get(a, s.b));
+        } while (s.n == 0 && s.b < a.batch);
+    }
 }
 
 // Partial records travel between waves on different XCDs (each with its own
@@ -102,17 +156,26 @@ struct Range {
     int workers;
 };
 
-// Total pages over all segments and this wave's share; empty rows are
-// zero-filled here, row b by worker b mod workers.
+// Total pages over all segments and this wave's share.  Rows are handed out
+// round-robin (row b to worker b mod workers) for the per-row chores: zero
+// fill of rows without keys, and in fused mode the new lengths.  The first
+// 64 raw lengths stay in `rl`.
 template <typename OutT>
-__device__ __forceinline__ bool worker_range(const DecodeArgs &a, int w, int D, Range &r) {
+__device__ __forceinline__ bool plan(const DecodeArgs &a, int w, int D, RowLens &rl, Range &r) {
     const int l = lane_id();
     int64_t pages = 0;
     for (int base = 0; base < a.batch; base += kWave) {
         const int b = base + l;
-        const int n = b < a.batch ? row_len(a, b) : -1;
-        pages += n > 0 ? ceil_div(n, kPage) : 0;
-        uint64_t empty = __ballot(n == 0 && b % a.workers == w);
+        const int raw = raw_len(a, b);
+        if (base == 0) {
+            rl.base = 0;
+            rl.raw = raw;
+        }
+        const int n = attended(a, raw);
+        pages += ceil_div(n, kPage);
+        const bool mine = b < a.batch && b % a.workers == w;
+        if (mine && a.seqlens_out) a.seqlens_out[b] = raw + 1;
+        uint64_t empty = __ballot(mine && n == 0);
         while (empty) {
             const int e = uniform((int)__builtin_ctzll(empty));
             empty &= empty - 1;
@@ -129,28 +192,29 @@ __device__ __forceinline__ bool worker_range(const DecodeArgs &a, int w, int D, 
     return true;
 }
 
-// Sequence b whose segments contain flat page index f, and the flat index of
-// its first page (kv head 0, page 0).
-__device__ __forceinline__ void locate(const DecodeArgs &a, int64_t f, int &b_out, int64_t &start_out) {
+// The segment holding flat page f (f < total).  Uses the first 64 lengths
+// from `rl` (as left by plan) and reads further chunks of rows if needed.
+__device__ __forceinline__ void locate(const DecodeArgs &a, int64_t f, const RowLens &rl, Seg &s) {
     const int l = lane_id();
     int64_t run = 0;
     for (int base = 0; base < a.batch; base += kWave) {
-        const int b = base + l;
-        const int n = b < a.batch ? row_len(a, b) : 0;
+        const int raw = base == 0 ? rl.raw : raw_len(a, base + l);
+        const int n = attended(a, raw);
         const int64_t np = (int64_t)ceil_div(n, kPage) * a.hkv;
         const int64_t incl = wave_incl_scan64(np);
         const int64_t tot = uniform64(__shfl(incl, kWave - 1, kWave));
         if (run + tot > f) {
             const uint64_t hit = __ballot(run + incl > f);
             const int first = uniform((int)__builtin_ctzll(hit));
-            b_out = base + first;
-            start_out = run + uniform64(__shfl(incl - np, first, kWave));
+            const int64_t start = run + uniform64(__shfl(incl - np, first, kWave));
+            s.b = base + first;
+            seg_row(a, s, uniform(__shfl(raw, first, kWave)));
+            s.g = (int)((f - start) / s.np);
+            s.f = start + (int64_t)s.g * s.np;
             return;
         }
         run += tot;
     }
-    b_out = a.batch - 1;  // not reached for f < total
-    start_out = run;
 }
 
 // Worker whose range holds flat page p.
@@ -158,87 +222,272 @@ __device__ __forceinline__ int64_t worker_of(int64_t p, const Range &r) {
     return ((p + 1) * r.workers - 1) / r.total;
 }
 
+// ---------------------------------------------------------------------------
+// partial records and their merge
+// ---------------------------------------------------------------------------
+//
+// A record holds the G x D unnormalised outputs of one piece as D/8 blocks,
+// one per store instruction of the engine: block t holds, at pair index
+// t*4G + quad*G + col, the two fp32 values the lane (quad, col) stores with
+// it, so each instruction writes one contiguous run and the merge reads the
+// record with consecutive lanes on consecutive pairs.  Eng::dim_of(t, quad)
+// gives the (even) output dim of such a pair.  (m, l) per head follow in a
+// second array.
+
+template <typename OutT>
+__device__ __forceinline__ void store_out_pair(OutT *p, float x, float y);
+template <>
+__device__ __forceinline__ void store_out_pair<__bf16>(__bf16 *p, float x, float y) {
+    *reinterpret_cast<uint32_t *>(p) = pack_bf16x2(x, y);
+}
+template <>
+__device__ __forceinline__ void store_out_pair<float>(float *p, float x, float y) {
+    *reinterpret_cast<f32x2 *>(p) = f32x2{x, y};
+}
+
 // Merge the partial records of split segment s (pieces of workers wf ..
-// wf+cnt-1, record ids w + s) in piece order and write its output rows.  A
-// lane owns 8 consecutive outputs of one head; pieces are taken 8 at a time
-// with every load of a batch issued before any is used (two memory round
-// trips per batch), and batches are folded with the log-sum-exp rule.
-template <typename OutT, int D>
+// wf+cnt-1, record ids w + s) in piece order and write its output rows.
+// Pieces are taken 8 at a time with every load of a batch issued before any
+// is used, and batches are folded with the log-sum-exp rule.
+template <typename OutT, class Eng, int D>
 __device__ void merge_segment(const DecodeArgs &a, int64_t s, int b, int g, int64_t wf, int cnt) {
-    constexpr int kBatch = 8;
+    constexpr int kBatch = 8, kPairs = 4;
     const int G = a.hq / a.hkv;
+    const int npairs = G * D / 2;
+    const int64_t ostride = (int64_t)G * D;
     OutT *out = (OutT *)a.out + ((int64_t)b * a.hq + (int64_t)g * G) * D;
-    for (int base = lane_id() * 8; base < G * D; base += kWave * 8) {
-        const int c = base / D;
-        const int d0 = base - c * D;
-        float M = kNegInf, den = 0.f;
-        float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int u0 = 0; u0 < npairs; u0 += kWave * kPairs) {
+        int uu[kPairs], col[kPairs], dim[kPairs];
+        float M[kPairs], den[kPairs], n0[kPairs], n1[kPairs];
+#pragma unroll
+        for (int k = 0; k < kPairs; ++k) {
+            const int u = u0 + k * kWave + lane_id();
+            uu[k] = u < npairs ? u : npairs - 1;
+            const int t = uu[k] / (4 * G);
+            const int rem = uu[k] - t * 4 * G;
+            const int quad = rem / G;
+            col[k] = rem - quad * G;
+            dim[k] = Eng::dim_of(t, quad);
+            M[k] = kNegInf;
+            den[k] = n0[k] = n1[k] = 0.f;
+        }
         for (int k0 = 0; k0 < cnt; k0 += kBatch) {
             const int nb = min(kBatch, cnt - k0);
-            f32x2 ml[kBatch];
-            f32x2 o[kBatch][4];
+            f32x2 ml[kBatch][kPairs], o[kBatch][kPairs];
 #pragma unroll
-            for (int k = 0; k < kBatch; ++k) {
-                if (k < nb) {
-                    const int64_t rec = (wf + k0 + k + s) * G + c;
-                    ml[k] = ld_shared2(a.part_ml + rec * 2);
+            for (int j = 0; j < kBatch; ++j) {
+                if (j < nb) {
+                    const int64_t rec = wf + k0 + j + s;
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) o[k][t] = ld_shared2(a.part_o + rec * D + d0 + 2 * t);
-                }
-            }
-            float Mb = M;
-#pragma unroll
-            for (int k = 0; k < kBatch; ++k)
-                if (k < nb) Mb = fmaxf(Mb, ml[k][0]);
-            const float r = fast_exp2(M - Mb);
-            den *= r;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) num[t] *= r;
-#pragma unroll
-            for (int k = 0; k < kBatch; ++k) {
-                if (k < nb) {
-                    const float wgt = fast_exp2(ml[k][0] - Mb);
-                    den += wgt * ml[k][1];
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        num[2 * t] += wgt * o[k][t][0];
-                        num[2 * t + 1] += wgt * o[k][t][1];
+                    for (int k = 0; k < kPairs; ++k) {
+                        ml[j][k] = ld_shared2(a.part_ml + (rec * G + col[k]) * 2);
+                        o[j][k] = ld_shared2(a.part_o + rec * ostride + 2 * uu[k]);
                     }
                 }
             }
-            M = Mb;
-        }
-        const float inv = 1.f / den;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) out[base + t] = OutT(num[t] * inv);
-        if (d0 == 0 && a.lse) a.lse[(int64_t)b * a.hq + (int64_t)g * G + c] = (M + log2f(den)) * kLn2;
+            for (int k = 0; k < kPairs; ++k) {
+                float Mb = M[k];
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j)
+                    if (j < nb) Mb = fmaxf(Mb, ml[j][k][0]);
+                const float r = fast_exp2(M[k] - Mb);
+                den[k] *= r;
+                n0[k] *= r;
+                n1[k] *= r;
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    if (j < nb) {
+                        const float wgt = fast_exp2(ml[j][k][0] - Mb);
+                        den[k] += wgt * ml[j][k][1];
+                        n0[k] += wgt * o[j][k][0];
+                        n1[k] += wgt * o[j][k][1];
+                    }
+                }
+                M[k] = Mb;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kPairs; ++k) {
+            if (u0 + k * kWave + lane_id() < npairs) {
+                const float inv = 1.f / den[k];
+                store_out_pair<OutT>(out + (int64_t)col[k] * D + dim[k], n0[k] * inv, n1[k] * inv);
+                if (dim[k] == 0 && a.lse)
+                    a.lse[(int64_t)b * a.hq + (int64_t)g * G + col[k]] = (M[k] + log2f(den[k])) * kLn2;
+            }
+        }
+    }
+}
+
+// Split pieces a wave leaves for the merge (at most its first and its last).
+struct Pending {
+    int n, saved;  // saved: the first record is still held in registers
+    int64_t s0, s1, wf0, wf1;
+    int cnt0, cnt1, b0, b1, g0, g1;
+};
+
+__device__ __forceinline__ void pending_add(Pending &p, int64_t s, int b, int g, int64_t wf, int cnt) {
+    if (p.n == 0) {
+        p.s0 = s, p.b0 = b, p.g0 = g, p.wf0 = wf, p.cnt0 = cnt;
+    } else {
+        p.s1 = s, p.b1 = b, p.g1 = g, p.wf1 = wf, p.cnt1 = cnt;
+    }
+    ++p.n;
+}
+
+// Count the wave's split pieces in their segments' arrival counters (after
+// its record stores have completed); the last piece of a segment merges it.
+template <typename OutT, class Eng, int D>
+__device__ void settle(const DecodeArgs &a, const Pending &p) {
+    if (p.n == 0) return;
+    wait_stores_complete();  // the records are visible before they are counted
+    int prior0 = 0, prior1 = 0;
+    if (lane_id() == 0) {
+        prior0 = __hip_atomic_fetch_add(a.arrivals + p.s0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (p.n > 1)
+            prior1 = __hip_atomic_fetch_add(a.arrivals + p.s1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    prior0 = __shfl(prior0, 0, kWave);
+    prior1 = __shfl(prior1, 0, kWave);
+    if (prior0 == p.cnt0 - 1) {
+        merge_segment<OutT, Eng, D>(a, p.s0, p.b0, p.g0, p.wf0, p.cnt0);
+        if (lane_id() == 0) __hip_atomic_store(a.arrivals + p.s0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (p.n > 1 && prior1 == p.cnt1 - 1) {
+        merge_segment<OutT, Eng, D>(a, p.s1, p.b1, p.g1, p.wf1, p.cnt1);
+        if (lane_id() == 0) __hip_atomic_store(a.arrivals + p.s1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
 // ---------------------------------------------------------------------------
-// bf16 engine: MFMA 16x16x32 bf16, two pages per step, one pair prefetched
+// bf16 stream: cursor over the wave's range, page pairs, MFMA 16x16x32 bf16
 // ---------------------------------------------------------------------------
 
+// Position of the next page to load.
+struct Cursor {
+    Seg s;
+    int p, pend, pstart;  // next page, end of the piece in this segment, first page of the piece
+    int live;
+    __device__ __forceinline__ int64_t f() const { return s.f + p; }
+};
+
+// One page pair as the compute side sees it (wave-uniform).
+struct Desc {
+    int b, g, n, np, pa, npg;
+    int last;    // last pair of its piece
+    int whole;   // the piece covers the whole segment
+    int newtok;  // fused mode: the pair's last token is the new one
+    int ida, idb;
+    int raw_last;  // table entry of the pair's last page (unclamped)
+    int64_t segf;
+};
+
+// Fill ids[i] with the table entry of flat page c.f() + i, for i < min(kStage,
+// f1 - c.f()): one pass of coalesced table reads, eight 64-entry chunks at a
+// time with all loads of a group issued before any is used.
+__device__ void stage(const DecodeArgs &a, int *ids, const Cursor &c, int64_t f1, RowLens &rl) {
+    const int64_t f0 = c.f();
+    const int len = (int)(f1 - f0 < kStage ? f1 - f0 : kStage);
+    const int l = lane_id();
+    Seg s = c.s;
+    for (int c0 = 0; c0 < len; c0 += 8 * kWave) {
+        const int64_t gend = f0 + (c0 + 8 * kWave < len ? c0 + 8 * kWave : len);
+        int64_t off[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) off[u] = -1;
+        for (;;) {  // the segments overlapping [f0 + c0, gend)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t fl = f0 + c0 + u * kWave + l;
+                if (fl < gend && fl >= s.f && fl < s.f + s.np) off[u] = (int64_t)s.b * a.bt_cols + (fl - s.f);
+            }
+            if (s.f + s.np >= gend) break;
+            seg_next(a, s, rl);
+        }
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = off[u] >= 0 ? a.block_table[off[u]] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = c0 + u * kWave + l;
+            if (i < len) ids[i] = v[u];
+        }
+    }
+}
+
+// The next pair at the cursor, then advance.  Restages the id window when
+// the cursor has run past it.
+__device__ __forceinline__ void take(const DecodeArgs &a, Cursor &c, int *ids, int64_t &fbase, int64_t f1,
+                                     RowLens &rl, Desc &d) {
+    if (c.f() - fbase >= kStage) {
+        fbase = c.f();
+        stage(a, ids, c, f1, rl);
+    }
+    const int64_t i = c.f() - fbase;
+    d.b = c.s.b;
+    d.g = c.s.g;
+    d.n = c.s.n;
+    d.np = c.s.np;
+    d.pa = c.p;
+    d.segf = c.s.f;
+    d.npg = (c.p + 1 < c.pend && i + 1 < kStage) ? 2 : 1;
+    d.last = c.p + d.npg == c.pend;
+    d.whole = c.pstart == 0 && c.pend == c.s.np;
+    d.newtok = c.s.fresh && c.p + d.npg == c.s.np;
+    const int ra = uniform(ids[i]);
+    const int rb = d.npg == 2 ? uniform(ids[i + 1]) : ra;
+    d.ida = clamp_page(a, ra);
+    d.idb = clamp_page(a, rb);
+    d.raw_last = rb;
+    c.p += d.npg;
+    if (c.p == c.pend) {
+        if (c.f() >= f1) {
+            c.live = 0;
+        } else {
+            seg_next(a, c.s, rl);
+            c.p = c.pstart = 0;
+            c.pend = (int)(c.s.np < f1 - c.s.f ? c.s.np : f1 - c.s.f);
+        }
+    }
+}
+
 template <int D>
-struct EngBf16 {
+struct Bf16 {
     using Out = __bf16;
     static constexpr int KC = D / 32;   // QK MFMAs per page
     static constexpr int DPL = D / 16;  // V elements per lane per token = PV MFMAs per pair
     static constexpr int VW = DPL / 2;  // dwords per lane per V token row
 
     struct Buf {
+        u32x4 q[KC];
         u32x4 kA[KC], kB[KC];
         uint32_t vA[4][VW], vB[4][VW];
+        u32x4 kn[KC];     // fused append: the new token's K (lanes col == slot)
+        uint32_t vn[VW];  // and V (lanes quad == slot / 4)
     };
 
-    u32x4 qop[KC];
     f32x4 acc[DPL];
     float m, l;
+    f32x4 sacc[DPL];  // a split piece's state held until the range is done
+    float sm, sl;
     int G, quad, col;
     uint32_t koff;     // lane's byte offset in a page for K (token col, dims 8quad..)
     uint32_t voff[4];  // lane's byte offsets for V (token 4quad+e, dims DPL*col..)
 
-    __device__ __forceinline__ void init(const DecodeArgs &a, int b, int g) {
+    // Output dim of record pair (t, quad): acc[2jj][i], acc[2jj+1][i] with t = i*VW + jj.
+    __device__ static __forceinline__ int dim_of(int t, int quad) {
+        const int i = t / VW, jj = t - i * VW;
+        return DPL * (4 * quad + i) + 2 * jj;
+    }
+
+    __device__ __forceinline__ void reset() {
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m = kNegInf;
+        l = 0.f;
+    }
+
+    __device__ __forceinline__ void init(const DecodeArgs &a) {
         G = a.hq / a.hkv;
         const int ln = lane_id();
         quad = ln >> 4;
@@ -247,65 +496,121 @@ struct EngBf16 {
         koff = col * st + 16u * quad;
 #pragma unroll
         for (int e = 0; e < 4; ++e) voff[e] = (4u * quad + e) * st + 2u * DPL * col;
-        const int qc = col < G ? col : G - 1;  // lanes past the group read nothing
-        const uint16_t *q = (const uint16_t *)a.q + ((int64_t)b * a.hq + (int64_t)g * G + qc) * D;
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-            u32x4 z = {0u, 0u, 0u, 0u};
-            qop[kc] = col < G ? ld16(q + 32 * kc + 8 * quad) : z;
-        }
-#pragma unroll
-        for (int j = 0; j < DPL; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m = kNegInf;
-        l = 0.f;
+        reset();
     }
 
-    // kp / vp are wave-uniform page bases and the lane parts zero-extended
+    // kb / vb are wave-uniform page bases and the lane parts zero-extended
     // 32-bit byte offsets, so the loads use scalar-base + vector-offset
     // addressing and need no per-lane 64-bit address registers.
-    __device__ __forceinline__ void load_page(const uint16_t *kp, const uint16_t *vp, u32x4 (&k)[KC],
+    __device__ __forceinline__ void load_page(const char *kb, const char *vb, u32x4 (&k)[KC],
                                               uint32_t (&v)[4][VW]) {
-        const char *kb = (const char *)kp;
-        const char *vb = (const char *)vp;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) k[kc] = ld16(kb + (uint64_t)koff + 64 * kc);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint16_t *src = (const uint16_t *)(vb + (uint64_t)voff[e]);
-            if constexpr (VW == 2) {
-                u32x2 x = ld8(src);
-                v[e][0] = x[0];
-                v[e][1] = x[1];
-            } else {
+        for (int e = 0; e < 4; ++e) load_vrow(vb + (uint64_t)voff[e], v[e]);
+    }
+
+    __device__ __forceinline__ static void load_vrow(const char *src, uint32_t (&v)[VW]) {
+        if constexpr (VW == 2) {
+            const u32x2 x = ld8(src);
+            v[0] = x[0];
+            v[1] = x[1];
+        } else {
 #pragma unroll
-                for (int c4 = 0; c4 < VW / 4; ++c4) {
-                    u32x4 x = ld16(src + 8 * c4);
-                    v[e][4 * c4 + 0] = x[0];
-                    v[e][4 * c4 + 1] = x[1];
-                    v[e][4 * c4 + 2] = x[2];
-                    v[e][4 * c4 + 3] = x[3];
+            for (int c4 = 0; c4 < VW / 4; ++c4) {
+                const u32x4 x = ld16(src + 16 * c4);
+                v[4 * c4 + 0] = x[0];
+                v[4 * c4 + 1] = x[1];
+                v[4 * c4 + 2] = x[2];
+                v[4 * c4 + 3] = x[3];
+            }
+        }
+    }
+
+    __device__ __forceinline__ static void store_vrow(char *dst, const uint32_t (&v)[VW]) {
+        if constexpr (VW == 2) {
+            *reinterpret_cast<u32x2 *>(dst) = u32x2{v[0], v[1]};
+        } else {
+#pragma unroll
+            for (int c4 = 0; c4 < VW / 4; ++c4)
+                st16(dst + 16 * c4, u32x4{v[4 * c4], v[4 * c4 + 1], v[4 * c4 + 2], v[4 * c4 + 3]});
+        }
+    }
+
+    // Loads of pair d: K and V of its pages, the query rows of (b, g) and, in
+    // fused mode, the new token.
+    __device__ __forceinline__ void issue(const DecodeArgs &a, const Desc &d, Buf &buf) {
+        const int64_t hoff = (int64_t)d.g * a.s_head * 2;
+        const char *kc = (const char *)a.k_cache + hoff;
+        const char *vc = (const char *)a.v_cache + hoff;
+        const int64_t ps = a.s_page * 2;
+        load_page(kc + d.ida * ps, vc + d.ida * ps, buf.kA, buf.vA);
+        load_page(kc + d.idb * ps, vc + d.idb * ps, buf.kB, buf.vB);
+        const int qc = col < G ? col : G - 1;  // lanes past the group read nothing
+        const char *q = (const char *)a.q + ((int64_t)d.b * a.hq + (int64_t)d.g * G + qc) * D * 2;
+#pragma unroll
+        for (int kc2 = 0; kc2 < KC; ++kc2) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            buf.q[kc2] = col < G ? ld16(q + 64 * kc2 + 16 * quad) : z;
+        }
+        if (d.newtok) {
+            const int sl = (d.n - 1) & (kPage - 1);
+            const int64_t row = ((int64_t)d.b * a.hkv + d.g) * D * 2;
+            if (col == sl) {
+#pragma unroll
+                for (int kc2 = 0; kc2 < KC; ++kc2)
+                    buf.kn[kc2] = ld16((const char *)a.k_new + row + 64 * kc2 + 16 * quad);
+            }
+            if (quad == (sl >> 2)) load_vrow((const char *)a.v_new + row + 2 * DPL * col, buf.vn);
+        }
+    }
+
+    // Fused mode: put the new token into the pair's registers in place of
+    // its (stale) slot and write it into the pool.
+    __device__ __forceinline__ void splice(const DecodeArgs &a, const Desc &d, Buf &buf) {
+        const int sl = (d.n - 1) & (kPage - 1);
+        const int e = sl & 3;
+        const bool inB = d.npg == 2;
+        const bool writable = d.raw_last >= 1 && d.raw_last < a.num_pages;
+        const int64_t base = (int64_t)d.g * a.s_head * 2 + (int64_t)d.raw_last * a.s_page * 2;
+        if (col == sl) {
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                if (inB)
+                    buf.kB[kc] = buf.kn[kc];
+                else
+                    buf.kA[kc] = buf.kn[kc];
+                if (writable) st16((char *)a.k_cache + base + koff + 64 * kc, buf.kn[kc]);
+            }
+        }
+        if (quad == (sl >> 2)) {
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                if (e2 == e) {
+#pragma unroll
+                    for (int w = 0; w < VW; ++w) {
+                        if (inB)
+                            buf.vB[e2][w] = buf.vn[w];
+                        else
+                            buf.vA[e2][w] = buf.vn[w];
+                    }
+                    if (writable) store_vrow((char *)a.v_cache + base + voff[e2], buf.vn);
                 }
             }
         }
     }
 
-    // Loads of pages pa and pb (pb == pa when the pair has one page).
-    __device__ __forceinline__ void issue(const DecodeArgs &a, const uint16_t *kbase, const uint16_t *vbase, int pa,
-                                          int pb, Buf &buf) {
-        load_page(kbase + (int64_t)pa * a.s_page, vbase + (int64_t)pa * a.s_page, buf.kA, buf.vA);
-        load_page(kbase + (int64_t)pb * a.s_page, vbase + (int64_t)pb * a.s_page, buf.kB, buf.vB);
-    }
-
-    // One page pair: vcA / vcB valid tokens in the two pages (vcB = 0 for a
-    // pair with one page).
-    __device__ __forceinline__ void compute(Buf &buf, int vcA, int vcB, float c) {
+    __device__ __forceinline__ void compute(const DecodeArgs &a, Buf &buf, const Desc &d, float c) {
+        if (d.newtok) splice(a, d, buf);
+        const int vcA = min(d.n - d.pa * kPage, kPage);
+        const int vcB = d.npg == 2 ? min(d.n - (d.pa + 1) * kPage, kPage) : 0;
         f32x4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
             sA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf.kA[kc]),
-                                                         __builtin_bit_cast(bf16x8, qop[kc]), sA, 0, 0, 0);
+                                                         __builtin_bit_cast(bf16x8, buf.q[kc]), sA, 0, 0, 0);
             sB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf.kB[kc]),
-                                                         __builtin_bit_cast(bf16x8, qop[kc]), sB, 0, 0, 0);
+                                                         __builtin_bit_cast(bf16x8, buf.q[kc]), sB, 0, 0, 0);
         }
         float x[8];
 #pragma unroll
@@ -316,9 +621,7 @@ struct EngBf16 {
         float mx = x[0];
 #pragma unroll
         for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
-        const float mn = fmaxf(m, mx);
+        const float mn = fmaxf(m, rows4_max(mx));
         const float alpha = fast_exp2(m - mn);
         float p[8], sum = 0.f;
 #pragma unroll
@@ -366,78 +669,9 @@ struct EngBf16 {
         }
     }
 
-    __device__ __forceinline__ void run(const DecodeArgs &a, int b, int g, int n, int p0, int p1) {
-        const int32_t *bt = a.block_table + (int64_t)b * a.bt_cols;
-        const uint16_t *kbase = (const uint16_t *)a.k_cache + (int64_t)g * a.s_head;
-        const uint16_t *vbase = (const uint16_t *)a.v_cache + (int64_t)g * a.s_head;
-        const float c = a.scale_log2;
-        const int ln = lane_id();
-        Buf b0, b1;
-        // pages in chunks of 64: the chunk's table entries sit one per lane
-        for (int c0 = p0; c0 < p1; c0 += kWave) {
-            const int cn = min(p1 - c0, kWave);
-            const int tb = ln < cn ? bt[c0 + ln] : 0;
-            const int npairs = (cn + 1) >> 1;
-            auto pages_of = [&](int i, int &pa, int &pb) {
-                pa = clamp_page(a, __builtin_amdgcn_readlane(tb, 2 * i));
-                pb = 2 * i + 1 < cn ? clamp_page(a, __builtin_amdgcn_readlane(tb, 2 * i + 1)) : pa;
-            };
-            auto valid = [&](int i, int &va, int &vb) {
-                const int first = (c0 + 2 * i) * kPage;
-                va = min(n - first, kPage);
-                vb = 2 * i + 1 < cn ? min(n - first - kPage, kPage) : 0;
-            };
-            int pa, pb, va, vb;
-#if !PKV_DECODE_PREFETCH
-            for (int i = 0; i < npairs; ++i) {
-                pages_of(i, pa, pb);
-                issue(a, kbase, vbase, pa, pb, b0);
-                valid(i, va, vb);
-                compute(b0, va, vb, c);
-            }
-            continue;
-#endif
-            pages_of(0, pa, pb);
-            issue(a, kbase, vbase, pa, pb, b0);
-            // Two buffers in turn; the next pair's loads are issued before the
-            // current pair is computed, and no load is left unconsumed at the
-            // end, so the compiler's wait counts stay exact across iterations.
-            // The scheduling barriers keep the loads ahead of the compute.
-            for (int i = 0;; i += 2) {
-                valid(i, va, vb);
-                if (i + 1 < npairs) {
-                    pages_of(i + 1, pa, pb);
-                    __builtin_amdgcn_sched_barrier(0);
-                    issue(a, kbase, vbase, pa, pb, b1);
-                    __builtin_amdgcn_sched_barrier(0);
-                    compute(b0, va, vb, c);
-                } else {
-                    compute(b0, va, vb, c);
-                    break;
-                }
-                valid(i + 1, va, vb);
-                if (i + 2 < npairs) {
-                    pages_of(i + 2, pa, pb);
-                    __builtin_amdgcn_sched_barrier(0);
-                    issue(a, kbase, vbase, pa, pb, b0);
-                    __builtin_amdgcn_sched_barrier(0);
-                    compute(b1, va, vb, c);
-                } else {
-                    compute(b1, va, vb, c);
-                    break;
-                }
-            }
-        }
-    }
-
     // acc[j][i] is O^T[dim DPL*(4quad+i) + j][head col].
-    __device__ __forceinline__ float row_sum() const {
-        float t = l + shfl_xor(l, 16);
-        return t + shfl_xor(t, 32);
-    }
-
     __device__ __forceinline__ void store_final(const DecodeArgs &a, int b, int g) {
-        const float lt = row_sum();
+        const float lt = rows4_sum(l);
         if (col >= G) return;
         const int h = g * G + col;
         const float inv = 1.f / lt;
@@ -447,32 +681,120 @@ struct EngBf16 {
             uint32_t wv[VW];
 #pragma unroll
             for (int w = 0; w < VW; ++w) wv[w] = pack_bf16x2(acc[2 * w][i] * inv, acc[2 * w + 1][i] * inv);
-            uint16_t *dst = o + DPL * (4 * quad + i);
-            if constexpr (VW == 2) {
-                *reinterpret_cast<u32x2 *>(dst) = u32x2{wv[0], wv[1]};
-            } else {
-#pragma unroll
-                for (int c4 = 0; c4 < VW / 4; ++c4)
-                    st16(dst + 8 * c4, u32x4{wv[4 * c4], wv[4 * c4 + 1], wv[4 * c4 + 2], wv[4 * c4 + 3]});
-            }
+            store_vrow((char *)(o + DPL * (4 * quad + i)), wv);
         }
         if (quad == 0 && a.lse) a.lse[(int64_t)b * a.hq + h] = (m + log2f(lt)) * kLn2;
     }
 
-    __device__ __forceinline__ void store_partial(const DecodeArgs &a, int64_t rec) {
-        const float lt = row_sum();
+    __device__ __forceinline__ void store_record(const DecodeArgs &a, int64_t rec, const f32x4 (&o4)[DPL], float mm,
+                                                 float ll) {
+        const float lt = rows4_sum(ll);
         if (col >= G) return;
-        float *o = a.part_o + (rec * G + col) * D;
+        float *o = a.part_o + rec * G * D;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < DPL; j += 2) st_shared2(o + DPL * (4 * quad + i) + j, acc[j][i], acc[j + 1][i]);
-        if (quad == 0) st_shared2(a.part_ml + (rec * G + col) * 2, m, lt);
+            for (int jj = 0; jj < VW; ++jj)
+                st_shared2(o + ((i * VW + jj) * 4 * G + quad * G + col) * 2, o4[2 * jj][i], o4[2 * jj + 1][i]);
+        if (quad == 0) st_shared2(a.part_ml + (rec * G + col) * 2, mm, lt);
     }
+    __device__ __forceinline__ void store_partial(const DecodeArgs &a, int64_t rec) { store_record(a, rec, acc, m, l); }
+
+    // Keep the state for a record written after the range (record stores
+    // complete at memory, and loads issued behind them would wait for that).
+    __device__ __forceinline__ void save() {
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) sacc[j] = acc[j];
+        sm = m;
+        sl = l;
+    }
+    __device__ __forceinline__ void store_saved(const DecodeArgs &a, int64_t rec) { store_record(a, rec, sacc, sm, sl); }
 };
 
+// End of a piece: its output, or its record (then the merge is pending).
+// With more pages to follow, a record is kept in registers and written
+// after the range.
+template <class Eng>
+__device__ __forceinline__ void finish_piece(const DecodeArgs &a, Eng &eng, const Desc &d, int w, const Range &r,
+                                             Pending &pend, bool more) {
+    if (d.whole) {
+        eng.store_final(a, d.b, d.g);
+    } else {
+        const int64_t s = (int64_t)d.b * a.hkv + d.g;
+        if (more) {
+            eng.save();
+            pend.saved = 1;
+        } else {
+            eng.store_partial(a, (int64_t)w + s);
+        }
+        const int64_t wf = worker_of(d.segf, r);
+        const int cnt = (int)(worker_of(d.segf + d.np - 1, r) - wf + 1);
+        pending_add(pend, s, d.b, d.g, wf, cnt);
+    }
+    eng.reset();
+}
+
+template <int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D <= 128 ? PKV_DECODE_WAVES_PER_EU : 1)))
+void decode_bf16_kernel(DecodeArgs a) {
+    using Eng = Bf16<D>;
+    __shared__ int ids[kStage];
+    const int w = blockIdx.x;
+    RowLens rl;
+    Range r;
+    if (!plan<__bf16>(a, w, D, rl, r)) return;
+    Cursor cur;
+    locate(a, r.f0, rl, cur.s);
+    cur.p = cur.pstart = (int)(r.f0 - cur.s.f);
+    cur.pend = (int)(cur.s.np < r.f1 - cur.s.f ? cur.s.np : r.f1 - cur.s.f);
+    cur.live = 1;
+    int64_t fbase = r.f0;
+    stage(a, ids, cur, r.f1, rl);
+    Eng eng;
+    eng.init(a);
+    Pending pend;
+    pend.n = pend.saved = 0;
+    const float c = a.scale_log2;
+    typename Eng::Buf b0, b1;
+    Desc d0, d1;
+    take(a, cur, ids, fbase, r.f1, rl, d0);
+    eng.issue(a, d0, b0);
+    // Two buffers in turn: the next pair's loads are issued before the
+    // current pair is computed, and no load is left unconsumed at the end, so
+    // the compiler's wait counts stay exact across iterations.  The
+    // scheduling barriers keep the loads ahead of the compute.
+    for (;;) {
+        if (cur.live) {
+            take(a, cur, ids, fbase, r.f1, rl, d1);
+            __builtin_amdgcn_sched_barrier(0);
+            eng.issue(a, d1, b1);
+            __builtin_amdgcn_sched_barrier(0);
+            eng.compute(a, b0, d0, c);
+            if (d0.last) finish_piece(a, eng, d0, w, r, pend, true);
+        } else {
+            eng.compute(a, b0, d0, c);
+            if (d0.last) finish_piece(a, eng, d0, w, r, pend, false);
+            break;
+        }
+        if (cur.live) {
+            take(a, cur, ids, fbase, r.f1, rl, d0);
+            __builtin_amdgcn_sched_barrier(0);
+            eng.issue(a, d0, b0);
+            __builtin_amdgcn_sched_barrier(0);
+            eng.compute(a, b1, d1, c);
+            if (d1.last) finish_piece(a, eng, d1, w, r, pend, true);
+        } else {
+            eng.compute(a, b1, d1, c);
+            if (d1.last) finish_piece(a, eng, d1, w, r, pend, false);
+            break;
+        }
+    }
+    if (pend.saved) eng.store_saved(a, (int64_t)w + pend.s0);
+    settle<__bf16, Eng, D>(a, pend);
+}
+
 // ---------------------------------------------------------------------------
-// fp32 engine: MFMA 16x16x4 f32, one page per step
+// fp32: MFMA 16x16x4 f32, one page per step (no fused append)
 // ---------------------------------------------------------------------------
 
 template <int D>
@@ -485,6 +807,9 @@ struct EngF32 {
     f32x4 acc[DC];
     float m, l;
     int G, quad, col;
+
+    // Output dim of record pair (t, quad): acc[dc][2ii], acc[dc][2ii+1] with t = 2dc + ii.
+    __device__ static __forceinline__ int dim_of(int t, int quad) { return 16 * (t >> 1) + 4 * quad + 2 * (t & 1); }
 
     __device__ __forceinline__ void init(const DecodeArgs &a, int b, int g) {
         G = a.hq / a.hkv;
@@ -519,10 +844,8 @@ struct EngF32 {
             float x[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) x[i] = (4 * quad + i < vc) ? s[i] * c : kNegInf;
-            float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-            mx = fmaxf(mx, shfl_xor(mx, 16));
-            mx = fmaxf(mx, shfl_xor(mx, 32));
-            const float mn = fmaxf(m, mx);
+            const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+            const float mn = fmaxf(m, rows4_max(mx));
             const float alpha = fast_exp2(m - mn);
             float pr[4], sum = 0.f;
 #pragma unroll
@@ -549,13 +872,8 @@ struct EngF32 {
     }
 
     // acc[dc][i] is O^T[dim 16dc + 4quad + i][head col].
-    __device__ __forceinline__ float row_sum() const {
-        float t = l + shfl_xor(l, 16);
-        return t + shfl_xor(t, 32);
-    }
-
     __device__ __forceinline__ void store_final(const DecodeArgs &a, int b, int g) {
-        const float lt = row_sum();
+        const float lt = rows4_sum(l);
         if (col >= G) return;
         const int h = g * G + col;
         float *o = (float *)a.out + ((int64_t)b * a.hq + h) * D;
@@ -565,87 +883,62 @@ struct EngF32 {
     }
 
     __device__ __forceinline__ void store_partial(const DecodeArgs &a, int64_t rec) {
-        const float lt = row_sum();
+        const float lt = rows4_sum(l);
         if (col >= G) return;
-        float *o = a.part_o + (rec * G + col) * D;
+        float *o = a.part_o + rec * G * D;
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) {
-            st_shared2(o + 16 * dc + 4 * quad, acc[dc][0], acc[dc][1]);
-            st_shared2(o + 16 * dc + 4 * quad + 2, acc[dc][2], acc[dc][3]);
+            st_shared2(o + ((2 * dc) * 4 * G + quad * G + col) * 2, acc[dc][0], acc[dc][1]);
+            st_shared2(o + ((2 * dc + 1) * 4 * G + quad * G + col) * 2, acc[dc][2], acc[dc][3]);
         }
         if (quad == 0) st_shared2(a.part_ml + (rec * G + col) * 2, m, lt);
     }
 };
 
-// ---------------------------------------------------------------------------
-// kernel
-// ---------------------------------------------------------------------------
-
-// Resident waves per SIMD the register allocation is capped to (head_dim <= 128).
-template <class Eng, int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D <= 128 ? PKV_DECODE_WAVES_PER_EU : 1)))
-void decode_kernel(DecodeArgs a) {
-    using OutT = typename Eng::Out;
+template <int D>
+__global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
+    using Eng = EngF32<D>;
     const int w = blockIdx.x;
+    RowLens rl;
     Range r;
-    if (!worker_range<OutT>(a, w, D, r)) return;
-    int b;
-    int64_t seq_start;
-    locate(a, r.f0, b, seq_start);
-    int n = uniform(row_len(a, b));
-    int np = ceil_div(n, kPage);
-    const int64_t off = r.f0 - seq_start;
-    int g = (int)(off / np);
-    int p0 = (int)(off - (int64_t)g * np);
+    if (!plan<float>(a, w, D, rl, r)) return;
+    Seg s;
+    locate(a, r.f0, rl, s);
+    int p0 = (int)(r.f0 - s.f);
     int64_t f = r.f0;
     Eng eng;
+    Pending pend;
+    pend.n = pend.saved = 0;
     for (;;) {
-        const int64_t seg_start = f - p0;
         const int64_t left = r.f1 - f;
-        const int p1 = left < (int64_t)(np - p0) ? p0 + (int)left : np;
-        const int64_t s = (int64_t)b * a.hkv + g;
-        eng.init(a, b, g);
-        eng.run(a, b, g, n, p0, p1);
-        if (p0 == 0 && p1 == np) {
-            eng.store_final(a, b, g);
+        const int p1 = left < (int64_t)(s.np - p0) ? p0 + (int)left : s.np;
+        eng.init(a, s.b, s.g);
+        eng.run(a, s.b, s.g, s.n, p0, p1);
+        if (p0 == 0 && p1 == s.np) {
+            eng.store_final(a, s.b, s.g);
         } else {
-            eng.store_partial(a, (int64_t)w + s);
-            const int64_t wf = worker_of(seg_start, r);
-            const int cnt = (int)(worker_of(seg_start + np - 1, r) - wf + 1);
-            wait_stores_complete();  // the record is visible before it is counted
-            int prior = 0;
-            if (lane_id() == 0)
-                prior = __hip_atomic_fetch_add(a.arrivals + s, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            prior = __shfl(prior, 0, kWave);
-            if (prior == cnt - 1) {  // last piece of this segment: merge all of them
-                merge_segment<OutT, D>(a, s, b, g, wf, cnt);
-                if (lane_id() == 0)
-                    __hip_atomic_store(a.arrivals + s, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            const int64_t seg = (int64_t)s.b * a.hkv + s.g;
+            eng.store_partial(a, (int64_t)w + seg);
+            const int64_t wf = worker_of(s.f, r);
+            pending_add(pend, seg, s.b, s.g, wf, (int)(worker_of(s.f + s.np - 1, r) - wf + 1));
         }
         f += p1 - p0;
         if (f >= r.f1) break;
+        seg_next(a, s, rl);
         p0 = 0;
-        if (++g == a.hkv) {
-            g = 0;
-            do {
-                ++b;
-                n = uniform(row_len(a, b));
-                np = ceil_div(n, kPage);
-            } while (np == 0);
-        }
     }
+    settle<float, Eng, D>(a, pend);
 }
 
 const void *pick_kernel(int dtype, int d) {
     if (dtype == 1) {
-        if (d == 64) return reinterpret_cast<const void *>(&decode_kernel<EngBf16<64>, 64>);
-        if (d == 128) return reinterpret_cast<const void *>(&decode_kernel<EngBf16<128>, 128>);
-        if (d == 256) return reinterpret_cast<const void *>(&decode_kernel<EngBf16<256>, 256>);
+        if (d == 64) return reinterpret_cast<const void *>(&decode_bf16_kernel<64>);
+        if (d == 128) return reinterpret_cast<const void *>(&decode_bf16_kernel<128>);
+        if (d == 256) return reinterpret_cast<const void *>(&decode_bf16_kernel<256>);
     } else {
-        if (d == 64) return reinterpret_cast<const void *>(&decode_kernel<EngF32<64>, 64>);
-        if (d == 128) return reinterpret_cast<const void *>(&decode_kernel<EngF32<128>, 128>);
-        if (d == 256) return reinterpret_cast<const void *>(&decode_kernel<EngF32<256>, 256>);
+        if (d == 64) return reinterpret_cast<const void *>(&decode_f32_kernel<64>);
+        if (d == 128) return reinterpret_cast<const void *>(&decode_f32_kernel<128>);
+        if (d == 256) return reinterpret_cast<const void *>(&decode_f32_kernel<256>);
     }
     return nullptr;
 }

@@ -46,6 +46,12 @@ struct DecodeArgs {
     float *part_o;      // [(workers + batch*hkv) * group * head_dim]
     float *part_ml;     // [(workers + batch*hkv) * group * 2]
     int32_t *arrivals;  // [batch*hkv]: pieces finished per split row; zero between calls
+    // Fused append (bf16 only): when k_new is set, seqlens holds the pre-append
+    // lengths L, each row attends L+1 keys, and the token at position L is taken
+    // from k_new / v_new [batch, hkv, head_dim] and written into the pool.
+    const void *k_new;
+    const void *v_new;
+    int32_t *seqlens_out;  // nullable: L+1 per row (fused mode only)
 };
 
 // Workers the decode kernel uses on `device` when the caller asks for

@@ -127,18 +127,29 @@ size_t pkv_decode_workspace_bytes(const pkv_cache_desc *cache, int32_t batch, in
     return pkv_decode_workspace_bytes_ex(cache, batch, num_q_heads, max_kv_len, 0);
 }
 
-pkv_status pkv_decode_attn_ex(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
-                              int32_t num_q_heads, const void *k_cache, const void *v_cache,
-                              const int32_t *block_table, int32_t bt_cols, const int32_t *cache_seqlens,
-                              int32_t batch, int32_t max_kv_len, float scale, void *workspace,
-                              size_t workspace_bytes, int32_t workers, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Decode, optionally with the step's token appended in the same launch
+// (k_new != NULL).
+pkv_status decode_common(const pkv_cache_desc *cache, void *out, float *lse, const void *q, int32_t num_q_heads,
+                         const void *k_cache, const void *v_cache, const void *k_new, const void *v_new,
+                         const int32_t *block_table, int32_t bt_cols, const int32_t *cache_seqlens,
+                         int32_t *seqlens_out, int32_t batch, int32_t max_kv_len, float scale, void *workspace,
+                         size_t workspace_bytes, int32_t workers, void *stream) {
     PoolGeom g;
     pkv_status st = check_desc(cache, &g);
     if (st) return st;
     if ((st = check_heads(g, num_q_heads))) return st;
+    const bool fused = k_new != nullptr || v_new != nullptr;
+    if (fused && g.dtype != 1) return PKV_EUNSUPPORTED;
     if (batch < 0 || max_kv_len < 0 || bt_cols < 0 || workers < 0) return PKV_EINVAL;
+    if (fused && (!k_new || !v_new)) return PKV_EINVAL;
+    if (seqlens_out && (!fused || seqlens_out == cache_seqlens)) return PKV_EINVAL;
     if (batch == 0) return PKV_OK;
     if (!out || !q || !k_cache || !v_cache || !block_table || !cache_seqlens) return PKV_EINVAL;
+    if (fused && (!aligned16(k_new) || !aligned16(v_new))) return PKV_EUNSUPPORTED;
     if ((int64_t)max_kv_len > (int64_t)bt_cols * kPageSize) return PKV_EINVAL;
     if (!isfinite(scale)) return PKV_EINVAL;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
@@ -173,7 +184,47 @@ pkv_status pkv_decode_attn_ex(const pkv_cache_desc *cache, void *out, float *lse
     a.part_o = (float *)workspace;
     a.part_ml = nullptr;
     a.arrivals = nullptr;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.seqlens_out = seqlens_out;
     return launch_status(pkv::launch_decode(g, a, max_kv_len, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_decode_attn_ex(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
+                              int32_t num_q_heads, const void *k_cache, const void *v_cache,
+                              const int32_t *block_table, int32_t bt_cols, const int32_t *cache_seqlens,
+                              int32_t batch, int32_t max_kv_len, float scale, void *workspace,
+                              size_t workspace_bytes, int32_t workers, void *stream) {
+    return decode_common(cache, out, lse, q, num_q_heads, k_cache, v_cache, nullptr, nullptr, block_table,
+                         bt_cols, cache_seqlens, nullptr, batch, max_kv_len, scale, workspace, workspace_bytes,
+                         workers, stream);
+}
+
+pkv_status pkv_append_decode_attn_ex(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
+                                     int32_t num_q_heads, void *k_cache, void *v_cache, const void *k_new,
+                                     const void *v_new, const int32_t *block_table, int32_t bt_cols,
+                                     const int32_t *cache_seqlens, int32_t *seqlens_out, int32_t batch,
+                                     int32_t max_kv_len, float scale, void *workspace, size_t workspace_bytes,
+                                     int32_t workers, void *stream) {
+    if (!k_new || !v_new) return PKV_EINVAL;
+    return decode_common(cache, out, lse, q, num_q_heads, k_cache, v_cache, k_new, v_new, block_table, bt_cols,
+                         cache_seqlens, seqlens_out, batch, max_kv_len, scale, workspace, workspace_bytes, workers,
+                         stream);
+}
+
+pkv_status pkv_append_decode_attn(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
+                                  int32_t num_q_heads, void *k_cache, void *v_cache, const void *k_new,
+                                  const void *v_new, const int32_t *block_table, int32_t bt_cols,
+                                  const int32_t *cache_seqlens, int32_t *seqlens_out, int32_t batch,
+                                  int32_t max_kv_len, float scale, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+    return pkv_append_decode_attn_ex(cache, out, lse, q, num_q_heads, k_cache, v_cache, k_new, v_new, block_table,
+                                     bt_cols, cache_seqlens, seqlens_out, batch, max_kv_len, scale, workspace,
+                                     workspace_bytes, 0, stream);
 }
 
 pkv_status pkv_decode_attn(const pkv_cache_desc *cache, void *out, float *lse, const void *q,

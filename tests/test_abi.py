@@ -93,6 +93,22 @@ def test_append_rejects_scalars():
     assert call(desc=_desc(head_dim=32)) == EUNSUPPORTED
 
 
+def test_fused_decode_rejects_scalars():
+    d = _desc()
+    lib = api.lib()
+    SEQ = ctypes.c_void_p((1 << 20) + 4096)
+    call = lambda **kw: lib.pkv_append_decode_attn(
+        ctypes.byref(kw.get("desc", d)), FAKE, None, FAKE, 32, FAKE, FAKE, kw.get("k_new", FAKE),
+        kw.get("v_new", FAKE), FAKE, 4, SEQ, kw.get("out", None), kw.get("batch", 4), 64, 0.1, FAKE, 1 << 30, None)
+    assert call(k_new=None) == EINVAL
+    assert call(v_new=None) == EINVAL
+    assert call(out=SEQ) == EINVAL                   # seqlens_out aliases cache_seqlens
+    assert call(batch=0) == OK
+    assert call(k_new=ctypes.c_void_p((1 << 20) + 8)) == EUNSUPPORTED  # misaligned
+    f32 = _desc(dtype=api.PKV_F32)
+    assert call(desc=f32) == EUNSUPPORTED            # fused append is bf16 only
+
+
 def test_prefill_rejects_scalars():
     lib = api.lib()
     call = lambda desc, **kw: lib.pkv_prefill_attn(
