@@ -90,6 +90,15 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
     return __builtin_bit_cast(float, bits16 << 16);
 }
 
+// Raw buffer resources (gfx9 descriptor, no stride): a wave-uniform base in
+// scalar registers, a 32-bit per-lane byte offset, and a byte range outside
+// which loads return zero.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, int32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bld16(Rsrc r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0); }
+
 // 16-byte global load / store.
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ u32x2 ld8(const void *p) { return *reinterpret_cast<const u32x2 *>(p); }

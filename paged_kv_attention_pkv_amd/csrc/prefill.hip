@@ -66,34 +66,42 @@ struct TileRegs {
     u32x4 k[CHUNKS], v[CHUNKS];
 };
 
+// The 64 lanes of one wave-instruction load chunks of consecutive keys that
+// lie in one page, so each instruction goes through that page's buffer
+// resource; its byte range stops at the page's last valid key, so keys at or
+// past kv (and whole pages past it) load as zeros, without branches.
 template <int D>
 __device__ __forceinline__ void load_tile(const PrefillArgs &a, const int32_t *bt, int g, int tile, int kv,
                                           TileRegs<D> &t) {
-    const int tid = threadIdx.x;
-    const int blk0 = tile * (kBN / kPage);
-    const int nblk = (kv + kPage - 1) / kPage;
-    int page[kBN / kPage];
+    constexpr int CPK = D / 8;  // 16-byte chunks per key row
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int64_t tok_bytes = a.s_tok * 2;
+    Rsrc rk[kBN / kPage], rv[kBN / kPage];
 #pragma unroll
     for (int u = 0; u < kBN / kPage; ++u) {
-        const int p = blk0 + u < nblk ? bt[blk0 + u] : 0;
-        page[u] = p < 0 ? 0 : (p >= a.num_pages ? a.num_pages - 1 : p);
+        const int blk = tile * (kBN / kPage) + u;
+        const int valid = min(max(kv - blk * kPage, 0), kPage);
+        int pg = valid > 0 ? bt[blk] : 0;
+        pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+        const int64_t off = ((int64_t)pg * a.s_page + (int64_t)g * a.s_head) * 2;
+        const int32_t bytes = (int32_t)(valid * tok_bytes);
+        rk[u] = make_rsrc((const char *)a.k_cache + off, bytes);
+        rv[u] = make_rsrc((const char *)a.v_cache + off, bytes);
     }
 #pragma unroll
     for (int i = 0; i < TileRegs<D>::CHUNKS; ++i) {
-        const int c = tid + kThreads * i;
-        const int key = c / (D / 8);
-        const int d8 = c - key * (D / 8);
-        const int j = tile * kBN + key;
-        u32x4 z = {0u, 0u, 0u, 0u};
-        if (j < kv) {
-            const int pg = page[key >> 4];
-            const int64_t off = pg * a.s_page + g * a.s_head + (int64_t)(key & 15) * a.s_tok + d8 * 8;
-            t.k[i] = ld16((const uint16_t *)a.k_cache + off);
-            t.v[i] = ld16((const uint16_t *)a.v_cache + off);
-        } else {
-            t.k[i] = z;
-            t.v[i] = z;
-        }
+        const int c0 = kWave * wave + kThreads * i;  // first chunk of this wave-instruction
+        const int u = uniform((c0 / CPK) >> 4);      // its page within the tile
+        const int c = c0 + lane;
+        const int key = c / CPK;
+        const uint32_t voff = (uint32_t)((key & 15) * tok_bytes) + (uint32_t)(c - key * CPK) * 16u;
+        Rsrc k = rk[0], v = rv[0];
+#pragma unroll
+        for (int w = 1; w < kBN / kPage; ++w)
+            if (u == w) k = rk[w], v = rv[w];
+        t.k[i] = bld16(k, voff);
+        t.v[i] = bld16(v, voff);
     }
 }
 
