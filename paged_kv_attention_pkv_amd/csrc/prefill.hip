@@ -212,16 +212,32 @@ void prefill_kernel(PrefillArgs a, int n_qtiles) {
         if (tile * kBN <= last_key_wave) {
             const uint16_t *ks = cur;
             const uint16_t *vs = cur + S::TILE;
-            // S^T = K . Q^T, one 32x32 block per 32 keys
+            // S^T = K . Q^T, one 32x32 block per 32 keys.  K operands are read
+            // from LDS in groups (k-steps k0, k0+1 of both key blocks, so
+            // consecutive MFMAs alternate accumulators), the next group's reads
+            // issued before the current group's MFMAs.
             f32x16 sc[NS];
 #pragma unroll
-            for (int u = 0; u < NS; ++u) {
-                sc[u] = f32x16{};
+            for (int u = 0; u < NS; ++u) sc[u] = f32x16{};
+            constexpr int KG = 2;                 // k-steps per group
+            constexpr int GN = NS * KG;           // operands per group
+            constexpr int NGRP = KS / KG;
+            u32x4 kb[2][GN];
+            auto read_group = [&](int gi, u32x4 (&dst)[GN]) {
 #pragma unroll
-                for (int k = 0; k < KS; ++k) {
-                    const u32x4 kop =
-                        *reinterpret_cast<const u32x4 *>(ks + (32 * u + col) * S::STRIDE + 16 * k + 8 * half);
-                    sc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kop),
+                for (int j = 0; j < GN; ++j) {
+                    const int u = j % NS, k = gi * KG + j / NS;
+                    dst[j] = *reinterpret_cast<const u32x4 *>(ks + (32 * u + col) * S::STRIDE + 16 * k + 8 * half);
+                }
+            };
+            read_group(0, kb[0]);
+#pragma unroll
+            for (int gi = 0; gi < NGRP; ++gi) {
+                if (gi + 1 < NGRP) read_group(gi + 1, kb[(gi + 1) & 1]);
+#pragma unroll
+                for (int j = 0; j < GN; ++j) {
+                    const int u = j % NS, k = gi * KG + j / NS;
+                    sc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kb[gi & 1][j]),
                                                                     __builtin_bit_cast(bf16x8, qop[k]), sc[u], 0, 0,
                                                                     0);
                 }
@@ -267,19 +283,33 @@ void prefill_kernel(PrefillArgs a, int n_qtiles) {
                                            pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
                 }
             l += sum;
-            // O^T += V^T . P^T; per 16-key step tt: keys 16tt + 4half .. +3 and 16tt + 8 + 4half .. +3
+            // O^T += V^T . P^T; per 16-key step tt: keys 16tt + 4half .. +3 and
+            // 16tt + 8 + 4half .. +3.  V^T operands are read (transposing
+            // reads) in groups of VG output blocks, the next group's reads
+            // issued before the current group's MFMAs.
+            constexpr int VG = DB < 4 ? DB : 4;
+            constexpr int NVG = 2 * NS * (DB / VG);
+            u32x4 vb[2][VG];
+            auto read_v = [&](int gi, u32x4 (&dst)[VG]) {
+                const int tt = gi / (DB / VG), db0 = (gi % (DB / VG)) * VG;
 #pragma unroll
-            for (int tt = 0; tt < 2 * NS; ++tt) {
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const uint16_t *base = vs + (16 * tt + tr_key) * S::STRIDE + 32 * db + tr_dim;
+                for (int j = 0; j < VG; ++j) {
+                    const uint16_t *base = vs + (16 * tt + tr_key) * S::STRIDE + 32 * (db0 + j) + tr_dim;
                     const u32x2 lo = ld_tr(base);
                     const u32x2 hi = ld_tr(base + 8 * S::STRIDE);
-                    const u32x4 vop = {lo[0], lo[1], hi[0], hi[1]};
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vop),
-                                                                      __builtin_bit_cast(bf16x8, pop[tt]), acc[db],
-                                                                      0, 0, 0);
+                    dst[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
                 }
+            };
+            read_v(0, vb[0]);
+#pragma unroll
+            for (int gi = 0; gi < NVG; ++gi) {
+                if (gi + 1 < NVG) read_v(gi + 1, vb[(gi + 1) & 1]);
+                const int tt = gi / (DB / VG), db0 = (gi % (DB / VG)) * VG;
+#pragma unroll
+                for (int j = 0; j < VG; ++j)
+                    acc[db0 + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, vb[gi & 1][j]), __builtin_bit_cast(bf16x8, pop[tt]), acc[db0 + j],
+                        0, 0, 0);
             }
         }
         if (more) {
