@@ -223,9 +223,13 @@ def bench_decode(args, torch, pkv, wl):
     app_mean = None if fused else events_per_call(torch, [a for a, _, _ in layers])[0]
     kv_bytes_step = acc["kv"] * L
     value = kv_bytes_step / (ms * 1e-3) / 1e9
-    achieved = acc["total"] / (dec_mean * 1e-3) / 1e9
+    # the kernel's average launch duration: in the fused step the timed region
+    # holds exactly L launches of it (HIP events around the graph replays);
+    # in the two-launch step, per-call event brackets of the decode launches
+    launch_ms = ms / L if fused else dec_mean
+    achieved = acc["total"] / (launch_ms * 1e-3) / 1e9
     traffic = traffic_from_profile(os.path.join(ROOT, "paged_kv_attention_pkv_amd", "csrc", "decode.hip"),
-                                   f"decode_kernel_{spec.name}_pmc.txt")
+                                   f"decode_kernel_{spec.name}_pmc.txt") if fused else None
     result = {
         "metric": "paged decode attn: KV-read GB/s (% HBM peak) + us/call at B=64, Hq32/Hkv8/D128",
         "value": round(value, 1),
@@ -249,6 +253,7 @@ def bench_decode(args, torch, pkv, wl):
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "decode_us_per_call_events": round(dec_mean * 1e3, 2),
         "append_us_per_call_events": None if app_mean is None else round(app_mean * 1e3, 2),
+        "kernel_us_per_launch": round(launch_ms * 1e3, 2),
         "roofline": {"bound": "hbm",
                      "kernel": "decode_bf16_kernel (one launch per pkv_append_decode_attn)" if fused
                      else "decode kernel (one launch per pkv_decode_attn)",
@@ -317,7 +322,7 @@ def bench_prefill(args, torch, pkv, wl):
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     call = pkv.api.prepare_prefill(inp.q, kc, vc, inp.block_table, kv_lens, inp.qo_indptr, max_q, max_kv, out, ws)
     ms, _ = time_steps(torch, call, args.steps, args.warmup, not args.eager)
-    mean, _ = events_per_call(torch, [call] * 8)
+    mean = ms  # one launch per step: the timed region's HIP events give its average duration
     tfs = flops / (mean * 1e-3) / 1e12
     traffic = traffic_from_profile(os.path.join(ROOT, "paged_kv_attention_pkv_amd", "csrc", "prefill.hip"),
                                    f"prefill_kernel_{spec.name}_pmc.txt")
