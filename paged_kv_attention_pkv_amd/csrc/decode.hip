@@ -245,20 +245,31 @@ __device__ __forceinline__ void store_out_pair<float>(float *p, float x, float y
     *reinterpret_cast<f32x2 *>(p) = f32x2{x, y};
 }
 
-// Merge the partial records of split segment s (pieces of workers wf ..
-// wf+cnt-1, record ids w + s) in piece order and write its output rows.
+// One split segment to merge: pieces of workers wf .. wf+cnt-1, record ids
+// w + s, output row b, kv head g.
+struct MergeJob {
+    int64_t s, wf;
+    int b, g, cnt;
+};
+
+// Merge the partial records of NJ split segments (NJ = 1, or 2 when their
+// pieces fit in one batch) in piece order and write their output rows.
 // Pieces are taken 8 at a time with every load of a batch issued before any
-// is used, and batches are folded with the log-sum-exp rule.
-template <typename OutT, class Eng, int D>
-__device__ void merge_segment(const DecodeArgs &a, int64_t s, int b, int g, int64_t wf, int cnt) {
+// is used, so two segments merged together have all their loads in flight at
+// once.  A segment's arithmetic (batches, order of the folds) is the same
+// whether it is merged alone or beside another, so results do not depend on
+// which wave merges it.  Batches are folded with the log-sum-exp rule.
+template <typename OutT, class Eng, int D, int NJ>
+__device__ void merge_jobs(const DecodeArgs &a, const MergeJob *job) {
     constexpr int kBatch = 8, kPairs = 4;
     const int G = a.hq / a.hkv;
     const int npairs = G * D / 2;
     const int64_t ostride = (int64_t)G * D;
-    OutT *out = (OutT *)a.out + ((int64_t)b * a.hq + (int64_t)g * G) * D;
+    const int c0 = job[0].cnt;
+    const int total = NJ == 1 ? c0 : c0 + job[NJ - 1].cnt;
     for (int u0 = 0; u0 < npairs; u0 += kWave * kPairs) {
         int uu[kPairs], col[kPairs], dim[kPairs];
-        float M[kPairs], den[kPairs], n0[kPairs], n1[kPairs];
+        float M[NJ][kPairs], den[NJ][kPairs], n0[NJ][kPairs], n1[NJ][kPairs];
 #pragma unroll
         for (int k = 0; k < kPairs; ++k) {
             const int u = u0 + k * kWave + lane_id();
@@ -268,16 +279,23 @@ __device__ void merge_segment(const DecodeArgs &a, int64_t s, int b, int g, int6
             const int quad = rem / G;
             col[k] = rem - quad * G;
             dim[k] = Eng::dim_of(t, quad);
-            M[k] = kNegInf;
-            den[k] = n0[k] = n1[k] = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < NJ; ++jj) {
+                M[jj][k] = kNegInf;
+                den[jj][k] = n0[jj][k] = n1[jj][k] = 0.f;
+            }
         }
-        for (int k0 = 0; k0 < cnt; k0 += kBatch) {
-            const int nb = min(kBatch, cnt - k0);
+        for (int k0 = 0; k0 < total; k0 += kBatch) {
+            const int nb = min(kBatch, total - k0);
             f32x2 ml[kBatch][kPairs], o[kBatch][kPairs];
+            int owner[kBatch];  // job of batch entry j (wave-uniform)
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
+                const int q = k0 + j;
+                owner[j] = j >= nb ? -1 : (NJ == 2 && q >= c0 ? 1 : 0);
                 if (j < nb) {
-                    const int64_t rec = wf + k0 + j + s;
+                    const int64_t rec = owner[j] == 0 ? job[0].wf + q + job[0].s
+                                                      : job[NJ - 1].wf + (q - c0) + job[NJ - 1].s;
 #pragma unroll
                     for (int k = 0; k < kPairs; ++k) {
                         ml[j][k] = ld_shared2(a.part_ml + (rec * G + col[k]) * 2);
@@ -287,33 +305,42 @@ __device__ void merge_segment(const DecodeArgs &a, int64_t s, int b, int g, int6
             }
 #pragma unroll
             for (int k = 0; k < kPairs; ++k) {
-                float Mb = M[k];
 #pragma unroll
-                for (int j = 0; j < kBatch; ++j)
-                    if (j < nb) Mb = fmaxf(Mb, ml[j][k][0]);
-                const float r = fast_exp2(M[k] - Mb);
-                den[k] *= r;
-                n0[k] *= r;
-                n1[k] *= r;
+                for (int jj = 0; jj < NJ; ++jj) {
+                    float Mb = M[jj][k];
 #pragma unroll
-                for (int j = 0; j < kBatch; ++j) {
-                    if (j < nb) {
-                        const float wgt = fast_exp2(ml[j][k][0] - Mb);
-                        den[k] += wgt * ml[j][k][1];
-                        n0[k] += wgt * o[j][k][0];
-                        n1[k] += wgt * o[j][k][1];
+                    for (int j = 0; j < kBatch; ++j)
+                        if (owner[j] == jj) Mb = fmaxf(Mb, ml[j][k][0]);
+                    const float r = fast_exp2(M[jj][k] - Mb);
+                    den[jj][k] *= r;
+                    n0[jj][k] *= r;
+                    n1[jj][k] *= r;
+#pragma unroll
+                    for (int j = 0; j < kBatch; ++j) {
+                        if (owner[j] == jj) {
+                            const float wgt = fast_exp2(ml[j][k][0] - Mb);
+                            den[jj][k] = fmaf(wgt, ml[j][k][1], den[jj][k]);
+                            n0[jj][k] = fmaf(wgt, o[j][k][0], n0[jj][k]);
+                            n1[jj][k] = fmaf(wgt, o[j][k][1], n1[jj][k]);
+                        }
                     }
+                    M[jj][k] = Mb;
                 }
-                M[k] = Mb;
             }
         }
 #pragma unroll
-        for (int k = 0; k < kPairs; ++k) {
-            if (u0 + k * kWave + lane_id() < npairs) {
-                const float inv = 1.f / den[k];
-                store_out_pair<OutT>(out + (int64_t)col[k] * D + dim[k], n0[k] * inv, n1[k] * inv);
-                if (dim[k] == 0 && a.lse)
-                    a.lse[(int64_t)b * a.hq + (int64_t)g * G + col[k]] = (M[k] + log2f(den[k])) * kLn2;
+        for (int jj = 0; jj < NJ; ++jj) {
+            const int b = job[jj].b;
+            OutT *out = (OutT *)a.out + ((int64_t)b * a.hq + (int64_t)job[jj].g * G) * D;
+#pragma unroll
+            for (int k = 0; k < kPairs; ++k) {
+                if (u0 + k * kWave + lane_id() < npairs) {
+                    const float inv = 1.f / den[jj][k];
+                    store_out_pair<OutT>(out + (int64_t)col[k] * D + dim[k], n0[jj][k] * inv, n1[jj][k] * inv);
+                    if (dim[k] == 0 && a.lse)
+                        a.lse[(int64_t)b * a.hq + (int64_t)job[jj].g * G + col[k]] =
+                            (M[jj][k] + log2f(den[jj][k])) * kLn2;
+                }
             }
         }
     }
@@ -322,40 +349,41 @@ __device__ void merge_segment(const DecodeArgs &a, int64_t s, int b, int g, int6
 // Split pieces a wave leaves for the merge (at most its first and its last).
 struct Pending {
     int n, saved;  // saved: the first record is still held in registers
-    int64_t s0, s1, wf0, wf1;
-    int cnt0, cnt1, b0, b1, g0, g1;
+    MergeJob job[2];
 };
 
 __device__ __forceinline__ void pending_add(Pending &p, int64_t s, int b, int g, int64_t wf, int cnt) {
-    if (p.n == 0) {
-        p.s0 = s, p.b0 = b, p.g0 = g, p.wf0 = wf, p.cnt0 = cnt;
-    } else {
-        p.s1 = s, p.b1 = b, p.g1 = g, p.wf1 = wf, p.cnt1 = cnt;
-    }
+    MergeJob &j = p.job[p.n == 0 ? 0 : 1];
+    j.s = s, j.b = b, j.g = g, j.wf = wf, j.cnt = cnt;
     ++p.n;
 }
 
 // Count the wave's split pieces in their segments' arrival counters (after
 // its record stores have completed); the last piece of a segment merges it.
+// When the wave is last for both of its segments, the two merges run as one.
 template <typename OutT, class Eng, int D>
 __device__ void settle(const DecodeArgs &a, const Pending &p) {
     if (p.n == 0) return;
     wait_stores_complete();  // the records are visible before they are counted
     int prior0 = 0, prior1 = 0;
     if (lane_id() == 0) {
-        prior0 = __hip_atomic_fetch_add(a.arrivals + p.s0, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        prior0 = __hip_atomic_fetch_add(a.arrivals + p.job[0].s, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (p.n > 1)
-            prior1 = __hip_atomic_fetch_add(a.arrivals + p.s1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            prior1 = __hip_atomic_fetch_add(a.arrivals + p.job[1].s, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     prior0 = __shfl(prior0, 0, kWave);
     prior1 = __shfl(prior1, 0, kWave);
-    if (prior0 == p.cnt0 - 1) {
-        merge_segment<OutT, Eng, D>(a, p.s0, p.b0, p.g0, p.wf0, p.cnt0);
-        if (lane_id() == 0) __hip_atomic_store(a.arrivals + p.s0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last0 = prior0 == p.job[0].cnt - 1;
+    const bool last1 = p.n > 1 && prior1 == p.job[1].cnt - 1;
+    if (last0 && last1 && p.job[0].cnt + p.job[1].cnt <= 8) {
+        merge_jobs<OutT, Eng, D, 2>(a, p.job);
+    } else {
+        if (last0) merge_jobs<OutT, Eng, D, 1>(a, &p.job[0]);
+        if (last1) merge_jobs<OutT, Eng, D, 1>(a, &p.job[1]);
     }
-    if (p.n > 1 && prior1 == p.cnt1 - 1) {
-        merge_segment<OutT, Eng, D>(a, p.s1, p.b1, p.g1, p.wf1, p.cnt1);
-        if (lane_id() == 0) __hip_atomic_store(a.arrivals + p.s1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane_id() == 0) {
+        if (last0) __hip_atomic_store(a.arrivals + p.job[0].s, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (last1) __hip_atomic_store(a.arrivals + p.job[1].s, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -789,7 +817,7 @@ void decode_bf16_kernel(DecodeArgs a) {
             break;
         }
     }
-    if (pend.saved) eng.store_saved(a, (int64_t)w + pend.s0);
+    if (pend.saved) eng.store_saved(a, (int64_t)w + pend.job[0].s);
     settle<__bf16, Eng, D>(a, pend);
 }
 
