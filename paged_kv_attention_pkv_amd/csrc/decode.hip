@@ -258,9 +258,12 @@ struct MergeJob {
 // is used, so two segments merged together have all their loads in flight at
 // once.  A segment's arithmetic (batches, order of the folds) is the same
 // whether it is merged alone or beside another, so results do not depend on
-// which wave merges it.  Batches are folded with the log-sum-exp rule.
+// which wave merges it.  Batches are folded with the log-sum-exp rule.  The
+// merging wave's own piece (piece own_piece of job own_job) may come from
+// LDS (own_o, own_ml: the same record layout and values) instead of memory.
 template <typename OutT, class Eng, int D, int NJ>
-__device__ void merge_jobs(const DecodeArgs &a, const MergeJob *job) {
+__device__ void merge_jobs(const DecodeArgs &a, const MergeJob *job, int own_job = -1, int own_piece = -1,
+                           const float *own_o = nullptr, const float *own_ml = nullptr) {
     constexpr int kBatch = 8, kPairs = 4;
     const int G = a.hq / a.hkv;
     const int npairs = G * D / 2;
@@ -294,12 +297,21 @@ __device__ void merge_jobs(const DecodeArgs &a, const MergeJob *job) {
                 const int q = k0 + j;
                 owner[j] = j >= nb ? -1 : (NJ == 2 && q >= c0 ? 1 : 0);
                 if (j < nb) {
-                    const int64_t rec = owner[j] == 0 ? job[0].wf + q + job[0].s
-                                                      : job[NJ - 1].wf + (q - c0) + job[NJ - 1].s;
+                    const int piece = owner[j] == 0 ? q : q - c0;
+                    if (owner[j] == own_job && piece == own_piece) {
 #pragma unroll
-                    for (int k = 0; k < kPairs; ++k) {
-                        ml[j][k] = ld_shared2(a.part_ml + (rec * G + col[k]) * 2);
-                        o[j][k] = ld_shared2(a.part_o + rec * ostride + 2 * uu[k]);
+                        for (int k = 0; k < kPairs; ++k) {
+                            ml[j][k] = *reinterpret_cast<const f32x2 *>(own_ml + col[k] * 2);
+                            o[j][k] = *reinterpret_cast<const f32x2 *>(own_o + 2 * uu[k]);
+                        }
+                    } else {
+                        const int64_t rec = owner[j] == 0 ? job[0].wf + piece + job[0].s
+                                                          : job[NJ - 1].wf + piece + job[NJ - 1].s;
+#pragma unroll
+                        for (int k = 0; k < kPairs; ++k) {
+                            ml[j][k] = ld_shared2(a.part_ml + (rec * G + col[k]) * 2);
+                            o[j][k] = ld_shared2(a.part_o + rec * ostride + 2 * uu[k]);
+                        }
                     }
                 }
             }
@@ -348,42 +360,103 @@ __device__ void merge_jobs(const DecodeArgs &a, const MergeJob *job) {
 
 // Split pieces a wave leaves for the merge (at most its first and its last).
 struct Pending {
-    int n, saved;  // saved: the first record is still held in registers
+    int n;
     MergeJob job[2];
+    int state[2];  // kStored, kSaved or kHeld
+    int prior[2];  // the count before this piece's arrival (lane 0)
+    int check;     // held job: its arrival count read ahead (lane 0), -1 if not read
 };
+// kStored: record written, not yet counted.  kSaved: the range's first
+// piece, its state copied aside in the engine's registers (record stores are
+// agent-coherent and complete only at memory; loads issued behind them wait
+// for that, so a record written mid-range stalls the page stream).  kHeld:
+// the range's last piece, still in the engine's accumulators.
+constexpr int kStored = 0, kSaved = 1, kHeld = 2;
 
-__device__ __forceinline__ void pending_add(Pending &p, int64_t s, int b, int g, int64_t wf, int cnt) {
-    MergeJob &j = p.job[p.n == 0 ? 0 : 1];
-    j.s = s, j.b = b, j.g = g, j.wf = wf, j.cnt = cnt;
+__device__ __forceinline__ void pending_init(Pending &p) {
+    p.n = 0;
+    p.check = -1;
+}
+
+__device__ __forceinline__ void pending_add(Pending &p, int64_t s, int b, int g, int64_t wf, int cnt, int state) {
+    const MergeJob j{s, wf, b, g, cnt};
+    if (p.n == 0) {
+        p.job[0] = j;
+        p.state[0] = state;
+    } else {
+        p.job[1] = j;
+        p.state[1] = state;
+    }
     ++p.n;
 }
 
-// Count the wave's split pieces in their segments' arrival counters (after
-// its record stores have completed); the last piece of a segment merges it.
-// When the wave is last for both of its segments, the two merges run as one.
+__device__ __forceinline__ int count_arrival(const DecodeArgs &a, int64_t s) {
+    int prior = 0;
+    if (lane_id() == 0) prior = __hip_atomic_fetch_add(a.arrivals + s, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return prior;
+}
+
+// Read ahead the arrival count of the segment of the wave's last piece
+// (issued behind the last pair's loads, looked at after the range).
+__device__ __forceinline__ int peek_arrivals(const DecodeArgs &a, int64_t s) {
+    int v = 0;
+    if (lane_id() == 0) v = __hip_atomic_load(a.arrivals + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return v;
+}
+
+// After the range: write the saved record, then count the pieces (once
+// their record stores have completed); the piece that completes a segment's
+// count merges it.  A held last piece whose segment has every other piece
+// counted already (as read ahead) is merged straight from the registers,
+// through LDS, with no record written and no count taken.  When the wave
+// merges both of its segments, the two merges run as one.
 template <typename OutT, class Eng, int D>
-__device__ void settle(const DecodeArgs &a, const Pending &p) {
+__device__ void settle(const DecodeArgs &a, Eng &eng, Pending &p, int w, float *own_o, float *own_ml) {
     if (p.n == 0) return;
-    wait_stores_complete();  // the records are visible before they are counted
-    int prior0 = 0, prior1 = 0;
-    if (lane_id() == 0) {
-        prior0 = __hip_atomic_fetch_add(a.arrivals + p.job[0].s, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (p.n > 1)
-            prior1 = __hip_atomic_fetch_add(a.arrivals + p.job[1].s, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (Eng::kHolds) {
+        if (p.state[0] == kSaved) {
+            eng.store_saved(a, (int64_t)w + p.job[0].s);
+            p.state[0] = kStored;
+        }
     }
-    prior0 = __shfl(prior0, 0, kWave);
-    prior1 = __shfl(prior1, 0, kWave);
-    const bool last0 = prior0 == p.job[0].cnt - 1;
-    const bool last1 = p.n > 1 && prior1 == p.job[1].cnt - 1;
-    if (last0 && last1 && p.job[0].cnt + p.job[1].cnt <= 8) {
-        merge_jobs<OutT, Eng, D, 2>(a, p.job);
+    const int H = (p.n == 2 ? p.state[1] : p.state[0]) == kHeld ? p.n - 1 : -1;
+    const MergeJob &hj = H == 1 ? p.job[1] : p.job[0];
+    bool fast = false;
+    if constexpr (Eng::kHolds) {
+        if (H >= 0) {
+            const int seen = __shfl(p.check >= 0 ? p.check : peek_arrivals(a, hj.s), 0, kWave);
+            fast = seen == hj.cnt - 1;
+            if (fast) {
+                eng.stage_record(own_o, own_ml);
+                __syncthreads();
+            } else {
+                eng.store_partial(a, (int64_t)w + hj.s);
+                if (H == 1)
+                    p.state[1] = kStored;
+                else
+                    p.state[0] = kStored;
+            }
+        }
+    }
+    const bool st0 = p.state[0] == kStored, st1 = p.n == 2 && p.state[1] == kStored;
+    if (st0 || st1) wait_stores_complete();  // the records are visible before they are counted
+    if (st0) p.prior[0] = count_arrival(a, p.job[0].s);
+    if (st1) p.prior[1] = count_arrival(a, p.job[1].s);
+    bool last[2];
+    last[0] = (H == 0 && fast) || __shfl(p.prior[0], 0, kWave) == p.job[0].cnt - 1;
+    last[1] = p.n == 2 && ((H == 1 && fast) || __shfl(p.prior[1], 0, kWave) == p.job[1].cnt - 1);
+    const int own_job = fast ? H : -1;
+    const int own_piece = fast ? (int)((int64_t)w - hj.wf) : -1;
+    if (p.n == 2 && last[0] && last[1] && p.job[0].cnt + p.job[1].cnt <= 8) {
+        merge_jobs<OutT, Eng, D, 2>(a, p.job, own_job, own_piece, own_o, own_ml);
     } else {
-        if (last0) merge_jobs<OutT, Eng, D, 1>(a, &p.job[0]);
-        if (last1) merge_jobs<OutT, Eng, D, 1>(a, &p.job[1]);
+        if (last[0]) merge_jobs<OutT, Eng, D, 1>(a, &p.job[0], own_job == 0 ? 0 : -1, own_piece, own_o, own_ml);
+        if (p.n == 2 && last[1])
+            merge_jobs<OutT, Eng, D, 1>(a, &p.job[1], own_job == 1 ? 0 : -1, own_piece, own_o, own_ml);
     }
     if (lane_id() == 0) {
-        if (last0) __hip_atomic_store(a.arrivals + p.job[0].s, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (last1) __hip_atomic_store(a.arrivals + p.job[1].s, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (last[0]) __hip_atomic_store(a.arrivals + p.job[0].s, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (last[1]) __hip_atomic_store(a.arrivals + p.job[1].s, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -482,6 +555,7 @@ __device__ __forceinline__ void take(const DecodeArgs &a, Cursor &c, int *ids, i
 template <int D>
 struct Bf16 {
     using Out = __bf16;
+    static constexpr bool kHolds = true;  // can hold its last piece for a merge from registers
     static constexpr int KC = D / 32;   // QK MFMAs per page
     static constexpr int DPL = D / 16;  // V elements per lane per token = PV MFMAs per pair
     static constexpr int VW = DPL / 2;  // dwords per lane per V token row
@@ -496,7 +570,7 @@ struct Bf16 {
 
     f32x4 acc[DPL];
     float m, l;
-    f32x4 sacc[DPL];  // a split piece's state held until the range is done
+    f32x4 sacc[DPL];  // the range's first split piece, written after the range
     float sm, sl;
     int G, quad, col;
     uint32_t koff;     // lane's byte offset in a page for K (token col, dims 8quad..)
@@ -728,8 +802,6 @@ struct Bf16 {
     }
     __device__ __forceinline__ void store_partial(const DecodeArgs &a, int64_t rec) { store_record(a, rec, acc, m, l); }
 
-    // Keep the state for a record written after the range (record stores
-    // complete at memory, and loads issued behind them would wait for that).
     __device__ __forceinline__ void save() {
 #pragma unroll
         for (int j = 0; j < DPL; ++j) sacc[j] = acc[j];
@@ -737,11 +809,25 @@ struct Bf16 {
         sl = l;
     }
     __device__ __forceinline__ void store_saved(const DecodeArgs &a, int64_t rec) { store_record(a, rec, sacc, sm, sl); }
+
+    // The same record, values and layout, written to LDS (o: G*D floats, ml: 2G).
+    __device__ __forceinline__ void stage_record(float *o, float *ml) {
+        const float lt = rows4_sum(l);
+        if (col >= G) return;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int jj = 0; jj < VW; ++jj)
+                *reinterpret_cast<f32x2 *>(o + ((i * VW + jj) * 4 * G + quad * G + col) * 2) =
+                    f32x2{acc[2 * jj][i], acc[2 * jj + 1][i]};
+        if (quad == 0) *reinterpret_cast<f32x2 *>(ml + col * 2) = f32x2{m, lt};
+    }
 };
 
 // End of a piece: its output, or its record (then the merge is pending).
-// With more pages to follow, a record is kept in registers and written
-// after the range.
+// A split piece with more pages to follow (the range's first) is copied
+// aside in registers; the range's last split piece stays in the
+// accumulators.  settle() deals with both after the range.
 template <class Eng>
 __device__ __forceinline__ void finish_piece(const DecodeArgs &a, Eng &eng, const Desc &d, int w, const Range &r,
                                              Pending &pend, bool more) {
@@ -749,15 +835,15 @@ __device__ __forceinline__ void finish_piece(const DecodeArgs &a, Eng &eng, cons
         eng.store_final(a, d.b, d.g);
     } else {
         const int64_t s = (int64_t)d.b * a.hkv + d.g;
-        if (more) {
-            eng.save();
-            pend.saved = 1;
-        } else {
-            eng.store_partial(a, (int64_t)w + s);
-        }
         const int64_t wf = worker_of(d.segf, r);
         const int cnt = (int)(worker_of(d.segf + d.np - 1, r) - wf + 1);
-        pending_add(pend, s, d.b, d.g, wf, cnt);
+        if (more) {
+            eng.save();
+            pending_add(pend, s, d.b, d.g, wf, cnt, kSaved);
+        } else {
+            pending_add(pend, s, d.b, d.g, wf, cnt, kHeld);
+            return;
+        }
     }
     eng.reset();
 }
@@ -767,6 +853,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D <= 128 ? P
 void decode_bf16_kernel(DecodeArgs a) {
     using Eng = Bf16<D>;
     __shared__ int ids[kStage];
+    __shared__ __align__(16) float own_o[16 * D];  // the held piece's record for a merge from registers (G <= 16)
+    __shared__ __align__(16) float own_ml[2 * 16];
     const int w = blockIdx.x;
     RowLens rl;
     Range r;
@@ -781,7 +869,7 @@ void decode_bf16_kernel(DecodeArgs a) {
     Eng eng;
     eng.init(a);
     Pending pend;
-    pend.n = pend.saved = 0;
+    pending_init(pend);
     const float c = a.scale_log2;
     typename Eng::Buf b0, b1;
     Desc d0, d1;
@@ -791,11 +879,15 @@ void decode_bf16_kernel(DecodeArgs a) {
     // current pair is computed, and no load is left unconsumed at the end, so
     // the compiler's wait counts stay exact across iterations.  The
     // scheduling barriers keep the loads ahead of the compute.
+    // After the last pair's loads, the arrival count of its segment is read
+    // ahead when its piece is split (it is then the range's held piece).
+    if (!cur.live && !d0.whole) pend.check = peek_arrivals(a, (int64_t)d0.b * a.hkv + d0.g);
     for (;;) {
         if (cur.live) {
             take(a, cur, ids, fbase, r.f1, rl, d1);
             __builtin_amdgcn_sched_barrier(0);
             eng.issue(a, d1, b1);
+            if (!cur.live && !d1.whole) pend.check = peek_arrivals(a, (int64_t)d1.b * a.hkv + d1.g);
             __builtin_amdgcn_sched_barrier(0);
             eng.compute(a, b0, d0, c);
             if (d0.last) finish_piece(a, eng, d0, w, r, pend, true);
@@ -808,6 +900,7 @@ void decode_bf16_kernel(DecodeArgs a) {
             take(a, cur, ids, fbase, r.f1, rl, d0);
             __builtin_amdgcn_sched_barrier(0);
             eng.issue(a, d0, b0);
+            if (!cur.live && !d0.whole) pend.check = peek_arrivals(a, (int64_t)d0.b * a.hkv + d0.g);
             __builtin_amdgcn_sched_barrier(0);
             eng.compute(a, b1, d1, c);
             if (d1.last) finish_piece(a, eng, d1, w, r, pend, true);
@@ -817,8 +910,7 @@ void decode_bf16_kernel(DecodeArgs a) {
             break;
         }
     }
-    if (pend.saved) eng.store_saved(a, (int64_t)w + pend.job[0].s);
-    settle<__bf16, Eng, D>(a, pend);
+    settle<__bf16, Eng, D>(a, eng, pend, w, own_o, own_ml);
 }
 
 // ---------------------------------------------------------------------------
@@ -827,6 +919,7 @@ void decode_bf16_kernel(DecodeArgs a) {
 
 template <int D>
 struct EngF32 {
+    static constexpr bool kHolds = false;
     using Out = float;
     static constexpr int KC = D / 4;   // QK MFMAs per page
     static constexpr int DC = D / 16;  // output dim chunks
@@ -936,7 +1029,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
     int64_t f = r.f0;
     Eng eng;
     Pending pend;
-    pend.n = pend.saved = 0;
+    pending_init(pend);
     for (;;) {
         const int64_t left = r.f1 - f;
         const int p1 = left < (int64_t)(s.np - p0) ? p0 + (int)left : s.np;
@@ -948,14 +1041,14 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
             const int64_t seg = (int64_t)s.b * a.hkv + s.g;
             eng.store_partial(a, (int64_t)w + seg);
             const int64_t wf = worker_of(s.f, r);
-            pending_add(pend, seg, s.b, s.g, wf, (int)(worker_of(s.f + s.np - 1, r) - wf + 1));
+            pending_add(pend, seg, s.b, s.g, wf, (int)(worker_of(s.f + s.np - 1, r) - wf + 1), kStored);
         }
         f += p1 - p0;
         if (f >= r.f1) break;
         seg_next(a, s, rl);
         p0 = 0;
     }
-    settle<float, Eng, D>(a, pend);
+    settle<float, Eng, D>(a, eng, pend, w, nullptr, nullptr);
 }
 
 const void *pick_kernel(int dtype, int d) {
