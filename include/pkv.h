@@ -145,7 +145,8 @@ size_t pkv_decode_workspace_bytes(const pkv_cache_desc *cache, int32_t batch, in
  *                  out = 0 and lse = -inf for that row
  *   max_kv_len     host upper bound of cache_seqlens (no device read-back is
  *                  made to find it; mini-infer 06 §5); must satisfy
- *                  max_kv_len <= bt_cols * page_size
+ *                  max_kv_len <= bt_cols * page_size; above 2^28 the call
+ *                  returns PKV_EUNSUPPORTED
  *   workspace      device buffer of at least pkv_decode_workspace_bytes(...)
  * Long rows are split across workers and merged by a log-sum-exp combine;
  * every row's result depends only on its logical keys, not on which physical

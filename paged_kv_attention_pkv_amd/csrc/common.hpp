@@ -31,21 +31,20 @@ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; 
 template <typename T>
 __device__ __forceinline__ T shfl_xor(T v, int mask) { return __shfl_xor(v, mask, kWave); }
 
-__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
-}
-
-// Inclusive prefix sum over the 64 lanes.
-__device__ __forceinline__ int64_t wave_incl_scan64(int64_t v) {
-    const int l = lane_id();
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        int64_t u = __shfl_up(v, d, kWave);
-        if (l >= d) v += u;
-    }
-    return v;
+// Inclusive prefix sum over the 64 lanes, 32-bit: row_shr steps 1, 2, 4, 8
+// inside each 16-lane row (DPP; a lane whose source would lie in another row
+// adds 0), then the totals of the rows before (scalar reads of lanes 15, 31,
+// 47).  No LDS round trip.
+__device__ __forceinline__ int wave_incl_scan32(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);
+    const int r0 = __builtin_amdgcn_readlane(v, 15);
+    const int r1 = __builtin_amdgcn_readlane(v, 31);
+    const int r2 = __builtin_amdgcn_readlane(v, 47);
+    const int row = lane_id() >> 4;
+    return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
 // Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)

@@ -89,9 +89,11 @@ __device__ __forceinline__ int clamp_page(const DecodeArgs &a, int p) {
     return p < 0 ? 0 : (p >= a.num_pages ? a.num_pages - 1 : p);
 }
 
-// Raw lengths of 64 consecutive rows, one per lane (rows past the batch: -1).
+// Raw lengths of 64 consecutive rows, one per lane (rows past the batch: -1),
+// and, as left by plan() for rows 0..63, the inclusive prefix sum of their
+// page counts.
 struct RowLens {
-    int base, raw;
+    int base, raw, incl;
     __device__ __forceinline__ int get(const DecodeArgs &a, int b) {
         if (b < base || b >= base + kWave) {
             base = b & ~(kWave - 1);
@@ -163,16 +165,18 @@ struct Range {
 template <typename OutT>
 __device__ __forceinline__ bool plan(const DecodeArgs &a, int w, int D, RowLens &rl, Range &r) {
     const int l = lane_id();
-    int64_t pages = 0;
+    int64_t pages = 0;  // pages of all rows, one kv head
     for (int base = 0; base < a.batch; base += kWave) {
         const int b = base + l;
         const int raw = raw_len(a, b);
+        const int n = attended(a, raw);
+        const int incl = wave_incl_scan32(ceil_div(n, kPage));
         if (base == 0) {
             rl.base = 0;
             rl.raw = raw;
+            rl.incl = incl;
         }
-        const int n = attended(a, raw);
-        pages += ceil_div(n, kPage);
+        pages += __builtin_amdgcn_readlane(incl, kWave - 1);
         const bool mine = b < a.batch && b % a.workers == w;
         if (mine && a.seqlens_out) a.seqlens_out[b] = raw + 1;
         uint64_t empty = __ballot(mine && n == 0);
@@ -182,7 +186,7 @@ __device__ __forceinline__ bool plan(const DecodeArgs &a, int w, int D, RowLens 
             zero_row<OutT>(a, base + e, D);
         }
     }
-    const int64_t total = uniform64(wave_sum64(pages)) * a.hkv;
+    const int64_t total = pages * a.hkv;
     const int64_t wmax = total < (int64_t)a.workers ? total : (int64_t)a.workers;
     if ((int64_t)w >= wmax) return false;
     r.total = total;
@@ -192,28 +196,32 @@ __device__ __forceinline__ bool plan(const DecodeArgs &a, int w, int D, RowLens 
     return true;
 }
 
-// The segment holding flat page f (f < total).  Uses the first 64 lengths
-// from `rl` (as left by plan) and reads further chunks of rows if needed.
+// The segment holding flat page f (f < total).  Segments are laid out row by
+// row, the kv heads of a row one after another, so row b starts at flat page
+// hkv * (pages of rows before b).  Uses rows 0..63 from `rl` (as left by
+// plan) and reads further chunks of rows if needed.
 __device__ __forceinline__ void locate(const DecodeArgs &a, int64_t f, const RowLens &rl, Seg &s) {
     const int l = lane_id();
-    int64_t run = 0;
+    int64_t run = 0;  // flat pages of the rows before this chunk
     for (int base = 0; base < a.batch; base += kWave) {
-        const int raw = base == 0 ? rl.raw : raw_len(a, base + l);
-        const int n = attended(a, raw);
-        const int64_t np = (int64_t)ceil_div(n, kPage) * a.hkv;
-        const int64_t incl = wave_incl_scan64(np);
-        const int64_t tot = uniform64(__shfl(incl, kWave - 1, kWave));
-        if (run + tot > f) {
-            const uint64_t hit = __ballot(run + incl > f);
+        int raw = rl.raw, incl = rl.incl;
+        if (base > 0) {
+            raw = raw_len(a, base + l);
+            incl = wave_incl_scan32(ceil_div(attended(a, raw), kPage));
+        }
+        const int64_t tot = run + (int64_t)__builtin_amdgcn_readlane(incl, kWave - 1) * a.hkv;
+        if (tot > f) {
+            const uint64_t hit = __ballot(run + (int64_t)incl * a.hkv > f);
             const int first = uniform((int)__builtin_ctzll(hit));
-            const int64_t start = run + uniform64(__shfl(incl - np, first, kWave));
+            const int incl_b = __builtin_amdgcn_readlane(incl, first);
             s.b = base + first;
-            seg_row(a, s, uniform(__shfl(raw, first, kWave)));
+            seg_row(a, s, __builtin_amdgcn_readlane(raw, first));
+            const int64_t start = run + (int64_t)(incl_b - s.np) * a.hkv;
             s.g = (int)((f - start) / s.np);
             s.f = start + (int64_t)s.g * s.np;
             return;
         }
-        run += tot;
+        run = tot;
     }
 }
 

@@ -15,6 +15,7 @@ using pkv::PoolGeom;
 namespace {
 
 constexpr int kPageSize = 16;
+constexpr int32_t kMaxDecodeKv = 1 << 28;  // decode: max_kv_len bound (PKV_EUNSUPPORTED above)
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -151,6 +152,7 @@ pkv_status decode_common(const pkv_cache_desc *cache, void *out, float *lse, con
     if (!out || !q || !k_cache || !v_cache || !block_table || !cache_seqlens) return PKV_EINVAL;
     if (fused && (!aligned16(k_new) || !aligned16(v_new))) return PKV_EUNSUPPORTED;
     if ((int64_t)max_kv_len > (int64_t)bt_cols * kPageSize) return PKV_EINVAL;
+    if (max_kv_len > kMaxDecodeKv) return PKV_EUNSUPPORTED;  // page counts of 64 rows are summed in 32 bits
     if (!isfinite(scale)) return PKV_EINVAL;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return PKV_EUNSUPPORTED;

@@ -74,6 +74,7 @@ def test_decode_rejects_scalars():
     assert _decode(d, batch=-1) == EINVAL
     assert _decode(d, batch=0) == OK              # nothing to do
     assert _decode(d, max_kv=65, bt_cols=4) == EINVAL  # table too narrow for max_kv_len
+    assert _decode(d, max_kv=(1 << 28) + 1, bt_cols=1 << 25) == EUNSUPPORTED  # beyond the 32-bit page sums
     assert _decode(d, out=None) == EINVAL
     assert _decode(d, out=ctypes.c_void_p((1 << 20) + 2)) == EUNSUPPORTED  # misaligned
     assert _decode(d, scale=float("nan")) == EINVAL
