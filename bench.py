@@ -180,7 +180,9 @@ def bench_decode(args, torch, pkv, wl):
     if args.workload == "long":
         free = torch.cuda.mem_get_info(dev)[0]
         per_layer = 2 * spec.num_pages * spec.hkv * spec.page_size * spec.head_dim * 2
-        fit = int((free - (8 << 30)) // per_layer)
+        # room for one layer's fp32 input draws on top of the pools
+        spare = 4 * int(spec.hist_lens.sum()) * spec.hkv * spec.head_dim * 4 + (8 << 30)
+        fit = int((free - spare) // per_layer)
         if fit < L:
             log(f"only {fit} layer caches fit in device memory; using {fit}")
             L = max(1, fit)
@@ -192,9 +194,12 @@ def bench_decode(args, torch, pkv, wl):
     max_kv = int(spec.hist_lens.max()) + spec.n_new
     workspace = None
     layers = []
+    # every layer's pools first, so the input draws below (freed after each
+    # layer) do not split the pools' memory into unusable pieces
+    pools = [(wl.empty_pool(spec, dev), wl.empty_pool(spec, dev)) for _ in range(L)]
     for layer in range(L):
         inp = wl.decode_inputs(spec, device=dev, seed_offset=layer)
-        kc, vc = wl.empty_pool(spec, dev), wl.empty_pool(spec, dev)
+        kc, vc = pools[layer]
         if workspace is None:
             ws_bytes = pkv.decode_workspace_bytes(kc, spec.batch, spec.hq, max_kv, workers=args.workers)
             workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
@@ -207,8 +212,9 @@ def bench_decode(args, torch, pkv, wl):
         else:
             app = pkv.api.prepare_append(kc, vc, inp.k_new, inp.v_new, bt, hist, lens)
             dec = pkv.api.prepare_decode(inp.q, kc, vc, bt, lens, max_kv, out, workspace, workers=args.workers)
-        layers.append((app, dec, inp if layer < 2 else None))
+        layers.append((app, dec, None))
         del inp
+    del pools
     torch.cuda.synchronize()
 
     def step():

@@ -160,8 +160,11 @@ pkv_status pkv_decode_attn(const pkv_cache_desc *cache, void *out, float *lse, c
 
 /*
  * Same as pkv_decode_attn with an explicit number of split workers (0 =
- * automatic).  For tests of split invariance and for tuning; the workspace
- * must be sized with pkv_decode_workspace_bytes_ex and the same count.
+ * automatic: one wave per resident slot of the device, and on the device
+ * fewer for small calls so that each keeps at least 8 pages).  A count > 0
+ * is used as given (capped at the call's page count).  For tests of split
+ * invariance and for tuning; the workspace must be sized with
+ * pkv_decode_workspace_bytes_ex and the same count.
  */
 size_t pkv_decode_workspace_bytes_ex(const pkv_cache_desc *cache, int32_t batch,
                                      int32_t num_q_heads, int32_t max_kv_len, int32_t workers);

@@ -52,6 +52,8 @@
 #include "common.hpp"
 #include "internal.hpp"
 
+// Fewest pages a split worker is given when the library picks the count.
+constexpr int64_t kMinPagesPerWorker = 8;
 // Resident waves per SIMD the bf16 kernel is register-capped to (head_dim <= 128).
 #ifndef PKV_DECODE_WAVES_PER_EU
 #define PKV_DECODE_WAVES_PER_EU 1
@@ -187,7 +189,12 @@ __device__ __forceinline__ bool plan(const DecodeArgs &a, int w, int D, RowLens 
         }
     }
     const int64_t total = pages * a.hkv;
-    const int64_t wmax = total < (int64_t)a.workers ? total : (int64_t)a.workers;
+    // Small calls use fewer waves, so each keeps at least kMinPagesPerWorker
+    // pages (a segment cut into many tiny pieces costs more in merges than
+    // the extra waves gain).  A count the caller fixed is used as given.
+    const int64_t by_pages = total / kMinPagesPerWorker > 0 ? total / kMinPagesPerWorker : 1;
+    int64_t wmax = by_pages < (int64_t)a.workers ? by_pages : (int64_t)a.workers;
+    if (a.fixed_workers) wmax = total < (int64_t)a.workers ? total : (int64_t)a.workers;
     if ((int64_t)w >= wmax) return false;
     r.total = total;
     r.workers = (int)wmax;

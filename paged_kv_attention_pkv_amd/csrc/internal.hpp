@@ -43,6 +43,7 @@ struct DecodeArgs {
     int32_t num_pages;  // page ids are clamped into 0..num_pages-1
     float scale_log2;   // softmax scale times log2(e)
     int32_t workers;    // split workers (one wave each)
+    int32_t fixed_workers;  // 1: the caller fixed the count (no cap by page count)
     float *part_o;      // [(workers + batch*hkv) * group * head_dim]
     float *part_ml;     // [(workers + batch*hkv) * group * 2]
     int32_t *arrivals;  // [batch*hkv]: pieces finished per split row; zero between calls

@@ -183,6 +183,7 @@ pkv_status decode_common(const pkv_cache_desc *cache, void *out, float *lse, con
     a.num_pages = g.num_pages;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.workers = w;
+    a.fixed_workers = workers > 0;
     a.part_o = (float *)workspace;
     a.part_ml = nullptr;
     a.arrivals = nullptr;

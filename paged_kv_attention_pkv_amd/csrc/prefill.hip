@@ -142,10 +142,22 @@ void prefill_kernel(PrefillArgs a, int n_qtiles) {
     constexpr int NS = kBN / 32;  // 32-key score blocks per tile
     extern __shared__ __align__(16) uint16_t smem[];
 
-    // grid: (request, tile, head) with tiles reversed (longest first)
+    // grid: (request, tile, head) with tiles reversed (longest first) and
+    // heads fastest, so the G heads of one KV head, which read the same K/V
+    // tiles, are G neighbours in that order.  Workgroups are dealt to the 8
+    // XCDs round-robin by blockIdx; the remap hands each XCD whole groups of
+    // G (groups in order, round-robin over the XCDs), so a group's heads run
+    // side by side on one XCD and share its L2, and the order stays longest
+    // first.  The last partial round keeps the identity.
+    const int G = a.hq / a.hkv;
+    int idx = blockIdx.x;
+    if (idx < (int)(gridDim.x / (8 * G)) * 8 * G) {
+        const int k = idx >> 3;
+        idx = ((k / G) * 8 + (idx & 7)) * G + k % G;
+    }
     const int per_req = n_qtiles * a.hq;
-    const int r = blockIdx.x / per_req;
-    const int rem = blockIdx.x - r * per_req;
+    const int r = idx / per_req;
+    const int rem = idx - r * per_req;
     const int qt = n_qtiles - 1 - rem / a.hq;
     const int h = rem - (rem / a.hq) * a.hq;
     // metadata is clamped so that every access stays inside the buffers
@@ -153,7 +165,6 @@ void prefill_kernel(PrefillArgs a, int n_qtiles) {
     const int q_len = min(max(a.qo_indptr[r + 1] - q0, 0), a.total_q - q0);
     if (qt * kBM >= q_len) return;
     const int kv = min(max(a.kv_lens[r], 0), a.max_kv);
-    const int G = a.hq / a.hkv;
     const int g = h / G;
     const int32_t *bt = a.block_table + (int64_t)r * a.bt_cols;
 
