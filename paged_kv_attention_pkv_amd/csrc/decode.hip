@@ -13,7 +13,9 @@
 //
 // Work decomposition ("stream-K" over pages), one kernel launch.  The pages
 // of all (sequence, kv head) segments are laid end to end, sequence-major,
-// and cut into `workers` equal ranges, one per wavefront.  A wave walks its
+// and cut into equal ranges, one per wavefront: `workers` of them, or fewer
+// on small calls (each wave keeps at least kMinPagesPerWorker pages; the
+// count is decided on the device from the lengths, with no host read-back).  A wave walks its
 // range as one stream of page pairs that crosses segment boundaries without
 // draining: the next pair's loads are always in flight while the current one
 // is computed.  Every maximal run of one segment inside a range is a
@@ -23,7 +25,9 @@
 // the segment's arrival counter; the piece that arrives last merges every
 // record of the segment in piece order (so the result does not depend on
 // which piece came last), writes the output and resets the counter to zero
-// for the next call.  Equal page counts per wave keep every CU busy to the
+// for the next call.  A wave whose last piece finds, by a read issued with
+// its last loads, every other piece already counted merges without writing
+// or counting that piece.  Equal page counts per wave keep every CU busy to the
 // end for any mix of lengths.  Rows with no keys are written (0, lse = -inf)
 // by the waves in a round-robin.
 //
