@@ -53,19 +53,22 @@ constexpr float kRescaleSlack = 8.f;
 // Key rows are padded by 48 B: row starts then fall 12 banks (of 64) apart,
 // which measured fastest for both the K-operand reads and the transposing
 // V reads (a 16 B pad left the transposing reads 2-way conflicted).
-template <int D>
+template <int D, int KPAD = 24, int VPAD = KPAD>
 struct Smem {
-    static constexpr int STRIDE = D + 24;        // bf16 elements per key row
-    static constexpr int TILE = kBN * STRIDE;    // one of K or V
-    static constexpr int BUF = 2 * TILE;         // K then V, one stage
-    static constexpr int BYTES = 2 * BUF * 2;    // two stages of bf16
+    static constexpr int KSTRIDE = D + KPAD;          // bf16 elements per K row
+    static constexpr int VSTRIDE = D + VPAD;          // and per V row
+    static constexpr int VOFF = kBN * KSTRIDE;        // the V tile follows the K tile
+    static constexpr int BUF = VOFF + kBN * VSTRIDE;  // K then V, one stage
+    static constexpr int BYTES = 2 * BUF * 2;         // two stages of bf16
+    static constexpr int STRIDE = KSTRIDE;            // equal pads: one stride for both
+    static constexpr int TILE = VOFF;
 };
 
-// Global loads of one key tile: thread t holds chunks t + kThreads*i
-// (8 dims each) of K and of V; keys past kv are zero.
-template <int D>
+// Global loads of one key tile by a workgroup of NT threads: thread t holds
+// chunks t + NT*i (8 dims each) of K and of V; keys past kv are zero.
+template <int D, int NT = kThreads>
 struct TileRegs {
-    static constexpr int CHUNKS = kBN * D / 8 / kThreads;  // per thread
+    static constexpr int CHUNKS = kBN * D / 8 / NT;  // per thread
     u32x4 k[CHUNKS], v[CHUNKS];
 };
 
@@ -73,9 +76,9 @@ struct TileRegs {
 // lie in one page, so each instruction goes through that page's buffer
 // resource; its byte range stops at the page's last valid key, so keys at or
 // past kv (and whole pages past it) load as zeros, without branches.
-template <int D>
+template <int D, int NT = kThreads>
 __device__ __forceinline__ void load_tile(const PrefillArgs &a, const int32_t *bt, int g, int tile, int kv,
-                                          TileRegs<D> &t) {
+                                          TileRegs<D, NT> &t) {
     constexpr int CPK = D / 8;  // 16-byte chunks per key row
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -93,8 +96,8 @@ __device__ __forceinline__ void load_tile(const PrefillArgs &a, const int32_t *b
         rv[u] = make_rsrc((const char *)a.v_cache + off, bytes);
     }
 #pragma unroll
-    for (int i = 0; i < TileRegs<D>::CHUNKS; ++i) {
-        const int c0 = kWave * wave + kThreads * i;  // first chunk of this wave-instruction
+    for (int i = 0; i < TileRegs<D, NT>::CHUNKS; ++i) {
+        const int c0 = kWave * wave + NT * i;  // first chunk of this wave-instruction
         const int u = uniform((c0 / CPK) >> 4);      // its page within the tile
         const int c = c0 + lane;
         const int key = c / CPK;
@@ -108,17 +111,16 @@ __device__ __forceinline__ void load_tile(const PrefillArgs &a, const int32_t *b
     }
 }
 
-template <int D>
-__device__ __forceinline__ void store_tile(uint16_t *buf, const TileRegs<D> &t) {
-    using S = Smem<D>;
+template <int D, int NT = kThreads, class S = Smem<D>>
+__device__ __forceinline__ void store_tile(uint16_t *buf, const TileRegs<D, NT> &t) {
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < TileRegs<D>::CHUNKS; ++i) {
-        const int c = tid + kThreads * i;
+    for (int i = 0; i < TileRegs<D, NT>::CHUNKS; ++i) {
+        const int c = tid + NT * i;
         const int key = c / (D / 8);
         const int d8 = c - key * (D / 8);
-        *reinterpret_cast<u32x4 *>(buf + key * S::STRIDE + d8 * 8) = t.k[i];
-        *reinterpret_cast<u32x4 *>(buf + S::TILE + key * S::STRIDE + d8 * 8) = t.v[i];
+        *reinterpret_cast<u32x4 *>(buf + key * S::KSTRIDE + d8 * 8) = t.k[i];
+        *reinterpret_cast<u32x4 *>(buf + S::VOFF + key * S::VSTRIDE + d8 * 8) = t.v[i];
     }
 }
 
@@ -348,8 +350,254 @@ void prefill_kernel(PrefillArgs a, int n_qtiles) {
     if (half == 0 && a.lse) a.lse[(int64_t)(q0 + i_row) * a.hq + h] = (m + log2f(lt)) * kLn2f;
 }
 
+// ---------------------------------------------------------------------------
+// 16 query rows per wave, 8 waves per workgroup (two per SIMD)
+// ---------------------------------------------------------------------------
+//
+// The same walk as prefill_kernel with v_mfma_f32_16x16x32_bf16 blocks:
+//   S^T[16 key x 16 q]  = K[16 x 32] . Q^T[32 x 16]       (D/32 k-steps per 16 keys)
+//   O^T[16 dim x 16 q] += V^T[16 dim x 32 key] . P^T[32 key x 16 q]
+// Lane (g = lane/16, c = lane%16) owns query row c of its wave; the softmax
+// statistics of a row live in lanes c, c+16, c+32, c+48 (row-swap permutes).
+// With half the rows per wave the accumulators take half the registers, so
+// two waves share each SIMD and one wave's softmax, barrier wait and LDS
+// reads overlap the other's MFMAs; each K/V byte read from LDS feeds half as
+// many rows as in prefill_kernel.
+//
+// Key order inside a 32-key PV step: lane group g takes keys 4g..4g+3 of the
+// first 16-key score block and 4g..4g+3 of the second, which is exactly where
+// the S^T accumulators leave them, so P^T needs no data movement; the V^T
+// operand is read in the same key order (two transposing reads per block).
+constexpr int kWaves16 = 8;
+constexpr int kRows16 = 16;
+constexpr int kBM16 = kWaves16 * kRows16;  // query rows per workgroup
+constexpr int kThreads16 = kWaves16 * kWave;
+#ifndef PKV_PF16_KPAD
+#define PKV_PF16_KPAD 16
+#endif
+#ifndef PKV_PF16_VPAD
+#define PKV_PF16_VPAD 16
+#endif
+template <int D>
+using Smem16 = Smem<D, PKV_PF16_KPAD, PKV_PF16_VPAD>;
+
+template <int D>
+__global__ __launch_bounds__(kThreads16) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill16_kernel(PrefillArgs a, int n_qtiles) {
+    using S = Smem16<D>;
+    constexpr int KS = D / 32;    // k-steps of the QK contraction
+    constexpr int DB = D / 16;    // 16-dim blocks of the output
+    constexpr int NB = kBN / 16;  // 16-key score blocks per tile
+    extern __shared__ __align__(16) uint16_t smem[];
+
+    // grid: (request, tile, head), longest tiles first, heads fastest; whole
+    // groups of the G heads of one KV head are dealt to one XCD (see
+    // prefill_kernel)
+    const int G = a.hq / a.hkv;
+    int idx = blockIdx.x;
+    if (idx < (int)(gridDim.x / (8 * G)) * 8 * G) {
+        const int k = idx >> 3;
+        idx = ((k / G) * 8 + (idx & 7)) * G + k % G;
+    }
+    const int per_req = n_qtiles * a.hq;
+    const int r = idx / per_req;
+    const int rem = idx - r * per_req;
+    const int qt = n_qtiles - 1 - rem / a.hq;
+    const int h = rem - (rem / a.hq) * a.hq;
+    const int q0 = min(max(a.qo_indptr[r], 0), a.total_q);
+    const int q_len = min(max(a.qo_indptr[r + 1] - q0, 0), a.total_q - q0);
+    if (qt * kBM16 >= q_len) return;
+    const int kv = min(max(a.kv_lens[r], 0), a.max_kv);
+    const int g = h / G;
+    const int32_t *bt = a.block_table + (int64_t)r * a.bt_cols;
+
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int grp = lane >> 4;
+    const int col = lane & 15;
+    const int i_row = qt * kBM16 + wave * kRows16 + col;
+    const bool row_ok = i_row < q_len;
+    const int i_eff = row_ok ? i_row : q_len - 1;
+    const int limit = a.causal ? kv - q_len + i_eff : kv - 1;
+
+    const int i_last_wg = min(qt * kBM16 + kBM16, q_len) - 1;
+    const int last_key_wg = a.causal ? kv - q_len + i_last_wg : kv - 1;
+    const int n_tiles = last_key_wg / kBN + 1;
+    const int wave_first = qt * kBM16 + wave * kRows16;
+    const int i_last_wave = min(wave_first + kRows16, q_len) - 1;
+    const int last_key_wave = wave_first >= q_len ? -1 : (a.causal ? kv - q_len + i_last_wave : kv - 1);
+    const int common_keys = wave_first >= q_len ? -1 : (a.causal ? kv - q_len + wave_first : kv - 1);
+    if (kv == 0 || (a.causal && kv < q_len)) {
+        if (row_ok) {
+            uint16_t *orow = (uint16_t *)a.out + ((int64_t)(q0 + i_row) * a.hq + h) * D;
+            for (int d = grp; d < D; d += 4) orow[d] = 0;
+            if (grp == 0 && a.lse) a.lse[(int64_t)(q0 + i_row) * a.hq + h] = kNegInff;
+        }
+        return;
+    }
+
+    // Q^T operand: lane holds Q[row][32ks + 8grp .. +7] for every k-step
+    u32x4 qop[KS];
+    {
+        const uint16_t *qrow = (const uint16_t *)a.q + ((int64_t)(q0 + i_eff) * a.hq + h) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qop[ks] = ld16(qrow + 32 * ks + 8 * grp);
+    }
+    f32x4 acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = kNegInff, l = 0.f;  // l: this lane's part of the row sum
+    const float c = a.scale_log2;
+    // transposing V reads: lane 4a+b of its group names key a, dims 4b..4b+3
+    const int tr_key = col >> 2;
+    const int tr_dim = 4 * (col & 3);
+
+    TileRegs<D, kThreads16> regs;
+    load_tile<D, kThreads16>(a, bt, g, 0, kv, regs);
+    store_tile<D, kThreads16, S>(smem, regs);
+    __syncthreads();
+    for (int tile = 0; tile < n_tiles; ++tile) {
+        uint16_t *cur = smem + (tile & 1) * S::BUF;
+        uint16_t *nxt = smem + ((tile + 1) & 1) * S::BUF;
+        const bool more = tile + 1 < n_tiles;
+        if (more) load_tile<D, kThreads16>(a, bt, g, tile + 1, kv, regs);
+
+        if (tile * kBN <= last_key_wave) {
+            const uint16_t *ks = cur;
+            const uint16_t *vs = cur + S::VOFF;
+            // S^T = K . Q^T: per k-step, the NB key blocks' K operands are
+            // read together, the next k-step's reads issued before this one's
+            // MFMAs
+            f32x4 sc[NB];
+#pragma unroll
+            for (int u = 0; u < NB; ++u) sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            u32x4 kb[2][NB];
+            auto read_k = [&](int k, u32x4 (&dst)[NB]) {
+#pragma unroll
+                for (int u = 0; u < NB; ++u)
+                    dst[u] = *reinterpret_cast<const u32x4 *>(ks + (16 * u + col) * S::KSTRIDE + 32 * k + 8 * grp);
+            };
+            read_k(0, kb[0]);
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                if (k + 1 < KS) read_k(k + 1, kb[(k + 1) & 1]);
+#pragma unroll
+                for (int u = 0; u < NB; ++u)
+                    sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[k & 1][u]),
+                                                                    __builtin_bit_cast(bf16x8, qop[k]), sc[u], 0, 0, 0);
+            }
+            // scores in log2 units; element i of block u is key tile*64 + 16u + 4grp + i
+            const bool need_mask = tile * kBN + kBN - 1 > common_keys;
+            float mx = kNegInff;
+#pragma unroll
+            for (int u = 0; u < NB; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float x = sc[u][i] * c;
+                    if (need_mask) {
+                        const int j = tile * kBN + 16 * u + 4 * grp + i;
+                        x = j <= limit ? x : kNegInff;
+                    }
+                    sc[u][i] = x;
+                    mx = fmaxf(mx, x);
+                }
+            mx = rows4_max(mx);
+            const bool raise = mx > m + kRescaleSlack;
+            if (__any(raise)) {
+                const float mn = raise ? mx : m;
+                const float alpha = fast_exp2(m - mn);
+                l *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+                m = mn;
+            }
+            // P^T operands, one per 32-key step t: keys 4grp.. of blocks 2t and 2t+1
+            u32x4 pop[NB / 2];
+#pragma unroll
+            for (int t = 0; t < NB / 2; ++t) {
+                float p[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[i] = fast_exp2(sc[2 * t][i] - m);
+                    p[4 + i] = fast_exp2(sc[2 * t + 1][i] - m);
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) l += p[i];
+                pop[t] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                               pack_bf16x2(p[6], p[7])};
+            }
+            // O^T += V^T . P^T; V^T operands read in groups of VG dim blocks,
+            // the next group's reads issued before the current group's MFMAs
+            constexpr int VG = DB < 4 ? DB : 4;
+            constexpr int NVG = (NB / 2) * (DB / VG);
+            u32x4 vb[2][VG];
+            auto read_v = [&](int gi, u32x4 (&dst)[VG]) {
+                const int t = gi / (DB / VG), db0 = (gi % (DB / VG)) * VG;
+#pragma unroll
+                for (int j = 0; j < VG; ++j) {
+                    const uint16_t *base = vs + (32 * t + 4 * grp + tr_key) * S::VSTRIDE + 16 * (db0 + j) + tr_dim;
+                    const u32x2 lo = ld_tr(base);
+                    const u32x2 hi = ld_tr(base + 16 * S::VSTRIDE);
+                    dst[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                }
+            };
+            read_v(0, vb[0]);
+#pragma unroll
+            for (int gi = 0; gi < NVG; ++gi) {
+                if (gi + 1 < NVG) read_v(gi + 1, vb[(gi + 1) & 1]);
+                const int t = gi / (DB / VG), db0 = (gi % (DB / VG)) * VG;
+#pragma unroll
+                for (int j = 0; j < VG; ++j)
+                    acc[db0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, vb[gi & 1][j]), __builtin_bit_cast(bf16x8, pop[t]), acc[db0 + j],
+                        0, 0, 0);
+            }
+        }
+        if (more) {
+            store_tile<D, kThreads16, S>(nxt, regs);
+            __syncthreads();
+        }
+    }
+
+    // normalise and write: acc[db][i] is O^T[dim 16db + 4grp + i][row]
+    const float lt = rows4_sum(l);
+    if (!row_ok) return;
+    const float inv = 1.f / lt;
+    uint16_t *orow = (uint16_t *)a.out + ((int64_t)(q0 + i_row) * a.hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        const u32x2 v = {pack_bf16x2(acc[db][0] * inv, acc[db][1] * inv),
+                         pack_bf16x2(acc[db][2] * inv, acc[db][3] * inv)};
+        *reinterpret_cast<u32x2 *>(orow + 16 * db + 4 * grp) = v;
+    }
+    if (grp == 0 && a.lse) a.lse[(int64_t)(q0 + i_row) * a.hq + h] = (m + log2f(lt)) * kLn2f;
+}
+
+template <int D>
+hipError_t launch16_d(const PrefillArgs &a, hipStream_t stream) {
+    const int n_qtiles = (a.max_q + kBM16 - 1) / kBM16;
+    const int64_t grid = (int64_t)a.batch * n_qtiles * a.hq;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill16_kernel<D>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, Smem16<D>::BYTES);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(prefill16_kernel<D>, dim3((unsigned)grid), dim3(kThreads16), Smem16<D>::BYTES, stream, a,
+                       n_qtiles);
+    return hipGetLastError();
+}
+
+#ifndef PKV_PREFILL16_DIMS
+#define PKV_PREFILL16_DIMS 4  // head dims on the 16-row kernel: bit 0: 64, bit 1: 128, bit 2: 256
+#endif
+
 template <int D>
 hipError_t launch_d(const PrefillArgs &a, hipStream_t stream) {
+    constexpr int bit = D == 64 ? 1 : (D == 128 ? 2 : 4);
+    if constexpr ((PKV_PREFILL16_DIMS & bit) != 0) return launch16_d<D>(a, stream);
     const int n_qtiles = (a.max_q + kBM - 1) / kBM;
     const int64_t grid = (int64_t)a.batch * n_qtiles * a.hq;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
