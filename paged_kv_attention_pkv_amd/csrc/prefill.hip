@@ -372,19 +372,62 @@ constexpr int kWaves16 = 8;
 constexpr int kRows16 = 16;
 constexpr int kBM16 = kWaves16 * kRows16;  // query rows per workgroup
 constexpr int kThreads16 = kWaves16 * kWave;
-#ifndef PKV_PF16_KPAD
-#define PKV_PF16_KPAD 16
-#endif
-#ifndef PKV_PF16_VPAD
-#define PKV_PF16_VPAD 16
-#endif
+
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS layout of a key tile for the 16-row kernel (D = 256), written by 1 KB
+// buffer-to-LDS transfers (64 lanes x 16 B, lane i to byte 16i): key rows in
+// pairs, one pair (1 KB) every PAIR elements; the odd row of a pair sits D
+// elements after the even one with its 16-byte chunks permuted (chunk j in
+// slot j ^ 8).  Measured on the device, both read patterns of the kernel run
+// as fast on it as on the best padded row layout.
 template <int D>
-using Smem16 = Smem<D, PKV_PF16_KPAD, PKV_PF16_VPAD>;
+struct Dma16 {
+    static_assert(D == 256, "the row-pair layout is for head_dim 256");
+    static constexpr int PAIR = 2 * D + 16;         // elements per row pair (1 KB + 32 B)
+    static constexpr int TILE = (kBN / 2) * PAIR;   // one of K or V
+    static constexpr int BUF = 2 * TILE;            // K then V, one stage
+    static constexpr int BYTES = 2 * BUF * 2;       // two stages of bf16
+    static constexpr int XS = 8;                    // chunk permutation of odd rows
+};
+
+// Issue this wave's transfers of key tile `tile` into the stage at dst: wave
+// w moves row pairs 4w .. 4w+3 of K and of V, which lie in page w / 2 of the
+// tile, through that page's buffer resource (byte range ending at its last
+// valid key, so keys at or past kv land as zeros).  The transfers bypass the
+// registers; the caller waits for them (vmcnt) and then for the barrier.
+template <int D>
+__device__ __forceinline__ void dma_tile16(const PrefillArgs &a, const int32_t *bt, int g, int tile, int kv,
+                                           uint16_t *dst) {
+    using L = Dma16<D>;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int64_t tok_bytes = a.s_tok * 2;
+    const int blk = tile * (kBN / kPage) + (wave >> 1);
+    const int valid = min(max(kv - blk * kPage, 0), kPage);
+    int pg = valid > 0 ? bt[blk] : 0;
+    pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+    const int64_t off = ((int64_t)pg * a.s_page + (int64_t)g * a.s_head) * 2;
+    const int32_t bytes = (int32_t)(valid * tok_bytes);
+    const Rsrc rk = make_rsrc((const char *)a.k_cache + off, bytes);
+    const Rsrc rv = make_rsrc((const char *)a.v_cache + off, bytes);
+    const int odd = lane >> 5;                       // second row of the pair
+    const int chunk = (lane & 31) ^ (odd * L::XS);   // the global chunk this lane's slot holds
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int x = 4 * wave + j;  // pair within the tile
+        const uint32_t voff = (uint32_t)(((2 * x + odd) & 15) * tok_bytes) + (uint32_t)chunk * 16u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(dst + x * L::PAIR), 16, voff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(dst + L::TILE + x * L::PAIR), 16, voff, 0, 0,
+                                                 0);
+    }
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads16) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill16_kernel(PrefillArgs a, int n_qtiles) {
-    using S = Smem16<D>;
+    using L = Dma16<D>;
     constexpr int KS = D / 32;    // k-steps of the QK contraction
     constexpr int DB = D / 16;    // 16-dim blocks of the output
     constexpr int NB = kBN / 16;  // 16-key score blocks per tile
@@ -448,23 +491,32 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
     for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = kNegInff, l = 0.f;  // l: this lane's part of the row sum
     const float c = a.scale_log2;
-    // transposing V reads: lane 4a+b of its group names key a, dims 4b..4b+3
-    const int tr_key = col >> 2;
-    const int tr_dim = 4 * (col & 3);
+    // Lane offsets in the row-pair layout.  A chunk index's bit 3 flips in
+    // odd rows, so each pattern has two lane bases: one for reads whose
+    // chunk has bit 3 clear (the odd rows' chunk moves up 8) and one for the
+    // rest (it moves down 8).
+    // K operand: row 16u + col, dims 32k + 8grp (chunk 4k + grp, bit 3 = bit 1 of k)
+    const int k_odd = col & 1;
+    const int k_base = (col >> 1) * L::PAIR + k_odd * D + 8 * grp;
+    const int k_lo = k_base + 64 * k_odd, k_hi = k_base - 64 * k_odd;
+    // V^T transposing reads: lane 4a+b of its group names key 32t + 4grp + a
+    // (and +16), dims 16db + 4b (chunk 2db + b/2, bit 3 = bit 2 of db)
+    const int v_odd = (col >> 2) & 1;
+    const int v_base = (2 * grp + (col >> 3)) * L::PAIR + v_odd * D + 8 * ((col & 3) >> 1) + 4 * (col & 1);
+    const int v_lo = v_base + 64 * v_odd, v_hi = v_base - 64 * v_odd;
 
-    TileRegs<D, kThreads16> regs;
-    load_tile<D, kThreads16>(a, bt, g, 0, kv, regs);
-    store_tile<D, kThreads16, S>(smem, regs);
+    dma_tile16<D>(a, bt, g, 0, kv, smem);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int tile = 0; tile < n_tiles; ++tile) {
-        uint16_t *cur = smem + (tile & 1) * S::BUF;
-        uint16_t *nxt = smem + ((tile + 1) & 1) * S::BUF;
+        uint16_t *cur = smem + (tile & 1) * L::BUF;
+        uint16_t *nxt = smem + ((tile + 1) & 1) * L::BUF;
         const bool more = tile + 1 < n_tiles;
-        if (more) load_tile<D, kThreads16>(a, bt, g, tile + 1, kv, regs);
+        if (more) dma_tile16<D>(a, bt, g, tile + 1, kv, nxt);
 
         if (tile * kBN <= last_key_wave) {
             const uint16_t *ks = cur;
-            const uint16_t *vs = cur + S::VOFF;
+            const uint16_t *vs = cur + L::TILE;
             // S^T = K . Q^T: per k-step, the NB key blocks' K operands are
             // read together, the next k-step's reads issued before this one's
             // MFMAs
@@ -475,7 +527,7 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
             auto read_k = [&](int k, u32x4 (&dst)[NB]) {
 #pragma unroll
                 for (int u = 0; u < NB; ++u)
-                    dst[u] = *reinterpret_cast<const u32x4 *>(ks + (16 * u + col) * S::KSTRIDE + 32 * k + 8 * grp);
+                    dst[u] = *reinterpret_cast<const u32x4 *>(ks + ((k & 2) ? k_hi : k_lo) + 8 * u * L::PAIR + 32 * k);
             };
             read_k(0, kb[0]);
 #pragma unroll
@@ -535,9 +587,10 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
                 const int t = gi / (DB / VG), db0 = (gi % (DB / VG)) * VG;
 #pragma unroll
                 for (int j = 0; j < VG; ++j) {
-                    const uint16_t *base = vs + (32 * t + 4 * grp + tr_key) * S::VSTRIDE + 16 * (db0 + j) + tr_dim;
+                    const int db = db0 + j;
+                    const uint16_t *base = vs + (((db & 4) ? v_hi : v_lo) + 16 * t * L::PAIR + 16 * db);
                     const u32x2 lo = ld_tr(base);
-                    const u32x2 hi = ld_tr(base + 16 * S::VSTRIDE);
+                    const u32x2 hi = ld_tr(base + 8 * L::PAIR);
                     dst[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
                 }
             };
@@ -554,8 +607,8 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
             }
         }
         if (more) {
-            store_tile<D, kThreads16, S>(nxt, regs);
-            __syncthreads();
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's transfers into nxt have landed
+            __syncthreads();                // and every other wave's
         }
     }
 
@@ -581,11 +634,11 @@ hipError_t launch16_d(const PrefillArgs &a, hipStream_t stream) {
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill16_kernel<D>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, Smem16<D>::BYTES);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, Dma16<D>::BYTES);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(prefill16_kernel<D>, dim3((unsigned)grid), dim3(kThreads16), Smem16<D>::BYTES, stream, a,
+    hipLaunchKernelGGL(prefill16_kernel<D>, dim3((unsigned)grid), dim3(kThreads16), Dma16<D>::BYTES, stream, a,
                        n_qtiles);
     return hipGetLastError();
 }
