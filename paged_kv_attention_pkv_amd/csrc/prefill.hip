@@ -376,6 +376,20 @@ constexpr int kThreads16 = kWaves16 * kWave;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Keys per tile and LDS stages of the 16-row kernel (transfers run kNST16-1
+// tiles ahead).  64 keys in two stages measured fastest: 32-key tiles in four
+// stages (three tiles ahead) lose more to twice the barriers and softmax
+// steps than they gain.
+#ifndef PKV_PF16_BN
+#define PKV_PF16_BN 64
+#endif
+#ifndef PKV_PF16_NST
+#define PKV_PF16_NST 2
+#endif
+constexpr int kBN16 = PKV_PF16_BN;
+constexpr int kNST16 = PKV_PF16_NST;
+static_assert(kBN16 % 32 == 0 && (kNST16 & (kNST16 - 1)) == 0 && kNST16 >= 2 && kNST16 <= 4, "tiling");
+
 // LDS layout of a key tile for the 16-row kernel (D = 256), written by 1 KB
 // buffer-to-LDS transfers (64 lanes x 16 B, lane i to byte 16i): key rows in
 // pairs, one pair (1 KB) every PAIR elements; the odd row of a pair sits D
@@ -386,41 +400,108 @@ template <int D>
 struct Dma16 {
     static_assert(D == 256, "the row-pair layout is for head_dim 256");
     static constexpr int PAIR = 2 * D + 16;         // elements per row pair (1 KB + 32 B)
-    static constexpr int TILE = (kBN / 2) * PAIR;   // one of K or V
-    static constexpr int BUF = 2 * TILE;            // K then V, one stage
-    static constexpr int BYTES = 2 * BUF * 2;       // two stages of bf16
+    static constexpr int TILE = (kBN16 / 2) * PAIR;  // one of K or V
+    static constexpr int BUF = 2 * TILE;             // K then V, one stage
+    static constexpr int BYTES = kNST16 * BUF * 2;   // kNST16 stages of bf16
+    static constexpr int IDS = kNST16 * BUF;          // then kIds16 int32 table entries (in elements)
+    static constexpr int PPW = kBN16 / 16;           // row pairs per wave per tile (K, and V)
     static constexpr int XS = 8;                    // chunk permutation of odd rows
 };
 
+// The page of key tile `tile` whose row pairs wave `wave` moves (see dma_tile16).
+__device__ __forceinline__ int dma_block16(int tile, int wave) { return tile * (kBN16 / kPage) + ((kBN16 / 16 * wave) >> 3); }
+
+// Table entries are staged in LDS, kIds16 at a time (the blocks of 2 * kIds16
+// / (kBN16 / 16) ... tiles), by the whole workgroup before the transfers
+// that use them: the compiler cannot tell the LDS transfers from stores to
+// the table, so a table read between them would be a vector load whose wait
+// covers every transfer in flight.  Entries at or past kv read as 0.
+constexpr int kIds16 = 4096;
+__device__ __forceinline__ void stage_ids16(const int32_t *bt, int b0, int kv, int *ids) {
+    constexpr int N = kIds16 / kThreads16;
+    const int last = (kv - 1) / kPage;  // last block holding a key (kv >= 1 here)
+    int v[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = bt[min(b0 + (int)threadIdx.x + i * kThreads16, last)];  // all in flight
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int blk = b0 + (int)threadIdx.x + i * kThreads16;
+        ids[threadIdx.x + i * kThreads16] = blk <= last ? v[i] : 0;
+    }
+}
+
 // Issue this wave's transfers of key tile `tile` into the stage at dst: wave
-// w moves row pairs 4w .. 4w+3 of K and of V, which lie in page w / 2 of the
-// tile, through that page's buffer resource (byte range ending at its last
-// valid key, so keys at or past kv land as zeros).  The transfers bypass the
-// registers; the caller waits for them (vmcnt) and then for the barrier.
+// w moves row pairs PPW*w .. PPW*w + PPW-1 of K and of V, which lie in one
+// page of the tile (raw table entry `entry`), through that page's buffer
+// resource (byte range ending at its last valid key, so keys at or past kv
+// land as zeros).  The transfers bypass the registers; the caller waits for
+// them (vmcnt) and then for the barrier.
 template <int D>
-__device__ __forceinline__ void dma_tile16(const PrefillArgs &a, const int32_t *bt, int g, int tile, int kv,
+__device__ __forceinline__ void dma_tile16(const PrefillArgs &a, int entry, int g, int tile, int wave, int kv,
                                            uint16_t *dst) {
     using L = Dma16<D>;
-    const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int64_t tok_bytes = a.s_tok * 2;
-    const int blk = tile * (kBN / kPage) + (wave >> 1);
+    const int blk = dma_block16(tile, wave);
     const int valid = min(max(kv - blk * kPage, 0), kPage);
-    int pg = valid > 0 ? bt[blk] : 0;
+    int pg = valid > 0 ? entry : 0;
     pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
-    const int64_t off = ((int64_t)pg * a.s_page + (int64_t)g * a.s_head) * 2;
-    const int32_t bytes = (int32_t)(valid * tok_bytes);
+    // scalar values, so the resources are known to be wave-uniform
+    const int64_t off = uniform64(((int64_t)pg * a.s_page + (int64_t)g * a.s_head) * 2);
+    const int32_t bytes = uniform((int)(valid * tok_bytes));
     const Rsrc rk = make_rsrc((const char *)a.k_cache + off, bytes);
     const Rsrc rv = make_rsrc((const char *)a.v_cache + off, bytes);
     const int odd = lane >> 5;                       // second row of the pair
     const int chunk = (lane & 31) ^ (odd * L::XS);   // the global chunk this lane's slot holds
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int x = 4 * wave + j;  // pair within the tile
+    for (int j = 0; j < L::PPW; ++j) {
+        const int x = L::PPW * wave + j;  // pair within the tile
         const uint32_t voff = (uint32_t)(((2 * x + odd) & 15) * tok_bytes) + (uint32_t)chunk * 16u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(dst + x * L::PAIR), 16, voff, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(dst + L::TILE + x * L::PAIR), 16, voff, 0, 0,
                                                  0);
+    }
+}
+
+// The transposing LDS read of ld_tr, written out: for the intrinsic the
+// compiler has no alias information, so while buffer-to-LDS transfers are in
+// flight it waits for all of them (vmcnt 0) before the read, which would
+// drain the transfers running ahead.  Here the read is opaque to the
+// compiler: the caller waits for it (lgkm_wait) before using the result.
+__device__ __forceinline__ u32x2 ld_tr_lds(uint32_t lds_byte_addr) {
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(lds_byte_addr) : "memory");
+    return r;
+}
+
+// Wait until at most N LDS reads are in flight, the values in `regs` (the
+// results of the reads before those) then being ready; the registers pass
+// through the wait so that nothing using them moves above it.
+template <int N, int K>
+__device__ __forceinline__ void lgkm_wait(u32x4 (&regs)[K]) {
+    static_assert(N < 16, "lgkmcnt field");
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+#pragma unroll
+    for (int k = 0; k < K; ++k) asm volatile("" : "+v"(regs[k]));
+}
+
+// Wait until this wave's transfers of the tile after the current one have
+// landed while `ahead` later tiles' transfers (TPW per tile) may still run.
+// Vector memory operations complete in order; in the s_waitcnt immediate,
+// expcnt 7 and lgkmcnt 15 mean no wait on those counters.
+template <int TPW>
+__device__ __forceinline__ void wait_transfers(int ahead) {
+    if constexpr (kNST16 > 2) {
+        static_assert(2 * TPW < 16, "vmcnt in the low field");
+        if (ahead >= 2)
+            __builtin_amdgcn_s_waitcnt((2 * TPW) | 0x0F70);
+        else if (ahead == 1)
+            __builtin_amdgcn_s_waitcnt(TPW | 0x0F70);
+        else
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+    } else {
+        (void)ahead;  // with two stages nothing runs further ahead
+        __builtin_amdgcn_s_waitcnt(0x0F70);
     }
 }
 
@@ -430,7 +511,8 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
     using L = Dma16<D>;
     constexpr int KS = D / 32;    // k-steps of the QK contraction
     constexpr int DB = D / 16;    // 16-dim blocks of the output
-    constexpr int NB = kBN / 16;  // 16-key score blocks per tile
+    constexpr int NB = kBN16 / 16;  // 16-key score blocks per tile
+    constexpr int TPW = 2 * Dma16<D>::PPW;  // transfers per wave per tile
     extern __shared__ __align__(16) uint16_t smem[];
 
     // grid: (request, tile, head), longest tiles first, heads fastest; whole
@@ -465,7 +547,7 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
 
     const int i_last_wg = min(qt * kBM16 + kBM16, q_len) - 1;
     const int last_key_wg = a.causal ? kv - q_len + i_last_wg : kv - 1;
-    const int n_tiles = last_key_wg / kBN + 1;
+    const int n_tiles = last_key_wg / kBN16 + 1;
     const int wave_first = qt * kBM16 + wave * kRows16;
     const int i_last_wave = min(wave_first + kRows16, q_len) - 1;
     const int last_key_wave = wave_first >= q_len ? -1 : (a.causal ? kv - q_len + i_last_wave : kv - 1);
@@ -505,16 +587,34 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
     const int v_base = (2 * grp + (col >> 3)) * L::PAIR + v_odd * D + 8 * ((col & 3) >> 1) + 4 * (col & 1);
     const int v_lo = v_base + 64 * v_odd, v_hi = v_base - 64 * v_odd;
 
-    dma_tile16<D>(a, bt, g, 0, kv, smem);
-    __builtin_amdgcn_s_waitcnt(0);
+    // table entries of blocks 0 .. kIds16-1, then tiles 0 .. kNST16-2 in
+    // flight, then wait for tile 0
+    const int wv = uniform(wave);
+    int *ids = reinterpret_cast<int *>(smem + L::IDS);
+    int window = 0;  // ids holds blocks window*kIds16 ..
+    stage_ids16(bt, 0, kv, ids);
+    __syncthreads();
+    auto entry = [&](int t) { return uniform(ids[dma_block16(t, wv) - window * kIds16]); };
+    const int pro = min(kNST16 - 1, n_tiles);
+    for (int t = 0; t < pro; ++t) dma_tile16<D>(a, entry(t), g, t, wv, kv, smem + t * L::BUF);
+    wait_transfers<TPW>(pro - 1);
     __syncthreads();
     for (int tile = 0; tile < n_tiles; ++tile) {
-        uint16_t *cur = smem + (tile & 1) * L::BUF;
-        uint16_t *nxt = smem + ((tile + 1) & 1) * L::BUF;
-        const bool more = tile + 1 < n_tiles;
-        if (more) dma_tile16<D>(a, bt, g, tile + 1, kv, nxt);
+        uint16_t *cur = smem + (tile & (kNST16 - 1)) * L::BUF;
+        const int pre = tile + kNST16 - 1;  // into the stage read in the tile before
+        if (pre < n_tiles) {
+            // past the staged entries (rows of more than 2 * kIds16 * 16 / (kBN16 / 16) keys): restage,
+            // every wave at the same tile; its loads' wait also drains the transfers in flight
+            if (dma_block16(pre, kWaves16 - 1) >= (window + 1) * kIds16) {
+                __syncthreads();
+                window = dma_block16(pre, 0) / kIds16;
+                stage_ids16(bt, window * kIds16, kv, ids);
+                __syncthreads();
+            }
+            dma_tile16<D>(a, entry(pre), g, pre, wv, kv, smem + (pre & (kNST16 - 1)) * L::BUF);
+        }
 
-        if (tile * kBN <= last_key_wave) {
+        if (tile * kBN16 <= last_key_wave) {
             const uint16_t *ks = cur;
             const uint16_t *vs = cur + L::TILE;
             // S^T = K . Q^T: per k-step, the NB key blocks' K operands are
@@ -539,7 +639,7 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
                                                                     __builtin_bit_cast(bf16x8, qop[k]), sc[u], 0, 0, 0);
             }
             // scores in log2 units; element i of block u is key tile*64 + 16u + 4grp + i
-            const bool need_mask = tile * kBN + kBN - 1 > common_keys;
+            const bool need_mask = tile * kBN16 + kBN16 - 1 > common_keys;
             float mx = kNegInff;
 #pragma unroll
             for (int u = 0; u < NB; ++u)
@@ -547,7 +647,7 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
                 for (int i = 0; i < 4; ++i) {
                     float x = sc[u][i] * c;
                     if (need_mask) {
-                        const int j = tile * kBN + 16 * u + 4 * grp + i;
+                        const int j = tile * kBN16 + 16 * u + 4 * grp + i;
                         x = j <= limit ? x : kNegInff;
                     }
                     sc[u][i] = x;
@@ -583,21 +683,28 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
             constexpr int VG = DB < 4 ? DB : 4;
             constexpr int NVG = (NB / 2) * (DB / VG);
             u32x4 vb[2][VG];
+            // LDS byte address of this lane's V reads in the current stage
+            const uint32_t vs_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t *)vs;
             auto read_v = [&](int gi, u32x4 (&dst)[VG]) {
                 const int t = gi / (DB / VG), db0 = (gi % (DB / VG)) * VG;
 #pragma unroll
                 for (int j = 0; j < VG; ++j) {
                     const int db = db0 + j;
-                    const uint16_t *base = vs + (((db & 4) ? v_hi : v_lo) + 16 * t * L::PAIR + 16 * db);
-                    const u32x2 lo = ld_tr(base);
-                    const u32x2 hi = ld_tr(base + 8 * L::PAIR);
+                    const uint32_t base = vs_addr + 2u * (uint32_t)(((db & 4) ? v_hi : v_lo) + 16 * t * L::PAIR + 16 * db);
+                    const u32x2 lo = ld_tr_lds(base);
+                    const u32x2 hi = ld_tr_lds(base + 2u * 8u * L::PAIR);
                     dst[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
                 }
             };
             read_v(0, vb[0]);
 #pragma unroll
             for (int gi = 0; gi < NVG; ++gi) {
-                if (gi + 1 < NVG) read_v(gi + 1, vb[(gi + 1) & 1]);
+                if (gi + 1 < NVG) {
+                    read_v(gi + 1, vb[(gi + 1) & 1]);
+                    lgkm_wait<2 * VG>(vb[gi & 1]);  // group gi's reads are done, gi+1's may run
+                } else {
+                    lgkm_wait<0>(vb[gi & 1]);
+                }
                 const int t = gi / (DB / VG), db0 = (gi % (DB / VG)) * VG;
 #pragma unroll
                 for (int j = 0; j < VG; ++j)
@@ -606,9 +713,10 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
                         0, 0, 0);
             }
         }
-        if (more) {
-            __builtin_amdgcn_s_waitcnt(0);  // this wave's transfers into nxt have landed
-            __syncthreads();                // and every other wave's
+        if (tile + 1 < n_tiles) {
+            // this wave's transfers of the next tile have landed, then every wave's
+            wait_transfers<TPW>(min(tile + kNST16 - 1, n_tiles - 1) - (tile + 1));
+            __syncthreads();
         }
     }
 
@@ -628,17 +736,18 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
 
 template <int D>
 hipError_t launch16_d(const PrefillArgs &a, hipStream_t stream) {
+    constexpr int kSmem16 = Dma16<D>::BYTES + kIds16 * 4;
     const int n_qtiles = (a.max_q + kBM16 - 1) / kBM16;
     const int64_t grid = (int64_t)a.batch * n_qtiles * a.hq;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill16_kernel<D>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, Dma16<D>::BYTES);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kSmem16);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(prefill16_kernel<D>, dim3((unsigned)grid), dim3(kThreads16), Dma16<D>::BYTES, stream, a,
+    hipLaunchKernelGGL(prefill16_kernel<D>, dim3((unsigned)grid), dim3(kThreads16), kSmem16, stream, a,
                        n_qtiles);
     return hipGetLastError();
 }
