@@ -675,26 +675,26 @@ struct Bf16 {
             buf.q[kc2] = col < G ? ld16(q + 64 * kc2 + 16 * quad) : z;
         }
         if (d.newtok) {
-            const int sl = (d.n - 1) & (kPage - 1);
+            const int slot = (d.n - 1) & (kPage - 1);
             const int64_t row = ((int64_t)d.b * a.hkv + d.g) * D * 2;
-            if (col == sl) {
+            if (col == slot) {
 #pragma unroll
                 for (int kc2 = 0; kc2 < KC; ++kc2)
                     buf.kn[kc2] = ld16((const char *)a.k_new + row + 64 * kc2 + 16 * quad);
             }
-            if (quad == (sl >> 2)) load_vrow((const char *)a.v_new + row + 2 * DPL * col, buf.vn);
+            if (quad == (slot >> 2)) load_vrow((const char *)a.v_new + row + 2 * DPL * col, buf.vn);
         }
     }
 
     // Fused mode: put the new token into the pair's registers in place of
     // its (stale) slot and write it into the pool.
     __device__ __forceinline__ void splice(const DecodeArgs &a, const Desc &d, Buf &buf) {
-        const int sl = (d.n - 1) & (kPage - 1);
-        const int e = sl & 3;
+        const int slot = (d.n - 1) & (kPage - 1);
+        const int e = slot & 3;
         const bool inB = d.npg == 2;
         const bool writable = d.raw_last >= 1 && d.raw_last < a.num_pages;
         const int64_t base = (int64_t)d.g * a.s_head * 2 + (int64_t)d.raw_last * a.s_page * 2;
-        if (col == sl) {
+        if (col == slot) {
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 if (inB)
@@ -704,7 +704,7 @@ struct Bf16 {
                 if (writable) st16((char *)a.k_cache + base + koff + 64 * kc, buf.kn[kc]);
             }
         }
-        if (quad == (sl >> 2)) {
+        if (quad == (slot >> 2)) {
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
                 if (e2 == e) {
