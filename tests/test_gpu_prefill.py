@@ -135,3 +135,12 @@ def test_no_visible_key_rows():
     o, l = out.float().cpu(), lse.cpu()
     assert torch.all(o[:3] == 0) and torch.all(torch.isneginf(l[:3]))
     assert torch.isfinite(o[3:]).all() and torch.isfinite(l[3:]).all()
+
+
+def test_long_kv_restages_table_window():
+    """One request of 70000 keys at D = 256: more than the 4096 page-table
+    entries (65536 keys) the 16-row kernel stages in LDS at a time, so it
+    restages the window during the walk.  The first and last 4 rows (the last
+    see every key) are checked."""
+    spec = wl.prefill_spec(q_lens=[40], kv_lens=[70000], hq=8, hkv=8, head_dim=256, seed=11)
+    _parity(spec, sample=4, gen_device="cuda")
