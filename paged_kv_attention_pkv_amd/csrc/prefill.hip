@@ -9,7 +9,11 @@
 // attention over the visible keys read through block_table, query head h
 // reading KV head h / G.
 //
-// Kernel.  One workgroup (4 waves) per (request, tile of 128 query rows,
+// Two kernels.  head_dim 256 runs prefill16_kernel (below: 16 query rows
+// per wave, 8 waves, two per SIMD, K/V tiles moved from HBM to LDS by
+// buffer-to-LDS transfers); head_dim 64 and 128 run prefill_kernel:
+//
+// One workgroup (4 waves) per (request, tile of 128 query rows,
 // query head); wave w owns query rows 32w .. 32w+31 of the tile.  Keys are
 // walked in tiles of 64 (four pages).  Per 32 keys, for every wave:
 //   S^T[32 key x 32 q]  = K[32 x D] . Q^T[D x 32]        (D/16 MFMA 32x32x16)

@@ -309,9 +309,10 @@ class PrefillInputs:
                              mv(self.qo_indptr), mv(self.block_table), mv(self.hist_lens))
 
 
-def prefill_inputs(spec: PrefillSpec, device="cpu") -> PrefillInputs:
+def prefill_inputs(spec: PrefillSpec, device="cpu", seed_offset: int = 0) -> PrefillInputs:
+    """Seeded tensors of a prefill workload; seed_offset draws another layer's."""
     gen = torch.Generator(device=device)
-    gen.manual_seed(spec.seed * 1_000_003 + 7)
+    gen.manual_seed(spec.seed * 1_000_003 + 7 + 1_009 * seed_offset)
     dt = spec.torch_dtype
     Hq, Hkv, D = spec.hq, spec.hkv, spec.head_dim
     total_q = int(spec.q_lens.sum())
