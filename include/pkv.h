@@ -245,6 +245,23 @@ pkv_status pkv_prefill_attn(const pkv_cache_desc *cache, void *out, float *lse, 
                             const int32_t *qo_indptr, int32_t batch, int32_t total_q,
                             int32_t max_q, int32_t max_kv_len, int32_t causal, float scale,
                             void *workspace, size_t workspace_bytes, void *stream);
+/*
+ * As pkv_prefill_attn, with the query rows per workgroup chosen by the caller
+ * (the outputs are the same; only the speed differs):
+ *   rows_per_workgroup  0: the library's choice (what pkv_prefill_attn does);
+ *                       128: 8 waves of 16 rows (head_dim 256) or 4 of 32 (64, 128);
+ *                       192: 12 waves of 16 rows, head_dim 256 only.
+ * Any other value, or 192 with another head_dim, gives PKV_EINVAL.  The
+ * library takes 192 once the call has work for about two rounds of 192-row
+ * workgroups on every CU, else 128.
+ */
+pkv_status pkv_prefill_attn_ex(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
+                               int32_t num_q_heads, const void *k_cache, const void *v_cache,
+                               const int32_t *block_table, int32_t bt_cols, const int32_t *kv_lens,
+                               const int32_t *qo_indptr, int32_t batch, int32_t total_q,
+                               int32_t max_q, int32_t max_kv_len, int32_t causal, float scale,
+                               void *workspace, size_t workspace_bytes, int32_t rows_per_workgroup,
+                               void *stream);
 
 /*
  * pkv_route -- debug/test entry point, not on the hot path: the element

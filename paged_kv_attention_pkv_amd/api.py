@@ -73,6 +73,8 @@ _SIGS = {
     "pkv_prefill_workspace_bytes": ([_DP, _I32, _I32, _I32, _I32, _I32], _SZ),
     "pkv_prefill_attn": ([_DP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32,
                           _I32, ctypes.c_float, _VP, _SZ, _VP], ctypes.c_int),
+    "pkv_prefill_attn_ex": ([_DP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32,
+                             _I32, ctypes.c_float, _VP, _SZ, _I32, _VP], ctypes.c_int),
     "pkv_route": ([_DP, _VP, _I32, _VP, _I32, _I32, _VP, _VP], ctypes.c_int),
     "pkv_validate_host": ([_DP, _VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32, _I32, ctypes.c_char_p, _SZ],
                           ctypes.c_int),
@@ -287,9 +289,10 @@ def prefill_workspace_bytes(k_cache, batch, num_q_heads, total_q, max_q, max_kv_
 
 def prefill_attn(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, max_q: int, max_kv_len: int,
                  causal: bool = True, scale: float | None = None, out=None, lse=None, workspace=None,
-                 layout: str = "HND", return_lse: bool = False):
+                 layout: str = "HND", return_lse: bool = False, rows_per_workgroup: int = 0):
     """pkv_prefill_attn: ragged queries q [total_q, Hq, D] (offsets qo_indptr)
-    against kv_lens[r] keys of each request, end-aligned causal mask."""
+    against kv_lens[r] keys of each request, end-aligned causal mask.
+    rows_per_workgroup != 0 calls pkv_prefill_attn_ex with that tiling."""
     desc = cache_desc(k_cache, v_cache, layout)
     dev = k_cache.device
     _need(q, "q", k_cache.dtype, dev, 3)
@@ -313,13 +316,17 @@ def prefill_attn(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, max_q: in
         need = lib().pkv_prefill_workspace_bytes(ctypes.byref(desc), batch, hq, total_q, max_q, max_kv_len)
         if workspace is None and need:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-        rc = lib().pkv_prefill_attn(ctypes.byref(desc), _ptr(out), _ptr(lse), _ptr(q), hq, _ptr(k_cache),
-                                    _ptr(v_cache), _ptr(block_table), block_table.shape[1], _ptr(kv_lens),
-                                    _ptr(qo_indptr), batch, total_q, int(max_q), int(max_kv_len),
-                                    int(bool(causal)), float(scale), _ptr(workspace),
-                                    0 if workspace is None else workspace.numel() * workspace.element_size(),
-                                    _stream(k_cache))
-    _check("pkv_prefill_attn", rc)
+        args = (ctypes.byref(desc), _ptr(out), _ptr(lse), _ptr(q), hq, _ptr(k_cache), _ptr(v_cache),
+                _ptr(block_table), block_table.shape[1], _ptr(kv_lens), _ptr(qo_indptr), batch, total_q,
+                int(max_q), int(max_kv_len), int(bool(causal)), float(scale), _ptr(workspace),
+                0 if workspace is None else workspace.numel() * workspace.element_size())
+        if rows_per_workgroup:
+            name = "pkv_prefill_attn_ex"
+            rc = lib().pkv_prefill_attn_ex(*args, int(rows_per_workgroup), _stream(k_cache))
+        else:
+            name = "pkv_prefill_attn"
+            rc = lib().pkv_prefill_attn(*args, _stream(k_cache))
+    _check(name, rc)
     return (out, lse) if lse is not None else out
 
 
@@ -461,7 +468,7 @@ def prepare_append_decode(q, k_cache, v_cache, k_new, v_new, block_table, cache_
 
 def prepare_prefill(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, max_q: int, max_kv_len: int, out,
                     workspace=None, lse=None, causal: bool = True, scale: float | None = None,
-                    layout: str = "HND") -> PreparedCall:
+                    layout: str = "HND", rows_per_workgroup: int = 0) -> PreparedCall:
     desc = cache_desc(k_cache, v_cache, layout)
     dev = k_cache.device
     _need(q, "q", k_cache.dtype, dev, 3)
@@ -477,5 +484,8 @@ def prepare_prefill(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, max_q:
     args = (ctypes.byref(desc), _ptr(out), _ptr(lse), _ptr(q), hq, _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
             block_table.shape[1], _ptr(kv_lens), _ptr(qo_indptr), batch, total_q, int(max_q), int(max_kv_len),
             int(bool(causal)), float(scale), _ptr(workspace), nbytes)
-    return PreparedCall("pkv_prefill_attn", args, (k_cache, v_cache, q, out, block_table, kv_lens, qo_indptr,
-                                                   workspace, lse, desc))
+    name = "pkv_prefill_attn"
+    if rows_per_workgroup:
+        name, args = "pkv_prefill_attn_ex", args + (int(rows_per_workgroup),)
+    return PreparedCall(name, args, (k_cache, v_cache, q, out, block_table, kv_lens, qo_indptr, workspace, lse,
+                                     desc))

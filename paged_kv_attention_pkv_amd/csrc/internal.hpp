@@ -77,6 +77,7 @@ struct PrefillArgs {
     int32_t num_pages;  // page ids are clamped into 0..num_pages-1
     int32_t causal;
     float scale_log2;
+    int32_t wg_rows;  // query rows per workgroup: 0 = the library's choice, else 128 or (head_dim 256) 192
 };
 size_t prefill_workspace(const PoolGeom &g, int batch, int hq, int total_q, int max_q, int max_kv);
 hipError_t launch_prefill(const PoolGeom &g, const PrefillArgs &args, hipStream_t stream);

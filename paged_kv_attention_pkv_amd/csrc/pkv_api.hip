@@ -249,18 +249,20 @@ size_t pkv_prefill_workspace_bytes(const pkv_cache_desc *cache, int32_t batch, i
     return pkv::prefill_workspace(g, batch, num_q_heads, total_q, max_q, max_kv_len);
 }
 
-pkv_status pkv_prefill_attn(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
-                            int32_t num_q_heads, const void *k_cache, const void *v_cache,
-                            const int32_t *block_table, int32_t bt_cols, const int32_t *kv_lens,
-                            const int32_t *qo_indptr, int32_t batch, int32_t total_q, int32_t max_q,
-                            int32_t max_kv_len, int32_t causal, float scale, void *workspace,
-                            size_t workspace_bytes, void *stream) {
+pkv_status pkv_prefill_attn_ex(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
+                               int32_t num_q_heads, const void *k_cache, const void *v_cache,
+                               const int32_t *block_table, int32_t bt_cols, const int32_t *kv_lens,
+                               const int32_t *qo_indptr, int32_t batch, int32_t total_q, int32_t max_q,
+                               int32_t max_kv_len, int32_t causal, float scale, void *workspace,
+                               size_t workspace_bytes, int32_t rows_per_workgroup, void *stream) {
     PoolGeom g;
     pkv_status st = check_desc(cache, &g);
     if (st) return st;
     if ((st = check_heads(g, num_q_heads))) return st;
     if (g.dtype != 1) return PKV_EUNSUPPORTED;
     if (batch < 0 || total_q < 0 || max_q < 0 || max_kv_len < 0 || bt_cols < 0) return PKV_EINVAL;
+    if (rows_per_workgroup != 0 && rows_per_workgroup != 128 && !(rows_per_workgroup == 192 && g.head_dim == 256))
+        return PKV_EINVAL;
     if (batch == 0 || total_q == 0) return batch == 0 && total_q != 0 ? PKV_EINVAL : PKV_OK;
     if (!out || !q || !k_cache || !v_cache || !block_table || !kv_lens || !qo_indptr) return PKV_EINVAL;
     if ((int64_t)max_kv_len > (int64_t)bt_cols * kPageSize) return PKV_EINVAL;
@@ -291,7 +293,19 @@ pkv_status pkv_prefill_attn(const pkv_cache_desc *cache, void *out, float *lse, 
     a.num_pages = g.num_pages;
     a.causal = causal ? 1 : 0;
     a.scale_log2 = scale * 1.4426950408889634f;
+    a.wg_rows = rows_per_workgroup;
     return launch_status(pkv::launch_prefill(g, a, (hipStream_t)stream));
+}
+
+pkv_status pkv_prefill_attn(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
+                            int32_t num_q_heads, const void *k_cache, const void *v_cache,
+                            const int32_t *block_table, int32_t bt_cols, const int32_t *kv_lens,
+                            const int32_t *qo_indptr, int32_t batch, int32_t total_q, int32_t max_q,
+                            int32_t max_kv_len, int32_t causal, float scale, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    return pkv_prefill_attn_ex(cache, out, lse, q, num_q_heads, k_cache, v_cache, block_table, bt_cols, kv_lens,
+                               qo_indptr, batch, total_q, max_q, max_kv_len, causal, scale, workspace,
+                               workspace_bytes, 0, stream);
 }
 
 pkv_status pkv_route(const pkv_cache_desc *cache, const int32_t *block_table, int32_t bt_cols,

@@ -355,7 +355,7 @@ void prefill_kernel(PrefillArgs a, int n_qtiles) {
 }
 
 // ---------------------------------------------------------------------------
-// 16 query rows per wave, 8 waves per workgroup (two per SIMD)
+// 16 query rows per wave, 8 or 12 waves per workgroup
 // ---------------------------------------------------------------------------
 //
 // The same walk as prefill_kernel with v_mfma_f32_16x16x32_bf16 blocks:
@@ -364,18 +364,37 @@ void prefill_kernel(PrefillArgs a, int n_qtiles) {
 // Lane (g = lane/16, c = lane%16) owns query row c of its wave; the softmax
 // statistics of a row live in lanes c, c+16, c+32, c+48 (row-swap permutes).
 // With half the rows per wave the accumulators take half the registers, so
-// two waves share each SIMD and one wave's softmax, barrier wait and LDS
-// reads overlap the other's MFMAs; each K/V byte read from LDS feeds half as
+// several waves share each SIMD and one wave's softmax, barrier wait and LDS
+// reads overlap another's MFMAs; each K/V byte read from LDS feeds half as
 // many rows as in prefill_kernel.
 //
 // Key order inside a 32-key PV step: lane group g takes keys 4g..4g+3 of the
 // first 16-key score block and 4g..4g+3 of the second, which is exactly where
 // the S^T accumulators leave them, so P^T needs no data movement; the V^T
 // operand is read in the same key order (two transposing reads per block).
-constexpr int kWaves16 = 8;
+//
+// Two workgroup sizes (Cfg16): 8 waves (128 query rows, two waves per SIMD)
+// and 12 waves (192 rows, three per SIMD, which fits only if a wave stays
+// within 168 registers).  Every K/V tile moved into LDS serves all the rows
+// of the workgroup, so the 12-wave kernel moves a third fewer bytes per flop
+// and has a third more waves to hide LDS latency; on few requests its
+// coarser tiles leave CUs idle at the end, and there the 8-wave kernel wins.
+// The LDS operand reads of a wave are issued ahead of the MFMAs that use
+// them (K: KD k-steps, V^T: VD groups of VG dim blocks), as many as the
+// registers allow: a wave alone is bound by LDS latency, not bandwidth.
 constexpr int kRows16 = 16;
-constexpr int kBM16 = kWaves16 * kRows16;  // query rows per workgroup
-constexpr int kThreads16 = kWaves16 * kWave;
+constexpr int kDmaWaves16 = 8;  // waves that issue a tile's transfers
+template <int W>
+struct Cfg16 {
+    static_assert(W == 8 || W == 12, "workgroup of 8 or 12 waves");
+    static constexpr int WAVES = W;
+    static constexpr int THREADS = W * kWave;
+    static constexpr int BM = W * kRows16;   // query rows per workgroup
+    static constexpr int PER_SIMD = W / 4;    // resident waves per SIMD
+    static constexpr int KD = W == 8 ? 2 : 1;  // k-steps of K reads in flight ahead of the MFMAs
+    static constexpr int VG = 2;               // dim blocks per group of V^T reads
+    static constexpr int VD = 3;               // groups of V^T reads in flight ahead of the MFMAs
+};
 
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -416,21 +435,22 @@ struct Dma16 {
 __device__ __forceinline__ int dma_block16(int tile, int wave) { return tile * (kBN16 / kPage) + ((kBN16 / 16 * wave) >> 3); }
 
 // Table entries are staged in LDS, kIds16 at a time (the blocks of 2 * kIds16
-// / (kBN16 / 16) ... tiles), by the whole workgroup before the transfers
-// that use them: the compiler cannot tell the LDS transfers from stores to
-// the table, so a table read between them would be a vector load whose wait
-// covers every transfer in flight.  Entries at or past kv read as 0.
+// / (kBN16 / 16) ... tiles), by the whole workgroup (NT threads) before the
+// transfers that use them: the compiler cannot tell the LDS transfers from
+// stores to the table, so a table read between them would be a vector load
+// whose wait covers every transfer in flight.  Entries at or past kv read as 0.
 constexpr int kIds16 = 4096;
+template <int NT>
 __device__ __forceinline__ void stage_ids16(const int32_t *bt, int b0, int kv, int *ids) {
-    constexpr int N = kIds16 / kThreads16;
+    constexpr int N = (kIds16 + NT - 1) / NT;
     const int last = (kv - 1) / kPage;  // last block holding a key (kv >= 1 here)
     int v[N];
 #pragma unroll
-    for (int i = 0; i < N; ++i) v[i] = bt[min(b0 + (int)threadIdx.x + i * kThreads16, last)];  // all in flight
+    for (int i = 0; i < N; ++i) v[i] = bt[min(b0 + (int)threadIdx.x + i * NT, last)];  // all in flight
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        const int blk = b0 + (int)threadIdx.x + i * kThreads16;
-        ids[threadIdx.x + i * kThreads16] = blk <= last ? v[i] : 0;
+        const int slot = (int)threadIdx.x + i * NT;
+        if (slot < kIds16) ids[slot] = b0 + slot <= last ? v[i] : 0;
     }
 }
 
@@ -472,9 +492,22 @@ __device__ __forceinline__ void dma_tile16(const PrefillArgs &a, int entry, int 
 // flight it waits for all of them (vmcnt 0) before the read, which would
 // drain the transfers running ahead.  Here the read is opaque to the
 // compiler: the caller waits for it (lgkm_wait) before using the result.
-__device__ __forceinline__ u32x2 ld_tr_lds(uint32_t lds_byte_addr) {
+// The byte offset `off` (a constant once the loops are unrolled) goes into
+// the instruction's offset field, so a lane keeps one address register per
+// pattern instead of one per read.
+__device__ __forceinline__ u32x2 ld_tr_lds(uint32_t lds_byte_addr, uint32_t off) {
     u32x2 r;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(lds_byte_addr) : "memory");
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(lds_byte_addr), "i"(off) : "memory");
+    return r;
+}
+
+// A 16-byte LDS read written out the same way.  Left to the compiler, the K
+// operand reads were hoisted into as many registers as it could find, which
+// leaves no room for a third wave per SIMD; written out, the kernel issues
+// them exactly KD k-steps ahead.
+__device__ __forceinline__ u32x4 ld_lds128(uint32_t lds_byte_addr, uint32_t off) {
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(lds_byte_addr), "i"(off) : "memory");
     return r;
 }
 
@@ -487,6 +520,26 @@ __device__ __forceinline__ void lgkm_wait(u32x4 (&regs)[K]) {
     asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
 #pragma unroll
     for (int k = 0; k < K; ++k) asm volatile("" : "+v"(regs[k]));
+}
+
+// lgkm_wait with a count n that is a constant once the loops are unrolled.
+template <int K>
+__device__ __forceinline__ void lgkm_wait_n(int n, u32x4 (&regs)[K]) {
+    if (n <= 0) lgkm_wait<0>(regs);
+    else if (n == 1) lgkm_wait<1>(regs);
+    else if (n == 2) lgkm_wait<2>(regs);
+    else if (n == 3) lgkm_wait<3>(regs);
+    else if (n == 4) lgkm_wait<4>(regs);
+    else if (n == 5) lgkm_wait<5>(regs);
+    else if (n == 6) lgkm_wait<6>(regs);
+    else if (n == 7) lgkm_wait<7>(regs);
+    else if (n == 8) lgkm_wait<8>(regs);
+    else if (n == 9) lgkm_wait<9>(regs);
+    else if (n == 10) lgkm_wait<10>(regs);
+    else if (n == 11) lgkm_wait<11>(regs);
+    else if (n == 12) lgkm_wait<12>(regs);
+    else if (n == 13) lgkm_wait<13>(regs);
+    else lgkm_wait<14>(regs);
 }
 
 // Wait until this wave's transfers of the tile after the current one have
@@ -509,10 +562,13 @@ __device__ __forceinline__ void wait_transfers(int ahead) {
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads16) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D, int W>
+__global__ __launch_bounds__(Cfg16<W>::THREADS) __attribute__((amdgpu_waves_per_eu(Cfg16<W>::PER_SIMD,
+                                                                                   Cfg16<W>::PER_SIMD)))
 void prefill16_kernel(PrefillArgs a, int n_qtiles) {
     using L = Dma16<D>;
+    using C = Cfg16<W>;
+    constexpr int kBM16 = C::BM;
     constexpr int KS = D / 32;    // k-steps of the QK contraction
     constexpr int DB = D / 16;    // 16-dim blocks of the output
     constexpr int NB = kBN16 / 16;  // 16-key score blocks per tile
@@ -540,7 +596,7 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
     const int g = h / G;
     const int32_t *bt = a.block_table + (int64_t)r * a.bt_cols;
 
-    const int wave = threadIdx.x >> 6;
+    const int wave = uniform(threadIdx.x >> 6);  // scalar: the per-wave tests below are scalar branches
     const int lane = threadIdx.x & 63;
     const int grp = lane >> 4;
     const int col = lane & 15;
@@ -593,14 +649,16 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
 
     // table entries of blocks 0 .. kIds16-1, then tiles 0 .. kNST16-2 in
     // flight, then wait for tile 0
-    const int wv = uniform(wave);
+    // waves 0 .. kDmaWaves16-1 issue the transfers
+    const int wv = wave;
     int *ids = reinterpret_cast<int *>(smem + L::IDS);
     int window = 0;  // ids holds blocks window*kIds16 ..
-    stage_ids16(bt, 0, kv, ids);
+    stage_ids16<C::THREADS>(bt, 0, kv, ids);
     __syncthreads();
     auto entry = [&](int t) { return uniform(ids[dma_block16(t, wv) - window * kIds16]); };
     const int pro = min(kNST16 - 1, n_tiles);
-    for (int t = 0; t < pro; ++t) dma_tile16<D>(a, entry(t), g, t, wv, kv, smem + t * L::BUF);
+    if (wv < kDmaWaves16)
+        for (int t = 0; t < pro; ++t) dma_tile16<D>(a, entry(t), g, t, wv, kv, smem + t * L::BUF);
     wait_transfers<TPW>(pro - 1);
     __syncthreads();
     for (int tile = 0; tile < n_tiles; ++tile) {
@@ -609,37 +667,45 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
         if (pre < n_tiles) {
             // past the staged entries (rows of more than 2 * kIds16 * 16 / (kBN16 / 16) keys): restage,
             // every wave at the same tile; its loads' wait also drains the transfers in flight
-            if (dma_block16(pre, kWaves16 - 1) >= (window + 1) * kIds16) {
+            if (dma_block16(pre, kDmaWaves16 - 1) >= (window + 1) * kIds16) {
                 __syncthreads();
                 window = dma_block16(pre, 0) / kIds16;
-                stage_ids16(bt, window * kIds16, kv, ids);
+                stage_ids16<C::THREADS>(bt, window * kIds16, kv, ids);
                 __syncthreads();
             }
-            dma_tile16<D>(a, entry(pre), g, pre, wv, kv, smem + (pre & (kNST16 - 1)) * L::BUF);
+            if (wv < kDmaWaves16)
+                dma_tile16<D>(a, entry(pre), g, pre, wv, kv, smem + (pre & (kNST16 - 1)) * L::BUF);
         }
 
         if (tile * kBN16 <= last_key_wave) {
             const uint16_t *ks = cur;
             const uint16_t *vs = cur + L::TILE;
             // S^T = K . Q^T: per k-step, the NB key blocks' K operands are
-            // read together, the next k-step's reads issued before this one's
-            // MFMAs
+            // read together, KD k-steps ahead of the MFMAs that use them
+            constexpr int KD = C::KD;
+            static_assert(NB * KD <= 15, "LDS read counter");
             f32x4 sc[NB];
 #pragma unroll
             for (int u = 0; u < NB; ++u) sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-            u32x4 kb[2][NB];
+            u32x4 kb[KD + 1][NB];
+            const uint32_t ks_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t *)ks;
+            const uint32_t ka_lo = ks_addr + 2u * (uint32_t)k_lo, ka_hi = ks_addr + 2u * (uint32_t)k_hi;
             auto read_k = [&](int k, u32x4 (&dst)[NB]) {
 #pragma unroll
                 for (int u = 0; u < NB; ++u)
-                    dst[u] = *reinterpret_cast<const u32x4 *>(ks + ((k & 2) ? k_hi : k_lo) + 8 * u * L::PAIR + 32 * k);
+                    dst[u] = ld_lds128((k & 2) ? ka_hi : ka_lo, 2u * (uint32_t)(8 * u * L::PAIR + 32 * k));
             };
-            read_k(0, kb[0]);
+#pragma unroll
+            for (int k = 0; k < KD; ++k) read_k(k, kb[k]);
 #pragma unroll
             for (int k = 0; k < KS; ++k) {
-                if (k + 1 < KS) read_k(k + 1, kb[(k + 1) & 1]);
+                // k-step k's reads are done once only the r later k-steps issued remain
+                const int r = KD - 1 < KS - 1 - k ? KD - 1 : KS - 1 - k;
+                lgkm_wait_n(NB * r, kb[k % (KD + 1)]);
+                if (k + KD < KS) read_k(k + KD, kb[(k + KD) % (KD + 1)]);
 #pragma unroll
                 for (int u = 0; u < NB; ++u)
-                    sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[k & 1][u]),
+                    sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[k % (KD + 1)][u]),
                                                                     __builtin_bit_cast(bf16x8, qop[k]), sc[u], 0, 0, 0);
             }
             // scores in log2 units; element i of block u is key tile*64 + 16u + 4grp + i
@@ -683,38 +749,39 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
                                pack_bf16x2(p[6], p[7])};
             }
             // O^T += V^T . P^T; V^T operands read in groups of VG dim blocks,
-            // the next group's reads issued before the current group's MFMAs
-            constexpr int VG = DB < 4 ? DB : 4;
+            // VD groups ahead of the MFMAs that use them
+            constexpr int VG = C::VG, VD = C::VD;
+            static_assert(DB % VG == 0 && 2 * VG * VD <= 15, "LDS read counter");
             constexpr int NVG = (NB / 2) * (DB / VG);
-            u32x4 vb[2][VG];
-            // LDS byte address of this lane's V reads in the current stage
+            u32x4 vb[VD + 1][VG];
+            // LDS byte addresses of this lane's two V read patterns in the current stage
             const uint32_t vs_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t *)vs;
+            const uint32_t va_lo = vs_addr + 2u * (uint32_t)v_lo, va_hi = vs_addr + 2u * (uint32_t)v_hi;
             auto read_v = [&](int gi, u32x4 (&dst)[VG]) {
                 const int t = gi / (DB / VG), db0 = (gi % (DB / VG)) * VG;
 #pragma unroll
                 for (int j = 0; j < VG; ++j) {
                     const int db = db0 + j;
-                    const uint32_t base = vs_addr + 2u * (uint32_t)(((db & 4) ? v_hi : v_lo) + 16 * t * L::PAIR + 16 * db);
-                    const u32x2 lo = ld_tr_lds(base);
-                    const u32x2 hi = ld_tr_lds(base + 2u * 8u * L::PAIR);
+                    const uint32_t off = 2u * (uint32_t)(16 * t * L::PAIR + 16 * db);
+                    const u32x2 lo = ld_tr_lds((db & 4) ? va_hi : va_lo, off);
+                    const u32x2 hi = ld_tr_lds((db & 4) ? va_hi : va_lo, off + 2u * 8u * L::PAIR);
                     dst[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
                 }
             };
-            read_v(0, vb[0]);
+#pragma unroll
+            for (int gi = 0; gi < VD && gi < NVG; ++gi) read_v(gi, vb[gi]);
 #pragma unroll
             for (int gi = 0; gi < NVG; ++gi) {
-                if (gi + 1 < NVG) {
-                    read_v(gi + 1, vb[(gi + 1) & 1]);
-                    lgkm_wait<2 * VG>(vb[gi & 1]);  // group gi's reads are done, gi+1's may run
-                } else {
-                    lgkm_wait<0>(vb[gi & 1]);
-                }
+                // group gi's reads are done once only the r later groups issued remain
+                const int r = VD - 1 < NVG - 1 - gi ? VD - 1 : NVG - 1 - gi;
+                lgkm_wait_n(2 * VG * r, vb[gi % (VD + 1)]);
+                if (gi + VD < NVG) read_v(gi + VD, vb[(gi + VD) % (VD + 1)]);
                 const int t = gi / (DB / VG), db0 = (gi % (DB / VG)) * VG;
 #pragma unroll
                 for (int j = 0; j < VG; ++j)
                     acc[db0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, vb[gi & 1][j]), __builtin_bit_cast(bf16x8, pop[t]), acc[db0 + j],
-                        0, 0, 0);
+                        __builtin_bit_cast(bf16x8, vb[gi % (VD + 1)][j]), __builtin_bit_cast(bf16x8, pop[t]),
+                        acc[db0 + j], 0, 0, 0);
             }
         }
         if (tile + 1 < n_tiles) {
@@ -738,22 +805,41 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
     if (grp == 0 && a.lse) a.lse[(int64_t)(q0 + i_row) * a.hq + h] = (m + log2f(lt)) * kLn2f;
 }
 
-template <int D>
+template <int D, int W>
 hipError_t launch16_d(const PrefillArgs &a, hipStream_t stream) {
     constexpr int kSmem16 = Dma16<D>::BYTES + kIds16 * 4;
-    const int n_qtiles = (a.max_q + kBM16 - 1) / kBM16;
+    constexpr int BM = Cfg16<W>::BM;
+    const int n_qtiles = (a.max_q + BM - 1) / BM;
     const int64_t grid = (int64_t)a.batch * n_qtiles * a.hq;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill16_kernel<D>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill16_kernel<D, W>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, kSmem16);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(prefill16_kernel<D>, dim3((unsigned)grid), dim3(kThreads16), kSmem16, stream, a,
-                       n_qtiles);
+    hipLaunchKernelGGL((prefill16_kernel<D, W>), dim3((unsigned)grid), dim3(Cfg16<W>::THREADS), kSmem16, stream,
+                       a, n_qtiles);
     return hipGetLastError();
+}
+
+// Query rows per workgroup of the 16-row kernel when the caller leaves the
+// choice to the library: 192 once the call has work for about two rounds of
+// 192-row workgroups on every CU (counted from total_q, which ragged tails
+// only raise), else 128, whose finer tiles end closer together.
+int auto_wg_rows16(const PrefillArgs &a) {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            cus = n;
+        else
+            cus = 256;
+    }
+    const int64_t wgs192 = ((int64_t)a.total_q + Cfg16<12>::BM - 1) / Cfg16<12>::BM * a.hq;
+    return wgs192 >= 2 * (int64_t)cus ? Cfg16<12>::BM : Cfg16<8>::BM;
 }
 
 #ifndef PKV_PREFILL16_DIMS
@@ -763,7 +849,13 @@ hipError_t launch16_d(const PrefillArgs &a, hipStream_t stream) {
 template <int D>
 hipError_t launch_d(const PrefillArgs &a, hipStream_t stream) {
     constexpr int bit = D == 64 ? 1 : (D == 128 ? 2 : 4);
-    if constexpr ((PKV_PREFILL16_DIMS & bit) != 0) return launch16_d<D>(a, stream);
+    if constexpr ((PKV_PREFILL16_DIMS & bit) != 0) {
+        const int rows = a.wg_rows > 0 ? a.wg_rows : auto_wg_rows16(a);
+        if (rows == Cfg16<12>::BM) return launch16_d<D, 12>(a, stream);
+        if (rows == Cfg16<8>::BM) return launch16_d<D, 8>(a, stream);
+        return hipErrorInvalidValue;
+    }
+    if (a.wg_rows != 0 && a.wg_rows != kBM) return hipErrorInvalidValue;
     const int n_qtiles = (a.max_q + kBM - 1) / kBM;
     const int64_t grid = (int64_t)a.batch * n_qtiles * a.hq;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;

@@ -2,7 +2,9 @@
 
 Bar: |d| <= 2e-2 + 2e-2|ref| element by element on out and lse.  Large
 workloads are checked on sampled rows: the first and last rows of requests,
-each computed by the oracle as its own chunked-prefill request."""
+each computed by the oracle as its own chunked-prefill request.  At head_dim
+256 both workgroup tilings (128 and 192 query rows, forced through
+pkv_prefill_attn_ex) are checked next to the library's own choice."""
 import numpy as np
 import pytest
 import torch
@@ -14,12 +16,13 @@ from gpu_common import BF16_TOL, PrefillCase, compare, say
 pytestmark = pytest.mark.gpu
 
 
-def _parity(spec, causal=True, sample=None, reqs=None, gen_device="cpu"):
+def _parity(spec, causal=True, sample=None, reqs=None, gen_device="cpu", rows=0):
     say(f"[prefill parity] {spec.name} B={spec.batch} Hq={spec.hq} Hkv={spec.hkv} D={spec.head_dim} "
-        f"q={spec.q_lens.tolist()[:8]} kv={spec.kv_lens.tolist()[:8]} causal={causal} seed={spec.seed}")
+        f"q={spec.q_lens.tolist()[:8]} kv={spec.kv_lens.tolist()[:8]} causal={causal} seed={spec.seed} "
+        f"rows/wg={rows or 'auto'}")
     case = PrefillCase(spec, gen_device=gen_device)
     kc, vc, kv = case.gpu_pools()
-    out, lse = case.gpu_prefill(kc, vc, kv, causal=causal)
+    out, lse = case.gpu_prefill(kc, vc, kv, causal=causal, rows=rows)
     torch.cuda.synchronize()
     assert np.array_equal(kv.cpu().numpy(), spec.kv_lens)
     okc, ovc, okv, obt, oreqs = case.oracle_pools(reqs)
@@ -42,10 +45,21 @@ def test_small_ragged(d, hq, hkv):
     _parity(spec)
 
 
-@pytest.mark.parametrize("d", [128, 256])
-def test_non_causal(d):
+@pytest.mark.parametrize("rows", [128, 192])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (48, 8)])
+def test_d256_tilings_ragged(rows, hq, hkv):
+    """Both workgroup tilings of head_dim 256, with requests ending inside,
+    at and just past a 192-row tile and one 128-row tile."""
+    q = [1, 17, 191, 192, 193, 400, 129]
+    kv = [1, 17, 300, 192, 611, 900, 129]
+    spec = wl.prefill_spec(q_lens=q, kv_lens=kv, hq=hq, hkv=hkv, head_dim=256, seed=rows + hq)
+    _parity(spec, rows=rows)
+
+
+@pytest.mark.parametrize("d,rows", [(128, 0), (256, 128), (256, 192)])
+def test_non_causal(d, rows):
     spec = wl.prefill_spec(q_lens=[3, 64, 130], kv_lens=[50, 64, 400], hq=12, hkv=4, head_dim=d, seed=7)
-    _parity(spec, causal=False)
+    _parity(spec, causal=False, rows=rows)
 
 
 def test_nhd_layout():
@@ -53,9 +67,10 @@ def test_nhd_layout():
     _parity(spec)
 
 
-def test_fixed_b1_q1023():
+@pytest.mark.parametrize("rows", [0, 192])
+def test_fixed_b1_q1023(rows):
     """The single request q_len = kv_len = 1023, Hq 48 / Hkv 8, D 256, every row."""
-    _parity(wl.prefill_spec(fixed_1023=True))
+    _parity(wl.prefill_spec(fixed_1023=True), rows=rows)
 
 
 @pytest.mark.parametrize("batch", [1, 2, 4, 8, 16, 32])
@@ -68,18 +83,28 @@ def test_random_batches_full_size(batch):
     _parity(spec, sample=4, reqs=reqs, gen_device="cuda")
 
 
-def test_permutation_invariance_and_determinism():
+@pytest.mark.parametrize("batch,rows", [(2, 192), (8, 128)])
+def test_random_batches_forced_tiling(batch, rows):
+    """Full-size random batches on the tiling the library would not pick for them."""
+    spec = wl.prefill_spec(batch=batch)
+    rng = np.random.default_rng(batch + 100)
+    reqs = sorted(rng.choice(batch, min(4, batch), replace=False).tolist())
+    _parity(spec, sample=4, reqs=reqs, gen_device="cuda", rows=rows)
+
+
+@pytest.mark.parametrize("rows", [128, 192])
+def test_permutation_invariance_and_determinism(rows):
     spec1 = wl.prefill_spec(q_lens=[100, 257], kv_lens=[300, 257], hq=12, hkv=2, head_dim=256, seed=21)
     spec2 = wl.prefill_spec(q_lens=[100, 257], kv_lens=[300, 257], hq=12, hkv=2, head_dim=256, seed=21)
     rng = np.random.default_rng(5)
     remap = np.concatenate([[0], rng.permutation(spec1.num_pages - 1) + 1]).astype(np.int32)
     spec2.block_table = np.where(spec1.block_table > 0, remap[spec1.block_table], 0).astype(np.int32)
-    say("[prefill] permutation invariance")
+    say(f"[prefill] permutation invariance, rows/wg {rows}")
     c1, c2 = PrefillCase(spec1), PrefillCase(spec2)
-    o1, l1 = c1.gpu_prefill(*c1.gpu_pools())
-    o2, l2 = c2.gpu_prefill(*c2.gpu_pools())
+    o1, l1 = c1.gpu_prefill(*c1.gpu_pools(), rows=rows)
+    o2, l2 = c2.gpu_prefill(*c2.gpu_pools(), rows=rows)
     k1, v1, kv1 = c1.gpu_pools()
-    o3, l3 = c1.gpu_prefill(k1, v1, kv1)
+    o3, l3 = c1.gpu_prefill(k1, v1, kv1, rows=rows)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
@@ -137,10 +162,11 @@ def test_no_visible_key_rows():
     assert torch.isfinite(o[3:]).all() and torch.isfinite(l[3:]).all()
 
 
-def test_long_kv_restages_table_window():
+@pytest.mark.parametrize("rows", [128, 192])
+def test_long_kv_restages_table_window(rows):
     """One request of 70000 keys at D = 256: more than the 4096 page-table
     entries (65536 keys) the 16-row kernel stages in LDS at a time, so it
     restages the window during the walk.  The first and last 4 rows (the last
     see every key) are checked."""
     spec = wl.prefill_spec(q_lens=[40], kv_lens=[70000], hq=8, hkv=8, head_dim=256, seed=11)
-    _parity(spec, sample=4, gen_device="cuda")
+    _parity(spec, sample=4, gen_device="cuda", rows=rows)
