@@ -349,6 +349,10 @@ def bench_prefill(args, torch, pkv, wl):
     tfs = flops / (mean * 1e-3) / 1e12
     traffic = traffic_from_profile(os.path.join(ROOT, "paged_kv_attention_pkv_amd", "csrc", "prefill.hip"),
                                    f"prefill16_kernel_{spec.name}_pmc.txt")
+    # the workgroup size the library picks for this call, by the rule stated
+    # in include/pkv.h (192 rows once ceil(total_q / 192) * Hq >= 2 * CUs)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    waves = 12 if -(-int(spec.q_lens.sum()) // 192) * spec.hq >= 2 * cus else 8
     result = {
         "metric": "paged causal prefill attn: TFLOP/s (% bf16 MFMA peak), D256 Hq48/Hkv8",
         "value": round(flops * L / (ms * 1e-3) / 1e12, 2),
@@ -361,7 +365,8 @@ def bench_prefill(args, torch, pkv, wl):
                    "step": "per layer: one pkv_prefill_attn call (own pools and inputs)",
                    "launch": "eager" if args.eager else "hip graph", "parallelism": "none (1 GPU)"},
         "us_per_call": round(ms * 1e3 / L, 2),
-        "roofline": {"bound": "mfma", "kernel": "prefill16_kernel<256> (one launch per pkv_prefill_attn)", "achieved": round(tfs, 2),
+        "roofline": {"bound": "mfma", "kernel": f"prefill16_kernel<256, {waves}> (one launch per pkv_prefill_attn, "
+                                                  f"{16 * waves} query rows per workgroup)", "achieved": round(tfs, 2),
                      "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s", "frac": round(tfs / BF16_MFMA_PEAK_TFS, 4),
                      "traffic": None if traffic is None else int(traffic),
                      "traffic_unit": "HBM bytes per launch", "flops_per_launch": flops},
