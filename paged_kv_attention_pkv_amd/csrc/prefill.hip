@@ -382,6 +382,8 @@ void prefill_kernel(PrefillArgs a, int n_qtiles) {
 // The LDS operand reads of a wave are issued ahead of the MFMAs that use
 // them (K: KD k-steps, V^T: VD groups of VG dim blocks), as many as the
 // registers allow: a wave alone is bound by LDS latency, not bandwidth.
+// At 12 waves the registers are full: the compiler keeps one value that only
+// the page-table restage (rows past 65536 keys) uses in scratch memory.
 constexpr int kRows16 = 16;
 constexpr int kDmaWaves16 = 8;  // waves that issue a tile's transfers
 template <int W>
@@ -391,7 +393,7 @@ struct Cfg16 {
     static constexpr int THREADS = W * kWave;
     static constexpr int BM = W * kRows16;   // query rows per workgroup
     static constexpr int PER_SIMD = W / 4;    // resident waves per SIMD
-    static constexpr int KD = W == 8 ? 2 : 1;  // k-steps of K reads in flight ahead of the MFMAs
+    static constexpr int KD = 2;               // k-steps of K reads in flight ahead of the MFMAs
     static constexpr int VG = 2;               // dim blocks per group of V^T reads
     static constexpr int VD = 3;               // groups of V^T reads in flight ahead of the MFMAs
 };
@@ -688,6 +690,9 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
 #pragma unroll
             for (int u = 0; u < NB; ++u) sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
             u32x4 kb[KD + 1][NB];
+            // raised wave priority while a wave issues MFMAs: when the waves of a
+            // SIMD compete for issue, the one feeding the matrix core goes first
+            __builtin_amdgcn_s_setprio(1);
             const uint32_t ks_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t *)ks;
             const uint32_t ka_lo = ks_addr + 2u * (uint32_t)k_lo, ka_hi = ks_addr + 2u * (uint32_t)k_hi;
             auto read_k = [&](int k, u32x4 (&dst)[NB]) {
@@ -708,6 +713,7 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
                     sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[k % (KD + 1)][u]),
                                                                     __builtin_bit_cast(bf16x8, qop[k]), sc[u], 0, 0, 0);
             }
+            __builtin_amdgcn_s_setprio(0);
             // scores in log2 units; element i of block u is key tile*64 + 16u + 4grp + i
             const bool need_mask = tile * kBN16 + kBN16 - 1 > common_keys;
             float mx = kNegInff;
@@ -754,6 +760,7 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
             static_assert(DB % VG == 0 && 2 * VG * VD <= 15, "LDS read counter");
             constexpr int NVG = (NB / 2) * (DB / VG);
             u32x4 vb[VD + 1][VG];
+            __builtin_amdgcn_s_setprio(1);
             // LDS byte addresses of this lane's two V read patterns in the current stage
             const uint32_t vs_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t *)vs;
             const uint32_t va_lo = vs_addr + 2u * (uint32_t)v_lo, va_hi = vs_addr + 2u * (uint32_t)v_hi;
@@ -783,6 +790,7 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
                         __builtin_bit_cast(bf16x8, vb[gi % (VD + 1)][j]), __builtin_bit_cast(bf16x8, pop[t]),
                         acc[db0 + j], 0, 0, 0);
             }
+            __builtin_amdgcn_s_setprio(0);
         }
         if (tile + 1 < n_tiles) {
             // this wave's transfers of the next tile have landed, then every wave's
