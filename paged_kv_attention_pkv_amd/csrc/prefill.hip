@@ -10,8 +10,9 @@
 // reading KV head h / G.
 //
 // Two kernels.  head_dim 256 runs prefill16_kernel (below: 16 query rows
-// per wave, 8 waves, two per SIMD, K/V tiles moved from HBM to LDS by
-// buffer-to-LDS transfers); head_dim 64 and 128 run prefill_kernel:
+// per wave, 8 or 12 waves by call size, two or three per SIMD, K/V tiles
+// moved from HBM to LDS by buffer-to-LDS transfers, output rows written
+// through LDS); head_dim 64 and 128 run prefill_kernel:
 //
 // One workgroup (4 waves) per (request, tile of 128 query rows,
 // query head); wave w owns query rows 32w .. 32w+31 of the tile.  Keys are
