@@ -100,7 +100,14 @@ __device__ __forceinline__ u32x4 bld16(Rsrc r, uint32_t off) { return __builtin_
 
 // 16-byte global load / store.
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+// A 16-byte load with the non-temporal hint (data read once).
+__device__ __forceinline__ u32x4 ld16_stream(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
 __device__ __forceinline__ u32x2 ld8(const void *p) { return *reinterpret_cast<const u32x2 *>(p); }
+__device__ __forceinline__ u32x2 ld8_stream(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+}
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
 
 }  // namespace pkv

