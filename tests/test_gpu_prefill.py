@@ -67,6 +67,15 @@ def test_nhd_layout():
     _parity(spec)
 
 
+@pytest.mark.parametrize("rows", [128, 192])
+def test_nhd_layout_d256(rows):
+    """NHD pools at head_dim 256: the 16-row kernel's tile transfers step by
+    the token stride Hkv*D, not D."""
+    spec = wl.prefill_spec(q_lens=[33, 200, 5], kv_lens=[90, 460, 5], hq=12, hkv=2, head_dim=256, seed=9,
+                           layout="NHD")
+    _parity(spec, rows=rows)
+
+
 @pytest.mark.parametrize("rows", [0, 192])
 def test_fixed_b1_q1023(rows):
     """The single request q_len = kv_len = 1023, Hq 48 / Hkv 8, D 256, every row."""
