@@ -1,0 +1,62 @@
+"""GPU parity on seeded random small shapes, decode and prefill, against the
+oracle: head counts and GQA ratios, head dims, dtypes, layouts, ragged and
+empty rows, forced split-worker counts and prefill tilings drawn at random
+(fixed seeds), every output row compared.  Bar as in the other parity tests."""
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_attention_pkv_amd import workloads as wl
+from gpu_common import BF16_TOL, DecodeCase, PrefillCase, compare, say, tol
+
+pytestmark = pytest.mark.gpu
+
+HEADS = [(4, 4), (8, 2), (12, 4), (16, 1), (32, 8), (6, 1), (24, 8), (2, 2)]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_decode(seed):
+    rng = np.random.default_rng(1000 + seed)
+    b = int(rng.integers(1, 41))
+    hq, hkv = HEADS[rng.integers(len(HEADS))]
+    d = int(rng.choice([64, 128, 128, 256]))
+    dtype = "f32" if rng.random() < 0.25 else "bf16"
+    layout = "NHD" if rng.random() < 0.3 else "HND"
+    lens = np.minimum(np.exp(rng.uniform(0, np.log(3000), size=b)).astype(np.int32) - 1, 2999)
+    lens[rng.random(b) < 0.1] = 0
+    workers = 0 if rng.random() < 0.6 else int(rng.integers(1, 1200))
+    say(f"[random decode {seed}] B={b} Hq={hq} Hkv={hkv} D={d} {dtype} {layout} workers={workers} "
+        f"lens[:6]={lens[:6].tolist()}")
+    spec = wl.custom_decode_spec(lens, hq=hq, hkv=hkv, head_dim=d, dtype=dtype, seed=2000 + seed, layout=layout)
+    case = DecodeCase(spec)
+    kc, vc, kl = case.gpu_pools()
+    out, lse = case.gpu_decode(kc, vc, kl, workers=workers)
+    torch.cuda.synchronize()
+    okc, ovc, olens, obt = case.oracle_pools()
+    ro, rl = case.oracle_decode(okc, ovc, olens, obt)
+    compare(out.cpu(), ro, *tol(spec), "out")
+    compare(lse.cpu(), rl, *tol(spec), "lse")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_prefill(seed):
+    rng = np.random.default_rng(3000 + seed)
+    b = int(rng.integers(1, 7))
+    hq, hkv = HEADS[rng.integers(len(HEADS))]
+    d = int(rng.choice([64, 128, 256, 256]))
+    layout = "NHD" if rng.random() < 0.3 else "HND"
+    q = rng.integers(1, 401, size=b).astype(np.int32)
+    kv = (q + rng.integers(0, 601, size=b)).astype(np.int32)
+    causal = bool(rng.random() < 0.8)
+    rows = int(rng.choice([0, 128] + ([192] if d == 256 else [])))
+    say(f"[random prefill {seed}] B={b} Hq={hq} Hkv={hkv} D={d} {layout} causal={causal} rows/wg={rows} "
+        f"q={q.tolist()} kv={kv.tolist()}")
+    spec = wl.prefill_spec(q_lens=q, kv_lens=kv, hq=hq, hkv=hkv, head_dim=d, seed=4000 + seed, layout=layout)
+    case = PrefillCase(spec)
+    kc, vc, kvl = case.gpu_pools()
+    out, lse = case.gpu_prefill(kc, vc, kvl, causal=causal, rows=rows)
+    torch.cuda.synchronize()
+    okc, ovc, okv, obt, oreqs = case.oracle_pools(None)
+    r, ro, rl = case.oracle_rows(okc, ovc, okv, obt, oreqs, causal=causal)
+    compare(out.cpu()[r], ro, *BF16_TOL, "out")
+    compare(lse.cpu()[r], rl, *BF16_TOL, "lse")
