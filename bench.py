@@ -350,9 +350,9 @@ def bench_prefill(args, torch, pkv, wl):
     traffic = traffic_from_profile(os.path.join(ROOT, "paged_kv_attention_pkv_amd", "csrc", "prefill.hip"),
                                    f"prefill16_kernel_{spec.name}_pmc.txt")
     # the workgroup size the library picks for this call, by the rule stated
-    # in include/pkv.h (192 rows once ceil(total_q / 192) * Hq >= 2 * CUs)
+    # in include/pkv.h (192 rows once ceil(total_q / 192) * Hq >= 1.5 * CUs)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    waves = 12 if -(-int(spec.q_lens.sum()) // 192) * spec.hq >= 2 * cus else 8
+    waves = 12 if 2 * (-(-int(spec.q_lens.sum()) // 192) * spec.hq) >= 3 * cus else 8
     result = {
         "metric": "paged causal prefill attn: TFLOP/s (% bf16 MFMA peak), D256 Hq48/Hkv8",
         "value": round(flops * L / (ms * 1e-3) / 1e12, 2),

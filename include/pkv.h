@@ -252,8 +252,8 @@ pkv_status pkv_prefill_attn(const pkv_cache_desc *cache, void *out, float *lse, 
  *                       128: 8 waves of 16 rows (head_dim 256) or 4 of 32 (64, 128);
  *                       192: 12 waves of 16 rows, head_dim 256 only.
  * Any other value, or 192 with another head_dim, gives PKV_EINVAL.  The
- * library takes 192 once the call has work for about two rounds of 192-row
- * workgroups on every CU, else 128.
+ * library takes 192 once the call has work for about one and a half rounds of
+ * 192-row workgroups on every CU, else 128.
  */
 pkv_status pkv_prefill_attn_ex(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
                                int32_t num_q_heads, const void *k_cache, const void *v_cache,

@@ -879,9 +879,11 @@ hipError_t launch16_d(const PrefillArgs &a, hipStream_t stream) {
 }
 
 // Query rows per workgroup of the 16-row kernel when the caller leaves the
-// choice to the library: 192 once the call has work for about two rounds of
-// 192-row workgroups on every CU (counted from total_q, which ragged tails
-// only raise), else 128, whose finer tiles end closer together.
+// choice to the library: 192 once the call has work for about one and a half
+// rounds of 192-row workgroups on every CU (counted from total_q, which
+// ragged tails only raise), else 128, whose finer tiles end closer together.
+// Measured: the single 1023-row request (1.1 rounds) runs faster at 128, two
+// requests of 910 and 627 rows (1.7 rounds) already at 192.
 int auto_wg_rows16(const PrefillArgs &a) {
     static int cus = 0;
     if (cus == 0) {
@@ -893,7 +895,7 @@ int auto_wg_rows16(const PrefillArgs &a) {
             cus = 256;
     }
     const int64_t wgs192 = ((int64_t)a.total_q + Cfg16<12>::BM - 1) / Cfg16<12>::BM * a.hq;
-    return wgs192 >= 2 * (int64_t)cus ? Cfg16<12>::BM : Cfg16<8>::BM;
+    return 2 * wgs192 >= 3 * (int64_t)cus ? Cfg16<12>::BM : Cfg16<8>::BM;
 }
 
 #ifndef PKV_PREFILL16_DIMS
