@@ -393,14 +393,16 @@ def cpu_baseline_prefill(args, torch, spec, inp):
     kv = orc.append(pool, kc, vc, host_bits(h.k_new), host_bits(h.v_new), spec.block_table, spec.hist_lens,
                     h.qo_indptr.numpy())
     # blocks of 32 consecutive query rows of request 0, from its last row
-    # backwards, each run as a chunked-prefill request over the keys it sees,
-    # until about --cpu-seconds have been spent
+    # backwards (starting over at the last row once the first is reached), each
+    # run as a chunked-prefill request over the keys it sees, until about
+    # --cpu-seconds have been spent
     r0, kvl = int(spec.q_lens[0]), int(kv[0])
     ip = h.qo_indptr.numpy()
     fl, spent, done, blk = 0, 0.0, 0, 32
-    while (spent < args.cpu_seconds or done == 0) and done < r0:
-        rows = min(blk, r0 - done)
-        a1 = r0 - done
+    while spent < args.cpu_seconds or done == 0:
+        pos = done % r0
+        rows = min(blk, r0 - pos)
+        a1 = r0 - pos
         a0 = a1 - rows
         q = host_bits(h.q[ip[0] + a0: ip[0] + a1])
         kv_seen = kvl - r0 + a1
@@ -411,7 +413,8 @@ def cpu_baseline_prefill(args, torch, spec, inp):
         fl += 4 * spec.head_dim * spec.hq * sum(kv_seen - rows + i + 1 for i in range(rows))
         done += rows
     return {"value": round(fl / spent / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"last {done} query rows of request 0 in blocks of {blk} ({fl / 1e9:.2f} GFLOP), "
+            "sample": f"{done} query rows of request 0 ({r0} rows, taken from its last row backwards, "
+                      f"cyclically) in blocks of {blk} ({fl / 1e9:.2f} GFLOP), "
                       f"fp64 oracle, {spent:.1f} s"}
 
 
