@@ -13,9 +13,11 @@
 //
 // Work decomposition ("stream-K" over pages), one kernel launch.  The pages
 // of all (sequence, kv head) segments are laid end to end, sequence-major,
-// and cut into equal ranges, one per wavefront: `workers` of them, or fewer
-// on small calls (each wave keeps at least kMinPagesPerWorker pages; the
-// count is decided on the device from the lengths, with no host read-back).  A wave walks its
+// and cut into ranges of equal cost, one per wavefront: `workers` of them, or
+// fewer on small calls (each wave keeps at least kMinPagesPerWorker pages; the
+// count is decided on the device from the lengths, with no host read-back).
+// A segment costs its pages plus a few virtual ones for the work its start
+// brings, so a range that starts a segment holds fewer pages.  A wave walks its
 // range as one stream of page pairs that crosses segment boundaries without
 // draining: the next pair's loads are always in flight while the current one
 // is computed.  Every maximal run of one segment inside a range is a
@@ -27,7 +29,7 @@
 // which piece came last), writes the output and resets the counter to zero
 // for the next call.  A wave whose last piece finds, by a read issued with
 // its last loads, every other piece already counted merges without writing
-// or counting that piece.  Equal page counts per wave keep every CU busy to the
+// or counting that piece.  Equal costs per wave keep every CU busy to the
 // end for any mix of lengths.  Rows with no keys are written (0, lse = -inf)
 // by the waves in a round-robin.
 //
@@ -58,6 +60,11 @@
 
 // Fewest pages a split worker is given when the library picks the count.
 constexpr int64_t kMinPagesPerWorker = 8;
+// Virtual pages charged for each segment start when ranges are cut.
+#ifndef PKV_SEG_COST
+#define PKV_SEG_COST 4
+#endif
+constexpr int kSegCostPages = PKV_SEG_COST;
 // Resident waves per SIMD the bf16 kernel is register-capped to (head_dim <= 128).
 #ifndef PKV_DECODE_WAVES_PER_EU
 #define PKV_DECODE_WAVES_PER_EU 1
@@ -109,10 +116,10 @@ struct RowLens {
     }
 };
 
-// One (sequence, kv head) segment of the flat page space.
+// One (sequence, kv head) segment of the page space.
 struct Seg {
     int b, g, n, np, fresh;  // row, kv head, attended length, pages, new-token flag
-    int64_t f;               // flat index of its page 0
+    int64_t f;               // position of its page 0 on the cost line (see plan)
 };
 
 __device__ __forceinline__ void seg_row(const DecodeArgs &a, Seg &s, int raw) {
@@ -123,7 +130,7 @@ __device__ __forceinline__ void seg_row(const DecodeArgs &a, Seg &s, int raw) {
 
 // The next non-empty segment (the caller knows one exists).
 __device__ __forceinline__ void seg_next(const DecodeArgs &a, Seg &s, RowLens &rl) {
-    s.f += s.np;
+    s.f += s.np + kSegCostPages;
     if (++s.g == a.hkv) {
         s.g = 0;
         do {
@@ -160,18 +167,83 @@ __device__ void zero_row(const DecodeArgs &a, int b, int D) {
 }
 
 struct Range {
-    int64_t f0, f1, total;
+    int64_t f0, f1;  // its pages lie in [f0, f1): the first page positions at or after its two cuts
+    int64_t total;   // length of the cost line
     int workers;
 };
 
-// Total pages over all segments and this wave's share.  Rows are handed out
-// round-robin (row b to worker b mod workers) for the per-row chores: zero
-// fill of rows without keys, and in fused mode the new lengths.  The first
-// 64 raw lengths stay in `rl`.
+// Work is measured on a "cost line": the non-empty segments in flat order,
+// each as kSegCostPages virtual positions (the extra time a segment start
+// brings: a new query row, a piece to settle after the range) followed by one
+// position per page.  Waves take equal shares of the line, so a range that
+// starts a segment holds that many fewer pages.  Page p of the i-th non-empty
+// segment sits at (pages of the segments before) + kSegCostPages * (i + 1) + p.
+// Cursors, page-id staging and piece bookkeeping all count in these positions.
+
+// Pages and positions of the rows of one 64-row chunk (one lane per row,
+// inclusive prefix over the chunk, per kv head).
+__device__ __forceinline__ int chunk_cost(const DecodeArgs &a, int raw, int incl) {
+    const int np = ceil_div(attended(a, raw), kPage);
+    const uint64_t ne = __ballot(np > 0);
+    const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(ne >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ne, 0));
+    return incl + kSegCostPages * (below + (np > 0 ? 1 : 0));
+}
+
+// First page position at or after each of x0 < x1 (x1 may be the line's
+// length), and the segment of the first into s.  One pass over the row
+// lengths: rows 0..63 from `rl` (as left by plan), further chunks read if
+// needed.
+__device__ __forceinline__ void locate2(const DecodeArgs &a, int64_t x0, int64_t x1, const RowLens &rl, Seg &s,
+                                        int64_t &f0, int64_t &f1) {
+    const int l = lane_id();
+    int64_t run = 0;  // positions of the rows before this chunk
+    bool need0 = true;
+    f1 = x1;  // x1 at the line's end
+    for (int base = 0; base < a.batch; base += kWave) {
+        int raw = rl.raw, incl = rl.incl;
+        if (base > 0) {
+            raw = raw_len(a, base + l);
+            incl = wave_incl_scan32(ceil_div(attended(a, raw), kPage));
+        }
+        const int cincl = chunk_cost(a, raw, incl);
+        const int64_t tot = run + (int64_t)__builtin_amdgcn_readlane(cincl, kWave - 1) * a.hkv;
+        // the first row whose positions end past x has pages (an empty row has none)
+        if (need0 && tot > x0) {
+            const int first = uniform((int)__builtin_ctzll(__ballot(run + (int64_t)cincl * a.hkv > x0)));
+            s.b = base + first;
+            seg_row(a, s, __builtin_amdgcn_readlane(raw, first));
+            const int per = s.np + kSegCostPages;
+            const int64_t start = run + (int64_t)(__builtin_amdgcn_readlane(cincl, first) - per) * a.hkv;
+            s.g = (int)((x0 - start) / per);
+            s.f = start + (int64_t)s.g * per + kSegCostPages;
+            f0 = x0 > s.f ? x0 : s.f;
+            need0 = false;
+        }
+        if (tot > x1) {
+            const int first = uniform((int)__builtin_ctzll(__ballot(run + (int64_t)cincl * a.hkv > x1)));
+            const int np = ceil_div(attended(a, __builtin_amdgcn_readlane(raw, first)), kPage);
+            const int per = np + kSegCostPages;
+            const int64_t start = run + (int64_t)(__builtin_amdgcn_readlane(cincl, first) - per) * a.hkv;
+            const int64_t e = start + ((x1 - start) / per) * per + kSegCostPages;
+            f1 = x1 > e ? x1 : e;
+            return;
+        }
+        run = tot;
+    }
+}
+
+// Line length and this wave's share, with the segment its range starts in.
+// The range is [f0, f1) with f0 and f1 the first page positions at or after
+// the two cuts, so a walk stops where the next segment would start at or past
+// f1.  Rows are handed out round-robin (row b to worker b mod workers) for
+// the per-row chores: zero fill of rows without keys, and in fused mode the
+// new lengths.  The first 64 raw lengths stay in `rl`.  False when the wave
+// has no pages.
 template <typename OutT>
-__device__ __forceinline__ bool plan(const DecodeArgs &a, int w, int D, RowLens &rl, Range &r) {
+__device__ __forceinline__ bool plan(const DecodeArgs &a, int w, int D, RowLens &rl, Range &r, Seg &s) {
     const int l = lane_id();
     int64_t pages = 0;  // pages of all rows, one kv head
+    int rows = 0;       // rows with pages
     for (int base = 0; base < a.batch; base += kWave) {
         const int b = base + l;
         const int raw = raw_len(a, b);
@@ -183,6 +255,7 @@ __device__ __forceinline__ bool plan(const DecodeArgs &a, int w, int D, RowLens 
             rl.incl = incl;
         }
         pages += __builtin_amdgcn_readlane(incl, kWave - 1);
+        rows += __builtin_popcountll(__ballot(n > 0));
         const bool mine = b < a.batch && b % a.workers == w;
         if (mine && a.seqlens_out) a.seqlens_out[b] = raw + 1;
         uint64_t empty = __ballot(mine && n == 0);
@@ -200,45 +273,16 @@ __device__ __forceinline__ bool plan(const DecodeArgs &a, int w, int D, RowLens 
     int64_t wmax = by_pages < (int64_t)a.workers ? by_pages : (int64_t)a.workers;
     if (a.fixed_workers) wmax = total < (int64_t)a.workers ? total : (int64_t)a.workers;
     if ((int64_t)w >= wmax) return false;
-    r.total = total;
+    const int64_t len = total + (int64_t)kSegCostPages * rows * a.hkv;
+    r.total = len;
     r.workers = (int)wmax;
-    r.f0 = (int64_t)w * total / wmax;
-    r.f1 = (int64_t)(w + 1) * total / wmax;
-    return true;
+    locate2(a, (int64_t)w * len / wmax, (int64_t)(w + 1) * len / wmax, rl, s, r.f0, r.f1);
+    return r.f0 < r.f1;
 }
 
-// The segment holding flat page f (f < total).  Segments are laid out row by
-// row, the kv heads of a row one after another, so row b starts at flat page
-// hkv * (pages of rows before b).  Uses rows 0..63 from `rl` (as left by
-// plan) and reads further chunks of rows if needed.
-__device__ __forceinline__ void locate(const DecodeArgs &a, int64_t f, const RowLens &rl, Seg &s) {
-    const int l = lane_id();
-    int64_t run = 0;  // flat pages of the rows before this chunk
-    for (int base = 0; base < a.batch; base += kWave) {
-        int raw = rl.raw, incl = rl.incl;
-        if (base > 0) {
-            raw = raw_len(a, base + l);
-            incl = wave_incl_scan32(ceil_div(attended(a, raw), kPage));
-        }
-        const int64_t tot = run + (int64_t)__builtin_amdgcn_readlane(incl, kWave - 1) * a.hkv;
-        if (tot > f) {
-            const uint64_t hit = __ballot(run + (int64_t)incl * a.hkv > f);
-            const int first = uniform((int)__builtin_ctzll(hit));
-            const int incl_b = __builtin_amdgcn_readlane(incl, first);
-            s.b = base + first;
-            seg_row(a, s, __builtin_amdgcn_readlane(raw, first));
-            const int64_t start = run + (int64_t)(incl_b - s.np) * a.hkv;
-            s.g = (int)((f - start) / s.np);
-            s.f = start + (int64_t)s.g * s.np;
-            return;
-        }
-        run = tot;
-    }
-}
-
-// Worker whose range holds flat page p.
-__device__ __forceinline__ int64_t worker_of(int64_t p, const Range &r) {
-    return ((p + 1) * r.workers - 1) / r.total;
+// Worker whose range holds the page at position x.
+__device__ __forceinline__ int64_t worker_of(int64_t x, const Range &r) {
+    return ((x + 1) * r.workers - 1) / r.total;
 }
 
 // ---------------------------------------------------------------------------
@@ -493,18 +537,23 @@ struct Cursor {
 
 // One page pair as the compute side sees it (wave-uniform).
 struct Desc {
-    int b, g, n, np, pa, npg;
-    int last;    // last pair of its piece
-    int whole;   // the piece covers the whole segment
-    int newtok;  // fused mode: the pair's last token is the new one
+    int b, g, n, np, pa;
+    // bit 0: two pages; bit 1: last pair of its piece; bit 2: the piece covers
+    // the whole segment; bit 3 (fused mode): the pair's last token is the new one
+    int flags;
     int ida, idb;
     int raw_last;  // table entry of the pair's last page (unclamped)
-    int64_t segf;
+    int64_t segf;  // position of its segment's page 0
+    __device__ __forceinline__ int npg() const { return 1 + (flags & 1); }
+    __device__ __forceinline__ bool last() const { return flags & 2; }
+    __device__ __forceinline__ bool whole() const { return flags & 4; }
+    __device__ __forceinline__ bool newtok() const { return flags & 8; }
 };
 
-// Fill ids[i] with the table entry of flat page c.f() + i, for i < min(kStage,
-// f1 - c.f()): one pass of coalesced table reads, eight 64-entry chunks at a
-// time with all loads of a group issued before any is used.
+// Fill ids[i] with the table entry of the page at position c.f() + i, for
+// i < min(kStage, f1 - c.f()) (0 at virtual positions): one pass of coalesced
+// table reads, eight 64-entry chunks at a time with all loads of a group
+// issued before any is used.
 __device__ void stage(const DecodeArgs &a, int *ids, const Cursor &c, int64_t f1, RowLens &rl) {
     const int64_t f0 = c.f();
     const int len = (int)(f1 - f0 < kStage ? f1 - f0 : kStage);
@@ -539,7 +588,7 @@ __device__ void stage(const DecodeArgs &a, int *ids, const Cursor &c, int64_t f1
 // the cursor has run past it.
 __device__ __forceinline__ void take(const DecodeArgs &a, Cursor &c, int *ids, int64_t &fbase, int64_t f1,
                                      RowLens &rl, Desc &d) {
-    if (c.f() - fbase >= kStage) {
+    if (__builtin_expect(c.f() - fbase >= kStage, 0)) {
         fbase = c.f();
         stage(a, ids, c, f1, rl);
     }
@@ -550,18 +599,17 @@ __device__ __forceinline__ void take(const DecodeArgs &a, Cursor &c, int *ids, i
     d.np = c.s.np;
     d.pa = c.p;
     d.segf = c.s.f;
-    d.npg = (c.p + 1 < c.pend && i + 1 < kStage) ? 2 : 1;
-    d.last = c.p + d.npg == c.pend;
-    d.whole = c.pstart == 0 && c.pend == c.s.np;
-    d.newtok = c.s.fresh && c.p + d.npg == c.s.np;
+    const int npg = (c.p + 1 < c.pend && i + 1 < kStage) ? 2 : 1;
+    d.flags = (npg - 1) | (c.p + npg == c.pend ? 2 : 0) | (c.pstart == 0 && c.pend == c.s.np ? 4 : 0) |
+              (c.s.fresh && c.p + npg == c.s.np ? 8 : 0);
     const int ra = uniform(ids[i]);
-    const int rb = d.npg == 2 ? uniform(ids[i + 1]) : ra;
+    const int rb = npg == 2 ? uniform(ids[i + 1]) : ra;
     d.ida = clamp_page(a, ra);
     d.idb = clamp_page(a, rb);
     d.raw_last = rb;
-    c.p += d.npg;
-    if (c.p == c.pend) {
-        if (c.f() >= f1) {
+    c.p += npg;
+    if (__builtin_expect(c.p == c.pend, 0)) {
+        if (c.f() + kSegCostPages >= f1) {  // stopped inside a segment, or the next one starts at or past f1
             c.live = 0;
         } else {
             seg_next(a, c.s, rl);
@@ -678,7 +726,7 @@ struct Bf16 {
             const u32x4 z = {0u, 0u, 0u, 0u};
             buf.q[kc2] = col < G ? ld16(q + 64 * kc2 + 16 * quad) : z;
         }
-        if (d.newtok) {
+        if (__builtin_expect(d.newtok(), 0)) {
             const int slot = (d.n - 1) & (kPage - 1);
             const int64_t row = ((int64_t)d.b * a.hkv + d.g) * D * 2;
             if (col == slot) {
@@ -695,7 +743,7 @@ struct Bf16 {
     __device__ __forceinline__ void splice(const DecodeArgs &a, const Desc &d, Buf &buf) {
         const int slot = (d.n - 1) & (kPage - 1);
         const int e = slot & 3;
-        const bool inB = d.npg == 2;
+        const bool inB = d.npg() == 2;
         const bool writable = d.raw_last >= 1 && d.raw_last < a.num_pages;
         const int64_t base = (int64_t)d.g * a.s_head * 2 + (int64_t)d.raw_last * a.s_page * 2;
         if (col == slot) {
@@ -726,9 +774,9 @@ struct Bf16 {
     }
 
     __device__ __forceinline__ void compute(const DecodeArgs &a, Buf &buf, const Desc &d, float c) {
-        if (d.newtok) splice(a, d, buf);
+        if (__builtin_expect(d.newtok(), 0)) splice(a, d, buf);
         const int vcA = min(d.n - d.pa * kPage, kPage);
-        const int vcB = d.npg == 2 ? min(d.n - (d.pa + 1) * kPage, kPage) : 0;
+        const int vcB = d.npg() == 2 ? min(d.n - (d.pa + 1) * kPage, kPage) : 0;
         f32x4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
@@ -854,7 +902,7 @@ struct Bf16 {
 template <class Eng>
 __device__ __forceinline__ void finish_piece(const DecodeArgs &a, Eng &eng, const Desc &d, int w, const Range &r,
                                              Pending &pend, bool more) {
-    if (d.whole) {
+    if (d.whole()) {
         eng.store_final(a, d.b, d.g);
     } else {
         const int64_t s = (int64_t)d.b * a.hkv + d.g;
@@ -881,9 +929,8 @@ void decode_bf16_kernel(DecodeArgs a) {
     const int w = blockIdx.x;
     RowLens rl;
     Range r;
-    if (!plan<__bf16>(a, w, D, rl, r)) return;
     Cursor cur;
-    locate(a, r.f0, rl, cur.s);
+    if (!plan<__bf16>(a, w, D, rl, r, cur.s)) return;
     cur.p = cur.pstart = (int)(r.f0 - cur.s.f);
     cur.pend = (int)(cur.s.np < r.f1 - cur.s.f ? cur.s.np : r.f1 - cur.s.f);
     cur.live = 1;
@@ -904,32 +951,34 @@ void decode_bf16_kernel(DecodeArgs a) {
     // scheduling barriers keep the loads ahead of the compute.
     // After the last pair's loads, the arrival count of its segment is read
     // ahead when its piece is split (it is then the range's held piece).
-    if (!cur.live && !d0.whole) pend.check = peek_arrivals(a, (int64_t)d0.b * a.hkv + d0.g);
+    // Piece ends, id restages and the last-pair read are rare: they are
+    // marked so, which keeps the per-pair path straight-line code.
+    if (__builtin_expect(!cur.live && !d0.whole(), 0)) pend.check = peek_arrivals(a, (int64_t)d0.b * a.hkv + d0.g);
     for (;;) {
         if (cur.live) {
             take(a, cur, ids, fbase, r.f1, rl, d1);
             __builtin_amdgcn_sched_barrier(0);
             eng.issue(a, d1, b1);
-            if (!cur.live && !d1.whole) pend.check = peek_arrivals(a, (int64_t)d1.b * a.hkv + d1.g);
+            if (__builtin_expect(!cur.live && !d1.whole(), 0)) pend.check = peek_arrivals(a, (int64_t)d1.b * a.hkv + d1.g);
             __builtin_amdgcn_sched_barrier(0);
             eng.compute(a, b0, d0, c);
-            if (d0.last) finish_piece(a, eng, d0, w, r, pend, true);
+            if (__builtin_expect(d0.last(), 0)) finish_piece(a, eng, d0, w, r, pend, true);
         } else {
             eng.compute(a, b0, d0, c);
-            if (d0.last) finish_piece(a, eng, d0, w, r, pend, false);
+            if (__builtin_expect(d0.last(), 0)) finish_piece(a, eng, d0, w, r, pend, false);
             break;
         }
         if (cur.live) {
             take(a, cur, ids, fbase, r.f1, rl, d0);
             __builtin_amdgcn_sched_barrier(0);
             eng.issue(a, d0, b0);
-            if (!cur.live && !d0.whole) pend.check = peek_arrivals(a, (int64_t)d0.b * a.hkv + d0.g);
+            if (__builtin_expect(!cur.live && !d0.whole(), 0)) pend.check = peek_arrivals(a, (int64_t)d0.b * a.hkv + d0.g);
             __builtin_amdgcn_sched_barrier(0);
             eng.compute(a, b1, d1, c);
-            if (d1.last) finish_piece(a, eng, d1, w, r, pend, true);
+            if (__builtin_expect(d1.last(), 0)) finish_piece(a, eng, d1, w, r, pend, true);
         } else {
             eng.compute(a, b1, d1, c);
-            if (d1.last) finish_piece(a, eng, d1, w, r, pend, false);
+            if (__builtin_expect(d1.last(), 0)) finish_piece(a, eng, d1, w, r, pend, false);
             break;
         }
     }
@@ -1045,16 +1094,14 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
     const int w = blockIdx.x;
     RowLens rl;
     Range r;
-    if (!plan<float>(a, w, D, rl, r)) return;
     Seg s;
-    locate(a, r.f0, rl, s);
+    if (!plan<float>(a, w, D, rl, r, s)) return;
     int p0 = (int)(r.f0 - s.f);
-    int64_t f = r.f0;
     Eng eng;
     Pending pend;
     pending_init(pend);
     for (;;) {
-        const int64_t left = r.f1 - f;
+        const int64_t left = r.f1 - (s.f + p0);
         const int p1 = left < (int64_t)(s.np - p0) ? p0 + (int)left : s.np;
         eng.init(a, s.b, s.g);
         eng.run(a, s.b, s.g, s.n, p0, p1);
@@ -1066,8 +1113,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
             const int64_t wf = worker_of(s.f, r);
             pending_add(pend, seg, s.b, s.g, wf, (int)(worker_of(s.f + s.np - 1, r) - wf + 1), kStored);
         }
-        f += p1 - p0;
-        if (f >= r.f1) break;
+        if (s.f + p1 + kSegCostPages >= r.f1) break;
         seg_next(a, s, rl);
         p0 = 0;
     }
