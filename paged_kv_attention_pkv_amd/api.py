@@ -21,7 +21,12 @@ import threading
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
+# The in-tree build by default.  PKV_LIB names another build of the same
+# library (a variant compiled with different tuning constants, to compare two
+# builds in one process environment); it must export the same ABI version.
 _LIB_PATH = os.environ.get("PKV_LIB", os.path.join(_HERE, "libpkv.so"))
+# PKV_ABI_VERSION of include/pkv.h that these bindings are written against.
+ABI_VERSION = 1
 
 PKV_F32, PKV_BF16 = 0, 1
 _STATUS = {
@@ -102,6 +107,9 @@ def lib():
                     f = getattr(handle, name)
                     f.argtypes = args
                     f.restype = res
+                got = handle.pkv_abi_version()
+                if got != ABI_VERSION:
+                    raise RuntimeError(f"{_LIB_PATH} has ABI version {got}; these bindings need {ABI_VERSION}")
                 _lib = handle
     return _lib
 

@@ -34,7 +34,8 @@ def test_library_exports_every_declared_symbol():
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
     assert sorted(api.EXPORTED) == names, "binding signatures out of sync with the header"
-    assert lib.pkv_abi_version() == 1
+    header_version = int(re.search(r"#define PKV_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert lib.pkv_abi_version() == header_version == api.ABI_VERSION
     for code in range(7):
         assert lib.pkv_status_string(code)
 
@@ -194,4 +195,12 @@ def test_binding_refuses_missing_library(monkeypatch):
     monkeypatch.setattr(api, "_lib", None)
     monkeypatch.setattr(api, "_LIB_PATH", "/nonexistent/libpkv.so")
     with pytest.raises(RuntimeError, match="libpkv.so not found"):
+        api.lib()
+
+
+def test_binding_refuses_other_abi_version(monkeypatch):
+    api.lib()  # the real library loads
+    monkeypatch.setattr(api, "_lib", None)
+    monkeypatch.setattr(api, "ABI_VERSION", api.ABI_VERSION + 1)
+    with pytest.raises(RuntimeError, match="ABI version"):
         api.lib()
