@@ -172,6 +172,52 @@ def _need(t: torch.Tensor, name: str, dtype=None, dev=None, ndim=None) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _shape(t: torch.Tensor | None, name: str, shape) -> None:
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _decode_operands(desc: _Desc, q, out, lse, block_table, cache_seqlens, k_new=None, v_new=None,
+                     seqlens_out=None) -> None:
+    """Shapes of a decode call's tensors against q [B, Hq, D] and the pool
+    (the library sees only pointers, so a wrong shape would be read or
+    written past its end)."""
+    dev = q.device
+    batch, hq, d = q.shape
+    if d != desc.head_dim:
+        raise ValueError(f"q head_dim {d} differs from the pool's {desc.head_dim}")
+    _shape(out, "out", q.shape)
+    _shape(cache_seqlens, "cache_seqlens", (batch,))
+    if block_table.shape[0] != batch:
+        raise ValueError("block_table rows must equal batch")
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev, 2)
+        _shape(lse, "lse", (batch, hq))
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        _shape(t, nm, (batch, desc.num_kv_heads, d))
+    if seqlens_out is not None:
+        _need(seqlens_out, "seqlens_out", torch.int32, dev, 1)
+        _shape(seqlens_out, "seqlens_out", (batch,))
+
+
+def _prefill_operands(desc: _Desc, q, out, lse, block_table, kv_lens, qo_indptr) -> None:
+    """Shapes of a prefill call's tensors against q [total_q, Hq, D] and the pool."""
+    dev = q.device
+    total_q, hq, d = q.shape
+    if d != desc.head_dim:
+        raise ValueError(f"q head_dim {d} differs from the pool's {desc.head_dim}")
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(kv_lens, "kv_lens", torch.int32, dev, 1)
+    _need(qo_indptr, "qo_indptr", torch.int32, dev, 1)
+    batch = kv_lens.shape[0]
+    if qo_indptr.shape[0] != batch + 1 or block_table.shape[0] != batch:
+        raise ValueError("batch mismatch between qo_indptr, block_table and kv_lens")
+    _shape(out, "out", q.shape)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev, 2)
+        _shape(lse, "lse", (total_q, hq))
+
+
 # --------------------------------------------------------------------------
 # entry points
 # --------------------------------------------------------------------------
@@ -184,6 +230,7 @@ def append(k_cache, v_cache, k_new, v_new, block_table, cache_seqlens, new_indpt
     dev = k_cache.device
     for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
         _need(t, nm, k_cache.dtype, dev, 3)
+        _shape(t, nm, (k_new.shape[0], desc.num_kv_heads, desc.head_dim))
     _need(block_table, "block_table", torch.int32, dev, 2)
     _need(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
     batch = cache_seqlens.shape[0]
@@ -232,8 +279,7 @@ def decode_attn(q, k_cache, v_cache, block_table, cache_seqlens, max_kv_len: int
     _need(out, "out", q.dtype, dev, 3)
     if lse is None and return_lse:
         lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
-    if lse is not None:
-        _need(lse, "lse", torch.float32, dev, 2)
+    _decode_operands(desc, q, out, lse, block_table, cache_seqlens)
     with torch.cuda.device(dev):
         need = lib().pkv_decode_workspace_bytes_ex(ctypes.byref(desc), batch, hq, max_kv_len, workers)
         if workspace is None:
@@ -274,8 +320,7 @@ def append_decode_attn(q, k_cache, v_cache, k_new, v_new, block_table, cache_seq
         seqlens_out = torch.empty_like(cache_seqlens)
     if lse is None and return_lse:
         lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
-    if lse is not None:
-        _need(lse, "lse", torch.float32, dev, 2)
+    _decode_operands(desc, q, out, lse, block_table, cache_seqlens, k_new, v_new, seqlens_out)
     with torch.cuda.device(dev):
         need = lib().pkv_decode_workspace_bytes_ex(ctypes.byref(desc), batch, hq, max_kv_len, workers)
         if workspace is None:
@@ -304,13 +349,8 @@ def prefill_attn(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, max_q: in
     desc = cache_desc(k_cache, v_cache, layout)
     dev = k_cache.device
     _need(q, "q", k_cache.dtype, dev, 3)
-    _need(block_table, "block_table", torch.int32, dev, 2)
-    _need(kv_lens, "kv_lens", torch.int32, dev, 1)
-    _need(qo_indptr, "qo_indptr", torch.int32, dev, 1)
     total_q, hq, d = q.shape
     batch = kv_lens.shape[0]
-    if qo_indptr.shape[0] != batch + 1 or block_table.shape[0] != batch:
-        raise ValueError("batch mismatch between qo_indptr, block_table and kv_lens")
     if scale is None:
         scale = d ** -0.5
     if out is None:
@@ -318,8 +358,7 @@ def prefill_attn(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, max_q: in
     _need(out, "out", q.dtype, dev, 3)
     if lse is None and return_lse:
         lse = torch.empty((total_q, hq), dtype=torch.float32, device=dev)
-    if lse is not None:
-        _need(lse, "lse", torch.float32, dev, 2)
+    _prefill_operands(desc, q, out, lse, block_table, kv_lens, qo_indptr)
     with torch.cuda.device(dev):
         need = lib().pkv_prefill_workspace_bytes(ctypes.byref(desc), batch, hq, total_q, max_q, max_kv_len)
         if workspace is None and need:
@@ -415,10 +454,17 @@ def prepare_append(k_cache, v_cache, k_new, v_new, block_table, cache_seqlens, s
     dev = k_cache.device
     for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
         _need(t, nm, k_cache.dtype, dev, 3)
+        _shape(t, nm, (k_new.shape[0], desc.num_kv_heads, desc.head_dim))
     _need(block_table, "block_table", torch.int32, dev, 2)
     _need(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
     _need(seqlens_out, "seqlens_out", torch.int32, dev, 1)
     batch = cache_seqlens.shape[0]
+    _shape(seqlens_out, "seqlens_out", (batch,))
+    if block_table.shape[0] != batch:
+        raise ValueError("block_table rows must equal batch")
+    if new_indptr is not None:
+        _need(new_indptr, "new_indptr", torch.int32, dev, 1)
+        _shape(new_indptr, "new_indptr", (batch + 1,))
     args = (ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(block_table),
             block_table.shape[1], _ptr(cache_seqlens), _ptr(new_indptr), batch, k_new.shape[0], _ptr(seqlens_out))
     return PreparedCall("pkv_append", args, (k_cache, v_cache, k_new, v_new, block_table, cache_seqlens,
@@ -434,6 +480,7 @@ def prepare_decode(q, k_cache, v_cache, block_table, cache_seqlens, max_kv_len: 
     _need(block_table, "block_table", torch.int32, dev, 2)
     _need(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
     batch, hq, d = q.shape
+    _decode_operands(desc, q, out, lse, block_table, cache_seqlens)
     if scale is None:
         scale = d ** -0.5
     with torch.cuda.device(dev):
@@ -460,6 +507,7 @@ def prepare_append_decode(q, k_cache, v_cache, k_new, v_new, block_table, cache_
     _need(block_table, "block_table", torch.int32, dev, 2)
     _need(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
     batch, hq, d = q.shape
+    _decode_operands(desc, q, out, lse, block_table, cache_seqlens, k_new, v_new, seqlens_out)
     if scale is None:
         scale = d ** -0.5
     with torch.cuda.device(dev):
@@ -481,6 +529,7 @@ def prepare_prefill(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, max_q:
     dev = k_cache.device
     _need(q, "q", k_cache.dtype, dev, 3)
     _need(out, "out", q.dtype, dev, 3)
+    _prefill_operands(desc, q, out, lse, block_table, kv_lens, qo_indptr)
     total_q, hq, d = q.shape
     batch = kv_lens.shape[0]
     if scale is None:

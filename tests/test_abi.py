@@ -204,3 +204,34 @@ def test_binding_refuses_other_abi_version(monkeypatch):
     monkeypatch.setattr(api, "ABI_VERSION", api.ABI_VERSION + 1)
     with pytest.raises(RuntimeError, match="ABI version"):
         api.lib()
+
+
+def test_binding_checks_operand_shapes():
+    """The library sees only pointers, so the binding rejects tensors whose
+    shapes disagree with the pool or with each other before any call."""
+    kc = _cpu_pool()  # [10, 2, 16, 64] bf16: Hkv 2, D 64
+    bt = torch.ones((3, 4), dtype=torch.int32)
+    lens = torch.full((3,), 5, dtype=torch.int32)
+    q = torch.zeros((3, 4, 64), dtype=torch.bfloat16)
+    kn = torch.zeros((3, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="head_dim"):
+        pkv.decode_attn(torch.zeros((3, 4, 32), dtype=torch.bfloat16), kc, kc, bt, lens, 16)
+    with pytest.raises(ValueError, match="out must have shape"):
+        pkv.decode_attn(q, kc, kc, bt, lens, 16, out=torch.zeros((3, 2, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="lse must have shape"):
+        pkv.decode_attn(q, kc, kc, bt, lens, 16, lse=torch.zeros((3, 2), dtype=torch.float32))
+    with pytest.raises(ValueError, match="k_new must have shape"):
+        pkv.append_decode_attn(q, kc, kc, torch.zeros((3, 1, 64), dtype=torch.bfloat16), kn, bt, lens, 16)
+    with pytest.raises(ValueError, match="v_new must have shape"):
+        pkv.append(kc, kc, kn, torch.zeros((3, 2, 32), dtype=torch.bfloat16), bt, lens)
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="seqlens_out must have shape"):
+        api.prepare_append_decode(q, kc, kc, kn, kn, bt, lens, 16, torch.empty_like(q), ws,
+                                  seqlens_out=torch.zeros(2, dtype=torch.int32))
+    ip = torch.tensor([0, 1, 2, 3], dtype=torch.int32)
+    with pytest.raises(ValueError, match="head_dim"):
+        pkv.prefill_attn(torch.zeros((3, 4, 128), dtype=torch.bfloat16), kc, kc, bt, lens, ip, 1, 16)
+    with pytest.raises(ValueError, match="batch mismatch"):
+        api.prepare_prefill(q, kc, kc, bt, lens, ip[:3], 1, 16, torch.empty_like(q))
+    with pytest.raises(ValueError, match="lse must have shape"):
+        pkv.prefill_attn(q, kc, kc, bt, lens, ip, 1, 16, lse=torch.zeros((3, 5), dtype=torch.float32))
