@@ -6,8 +6,9 @@ import numpy as np
 import pytest
 import torch
 
+import paged_kv_attention_pkv_amd as pkv
 from paged_kv_attention_pkv_amd import workloads as wl
-from gpu_common import BF16_TOL, DecodeCase, PrefillCase, compare, say, tol
+from gpu_common import BF16_TOL, DecodeCase, PrefillCase, compare, host_bits, say, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -33,6 +34,46 @@ def test_random_decode(seed):
     out, lse = case.gpu_decode(kc, vc, kl, workers=workers)
     torch.cuda.synchronize()
     okc, ovc, olens, obt = case.oracle_pools()
+    ro, rl = case.oracle_decode(okc, ovc, olens, obt)
+    compare(out.cpu(), ro, *tol(spec), "out")
+    compare(lse.cpu(), rl, *tol(spec), "lse")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_decode_wide(seed):
+    """Batches of 65..300 rows, so that the rows' lengths span several 64-row
+    chunks and ranges start and end in later chunks; empty rows; forced
+    worker counts up to 3000 (many ranges then hold no page); the fused
+    append + attend call on even seeds, with its pool writes bit-exact."""
+    rng = np.random.default_rng(5000 + seed)
+    b = int(rng.integers(65, 301))
+    hq, hkv = HEADS[rng.integers(len(HEADS))]
+    d = int(rng.choice([64, 128]))
+    fused = seed % 2 == 0
+    dtype = "bf16" if fused or rng.random() < 0.7 else "f32"
+    lens = np.minimum(np.exp(rng.uniform(0, np.log(3000), size=b)).astype(np.int32) - 1, 2999)
+    lens[rng.random(b) < 0.15] = 0
+    workers = 0 if seed < 4 else int(rng.integers(1, 3001))
+    say(f"[random wide decode {seed}] B={b} Hq={hq} Hkv={hkv} D={d} {dtype} fused={fused} workers={workers}")
+    spec = wl.custom_decode_spec(lens, hq=hq, hkv=hkv, head_dim=d, dtype=dtype, seed=6000 + seed)
+    case = DecodeCase(spec)
+    if fused:
+        i = case.inp
+        kc, vc = wl.empty_pool(spec, case.dev), wl.empty_pool(spec, case.dev)
+        pkv.append(kc, vc, i.k_hist, i.v_hist, i.block_table, torch.zeros(b, dtype=torch.int32, device=case.dev),
+                   i.hist_indptr)
+        out, lse, new_lens = pkv.append_decode_attn(i.q, kc, vc, i.k_new, i.v_new, i.block_table, i.hist_lens,
+                                                    int(spec.hist_lens.max()) + 1, scale=spec.scale,
+                                                    workers=workers, return_lse=True)
+    else:
+        kc, vc, kl = case.gpu_pools()
+        out, lse = case.gpu_decode(kc, vc, kl, workers=workers)
+    torch.cuda.synchronize()
+    okc, ovc, olens, obt = case.oracle_pools()
+    if fused:
+        assert np.array_equal(new_lens.cpu().numpy(), olens), "seqlens_out differs"
+        assert np.array_equal(host_bits(kc).view(np.uint8), okc.view(np.uint8)), "K pool not bit-exact"
+        assert np.array_equal(host_bits(vc).view(np.uint8), ovc.view(np.uint8)), "V pool not bit-exact"
     ro, rl = case.oracle_decode(okc, ovc, olens, obt)
     compare(out.cpu(), ro, *tol(spec), "out")
     compare(lse.cpu(), rl, *tol(spec), "lse")
