@@ -162,7 +162,9 @@ pkv_status pkv_decode_attn(const pkv_cache_desc *cache, void *out, float *lse, c
  * Same as pkv_decode_attn with an explicit number of split workers (0 =
  * automatic: one wave per resident slot of the device, and on the device
  * fewer for small calls so that each keeps at least 8 pages).  A count > 0
- * is used as given (capped at the call's page count).  For tests of split
+ * is used as given (capped at the call's page count; work is cut in equal
+ * shares of pages plus a fixed charge per row and kv head, so with many
+ * workers some shares hold no page and those workers do nothing).  For tests of split
  * invariance and for tuning; the workspace must be sized with
  * pkv_decode_workspace_bytes_ex and the same count.
  */
