@@ -209,11 +209,12 @@ def bench_decode(args, torch, pkv, wl):
         out = torch.empty_like(inp.q)
         if fused:
             app = None
-            dec = pkv.api.prepare_append_decode(inp.q, kc, vc, inp.k_new, inp.v_new, bt, hist, max_kv, out,
+            dec = pkv.api.prepare_append_decode(inp.q, kc, vc, inp.k_new, inp.v_new, bt, hist, max_kv, spec.scale, out,
                                                 workspace, seqlens_out=lens, workers=args.workers)
         else:
             app = pkv.api.prepare_append(kc, vc, inp.k_new, inp.v_new, bt, hist, lens)
-            dec = pkv.api.prepare_decode(inp.q, kc, vc, bt, lens, max_kv, out, workspace, workers=args.workers)
+            dec = pkv.api.prepare_decode(inp.q, kc, vc, bt, lens, max_kv, spec.scale, out, workspace,
+                                         workers=args.workers)
         layers.append((app, dec, None))
         del inp
     del pools
@@ -334,7 +335,7 @@ def bench_prefill(args, torch, pkv, wl):
             need = pkv.prefill_workspace_bytes(kc, spec.batch, spec.hq, int(spec.q_lens.sum()), max_q, max_kv)
             ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         calls.append(pkv.api.prepare_prefill(inp.q, kc, vc, inp.block_table, kv_lens, inp.qo_indptr, max_q,
-                                             max_kv, out, ws))
+                                             max_kv, spec.scale, out, ws))
         if layer == 0:
             inp0 = inp
         del inp

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 typedef enum pkv_status {
     PKV_OK = 0,
@@ -117,17 +117,33 @@ pkv_status pkv_append(const pkv_cache_desc *cache, void *k_cache, void *v_cache,
 /*
  * pkv_decode_workspace_bytes -- device workspace pkv_decode_attn needs for
  * these sizes on the current device (bytes; 0 only for invalid arguments).
- * Depends on batch, num_q_heads, the descriptor and the device, not on the
- * lengths, so one workspace serves every step of a batch shape.
+ * Depends on the descriptor, batch, num_q_heads and the device (its CU count
+ * and the decode kernel's occupancy), never on the lengths: max_kv_len is
+ * accepted and ignored, so one workspace serves every step of a batch shape
+ * however the lengths grow or shrink.
  *
- * The workspace holds the partial results of rows split across workers and
- * one arrival counter per (sequence, kv head).  It must be zero-filled before
- * its first use (and again before it is reused for a different batch or
- * kv-head count); every call leaves it ready for the next one.  Calls that
- * run concurrently must not share a workspace.
+ * Layout: one int32 arrival counter per (sequence, kv head) at the start,
+ * then the partial results of rows split across workers.  The counter
+ * region must be zero before a call: zero-fill the workspace before its
+ * first use (pkv_decode_workspace_reset, or any fill of zeros), and again
+ * when it is reused for a different batch or kv-head count.  Every call that
+ * completes leaves it zero.  A launch that did not complete (an aborted or
+ * faulted stream) can leave counters non-zero, which would corrupt the
+ * merges of later calls: reset the workspace after any such error.  Calls
+ * that run concurrently must not share a workspace.
  */
 size_t pkv_decode_workspace_bytes(const pkv_cache_desc *cache, int32_t batch, int32_t num_q_heads,
                                   int32_t max_kv_len);
+
+/*
+ * pkv_decode_workspace_reset -- enqueue a zero fill of the counter region of
+ * a decode workspace for `batch` rows (the first bytes of `workspace`), by a
+ * small kernel on `stream` (no memset node, so it may be recorded into a
+ * graph).  PKV_EWORKSPACE when the buffer is missing or too small for the
+ * counters.
+ */
+pkv_status pkv_decode_workspace_reset(const pkv_cache_desc *cache, int32_t batch, void *workspace,
+                                      size_t workspace_bytes, void *stream);
 
 /*
  * pkv_decode_attn -- GQA decode attention, one query token per sequence.
@@ -192,15 +208,19 @@ pkv_status pkv_decode_attn_ex(const pkv_cache_desc *cache, void *out, float *lse
  *   k_new, v_new      [batch, num_kv_heads, head_dim], dtype of the pool
  *   cache_seqlens     int32 [batch]: PRE-append length L_b; the new token goes
  *                     to position L_b and the row attends L_b + 1 keys
- *   seqlens_out       int32 [batch] or NULL: receives L_b + 1; must not alias
- *                     cache_seqlens
- *   max_kv_len        host upper bound of L_b + 1 (<= bt_cols * page_size);
- *                     a row with L_b + 1 > max_kv_len is cut to max_kv_len
- *                     keys and its token is not written
+ *   seqlens_out       int32 [batch] or NULL: the new length of each row,
+ *                     L_b + 1 where the token was stored and L_b where it
+ *                     was not (see below); must not alias cache_seqlens
+ *   max_kv_len        host upper bound of L_b + 1 (<= bt_cols * page_size)
  *   workspace         as for pkv_decode_attn (same size query)
- * The slot's page must be a real page (1..num_pages-1; otherwise the token
- * is not written) and no two sequences may share it.  The written bytes are a
- * bit copy of k_new / v_new.  Only PKV_BF16 is supported.
+ * Preconditions (checked on the host by pkv_validate_decode_step_host):
+ * L_b + 1 <= max_kv_len, the slot's page is a real page (1..num_pages-1) and
+ * no two sequences share a slot.  Where they are violated the call stays in
+ * bounds and reports it: a row with L_b + 1 > max_kv_len attends its first
+ * max_kv_len keys and stores nothing; a row whose slot page is not a real
+ * page attends its new token but does not store it.  Either way its
+ * seqlens_out entry stays L_b.  The written bytes are a bit copy of k_new /
+ * v_new.  Only PKV_BF16 is supported.
  */
 pkv_status pkv_append_decode_attn(const pkv_cache_desc *cache, void *out, float *lse,
                                   const void *q, int32_t num_q_heads, void *k_cache,
@@ -290,6 +310,18 @@ pkv_status pkv_validate_host(const pkv_cache_desc *cache, const int32_t *block_t
                              int32_t bt_cols, const int32_t *kv_lens, const int32_t *qo_indptr,
                              int32_t batch, int32_t total_q, int32_t max_q, int32_t max_kv_len,
                              int32_t causal, char *msg, size_t msg_len);
+
+/*
+ * pkv_validate_decode_step_host -- host-side check of the preconditions of
+ * pkv_append_decode_attn on HOST copies: 0 <= L_b and L_b + 1 <= max_kv_len
+ * <= bt_cols*page_size; every block of the L_b + 1 attended keys is a page
+ * in 1..num_pages-1; no two rows append into the same (page, slot).
+ *   block_table  host int32 [batch, bt_cols]; cache_seqlens host int32 [batch]
+ * Returns PKV_OK or PKV_EVALIDATE with a message in msg (host, may be NULL).
+ */
+pkv_status pkv_validate_decode_step_host(const pkv_cache_desc *cache, const int32_t *block_table,
+                                         int32_t bt_cols, const int32_t *cache_seqlens, int32_t batch,
+                                         int32_t max_kv_len, char *msg, size_t msg_len);
 
 /*
  * pkv_validate_append_host -- host-side check of pkv_append's preconditions

@@ -14,10 +14,12 @@ from .api import (  # noqa: F401
     append_decode_attn,
     decode_attn,
     decode_workspace_bytes,
+    decode_workspace_reset,
     lib_path,
     prefill_attn,
     prefill_workspace_bytes,
     route,
     validate_append_host,
+    validate_decode_step_host,
     validate_host,
 )

@@ -21,12 +21,10 @@ import threading
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# The in-tree build by default.  PKV_LIB names another build of the same
-# library (a variant compiled with different tuning constants, to compare two
-# builds in one process environment); it must export the same ABI version.
-_LIB_PATH = os.environ.get("PKV_LIB", os.path.join(_HERE, "libpkv.so"))
+# The in-tree build (python -m paged_kv_attention_pkv_amd.build).
+_LIB_PATH = os.path.join(_HERE, "libpkv.so")
 # PKV_ABI_VERSION of include/pkv.h that these bindings are written against.
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 PKV_F32, PKV_BF16 = 0, 1
 _STATUS = {
@@ -67,6 +65,7 @@ _SIGS = {
     "pkv_append": ([_DP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _VP, _VP], ctypes.c_int),
     "pkv_decode_workspace_bytes": ([_DP, _I32, _I32, _I32], _SZ),
     "pkv_decode_workspace_bytes_ex": ([_DP, _I32, _I32, _I32, _I32], _SZ),
+    "pkv_decode_workspace_reset": ([_DP, _I32, _VP, _SZ, _VP], ctypes.c_int),
     "pkv_decode_attn": ([_DP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _VP, _I32, _I32, ctypes.c_float,
                          _VP, _SZ, _VP], ctypes.c_int),
     "pkv_decode_attn_ex": ([_DP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _VP, _I32, _I32, ctypes.c_float,
@@ -84,6 +83,7 @@ _SIGS = {
     "pkv_validate_host": ([_DP, _VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32, _I32, ctypes.c_char_p, _SZ],
                           ctypes.c_int),
     "pkv_validate_append_host": ([_DP, _VP, _I32, _VP, _VP, _I32, _I32, ctypes.c_char_p, _SZ], ctypes.c_int),
+    "pkv_validate_decode_step_host": ([_DP, _VP, _I32, _VP, _I32, _I32, ctypes.c_char_p, _SZ], ctypes.c_int),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -170,6 +170,13 @@ def _need(t: torch.Tensor, name: str, dtype=None, dev=None, ndim=None) -> None:
         raise ValueError(f"{name} must be {ndim}-D")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _scale(scale) -> None:
+    """The softmax scale is the caller's (1/sqrt(head_dim) in the usual
+    attention); the binding does no arithmetic of the method."""
+    if scale is None:
+        raise TypeError("scale must be given (a float)")
 
 
 def _shape(t: torch.Tensor | None, name: str, shape) -> None:
@@ -259,7 +266,16 @@ def decode_workspace_bytes(k_cache, batch: int, num_q_heads: int, max_kv_len: in
     return int(n)
 
 
-def decode_attn(q, k_cache, v_cache, block_table, cache_seqlens, max_kv_len: int, scale: float | None = None,
+def decode_workspace_reset(k_cache, batch: int, workspace, layout: str = "HND") -> None:
+    """pkv_decode_workspace_reset: enqueue a zero fill of the workspace's
+    arrival counters for `batch` rows on the current stream."""
+    desc = cache_desc(k_cache, None, layout)
+    rc = lib().pkv_decode_workspace_reset(ctypes.byref(desc), int(batch), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(), _stream(workspace))
+    _check("pkv_decode_workspace_reset", rc)
+
+
+def decode_attn(q, k_cache, v_cache, block_table, cache_seqlens, max_kv_len: int, scale: float,
                 out=None, lse=None, workspace=None, layout: str = "HND", workers: int = 0,
                 return_lse: bool = False):
     """pkv_decode_attn: q [B, Hq, D] against the first cache_seqlens[b] keys
@@ -272,8 +288,7 @@ def decode_attn(q, k_cache, v_cache, block_table, cache_seqlens, max_kv_len: int
     batch, hq, d = q.shape
     if cache_seqlens.shape[0] != batch or block_table.shape[0] != batch:
         raise ValueError("batch mismatch between q, block_table and cache_seqlens")
-    if scale is None:
-        scale = d ** -0.5
+    _scale(scale)
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", q.dtype, dev, 3)
@@ -295,7 +310,7 @@ def decode_attn(q, k_cache, v_cache, block_table, cache_seqlens, max_kv_len: int
 
 
 def append_decode_attn(q, k_cache, v_cache, k_new, v_new, block_table, cache_seqlens, max_kv_len: int,
-                       scale: float | None = None, out=None, lse=None, seqlens_out=None, workspace=None,
+                       scale: float, out=None, lse=None, seqlens_out=None, workspace=None,
                        layout: str = "HND", workers: int = 0, return_lse: bool = False):
     """pkv_append_decode_attn: append k_new/v_new [B, Hkv, D] at each row's
     pre-append length cache_seqlens[b], then attend q [B, Hq, D] over the
@@ -311,8 +326,7 @@ def append_decode_attn(q, k_cache, v_cache, k_new, v_new, block_table, cache_seq
     batch, hq, d = q.shape
     if cache_seqlens.shape[0] != batch or block_table.shape[0] != batch or k_new.shape[0] != batch:
         raise ValueError("batch mismatch between q, k_new, block_table and cache_seqlens")
-    if scale is None:
-        scale = d ** -0.5
+    _scale(scale)
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", q.dtype, dev, 3)
@@ -341,7 +355,7 @@ def prefill_workspace_bytes(k_cache, batch, num_q_heads, total_q, max_q, max_kv_
 
 
 def prefill_attn(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, max_q: int, max_kv_len: int,
-                 causal: bool = True, scale: float | None = None, out=None, lse=None, workspace=None,
+                 scale: float, causal: bool = True, out=None, lse=None, workspace=None,
                  layout: str = "HND", return_lse: bool = False, rows_per_workgroup: int = 0):
     """pkv_prefill_attn: ragged queries q [total_q, Hq, D] (offsets qo_indptr)
     against kv_lens[r] keys of each request, end-aligned causal mask.
@@ -351,8 +365,7 @@ def prefill_attn(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, max_q: in
     _need(q, "q", k_cache.dtype, dev, 3)
     total_q, hq, d = q.shape
     batch = kv_lens.shape[0]
-    if scale is None:
-        scale = d ** -0.5
+    _scale(scale)
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", q.dtype, dev, 3)
@@ -424,6 +437,19 @@ def validate_append_host(k_cache, block_table, cache_seqlens, new_indptr=None, t
     _check("pkv_validate_append_host", rc, msg.value.decode())
 
 
+def validate_decode_step_host(k_cache, block_table, cache_seqlens, max_kv_len: int, layout: str = "HND") -> None:
+    """pkv_validate_decode_step_host: the preconditions of
+    pkv_append_decode_attn on host copies; raises PkvError naming the first
+    violated one."""
+    desc = cache_desc(k_cache, None, layout)
+    bt = block_table.detach().to("cpu", torch.int32).contiguous()
+    cs = cache_seqlens.detach().to("cpu", torch.int32).contiguous()
+    msg = ctypes.create_string_buffer(256)
+    rc = lib().pkv_validate_decode_step_host(ctypes.byref(desc), _ptr(bt), bt.shape[1], _ptr(cs), cs.shape[0],
+                                             int(max_kv_len), msg, 256)
+    _check("pkv_validate_decode_step_host", rc, msg.value.decode())
+
+
 # --------------------------------------------------------------------------
 # prepared calls: validate once, then launch with stored ctypes arguments
 # --------------------------------------------------------------------------
@@ -471,8 +497,8 @@ def prepare_append(k_cache, v_cache, k_new, v_new, block_table, cache_seqlens, s
                                              seqlens_out, new_indptr, desc))
 
 
-def prepare_decode(q, k_cache, v_cache, block_table, cache_seqlens, max_kv_len: int, out, workspace,
-                   lse=None, scale: float | None = None, layout: str = "HND", workers: int = 0) -> PreparedCall:
+def prepare_decode(q, k_cache, v_cache, block_table, cache_seqlens, max_kv_len: int, scale: float, out,
+                   workspace, lse=None, layout: str = "HND", workers: int = 0) -> PreparedCall:
     desc = cache_desc(k_cache, v_cache, layout)
     dev = k_cache.device
     _need(q, "q", k_cache.dtype, dev, 3)
@@ -481,8 +507,7 @@ def prepare_decode(q, k_cache, v_cache, block_table, cache_seqlens, max_kv_len: 
     _need(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
     batch, hq, d = q.shape
     _decode_operands(desc, q, out, lse, block_table, cache_seqlens)
-    if scale is None:
-        scale = d ** -0.5
+    _scale(scale)
     with torch.cuda.device(dev):
         need = lib().pkv_decode_workspace_bytes_ex(ctypes.byref(desc), batch, hq, max_kv_len, workers)
     nbytes = workspace.numel() * workspace.element_size()
@@ -495,8 +520,8 @@ def prepare_decode(q, k_cache, v_cache, block_table, cache_seqlens, max_kv_len: 
                                                      workspace, lse, desc))
 
 
-def prepare_append_decode(q, k_cache, v_cache, k_new, v_new, block_table, cache_seqlens, max_kv_len: int, out,
-                          workspace, seqlens_out=None, lse=None, scale: float | None = None, layout: str = "HND",
+def prepare_append_decode(q, k_cache, v_cache, k_new, v_new, block_table, cache_seqlens, max_kv_len: int,
+                          scale: float, out, workspace, seqlens_out=None, lse=None, layout: str = "HND",
                           workers: int = 0) -> PreparedCall:
     desc = cache_desc(k_cache, v_cache, layout)
     dev = k_cache.device
@@ -508,8 +533,7 @@ def prepare_append_decode(q, k_cache, v_cache, k_new, v_new, block_table, cache_
     _need(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
     batch, hq, d = q.shape
     _decode_operands(desc, q, out, lse, block_table, cache_seqlens, k_new, v_new, seqlens_out)
-    if scale is None:
-        scale = d ** -0.5
+    _scale(scale)
     with torch.cuda.device(dev):
         need = lib().pkv_decode_workspace_bytes_ex(ctypes.byref(desc), batch, hq, max_kv_len, workers)
     nbytes = workspace.numel() * workspace.element_size()
@@ -522,8 +546,8 @@ def prepare_append_decode(q, k_cache, v_cache, k_new, v_new, block_table, cache_
                                                             cache_seqlens, seqlens_out, workspace, lse, desc))
 
 
-def prepare_prefill(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, max_q: int, max_kv_len: int, out,
-                    workspace=None, lse=None, causal: bool = True, scale: float | None = None,
+def prepare_prefill(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, max_q: int, max_kv_len: int,
+                    scale: float, out, workspace=None, lse=None, causal: bool = True,
                     layout: str = "HND", rows_per_workgroup: int = 0) -> PreparedCall:
     desc = cache_desc(k_cache, v_cache, layout)
     dev = k_cache.device
@@ -532,8 +556,7 @@ def prepare_prefill(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, max_q:
     _prefill_operands(desc, q, out, lse, block_table, kv_lens, qo_indptr)
     total_q, hq, d = q.shape
     batch = kv_lens.shape[0]
-    if scale is None:
-        scale = d ** -0.5
+    _scale(scale)
     need = lib().pkv_prefill_workspace_bytes(ctypes.byref(desc), batch, hq, total_q, max_q, max_kv_len)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if nbytes < need:

@@ -1,5 +1,5 @@
-// append.hip -- in-place write of new K/V tokens into the paged pool, and the
-// debug routing kernel.
+// append.hip -- in-place write of new K/V tokens into the paged pool, the
+// debug routing kernel and a word fill.
 //
 // The append is the write half of flash_attn_with_kvcache in mini-infer 06
 // "True PagedAttention" §1: token t of sequence b goes to logical position
@@ -83,6 +83,12 @@ __global__ __launch_bounds__(256) void route_kernel(const int32_t *__restrict__ 
     }
 }
 
+// Zero fill of a word range (the decode workspace's arrival counters).
+__global__ __launch_bounds__(256) void zero_words_kernel(int32_t *__restrict__ p, int64_t words) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
 int grid_for(int64_t work, int block) {
     int64_t g = (work + block - 1) / block;
     if (g < 1) g = 1;
@@ -113,6 +119,12 @@ hipError_t launch_route(const PoolGeom &g, const int32_t *block_table, int bt_co
     hipLaunchKernelGGL(route_kernel, dim3(grid_for((int64_t)batch * max_len, 256)), dim3(256), 0,
                        stream, block_table, bt_cols, seqlens, batch, max_len, g.s_page, g.s_tok,
                        offsets);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_words(int32_t *p, int64_t words, hipStream_t stream) {
+    if (words <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_words_kernel, dim3(grid_for(words, 256)), dim3(256), 0, stream, p, words);
     return hipGetLastError();
 }
 

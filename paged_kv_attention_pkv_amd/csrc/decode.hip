@@ -55,20 +55,15 @@
 // pair are self-contained.
 #include <math.h>
 
+#include <atomic>
+
 #include "common.hpp"
 #include "internal.hpp"
 
 // Fewest pages a split worker is given when the library picks the count.
 constexpr int64_t kMinPagesPerWorker = 8;
 // Virtual pages charged for each segment start when ranges are cut.
-#ifndef PKV_SEG_COST
-#define PKV_SEG_COST 4
-#endif
-constexpr int kSegCostPages = PKV_SEG_COST;
-// Resident waves per SIMD the bf16 kernel is register-capped to (head_dim <= 128).
-#ifndef PKV_DECODE_WAVES_PER_EU
-#define PKV_DECODE_WAVES_PER_EU 1
-#endif
+constexpr int kSegCostPages = 4;
 
 namespace pkv {
 
@@ -257,7 +252,9 @@ __device__ __forceinline__ bool plan(const DecodeArgs &a, int w, int D, RowLens 
         pages += __builtin_amdgcn_readlane(incl, kWave - 1);
         rows += __builtin_popcountll(__ballot(n > 0));
         const bool mine = b < a.batch && b % a.workers == w;
-        if (mine && a.seqlens_out) a.seqlens_out[b] = raw + 1;
+        // a row whose token is not appended keeps its length; the others get
+        // theirs from the wave that writes the token (splice)
+        if (mine && a.seqlens_out && !fresh_token(a, raw)) a.seqlens_out[b] = raw;
         uint64_t empty = __ballot(mine && n == 0);
         while (empty) {
             const int e = uniform((int)__builtin_ctzll(empty));
@@ -745,6 +742,8 @@ struct Bf16 {
         const int e = slot & 3;
         const bool inB = d.npg() == 2;
         const bool writable = d.raw_last >= 1 && d.raw_last < a.num_pages;
+        // the new length counts the token only where it was stored
+        if (d.g == 0 && lane_id() == 0 && a.seqlens_out) a.seqlens_out[d.b] = writable ? d.n : d.n - 1;
         const int64_t base = (int64_t)d.g * a.s_head * 2 + (int64_t)d.raw_last * a.s_page * 2;
         if (col == slot) {
 #pragma unroll
@@ -920,7 +919,7 @@ __device__ __forceinline__ void finish_piece(const DecodeArgs &a, Eng &eng, cons
 }
 
 template <int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D <= 128 ? PKV_DECODE_WAVES_PER_EU : 1)))
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1)))
 void decode_bf16_kernel(DecodeArgs a) {
     using Eng = Bf16<D>;
     __shared__ int ids[kStage];
@@ -1135,9 +1134,12 @@ const void *pick_kernel(int dtype, int d) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Lazily filled per-device launch facts.  Several host threads may launch on
+// one device at once: each field is written with the same value by whichever
+// thread gets there first, through relaxed atomics.
 struct DeviceInfo {
-    int cus = 0;
-    int occ[2][3] = {{0, 0, 0}, {0, 0, 0}};  // resident decode waves per CU [dtype][d]
+    std::atomic<int> cus{0};
+    std::atomic<int> occ[2][3] = {{{0}, {0}, {0}}, {{0}, {0}, {0}}};  // resident decode waves per CU [dtype][d]
 };
 constexpr int kMaxDevices = 64;
 DeviceInfo g_info[kMaxDevices];
@@ -1152,21 +1154,27 @@ int decode_workers(int device, const PoolGeom &g, int hq, int64_t max_pages_boun
     if (w <= 0) {
         if (device < 0 || device >= kMaxDevices) return -1;
         DeviceInfo &info = g_info[device];
-        if (info.cus == 0) {
-            int cus = 0;
-            if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) return -1;
-            info.cus = cus;
+        int cus = info.cus.load(std::memory_order_relaxed);
+        if (cus == 0) {
+            if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
+                return -1;
+            info.cus.store(cus, std::memory_order_relaxed);
         }
-        int &occ = info.occ[g.dtype == 1 ? 1 : 0][dim_index(g.head_dim)];
+        std::atomic<int> &occ_slot = info.occ[g.dtype == 1 ? 1 : 0][dim_index(g.head_dim)];
+        int occ = occ_slot.load(std::memory_order_relaxed);
         if (occ == 0) {
             int blocks = 0;
-            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, pick_kernel(g.dtype, g.head_dim), kWave, 0) !=
+            int cur = -1;
+            // the occupancy query is answered for the current device
+            if (hipGetDevice(&cur) != hipSuccess || cur != device ||
+                hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, pick_kernel(g.dtype, g.head_dim), kWave, 0) !=
                     hipSuccess ||
                 blocks <= 0)
-                blocks = 8;
+                return -1;
             occ = blocks > 16 ? 16 : blocks;
+            occ_slot.store(occ, std::memory_order_relaxed);
         }
-        w = (int64_t)info.cus * occ;
+        w = (int64_t)cus * occ;
     }
     if (max_pages_bound >= 0 && w > max_pages_bound) w = max_pages_bound;
     if (w < 1) w = 1;
@@ -1174,24 +1182,29 @@ int decode_workers(int device, const PoolGeom &g, int hq, int64_t max_pages_boun
     return (int)w;
 }
 
-// Workspace: partial records (o: G*D fp32, (m, l): 2 fp32) for up to
-// workers + batch*hkv pieces, then one arrival counter per (sequence, kv
-// head).  The counters must be zero before the first call; every call leaves
-// them zero.
-size_t decode_workspace(const PoolGeom &g, int batch, int hq, int workers) {
+// Workspace: one int32 arrival counter per (sequence, kv head) first, then
+// the partial records (o: G*D fp32, (m, l): 2 fp32) for up to
+// `record_workers` + batch*hkv pieces.  `record_workers` is the worker count
+// before any cap by the call's page count, so the size and the layout depend
+// on the batch shape and the device only, never on the lengths.  The
+// counters must be zero before a call; every call that completes leaves them
+// zero.
+size_t decode_workspace(const PoolGeom &g, int batch, int hq, int record_workers) {
     const int G = hq / g.hkv;
-    const size_t recs = (size_t)workers + (size_t)batch * g.hkv;
-    return align256(recs * G * g.head_dim * sizeof(float)) + align256(recs * G * 2 * sizeof(float)) +
-           align256((size_t)batch * g.hkv * sizeof(int32_t));
+    const size_t recs = (size_t)record_workers + (size_t)batch * g.hkv;
+    return decode_counter_bytes(g, batch) + align256(recs * G * g.head_dim * sizeof(float)) +
+           align256(recs * G * 2 * sizeof(float));
 }
 
-hipError_t launch_decode(const PoolGeom &g, DecodeArgs a, int max_kv_len, hipStream_t stream) {
-    (void)max_kv_len;
+size_t decode_counter_bytes(const PoolGeom &g, int batch) { return align256((size_t)batch * g.hkv * sizeof(int32_t)); }
+
+hipError_t launch_decode(const PoolGeom &g, DecodeArgs a, void *workspace, int record_workers, hipStream_t stream) {
     const int G = a.hq / a.hkv;
-    const size_t recs = (size_t)a.workers + (size_t)a.batch * a.hkv;
-    char *ws = (char *)a.part_o;
-    a.part_ml = (float *)(ws + align256(recs * G * g.head_dim * sizeof(float)));
-    a.arrivals = (int32_t *)((char *)a.part_ml + align256(recs * G * 2 * sizeof(float)));
+    const size_t recs = (size_t)record_workers + (size_t)a.batch * a.hkv;
+    char *ws = (char *)workspace;
+    a.arrivals = (int32_t *)ws;
+    a.part_o = (float *)(ws + decode_counter_bytes(g, a.batch));
+    a.part_ml = (float *)((char *)a.part_o + align256(recs * G * g.head_dim * sizeof(float)));
     const void *k = pick_kernel(g.dtype, g.head_dim);
     void *args[] = {&a};
     hipError_t e = hipLaunchKernel(k, dim3(a.workers), dim3(kWave), args, 0, stream);

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace pkv {
 
 // Pool geometry after the ABI checks (element strides, dim stride 1).
@@ -44,22 +46,40 @@ struct DecodeArgs {
     float scale_log2;   // softmax scale times log2(e)
     int32_t workers;    // split workers (one wave each)
     int32_t fixed_workers;  // 1: the caller fixed the count (no cap by page count)
-    float *part_o;      // [(workers + batch*hkv) * group * head_dim]
-    float *part_ml;     // [(workers + batch*hkv) * group * 2]
+    float *part_o;      // [(record workers + batch*hkv) * group * head_dim]
+    float *part_ml;     // [(record workers + batch*hkv) * group * 2]
     int32_t *arrivals;  // [batch*hkv]: pieces finished per split row; zero between calls
     // Fused append (bf16 only): when k_new is set, seqlens holds the pre-append
     // lengths L, each row attends L+1 keys, and the token at position L is taken
     // from k_new / v_new [batch, hkv, head_dim] and written into the pool.
     const void *k_new;
     const void *v_new;
-    int32_t *seqlens_out;  // nullable: L+1 per row (fused mode only)
+    int32_t *seqlens_out;  // nullable (fused mode only): L+1 where the token was stored, else L
 };
 
 // Workers the decode kernel uses on `device` when the caller asks for
-// `requested` (0 = automatic); never more than `max_pages_bound`.
+// `requested` (0 = automatic); never more than `max_pages_bound` (< 0: no
+// bound).  -1 when the device cannot be queried.
 int decode_workers(int device, const PoolGeom &g, int hq, int64_t max_pages_bound, int requested);
-size_t decode_workspace(const PoolGeom &g, int batch, int hq, int workers);
-hipError_t launch_decode(const PoolGeom &g, DecodeArgs args, int max_kv_len, hipStream_t stream);
+// Bytes of the arrival-counter region at the start of the decode workspace.
+size_t decode_counter_bytes(const PoolGeom &g, int batch);
+// Whole decode workspace for `record_workers` (the uncapped worker count).
+size_t decode_workspace(const PoolGeom &g, int batch, int hq, int record_workers);
+// Launches the decode kernel on args.workers waves; the workspace layout
+// (counters, then records for record_workers + batch*hkv pieces) is derived
+// here and fills args.arrivals / part_o / part_ml.
+hipError_t launch_decode(const PoolGeom &g, DecodeArgs args, void *workspace, int record_workers,
+                         hipStream_t stream);
+// Zero `words` int32 values at p with a fill kernel (no memset node, so the
+// call can be recorded into a graph).
+hipError_t launch_zero_words(int32_t *p, int64_t words, hipStream_t stream);
+
+// Per-device facts of the current device, cached after the first query
+// (thread-safe).  CU count, or -1 when the device cannot be queried.
+int current_device_cus();
+// Raise a kernel's dynamic LDS limit to `bytes` once per device (thread-safe);
+// `done` holds one bit per device already set.
+hipError_t set_smem_once(const void *kernel, int bytes, std::atomic<uint64_t> &done);
 
 // Prefill (bf16, MFMA).
 struct PrefillArgs {

@@ -7,6 +7,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "internal.hpp"
 #include "pkv.h"
 
@@ -72,6 +75,38 @@ int current_device() {
 
 }  // namespace
 
+namespace pkv {
+
+namespace {
+constexpr int kMaxDev = 64;
+std::atomic<int> g_cus[kMaxDev];
+std::mutex g_attr_mutex;
+}  // namespace
+
+int current_device_cus() {
+    const int dev = current_device();
+    if (dev < 0 || dev >= kMaxDev) return -1;
+    int n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return -1;
+    g_cus[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+hipError_t set_smem_once(const void *kernel, int bytes, std::atomic<uint64_t> &done) {
+    const int dev = current_device();
+    if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+    const uint64_t bit = 1ull << dev;
+    if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+    std::lock_guard<std::mutex> lock(g_attr_mutex);
+    if (done.load(std::memory_order_relaxed) & bit) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
+
+}  // namespace pkv
+
 extern "C" {
 
 int32_t pkv_abi_version(void) { return PKV_ABI_VERSION; }
@@ -114,11 +149,10 @@ pkv_status pkv_append(const pkv_cache_desc *cache, void *k_cache, void *v_cache,
 
 size_t pkv_decode_workspace_bytes_ex(const pkv_cache_desc *cache, int32_t batch, int32_t num_q_heads,
                                      int32_t max_kv_len, int32_t workers) {
+    (void)max_kv_len;  // the size does not depend on the lengths
     PoolGeom g;
-    if (check_desc(cache, &g) || check_heads(g, num_q_heads) || batch < 1 || max_kv_len < 0 || workers < 0)
-        return 0;
-    const int64_t bound = (int64_t)batch * g.hkv * ceil_div64(max_kv_len, kPageSize);
-    const int w = pkv::decode_workers(current_device(), g, num_q_heads, bound, workers);
+    if (check_desc(cache, &g) || check_heads(g, num_q_heads) || batch < 1 || workers < 0) return 0;
+    const int w = pkv::decode_workers(current_device(), g, num_q_heads, -1, workers);
     if (w < 1) return 0;
     return pkv::decode_workspace(g, batch, num_q_heads, w);
 }
@@ -126,6 +160,18 @@ size_t pkv_decode_workspace_bytes_ex(const pkv_cache_desc *cache, int32_t batch,
 size_t pkv_decode_workspace_bytes(const pkv_cache_desc *cache, int32_t batch, int32_t num_q_heads,
                                   int32_t max_kv_len) {
     return pkv_decode_workspace_bytes_ex(cache, batch, num_q_heads, max_kv_len, 0);
+}
+
+pkv_status pkv_decode_workspace_reset(const pkv_cache_desc *cache, int32_t batch, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+    PoolGeom g;
+    pkv_status st = check_desc(cache, &g);
+    if (st) return st;
+    if (batch < 0) return PKV_EINVAL;
+    if (batch == 0) return PKV_OK;
+    const size_t n = pkv::decode_counter_bytes(g, batch);
+    if (!workspace || workspace_bytes < n || !aligned16(workspace)) return PKV_EWORKSPACE;
+    return launch_status(pkv::launch_zero_words((int32_t *)workspace, (int64_t)(n / 4), (hipStream_t)stream));
 }
 
 }  // extern "C"
@@ -158,10 +204,13 @@ pkv_status decode_common(const pkv_cache_desc *cache, void *out, float *lse, con
         return PKV_EUNSUPPORTED;
     const int dev = current_device();
     if (dev < 0) return PKV_EDEVICE;
+    // records are laid out for the uncapped count; the launch never has more
+    // waves than the call has pages
+    const int w_rec = pkv::decode_workers(dev, g, num_q_heads, -1, workers);
+    if (w_rec < 1) return PKV_EDEVICE;
     const int64_t bound = (int64_t)batch * g.hkv * ceil_div64(max_kv_len, kPageSize);
-    const int w = pkv::decode_workers(dev, g, num_q_heads, bound, workers);
-    if (w < 1) return PKV_EDEVICE;
-    const size_t need = pkv::decode_workspace(g, batch, num_q_heads, w);
+    const int w = bound < w_rec ? (int)(bound > 0 ? bound : 1) : w_rec;
+    const size_t need = pkv::decode_workspace(g, batch, num_q_heads, w_rec);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PKV_EWORKSPACE;
 
     pkv::DecodeArgs a;
@@ -184,13 +233,13 @@ pkv_status decode_common(const pkv_cache_desc *cache, void *out, float *lse, con
     a.scale_log2 = scale * 1.4426950408889634f;
     a.workers = w;
     a.fixed_workers = workers > 0;
-    a.part_o = (float *)workspace;
+    a.part_o = nullptr;  // filled by launch_decode from the workspace
     a.part_ml = nullptr;
     a.arrivals = nullptr;
     a.k_new = k_new;
     a.v_new = v_new;
     a.seqlens_out = seqlens_out;
-    return launch_status(pkv::launch_decode(g, a, max_kv_len, (hipStream_t)stream));
+    return launch_status(pkv::launch_decode(g, a, workspace, w_rec, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -366,6 +415,32 @@ pkv_status pkv_validate_host(const pkv_cache_desc *cache, const int32_t *block_t
     }
     if (msg && msg_len) msg[0] = 0;
     return PKV_OK;
+}
+
+pkv_status pkv_validate_decode_step_host(const pkv_cache_desc *cache, const int32_t *block_table, int32_t bt_cols,
+                                        const int32_t *cache_seqlens, int32_t batch, int32_t max_kv_len, char *msg,
+                                        size_t msg_len) {
+    PoolGeom g;
+    pkv_status st = check_desc(cache, &g);
+    if (st) return st;
+    if (batch < 0 || bt_cols < 0) return PKV_EINVAL;
+    if (batch > 0 && (!cache_seqlens || !block_table)) return PKV_EINVAL;
+    for (int b = 0; b < batch; ++b) {
+        if (cache_seqlens[b] < 0 || (int64_t)cache_seqlens[b] + 1 > max_kv_len) {
+            set_msg(msg, msg_len, "row %d: cached length %d + 1 outside 1..max_kv_len (%d)", b, cache_seqlens[b],
+                    max_kv_len);
+            return PKV_EVALIDATE;
+        }
+    }
+    // the attended rows (L + 1 keys each) route to real pages ...
+    int32_t *attended = (int32_t *)malloc(sizeof(int32_t) * (size_t)(batch > 0 ? batch : 1));
+    if (!attended) return PKV_EINVAL;
+    for (int b = 0; b < batch; ++b) attended[b] = cache_seqlens[b] + 1;
+    st = pkv_validate_host(cache, block_table, bt_cols, attended, nullptr, batch, 0, 0, max_kv_len, 0, msg, msg_len);
+    free(attended);
+    if (st) return st;
+    // ... and no two rows append into the same slot
+    return pkv_validate_append_host(cache, block_table, bt_cols, cache_seqlens, nullptr, batch, batch, msg, msg_len);
 }
 
 pkv_status pkv_validate_append_host(const pkv_cache_desc *cache, const int32_t *block_table, int32_t bt_cols,

@@ -407,14 +407,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 // tiles ahead).  64 keys in two stages measured fastest: 32-key tiles in four
 // stages (three tiles ahead) lose more to twice the barriers and softmax
 // steps than they gain.
-#ifndef PKV_PF16_BN
-#define PKV_PF16_BN 64
-#endif
-#ifndef PKV_PF16_NST
-#define PKV_PF16_NST 2
-#endif
-constexpr int kBN16 = PKV_PF16_BN;
-constexpr int kNST16 = PKV_PF16_NST;
+constexpr int kBN16 = 64;
+constexpr int kNST16 = 2;
 static_assert(kBN16 % 32 == 0 && (kNST16 & (kNST16 - 1)) == 0 && kNST16 >= 2 && kNST16 <= 4, "tiling");
 
 // LDS layout of a key tile for the 16-row kernel (D = 256), written by 1 KB
@@ -866,13 +860,9 @@ hipError_t launch16_d(const PrefillArgs &a, hipStream_t stream) {
     const int n_qtiles = (a.max_q + BM - 1) / BM;
     const int64_t grid = (int64_t)a.batch * n_qtiles * a.hq;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill16_kernel<D, W>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kSmem16);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> attr_set{0};
+    hipError_t e = set_smem_once(reinterpret_cast<const void *>(&prefill16_kernel<D, W>), kSmem16, attr_set);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((prefill16_kernel<D, W>), dim3((unsigned)grid), dim3(Cfg16<W>::THREADS), kSmem16, stream,
                        a, n_qtiles);
     return hipGetLastError();
@@ -885,46 +875,33 @@ hipError_t launch16_d(const PrefillArgs &a, hipStream_t stream) {
 // Measured: the single 1023-row request (1.1 rounds) runs faster at 128, two
 // requests of 910 and 627 rows (1.7 rounds) already at 192.
 int auto_wg_rows16(const PrefillArgs &a) {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-            cus = n;
-        else
-            cus = 256;
-    }
+    const int cus = current_device_cus();
+    if (cus <= 0) return -1;
     const int64_t wgs192 = ((int64_t)a.total_q + Cfg16<12>::BM - 1) / Cfg16<12>::BM * a.hq;
     return 2 * wgs192 >= 3 * (int64_t)cus ? Cfg16<12>::BM : Cfg16<8>::BM;
 }
 
-#ifndef PKV_PREFILL16_DIMS
-#define PKV_PREFILL16_DIMS 4  // head dims on the 16-row kernel: bit 0: 64, bit 1: 128, bit 2: 256
-#endif
-
+// head_dim 256 runs the 16-row kernel, 64 and 128 the 32-row kernel
 template <int D>
 hipError_t launch_d(const PrefillArgs &a, hipStream_t stream) {
-    constexpr int bit = D == 64 ? 1 : (D == 128 ? 2 : 4);
-    if constexpr ((PKV_PREFILL16_DIMS & bit) != 0) {
+    if constexpr (D == 256) {
         const int rows = a.wg_rows > 0 ? a.wg_rows : auto_wg_rows16(a);
+        if (rows < 0) return hipErrorInvalidDevice;
         if (rows == Cfg16<12>::BM) return launch16_d<D, 12>(a, stream);
         if (rows == Cfg16<8>::BM) return launch16_d<D, 8>(a, stream);
         return hipErrorInvalidValue;
-    }
-    if (a.wg_rows != 0 && a.wg_rows != kBM) return hipErrorInvalidValue;
-    const int n_qtiles = (a.max_q + kBM - 1) / kBM;
-    const int64_t grid = (int64_t)a.batch * n_qtiles * a.hq;
-    if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_kernel<D>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, Smem<D>::BYTES);
+    } else {
+        if (a.wg_rows != 0 && a.wg_rows != kBM) return hipErrorInvalidValue;
+        const int n_qtiles = (a.max_q + kBM - 1) / kBM;
+        const int64_t grid = (int64_t)a.batch * n_qtiles * a.hq;
+        if (grid > 0x7fffffff) return hipErrorInvalidValue;
+        static std::atomic<uint64_t> attr_set{0};
+        hipError_t e = set_smem_once(reinterpret_cast<const void *>(&prefill_kernel<D>), Smem<D>::BYTES, attr_set);
         if (e != hipSuccess) return e;
-        attr_set = true;
+        hipLaunchKernelGGL(prefill_kernel<D>, dim3((unsigned)grid), dim3(kThreads), Smem<D>::BYTES, stream, a,
+                           n_qtiles);
+        return hipGetLastError();
     }
-    hipLaunchKernelGGL(prefill_kernel<D>, dim3((unsigned)grid), dim3(kThreads), Smem<D>::BYTES, stream, a,
-                       n_qtiles);
-    return hipGetLastError();
 }
 
 }  // namespace

@@ -215,23 +215,81 @@ def test_binding_checks_operand_shapes():
     q = torch.zeros((3, 4, 64), dtype=torch.bfloat16)
     kn = torch.zeros((3, 2, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="head_dim"):
-        pkv.decode_attn(torch.zeros((3, 4, 32), dtype=torch.bfloat16), kc, kc, bt, lens, 16)
+        pkv.decode_attn(torch.zeros((3, 4, 32), dtype=torch.bfloat16), kc, kc, bt, lens, 16, 0.125)
     with pytest.raises(ValueError, match="out must have shape"):
-        pkv.decode_attn(q, kc, kc, bt, lens, 16, out=torch.zeros((3, 2, 64), dtype=torch.bfloat16))
+        pkv.decode_attn(q, kc, kc, bt, lens, 16, 0.125, out=torch.zeros((3, 2, 64), dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="lse must have shape"):
-        pkv.decode_attn(q, kc, kc, bt, lens, 16, lse=torch.zeros((3, 2), dtype=torch.float32))
+        pkv.decode_attn(q, kc, kc, bt, lens, 16, 0.125, lse=torch.zeros((3, 2), dtype=torch.float32))
     with pytest.raises(ValueError, match="k_new must have shape"):
-        pkv.append_decode_attn(q, kc, kc, torch.zeros((3, 1, 64), dtype=torch.bfloat16), kn, bt, lens, 16)
+        pkv.append_decode_attn(q, kc, kc, torch.zeros((3, 1, 64), dtype=torch.bfloat16), kn, bt, lens, 16, 0.125)
     with pytest.raises(ValueError, match="v_new must have shape"):
         pkv.append(kc, kc, kn, torch.zeros((3, 2, 32), dtype=torch.bfloat16), bt, lens)
     ws = torch.zeros(1 << 16, dtype=torch.uint8)
     with pytest.raises(ValueError, match="seqlens_out must have shape"):
-        api.prepare_append_decode(q, kc, kc, kn, kn, bt, lens, 16, torch.empty_like(q), ws,
+        api.prepare_append_decode(q, kc, kc, kn, kn, bt, lens, 16, 0.125, torch.empty_like(q), ws,
                                   seqlens_out=torch.zeros(2, dtype=torch.int32))
     ip = torch.tensor([0, 1, 2, 3], dtype=torch.int32)
     with pytest.raises(ValueError, match="head_dim"):
-        pkv.prefill_attn(torch.zeros((3, 4, 128), dtype=torch.bfloat16), kc, kc, bt, lens, ip, 1, 16)
+        pkv.prefill_attn(torch.zeros((3, 4, 128), dtype=torch.bfloat16), kc, kc, bt, lens, ip, 1, 16, 0.125)
     with pytest.raises(ValueError, match="batch mismatch"):
-        api.prepare_prefill(q, kc, kc, bt, lens, ip[:3], 1, 16, torch.empty_like(q))
+        api.prepare_prefill(q, kc, kc, bt, lens, ip[:3], 1, 16, 0.125, torch.empty_like(q))
     with pytest.raises(ValueError, match="lse must have shape"):
-        pkv.prefill_attn(q, kc, kc, bt, lens, ip, 1, 16, lse=torch.zeros((3, 5), dtype=torch.float32))
+        pkv.prefill_attn(q, kc, kc, bt, lens, ip, 1, 16, 0.125, lse=torch.zeros((3, 5), dtype=torch.float32))
+
+
+def test_workspace_size_ignores_lengths():
+    """With an explicit worker count (no device query) the decode workspace
+    size depends on the batch shape only: the same for every max_kv_len, and
+    the arrival counters sit at a fixed place (the start)."""
+    lib = api.lib()
+    d = _desc()
+    sizes = {lib.pkv_decode_workspace_bytes_ex(ctypes.byref(d), 8, 32, m, 37) for m in (0, 1, 16, 100, 2000, 1 << 20)}
+    assert len(sizes) == 1 and sizes.pop() > 0
+
+
+def test_validate_decode_step_paths():
+    """pkv_validate_decode_step_host: L + 1 within max_kv_len, attended blocks
+    on real pages, append slots distinct."""
+    kc = _cpu_pool()
+    bt = torch.tensor([[1, 2, 0], [3, 4, 5]], dtype=torch.int32)
+    pkv.validate_decode_step_host(kc, bt, torch.tensor([15, 40], dtype=torch.int32), 48)
+    with pytest.raises(pkv.PkvError, match="max_kv_len"):
+        pkv.validate_decode_step_host(kc, bt, torch.tensor([15, 40], dtype=torch.int32), 40)
+    with pytest.raises(pkv.PkvError, match="max_kv_len"):
+        pkv.validate_decode_step_host(kc, bt, torch.tensor([-1, 40], dtype=torch.int32), 48)
+    # row 0's token at position 32 opens block 2, which routes to page 0
+    with pytest.raises(pkv.PkvError, match="page 0"):
+        pkv.validate_decode_step_host(kc, bt, torch.tensor([32, 40], dtype=torch.int32), 48)
+    shared = torch.tensor([[1, 2, 0], [1, 4, 5]], dtype=torch.int32)
+    with pytest.raises(pkv.PkvError, match="written twice"):
+        pkv.validate_decode_step_host(kc, shared, torch.tensor([3, 3], dtype=torch.int32), 48)
+    with pytest.raises(pkv.PkvError, match="max_kv_len"):
+        pkv.validate_decode_step_host(kc, bt, torch.tensor([3, 3], dtype=torch.int32), 49)
+
+
+def test_workspace_reset_rejects_bad_buffers():
+    lib = api.lib()
+    d = _desc()
+    reset = lambda batch, ws, n: lib.pkv_decode_workspace_reset(ctypes.byref(d), batch, ws, n, None)
+    assert reset(-1, FAKE, 1 << 20) == EINVAL
+    assert reset(0, None, 0) == OK  # nothing to clear
+    assert reset(4, None, 1 << 20) == EWORKSPACE
+    assert reset(4, FAKE, 4 * 8 * 4 - 1) == EWORKSPACE  # 4 rows x 8 kv heads of int32 counters
+    assert reset(4, ctypes.c_void_p((1 << 20) + 4), 1 << 20) == EWORKSPACE  # misaligned
+
+
+def test_binding_requires_scale():
+    """The softmax scale is the caller's: the binding computes no default."""
+    kc = _cpu_pool()
+    bt = torch.ones((3, 4), dtype=torch.int32)
+    lens = torch.full((3,), 5, dtype=torch.int32)
+    q = torch.zeros((3, 4, 64), dtype=torch.bfloat16)
+    ip = torch.tensor([0, 1, 2, 3], dtype=torch.int32)
+    with pytest.raises(TypeError):
+        pkv.decode_attn(q, kc, kc, bt, lens, 16)
+    with pytest.raises(TypeError, match="scale"):
+        pkv.decode_attn(q, kc, kc, bt, lens, 16, None)
+    with pytest.raises(TypeError):
+        pkv.prefill_attn(q, kc, kc, bt, lens, ip, 1, 16)
+    with pytest.raises(TypeError, match="scale"):
+        pkv.prefill_attn(q, kc, kc, bt, lens, ip, 1, 16, None)

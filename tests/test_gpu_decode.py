@@ -170,7 +170,7 @@ def test_identical_keys_mean():
     kc, vc = wl.empty_pool(spec, dev), wl.empty_pool(spec, dev)
     lens = pkv.append(kc, vc, k, v, bt, torch.zeros(1, dtype=torch.int32, device=dev),
                       torch.tensor([0, n], dtype=torch.int32, device=dev))
-    out = pkv.decode_attn(q, kc, vc, bt, lens, n)
+    out = pkv.decode_attn(q, kc, vc, bt, lens, n, d ** -0.5)
     mean = v[:, 0].double().mean(0).cpu().numpy()
     compare(out[0].cpu(), np.broadcast_to(mean, (hq, d)), 2e-2, 2e-2, "identical keys")
 
@@ -237,9 +237,9 @@ def test_workspace_reuse_across_calls():
     need = max(pkv.decode_workspace_bytes(k1, 4, 32, m1, workers=37),
                pkv.decode_workspace_bytes(k2, 4, 32, m2, workers=37))
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
-    first = pkv.decode_attn(c1.inp.q, k1, v1, c1.inp.block_table, l1, m1, workspace=ws, workers=37)
-    second = pkv.decode_attn(c2.inp.q, k2, v2, c2.inp.block_table, l2, m2, workspace=ws, workers=37)
-    again = pkv.decode_attn(c1.inp.q, k1, v1, c1.inp.block_table, l1, m1, workspace=ws, workers=37)
+    first = pkv.decode_attn(c1.inp.q, k1, v1, c1.inp.block_table, l1, m1, s1.scale, workspace=ws, workers=37)
+    second = pkv.decode_attn(c2.inp.q, k2, v2, c2.inp.block_table, l2, m2, s2.scale, workspace=ws, workers=37)
+    again = pkv.decode_attn(c1.inp.q, k1, v1, c1.inp.block_table, l1, m1, s1.scale, workspace=ws, workers=37)
     torch.cuda.synchronize()
     assert torch.equal(first.view(torch.int16), again.view(torch.int16))
     for case, out in ((c1, first), (c2, second)):

@@ -52,7 +52,7 @@ def test_fused_decode_step_graph():
     lse = torch.empty((spec.batch, spec.hq), dtype=torch.float32, device=dev)
     lens = torch.empty_like(inp.hist_lens)
     call = pkv.api.prepare_append_decode(inp.q, kc, vc, inp.k_new, inp.v_new, inp.block_table, inp.hist_lens,
-                                         max_kv, out, ws, seqlens_out=lens, lse=lse)
+                                         max_kv, spec.scale, out, ws, seqlens_out=lens, lse=lse)
     call()
     torch.cuda.synchronize()
     assert lens.cpu().numpy().tolist() == (hist + 1).tolist()
@@ -72,7 +72,7 @@ def test_prefill_graph(rows):
     out = torch.empty_like(case.inp.q)
     lse = torch.empty((out.shape[0], spec.hq), dtype=torch.float32, device=case.dev)
     call = pkv.api.prepare_prefill(case.inp.q, kc, vc, case.inp.block_table, kv, case.inp.qo_indptr,
-                                   int(spec.q_lens.max()), int(spec.kv_lens.max()), out, lse=lse,
+                                   int(spec.q_lens.max()), int(spec.kv_lens.max()), spec.scale, out, lse=lse,
                                    rows_per_workgroup=rows)
     call()
     torch.cuda.synchronize()

@@ -165,7 +165,7 @@ def test_no_visible_key_rows():
                torch.tensor([0, 20], dtype=torch.int32, device=dev))
     q = torch.randn((8, 4, 128), device=dev).to(torch.bfloat16)
     qi = torch.tensor([0, 3, 8], dtype=torch.int32, device=dev)
-    out, lse = pkv.prefill_attn(q, kc, vc, bt, kvl, qi, 5, 20, causal=False, return_lse=True)
+    out, lse = pkv.prefill_attn(q, kc, vc, bt, kvl, qi, 5, 20, 128 ** -0.5, causal=False, return_lse=True)
     o, l = out.float().cpu(), lse.cpu()
     assert torch.all(o[:3] == 0) and torch.all(torch.isneginf(l[:3]))
     assert torch.isfinite(o[3:]).all() and torch.isfinite(l[3:]).all()
