@@ -69,10 +69,10 @@ def compare(gpu, ref, atol, rtol, what):
 class DecodeCase:
     """A decode workload materialised on both sides."""
 
-    def __init__(self, spec: wl.DecodeSpec, device="cuda", gen_device="cpu", oracle_rows=None):
+    def __init__(self, spec: wl.DecodeSpec, device="cuda", gen_device="cpu", oracle_rows=None, seed_offset=0):
         self.spec = spec
         self.dev = torch.device(device)
-        inp = wl.decode_inputs(spec, device=gen_device)
+        inp = wl.decode_inputs(spec, device=gen_device, seed_offset=seed_offset)
         self.inp_host = inp.to("cpu")
         self.inp = inp.to(self.dev)
         self.rows = None if oracle_rows is None else np.asarray(sorted(oracle_rows), dtype=np.int64)
@@ -212,6 +212,34 @@ class PrefillCase:
                 q_parts.append(h.q[qi[r] + a0: qi[r] + a1])
                 lens.append((a1 - a0, kvp, n))
                 rows.extend(range(qi[r] + a0, qi[r] + a1))
+        return self._run_parts(kc, vc, bt, q_parts, lens, rows, causal, nt)
+
+    def oracle_row_set(self, kc, vc, kv, bt, reqs, pick, causal=True, nthreads=None):
+        """Oracle output for the query rows pick(r, q_r) (sorted indices) of
+        each request of `reqs`.  Each run of consecutive rows [a0, a1) is its
+        own chunked-prefill request over the first kv_r - q_r + a1 keys, so
+        its rows see exactly the keys they see in the whole request."""
+        s, h = self.spec, self.inp_host
+        qi = h.qo_indptr.numpy()
+        nt = nthreads or min(16, os.cpu_count() or 1)
+        q_parts, lens, rows = [], [], []
+        for n, r in enumerate(reqs):
+            q_r, kv_r = int(s.q_lens[r]), int(kv[n])
+            sel = np.asarray(sorted(set(int(i) for i in pick(r, q_r) if 0 <= i < q_r)), np.int64)
+            if sel.size == 0:
+                continue
+            breaks = np.flatnonzero(np.diff(sel) != 1) + 1
+            for run in np.split(sel, breaks):
+                a0, a1 = int(run[0]), int(run[-1]) + 1
+                kvp = kv_r - q_r + a1 if causal else kv_r
+                q_parts.append(h.q[qi[r] + a0: qi[r] + a1])
+                lens.append((a1 - a0, kvp, n))
+                rows.extend(range(qi[r] + a0, qi[r] + a1))
+        return self._run_parts(kc, vc, bt, q_parts, lens, rows, causal, nt)
+
+    def _run_parts(self, kc, vc, bt, q_parts, lens, rows, causal, nt):
+        s = self.spec
+        orc = oracle.load()
         qcat = torch.cat(q_parts)
         ql = np.array([x[0] for x in lens], np.int32)
         kvl = np.array([x[1] for x in lens], np.int32)

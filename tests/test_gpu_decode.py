@@ -15,10 +15,10 @@ from gpu_common import DecodeCase, compare, host_bits, opool, say, tol
 pytestmark = pytest.mark.gpu
 
 
-def _run_parity(spec, workers=0, gen_device="cpu", oracle_rows=None, check_pool=True):
+def _run_parity(spec, workers=0, gen_device="cpu", oracle_rows=None, check_pool=True, seed_offset=0):
     say(f"[decode parity] {spec.name} B={spec.batch} Hq={spec.hq} Hkv={spec.hkv} D={spec.head_dim} "
-        f"{spec.dtype} {spec.layout} seed={spec.seed} workers={workers}")
-    case = DecodeCase(spec, gen_device=gen_device, oracle_rows=oracle_rows)
+        f"{spec.dtype} {spec.layout} seed={spec.seed} layer draw {seed_offset} workers={workers}")
+    case = DecodeCase(spec, gen_device=gen_device, oracle_rows=oracle_rows, seed_offset=seed_offset)
     kc, vc, lens = case.gpu_pools()
     out, lse = case.gpu_decode(kc, vc, lens, workers=workers)
     torch.cuda.synchronize()
@@ -212,15 +212,21 @@ def test_append_ragged_bit_exact():
     assert np.array_equal(host_bits(vc).view(np.uint8), ovc.view(np.uint8))
 
 
-def test_long_ragged_full_size_sampled():
+def test_long_ragged_full_size_whole_layer():
     """Batch 256, log-uniform lengths up to 32k, fully fragmented pool, at
-    full size; the oracle checks 12 sampled rows (the longest, the shortest
-    and 10 seeded picks)."""
+    full size: every row of one layer cache against the oracle."""
+    _run_parity(wl.decode_spec("long_ragged"), gen_device="cuda", check_pool=False)
+
+
+@pytest.mark.parametrize("layer", [1, 2])
+def test_long_ragged_other_layers_sampled(layer):
+    """Two more layer caches of the same workload (their own K/V/q draws),
+    checked on 24 seeded rows each plus the longest and the shortest."""
     spec = wl.decode_spec("long_ragged")
     n = spec.hist_lens
-    rng = np.random.default_rng(41)
-    rows = set(rng.choice(spec.batch, 10, replace=False).tolist()) | {int(n.argmax()), int(n.argmin())}
-    _run_parity(spec, gen_device="cuda", oracle_rows=rows, check_pool=False)
+    rng = np.random.default_rng(4000 + layer)
+    rows = set(rng.choice(spec.batch, 24, replace=False).tolist()) | {int(n.argmax()), int(n.argmin())}
+    _run_parity(spec, gen_device="cuda", oracle_rows=rows, check_pool=False, seed_offset=layer)
 
 
 def test_workspace_reuse_across_calls():
@@ -246,3 +252,52 @@ def test_workspace_reuse_across_calls():
         okc, ovc, olens, obt = case.oracle_pools()
         ro, _ = case.oracle_decode(okc, ovc, olens, obt)
         compare(out.cpu(), ro, *tol(case.spec), "workspace reuse")
+
+
+def test_workspace_reuse_automatic_workers_shrinking_lengths():
+    """One workspace, sized once, with the library's own worker count, serves
+    a batch whose lengths fall from ~2000 to ~100 (and rise again): the size
+    and layout do not depend on the lengths."""
+    say("[decode] workspace reuse, automatic workers, shrinking lengths")
+    specs = [wl.custom_decode_spec(L, hq=32, hkv=8, head_dim=128, dtype="bf16", seed=70 + k)
+             for k, L in enumerate(([1990, 2000, 1500, 1800, 1999, 1700, 1600, 1900],
+                                    [90, 100, 60, 99, 80, 70, 100, 95],
+                                    [5, 1, 0, 16, 17, 3, 2, 8],
+                                    [1000, 2000, 30, 700, 1999, 5, 400, 1200]))]
+    dev = torch.device("cuda")
+    kc0 = wl.empty_pool(specs[0], dev)
+    ws = torch.zeros(pkv.decode_workspace_bytes(kc0, 8, 32, 2001), dtype=torch.uint8, device=dev)
+    assert ws.numel() == pkv.decode_workspace_bytes(kc0, 8, 32, 1)
+    for spec in specs:
+        case = DecodeCase(spec)
+        kc, vc, lens = case.gpu_pools()
+        max_kv = int(spec.hist_lens.max()) + 1
+        out, lse = pkv.decode_attn(case.inp.q, kc, vc, case.inp.block_table, lens, max_kv, spec.scale,
+                                   workspace=ws, return_lse=True)
+        torch.cuda.synchronize()
+        okc, ovc, olens, obt = case.oracle_pools()
+        ro, rl = case.oracle_decode(okc, ovc, olens, obt)
+        say(f"  max_kv {max_kv}: out " + compare(out.cpu(), ro, *tol(spec), "reuse out"))
+        compare(lse.cpu(), rl, *tol(spec), "reuse lse")
+    counters = ws[: 8 * 8 * 4].view(torch.int32)
+    assert torch.all(counters == 0), "a call left arrival counters behind"
+
+
+def test_workspace_reset_clears_counters():
+    """pkv_decode_workspace_reset zeroes the arrival counters (here filled
+    with junk from the host, as an aborted launch could leave them), after
+    which the workspace gives the oracle's result."""
+    say("[decode] workspace reset")
+    spec = wl.custom_decode_spec([3000, 5, 700, 1500], hq=32, hkv=8, head_dim=128, dtype="bf16", seed=64)
+    case = DecodeCase(spec)
+    kc, vc, lens = case.gpu_pools()
+    ws = torch.zeros(pkv.decode_workspace_bytes(kc, 4, 32, 3001), dtype=torch.uint8, device=case.dev)
+    ws[:1024].fill_(0x5A)
+    pkv.decode_workspace_reset(kc, 4, ws)
+    torch.cuda.synchronize()
+    assert torch.all(ws[: 4 * 8 * 4] == 0)
+    out = pkv.decode_attn(case.inp.q, kc, vc, case.inp.block_table, lens, 3001, spec.scale, workspace=ws)
+    torch.cuda.synchronize()
+    okc, ovc, olens, obt = case.oracle_pools()
+    ro, _ = case.oracle_decode(okc, ovc, olens, obt)
+    compare(out.cpu(), ro, *tol(spec), "after reset")

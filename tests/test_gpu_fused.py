@@ -82,3 +82,36 @@ def test_fused_gqa_ratios(hq, hkv):
     spec = wl.custom_decode_spec([5, 40, 77, 200, 1000], hq=hq, hkv=hkv, head_dim=128, dtype="bf16",
                                  seed=hq + hkv)
     _fused(spec)
+
+
+def test_fused_rows_not_stored_keep_their_length():
+    """A row whose L + 1 exceeds max_kv_len, and a row whose slot page is page
+    0 (not a real page), attend what they can but store nothing: the pools
+    stay as they were and seqlens_out reports L for them, L + 1 elsewhere."""
+    say("[fused] rows whose token is not stored")
+    spec = wl.custom_decode_spec([40, 63, 32, 33], hq=8, hkv=2, head_dim=128, dtype="bf16", seed=31, extra_cols=1)
+    case = DecodeCase(spec)
+    i, dev = case.inp, case.dev
+    kc, vc = wl.empty_pool(spec, dev), wl.empty_pool(spec, dev)
+    pkv.append(kc, vc, i.k_hist, i.v_hist, i.block_table, torch.zeros(spec.batch, dtype=torch.int32, device=dev),
+               i.hist_indptr)
+    bt = i.block_table.clone()
+    bt[2, 32 // 16] = 0  # row 2's new token (position 32, alone in its block) routes to page 0
+    max_kv = 60          # row 1 (L = 63) is cut: 63 + 1 > 60
+    k0, v0 = kc.clone(), vc.clone()
+    out, lse, lens = pkv.append_decode_attn(i.q, kc, vc, i.k_new, i.v_new, bt, i.hist_lens, max_kv, spec.scale,
+                                            return_lse=True)
+    torch.cuda.synchronize()
+    assert lens.cpu().tolist() == [41, 63, 32, 34]
+    hist = spec.hist_lens
+    changed = (kc.view(torch.int16) != k0.view(torch.int16)).any(-1).nonzero().cpu().numpy()
+    # (page, head, slot) of every changed row: only rows 0 and 3 were stored, one slot per kv head each
+    want = set()
+    for b in (0, 3):
+        pos = int(hist[b])
+        for g in range(spec.hkv):
+            want.add((int(spec.block_table[b, pos // 16]), g, pos % 16))
+    assert set(map(tuple, changed.tolist())) == want
+    assert torch.equal((vc.view(torch.int16) != v0.view(torch.int16)).any(-1).nonzero(),
+                       (kc.view(torch.int16) != k0.view(torch.int16)).any(-1).nonzero())
+    assert not torch.isnan(out).any()
