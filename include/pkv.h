@@ -240,6 +240,32 @@ pkv_status pkv_append_decode_attn_ex(const pkv_cache_desc *cache, void *out, flo
                                      void *stream);
 
 /*
+ * pkv_append_decode_attn_noalloc -- pkv_append_decode_attn (automatic worker
+ * count) for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  It
+ * takes no workspace: the library keeps one fixed array of 32 MiB in device
+ * memory on each GPU it runs on (from module load until the process ends)
+ * and uses it as the workspace.  The call allocates and frees nothing; it
+ * enqueues a small fill kernel that clears the array's arrival counters, then
+ * the decode launch.  Arguments, results and preconditions are those of
+ * pkv_append_decode_attn.
+ *   Limit: the workspace this call would need (pkv_decode_workspace_bytes for
+ *   the same batch, num_q_heads and descriptor) must fit in 32 MiB, otherwise
+ *   PKV_EWORKSPACE and nothing is enqueued.
+ *   Every call on one GPU shares that GPU's array: calls that may overlap in
+ *   time on one GPU (different streams, threads or processes' graphs without
+ *   ordering) race on it and must not be issued; calls ordered on one stream
+ *   are safe.
+ */
+pkv_status pkv_append_decode_attn_noalloc(const pkv_cache_desc *cache, void *out, float *lse,
+                                          const void *q, int32_t num_q_heads, void *k_cache,
+                                          void *v_cache, const void *k_new, const void *v_new,
+                                          const int32_t *block_table, int32_t bt_cols,
+                                          const int32_t *cache_seqlens, int32_t *seqlens_out,
+                                          int32_t batch, int32_t max_kv_len, float scale,
+                                          void *stream);
+
+/*
  * pkv_prefill_workspace_bytes / pkv_prefill_attn -- causal (chunked) prefill
  * over the paged pool.
  *

@@ -12,6 +12,7 @@ from .api import (  # noqa: F401
     cache_desc,
     append,
     append_decode_attn,
+    append_decode_attn_noalloc,
     decode_attn,
     decode_workspace_bytes,
     decode_workspace_reset,

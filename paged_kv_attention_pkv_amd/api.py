@@ -74,6 +74,8 @@ _SIGS = {
                                 ctypes.c_float, _VP, _SZ, _VP], ctypes.c_int),
     "pkv_append_decode_attn_ex": ([_DP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32,
                                    ctypes.c_float, _VP, _SZ, _I32, _VP], ctypes.c_int),
+    "pkv_append_decode_attn_noalloc": ([_DP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _I32,
+                                        _I32, ctypes.c_float, _VP], ctypes.c_int),
     "pkv_prefill_workspace_bytes": ([_DP, _I32, _I32, _I32, _I32, _I32], _SZ),
     "pkv_prefill_attn": ([_DP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32,
                           _I32, ctypes.c_float, _VP, _SZ, _VP], ctypes.c_int),
@@ -345,6 +347,40 @@ def append_decode_attn(q, k_cache, v_cache, k_new, v_new, block_table, cache_seq
             int(max_kv_len), float(scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
             int(workers), _stream(k_cache))
     _check("pkv_append_decode_attn", rc)
+    return (out, lse, seqlens_out) if lse is not None else (out, seqlens_out)
+
+
+def append_decode_attn_noalloc(q, k_cache, v_cache, k_new, v_new, block_table, cache_seqlens, max_kv_len: int,
+                               scale: float, out=None, lse=None, seqlens_out=None, layout: str = "HND",
+                               return_lse: bool = False):
+    """pkv_append_decode_attn_noalloc: the fused decode step on the library's
+    fixed device workspace (no workspace argument; the library allocates
+    nothing).  Output tensors are allocated here only when not given."""
+    desc = cache_desc(k_cache, v_cache, layout)
+    dev = k_cache.device
+    _need(q, "q", k_cache.dtype, dev, 3)
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, nm, k_cache.dtype, dev, 3)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
+    batch, hq, d = q.shape
+    if cache_seqlens.shape[0] != batch or block_table.shape[0] != batch or k_new.shape[0] != batch:
+        raise ValueError("batch mismatch between q, k_new, block_table and cache_seqlens")
+    _scale(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, dev, 3)
+    if seqlens_out is None:
+        seqlens_out = torch.empty_like(cache_seqlens)
+    if lse is None and return_lse:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+    _decode_operands(desc, q, out, lse, block_table, cache_seqlens, k_new, v_new, seqlens_out)
+    with torch.cuda.device(dev):
+        rc = lib().pkv_append_decode_attn_noalloc(
+            ctypes.byref(desc), _ptr(out), _ptr(lse), _ptr(q), hq, _ptr(k_cache), _ptr(v_cache), _ptr(k_new),
+            _ptr(v_new), _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens), _ptr(seqlens_out), batch,
+            int(max_kv_len), float(scale), _stream(k_cache))
+    _check("pkv_append_decode_attn_noalloc", rc)
     return (out, lse, seqlens_out) if lse is not None else (out, seqlens_out)
 
 

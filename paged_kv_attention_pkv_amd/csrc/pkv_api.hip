@@ -75,10 +75,11 @@ int current_device() {
 
 }  // namespace
 
+constexpr int kMaxDev = 64;  // devices the per-device caches cover
+
 namespace pkv {
 
 namespace {
-constexpr int kMaxDev = 64;
 std::atomic<int> g_cus[kMaxDev];
 std::mutex g_attr_mutex;
 }  // namespace
@@ -106,6 +107,32 @@ hipError_t set_smem_once(const void *kernel, int bytes, std::atomic<uint64_t> &d
 }
 
 }  // namespace pkv
+
+namespace {
+
+// Device-resident workspace of pkv_append_decode_attn_noalloc, for callers
+// that cannot allocate.  Each GPU the library runs on holds its own copy from
+// module load until the process ends.  In host code `scratch` only names the
+// symbol: its device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDev];
+
+// Device address of this device's scratch array (the current device must be
+// `dev`), looked up on its first use; nullptr if the lookup fails.
+void *scratch_for(int dev) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -184,7 +211,7 @@ pkv_status decode_common(const pkv_cache_desc *cache, void *out, float *lse, con
                          const void *k_cache, const void *v_cache, const void *k_new, const void *v_new,
                          const int32_t *block_table, int32_t bt_cols, const int32_t *cache_seqlens,
                          int32_t *seqlens_out, int32_t batch, int32_t max_kv_len, float scale, void *workspace,
-                         size_t workspace_bytes, int32_t workers, void *stream) {
+                         size_t workspace_bytes, int32_t workers, void *stream, bool clear_counters = false) {
     PoolGeom g;
     pkv_status st = check_desc(cache, &g);
     if (st) return st;
@@ -239,6 +266,11 @@ pkv_status decode_common(const pkv_cache_desc *cache, void *out, float *lse, con
     a.k_new = k_new;
     a.v_new = v_new;
     a.seqlens_out = seqlens_out;
+    if (clear_counters) {
+        const pkv_status zs = launch_status(pkv::launch_zero_words(
+            (int32_t *)workspace, (int64_t)(pkv::decode_counter_bytes(g, batch) / 4), (hipStream_t)stream));
+        if (zs) return zs;
+    }
     return launch_status(pkv::launch_decode(g, a, workspace, w_rec, (hipStream_t)stream));
 }
 
@@ -277,6 +309,32 @@ pkv_status pkv_append_decode_attn(const pkv_cache_desc *cache, void *out, float 
     return pkv_append_decode_attn_ex(cache, out, lse, q, num_q_heads, k_cache, v_cache, k_new, v_new, block_table,
                                      bt_cols, cache_seqlens, seqlens_out, batch, max_kv_len, scale, workspace,
                                      workspace_bytes, 0, stream);
+}
+
+pkv_status pkv_append_decode_attn_noalloc(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
+                                          int32_t num_q_heads, void *k_cache, void *v_cache, const void *k_new,
+                                          const void *v_new, const int32_t *block_table, int32_t bt_cols,
+                                          const int32_t *cache_seqlens, int32_t *seqlens_out, int32_t batch,
+                                          int32_t max_kv_len, float scale, void *stream) {
+    PoolGeom g;
+    pkv_status st = check_desc(cache, &g);
+    if (st) return st;
+    if ((st = check_heads(g, num_q_heads))) return st;
+    if (batch < 0) return PKV_EINVAL;
+    if (batch == 0) return PKV_OK;
+    if (!k_new || !v_new) return PKV_EINVAL;
+    const int dev = current_device();
+    if (dev < 0 || dev >= kMaxDev) return PKV_EDEVICE;
+    const int w_rec = pkv::decode_workers(dev, g, num_q_heads, -1, 0);
+    if (w_rec < 1) return PKV_EDEVICE;
+    if (pkv::decode_workspace(g, batch, num_q_heads, w_rec) > kScratchBytes)
+        return PKV_EWORKSPACE;  // more than the fixed scratch array holds
+    void *ws = scratch_for(dev);
+    if (!ws) return PKV_EDEVICE;
+    // The array keeps the last call's contents: its arrival counters are
+    // cleared by a fill kernel on the call's stream before the decode launch.
+    return decode_common(cache, out, lse, q, num_q_heads, k_cache, v_cache, k_new, v_new, block_table, bt_cols,
+                         cache_seqlens, seqlens_out, batch, max_kv_len, scale, ws, kScratchBytes, 0, stream, true);
 }
 
 pkv_status pkv_decode_attn(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
