@@ -150,7 +150,9 @@ class Oracle:
         lib.pkvref_append.argtypes = [P, V, V, V, V, I32P, I, I32P, I32P, I, I, I32P]
         lib.pkvref_decode.argtypes = [P, DP, DP, V, I, V, V, I32P, I, I32P, I, D, I]
         lib.pkvref_prefill.argtypes = [P, DP, DP, V, I, V, V, I32P, I, I32P, I32P, I, I, D, I64P, I]
-        for f in (lib.pkvref_route, lib.pkvref_append, lib.pkvref_decode, lib.pkvref_prefill):
+        L = ctypes.c_int64
+        lib.pkvref_rope.argtypes = [I, V, L, I, I, I32P, V, V, L, I]
+        for f in (lib.pkvref_route, lib.pkvref_append, lib.pkvref_decode, lib.pkvref_prefill, lib.pkvref_rope):
             f.restype = ctypes.c_int
         self._lib = lib
 
@@ -193,6 +195,25 @@ class Oracle:
         if rc:
             raise OracleError(rc, "append")
         return out
+
+    # -- rotary position embedding --------------------------------------
+    def rope(self, dtype: int, x: np.ndarray, positions, cos_table, sin_table, interleaved: bool) -> None:
+        """Rotates x [rows, heads, head_dim] (numpy; bf16 as uint16 bits or
+        fp32) in place, row r by position positions[r], with fp32 tables
+        [table_rows, head_dim/2]."""
+        if not isinstance(x, np.ndarray) or not x.flags.c_contiguous or not x.flags.writeable or x.ndim != 3:
+            raise ValueError("x must be a writeable contiguous 3-D numpy array")
+        _check_elem(x, dtype, "x")
+        pos = _to_np(positions, np.int32)
+        c = _to_np(cos_table, np.float32)
+        s = _to_np(sin_table, np.float32)
+        rows, heads, d = x.shape
+        if pos.shape != (rows,) or c.shape != s.shape or c.ndim != 2 or c.shape[1] * 2 != d:
+            raise ValueError("positions must be [rows] and the tables [table_rows, head_dim/2]")
+        rc = self._lib.pkvref_rope(int(dtype), _ptr(x), rows, heads, d, _ptr(pos), _ptr(c), _ptr(s), c.shape[0],
+                                   int(bool(interleaved)))
+        if rc:
+            raise OracleError(rc, "rope")
 
     # -- attention -------------------------------------------------------
     def decode(self, pool: Pool, q, k_cache, v_cache, block_table, seqlens, scale: float,

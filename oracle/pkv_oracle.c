@@ -26,6 +26,11 @@
  *    page the table routes that position to, before attention reads the pool
  *    [mini-infer 06, §1, the three things flash_attn_with_kvcache does].
  *
+ *  - Rotary position embedding (optional, before the append).  The new
+ *    token's q and k head vectors are rotated pair by pair by the angle of
+ *    its position, from caller-given cos/sin tables, in the half-split or the
+ *    interleaved pair layout [mini-infer 06, §3]; see pkvref_rope.
+ *
  *  - Attention.  For query row i of request r (kv_len keys, q_len queries,
  *    end-aligned causal), the row sees keys 0 .. kv_len - q_len + i, i.e.
  *    kv_len - q_len + i + 1 keys [FlashInfer PR #9451 analysis, §1, the
@@ -193,6 +198,91 @@ int pkvref_append(const pkvref_pool *pool, void *k_cache, void *v_cache,
         }
         if (seqlens_out)
             seqlens_out[b] = (int32_t)(cache_seqlens[b] + n_new);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* rotary position embedding                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Round an fp64 value to the nearest bf16 value, ties to even, and return
+ * its bit pattern.  bf16 keeps 8 significant bits and fp32's exponent range:
+ * the value is scaled so that its rounding quantum becomes 1, rounded to the
+ * nearest integer with ties to even (rint in the default rounding mode), and
+ * scaled back, both scalings being exact powers of two.  Values below the
+ * smallest normal (2^-126) share the subnormal quantum 2^-133; results of
+ * magnitude 2^128 or more are infinities. */
+static uint16_t round_to_bf16(double v)
+{
+    float f;
+    if (isnan(v)) {
+        f = (float)v;
+    } else if (v == 0.0 || isinf(v)) {
+        f = (float)v;
+    } else {
+        int e;
+        frexp(v, &e);                        /* 2^(e-1) <= |v| < 2^e */
+        int qexp = (e < -125 ? -125 : e) - 8; /* quantum 2^qexp: 8 significant bits */
+        double r = ldexp(rint(ldexp(v, -qexp)), qexp);
+        f = fabs(r) >= ldexp(1.0, 128) ? (r > 0 ? INFINITY : -INFINITY) : (float)r; /* exact */
+    }
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(u >> 16);
+}
+
+/* Store an fp64 value as one element of the given dtype, rounded to nearest
+ * with ties to even. */
+static void store_rounded(void *base, int64_t idx, int dtype, double v)
+{
+    if (dtype == PKVREF_BF16) {
+        uint16_t h = round_to_bf16(v);
+        memcpy((char *)base + (size_t)idx * 2u, &h, 2);
+    } else {
+        float f = (float)v;
+        memcpy((char *)base + (size_t)idx * 4u, &f, 4);
+    }
+}
+
+/* Rotary position embedding of a token's head vectors (the rotation Qwen's
+ * attention applies to q and k before the paged call: mini-infer 06 "True
+ * PagedAttention", §3, which also names the two cos/sin layouts).  The
+ * head_dim values of a head form head_dim/2 pairs: pair i is (i, i +
+ * head_dim/2) in the half-split layout and (2i, 2i+1) in the interleaved
+ * one.  At position p pair i is turned by the angle whose cosine and sine
+ * are cos_table[p][i] and sin_table[p][i]:
+ *     a' = a cos - b sin,   b' = b cos + a sin,
+ * computed in fp64 from the exactly widened values and rounded once to the
+ * element dtype.  x is [rows, heads, head_dim], rotated in place; row r is at
+ * position positions[r]. */
+int pkvref_rope(int dtype, void *x, int64_t rows, int heads, int head_dim,
+                const int32_t *positions, const float *cos_table, const float *sin_table,
+                int64_t table_rows, int interleaved)
+{
+    if ((dtype != PKVREF_F32 && dtype != PKVREF_BF16) || rows < 0 || heads < 1 || head_dim < 2 ||
+        head_dim % 2 || !x || !positions || !cos_table || !sin_table)
+        return PKVREF_E_ARG;
+    for (int64_t r = 0; r < rows; ++r)
+        if (positions[r] < 0 || positions[r] >= table_rows)
+            return PKVREF_E_LENGTH;
+    const int half = head_dim / 2;
+    for (int64_t r = 0; r < rows; ++r) {
+        const float *c = cos_table + (int64_t)positions[r] * half;
+        const float *s = sin_table + (int64_t)positions[r] * half;
+        for (int h = 0; h < heads; ++h) {
+            int64_t base = (r * heads + h) * (int64_t)head_dim;
+            for (int i = 0; i < half; ++i) {
+                int64_t ia = base + (interleaved ? 2 * i : i);
+                int64_t ib = base + (interleaved ? 2 * i + 1 : i + half);
+                double a = load_elem(x, ia, dtype), b = load_elem(x, ib, dtype);
+                double ci = (double)c[i], si = (double)s[i];
+                double ra = a * ci - b * si;
+                double rb = b * ci + a * si;
+                store_rounded(x, ia, dtype, ra);
+                store_rounded(x, ib, dtype, rb);
+            }
+        }
     }
     return 0;
 }

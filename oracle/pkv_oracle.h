@@ -50,6 +50,14 @@ int pkvref_append(const pkvref_pool *pool, void *k_cache, void *v_cache,
                   int bt_cols, const int32_t *cache_seqlens, const int32_t *new_indptr,
                   int batch, int total_new, int32_t *seqlens_out);
 
+/* Rotary position embedding of x [rows, heads, head_dim] (dtype elements) in
+ * place: row r at position positions[r] < table_rows; cos_table and
+ * sin_table are fp32 [table_rows, head_dim/2]; interleaved selects pairs
+ * (2i, 2i+1) instead of (i, i + head_dim/2). */
+int pkvref_rope(int dtype, void *x, int64_t rows, int heads, int head_dim,
+                const int32_t *positions, const float *cos_table, const float *sin_table,
+                int64_t table_rows, int interleaved);
+
 int pkvref_decode(const pkvref_pool *pool, double *out, double *lse, const void *q,
                   int num_q_heads, const void *k_cache, const void *v_cache,
                   const int32_t *block_table, int bt_cols, const int32_t *seqlens,

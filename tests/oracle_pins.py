@@ -498,6 +498,184 @@ def pin_append_ragged(orc):
         _close(out[b], ro[:, 0].numpy(), 1e-12, 1e-13, "after ragged append")
 
 
+# --------------------------------------------------------------------------
+# rotary position embedding (mini-infer 06 "True PagedAttention", §3)
+# --------------------------------------------------------------------------
+
+def _rope_tables(rows, d, base=10000.0):
+    """fp32 cos/sin tables [rows, d/2] of the angles p * base^(-2i/d), the
+    usual rotary frequencies, computed in fp64 and rounded to fp32."""
+    half = d // 2
+    inv = base ** (-np.arange(half, dtype=np.float64) * 2.0 / d)
+    ang = np.arange(rows, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def _rope_np(orc, dtype, x: torch.Tensor, pos, cos, sin, interleaved):
+    xb = _bits(x)
+    orc.rope(dtype, xb, np.asarray(pos, np.int32), cos, sin, interleaved)
+    return xb
+
+
+def pin_rope_unit_vectors(orc):
+    """A pair (a, b) = (1, 0) turns into (cos, sin) and (0, 1) into
+    (-sin, cos): the rotation is counter-clockwise by the table's angle, in
+    the slots each layout names (half-split: i and i + D/2; interleaved: 2i
+    and 2i+1)."""
+    d, rows = 8, 5
+    cos, sin = _rope_tables(rows, d)
+    half = d // 2
+    for interleaved in (False, True):
+        for i in range(half):
+            ia, ib = (2 * i, 2 * i + 1) if interleaved else (i, i + half)
+            for p in range(rows):
+                for (a, b), want in (((1.0, 0.0), (cos[p, i], sin[p, i])), ((0.0, 1.0), (-sin[p, i], cos[p, i]))):
+                    x = torch.zeros((1, 1, d), dtype=torch.float32)
+                    x[0, 0, ia], x[0, 0, ib] = a, b
+                    y = _rope_np(orc, F32, x, [p], cos, sin, interleaved)
+                    assert y[0, 0, ia] == np.float32(want[0]) and y[0, 0, ib] == np.float32(want[1]), (
+                        interleaved, i, p, (a, b))
+                    others = np.delete(y[0, 0], [ia, ib])
+                    assert np.all(others == 0)
+
+
+def pin_rope_position_zero_identity(orc):
+    """At position 0 (angle 0: cos 1, sin 0) every bit is unchanged, bf16 and fp32."""
+    gen = torch.Generator().manual_seed(31)
+    cos, sin = _rope_tables(4, 64)
+    for dtype in (F32, BF16):
+        x = _rand((6, 3, 64), dtype, gen)
+        for interleaved in (False, True):
+            y = _rope_np(orc, dtype, x, [0] * 6, cos, sin, interleaved)
+            assert np.array_equal(y, _bits(x)), (dtype, interleaved)
+
+
+def pin_rope_orthogonal(orc):
+    """The rotation keeps every head vector's norm and the inner product of
+    two vectors turned by the same positions (fp32, up to fp32 rounding)."""
+    gen = torch.Generator().manual_seed(32)
+    d = 128
+    cos, sin = _rope_tables(5000, d)
+    pos = [0, 1, 17, 999, 4095, 4999]
+    x = _rand((6, 4, d), F32, gen)
+    y = _rand((6, 4, d), F32, gen)
+    for interleaved in (False, True):
+        rx = _rope_np(orc, F32, x, pos, cos, sin, interleaved).astype(np.float64)
+        ry = _rope_np(orc, F32, y, pos, cos, sin, interleaved).astype(np.float64)
+        x64, y64 = x.double().numpy(), y.double().numpy()
+        _close(np.linalg.norm(rx, axis=-1), np.linalg.norm(x64, axis=-1), 1e-6, 1e-6, "rope norm")
+        _close((rx * ry).sum(-1), (x64 * y64).sum(-1), 1e-5, 1e-6, "rope inner product")
+
+
+def pin_rope_relative_position(orc):
+    """q turned by position m and k by position n have an inner product that
+    depends on m - n only: shifting both positions by s leaves it unchanged
+    (fp32, up to the rounding of the tables and of the rotation)."""
+    gen = torch.Generator().manual_seed(33)
+    d = 64
+    cos, sin = _rope_tables(3000, d)
+    q = _rand((1, 1, d), F32, gen)
+    k = _rand((1, 1, d), F32, gen)
+    for interleaved in (False, True):
+        for m, n in ((5, 3), (100, 40), (700, 699)):
+            dots = []
+            for shift in (0, 11, 1200, 2200):
+                rq = _rope_np(orc, F32, q, [m + shift], cos, sin, interleaved).astype(np.float64)
+                rk = _rope_np(orc, F32, k, [n + shift], cos, sin, interleaved).astype(np.float64)
+                dots.append(float((rq * rk).sum()))
+            _close(np.array(dots), np.full(len(dots), dots[0]), 2e-4, 1e-5, f"relative position {m}-{n}")
+
+
+def pin_rope_layouts_are_one_rotation(orc):
+    """The interleaved layout is the half-split one with the dims reordered:
+    moving dim 2i to i and 2i+1 to i + D/2, rotating half-split and moving
+    back gives the interleaved result bit for bit."""
+    gen = torch.Generator().manual_seed(34)
+    d = 32
+    cos, sin = _rope_tables(200, d)
+    half = d // 2
+    perm = np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])  # half-split slot j holds dim perm[j]
+    pos = [3, 199, 0, 42]
+    for dtype in (F32, BF16):
+        x = _rand((4, 2, d), dtype, gen)
+        inter = _rope_np(orc, dtype, x, pos, cos, sin, True)
+        split = _rope_np(orc, dtype, x[..., torch.from_numpy(perm)].contiguous(), pos, cos, sin, False)
+        back = np.empty_like(split)
+        back[..., perm] = split
+        assert np.array_equal(inter, back), dtype
+    assert half == d // 2
+
+
+def pin_rope_matches_rotate_half(orc):
+    """The half-split rotation equals the rotate_half form of the model code
+    the pages call (apply_rotary_pos_emb: x cos + rotate_half(x) sin, with the
+    half tables repeated twice), evaluated with torch in fp64; and the
+    interleaved one equals the same form on interleaved pairs.  fp32 inputs:
+    the fp64 results are rounded once to fp32 by torch, bit for bit equal."""
+    gen = torch.Generator().manual_seed(35)
+    d = 64
+    cos, sin = _rope_tables(4096, d)
+    pos = np.array([0, 1, 2, 77, 1023, 4095], np.int64)
+    x = _rand((6, 3, d), F32, gen)
+    c = torch.from_numpy(cos[pos]).double()[:, None, :]
+    s = torch.from_numpy(sin[pos]).double()[:, None, :]
+    x64 = x.double()
+    half = d // 2
+    rot = torch.cat([-x64[..., half:], x64[..., :half]], -1)
+    want = (x64 * torch.cat([c, c], -1) + rot * torch.cat([s, s], -1)).float().numpy()
+    got = _rope_np(orc, F32, x, pos, cos, sin, False)
+    assert np.array_equal(got, want), "half-split vs rotate_half"
+    x1, x2 = x64[..., 0::2], x64[..., 1::2]
+    rot_i = torch.stack([-x2, x1], -1).flatten(-2)
+    want_i = (x64 * c.repeat_interleave(2, -1) + rot_i * s.repeat_interleave(2, -1)).float().numpy()
+    got_i = _rope_np(orc, F32, x, pos, cos, sin, True)
+    assert np.array_equal(got_i, want_i), "interleaved vs pairwise rotate_half"
+
+
+def _bf16_nearest_even(v: float) -> int:
+    """bf16 bits of the fp64 value v rounded to nearest, ties to even, by
+    exact rational arithmetic (finite, normal-range v)."""
+    from fractions import Fraction
+
+    if v == 0.0:
+        return 0x8000 if math.copysign(1.0, v) < 0 else 0
+    sign = 0x8000 if v < 0 else 0
+    f = Fraction(abs(v))
+    e = math.floor(math.log2(abs(v)))
+    while Fraction(2) ** e > f:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= f:
+        e += 1
+    q = f / Fraction(2) ** (e - 7)  # in [128, 256)
+    n = math.floor(q)
+    rem = q - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    if n == 256:
+        n, e = 128, e + 1
+    return sign | ((e + 127) << 7) | (n - 128)
+
+
+def pin_rope_bf16_rounding(orc):
+    """bf16 storage: each rotated value is the fp64 result of the rotation
+    rounded to nearest bf16 with ties to even (the fp64 value from the
+    rotate_half form in torch, the rounding by exact rational arithmetic)."""
+    gen = torch.Generator().manual_seed(36)
+    d = 32
+    cos, sin = _rope_tables(600, d)
+    pos = np.array([1, 5, 99, 598, 300], np.int64)
+    x = _rand((5, 4, d), BF16, gen)
+    c = torch.from_numpy(cos[pos]).double()[:, None, :]
+    s = torch.from_numpy(sin[pos]).double()[:, None, :]
+    x64 = x.double()
+    half = d // 2
+    rot = torch.cat([-x64[..., half:], x64[..., :half]], -1)
+    want64 = (x64 * torch.cat([c, c], -1) + rot * torch.cat([s, s], -1)).numpy()
+    want = np.vectorize(_bf16_nearest_even, otypes=[np.uint16])(want64)
+    got = _rope_np(orc, BF16, x, pos, cos, sin, False)
+    assert np.array_equal(got, want), f"{int((got != want).sum())} of {got.size} bf16 roundings differ"
+
+
 ALL_PINS = [
     pin_layout_contiguous,
     pin_sdpa_decode,
@@ -512,4 +690,11 @@ ALL_PINS = [
     pin_empty_rows,
     pin_route_matches_append,
     pin_append_ragged,
+    pin_rope_unit_vectors,
+    pin_rope_position_zero_identity,
+    pin_rope_orthogonal,
+    pin_rope_relative_position,
+    pin_rope_layouts_are_one_rotation,
+    pin_rope_matches_rotate_half,
+    pin_rope_bf16_rounding,
 ]

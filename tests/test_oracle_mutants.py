@@ -45,6 +45,17 @@ MUTANTS = {
     "q_head_index": ("(token * job->num_q_heads + h) * (int64_t)D",
                      "(token * job->num_q_heads) * (int64_t)D"),
     "pair_count_dropped": ("visible > 0 ? visible : 0", "visible > 1 ? visible - 1 : 0"),
+    "rope_sin_sign": ("double ra = a * ci - b * si;", "double ra = a * ci + b * si;"),
+    "rope_uses_rotated_a": ("double rb = b * ci + a * si;", "double rb = b * ci + ra * si;"),
+    "rope_half_pairing": ("(interleaved ? 2 * i + 1 : i + half)", "(interleaved ? 2 * i + 1 : half - 1 - i)"),
+    "rope_interleaved_pairing": ("(interleaved ? 2 * i : i)", "(interleaved ? i : i)"),
+    "rope_position_off_by_one": ("const float *c = cos_table + (int64_t)positions[r] * half;",
+                                 "const float *c = cos_table + (int64_t)(positions[r] + 1) * half;"),
+    "rope_cos_sin_swapped": ("double ci = (double)c[i], si = (double)s[i];",
+                             "double ci = (double)s[i], si = (double)c[i];"),
+    "rope_bf16_truncates": ("double r = ldexp(rint(ldexp(v, -qexp)), qexp);",
+                            "double r = ldexp(trunc(ldexp(v, -qexp)), qexp);"),
+    "rope_bf16_one_bit_short": ("int qexp = (e < -125 ? -125 : e) - 8;", "int qexp = (e < -125 ? -125 : e) - 7;"),
     "route_offset_head": ("token_offset(pool, block_table, bt_cols, b, j, 0) : -1",
                           "token_offset(pool, block_table, bt_cols, b, j, 1) : -1"),
 }
