@@ -1,35 +1,40 @@
 #!/usr/bin/env python3
 """Benchmark of the paged KV attention hot path on one MI355X.
 
-Default workload: the Qwen3-4B-shaped decode step at batch 64 (Hq 32 / Hkv 8 /
-head_dim 128, bf16, page size 16, cached lengths U{512..1024}, pages shuffled
-over a pool 1.25x the pages needed), one appended token per sequence, over 36
-independent layer caches (36 x 254 MB of pools, far more than the 256 MB
-last-level cache, so every layer's K/V comes from HBM).
+Default run (``python bench.py``): one JSON line whose headline is the
+Qwen3-4B-shaped decode step at batch 64 (Hq 32 / Hkv 8 / head_dim 128, bf16,
+page size 16, cached lengths U{512..1024}, pages shuffled over a pool 1.25x
+the pages needed), one appended token per sequence, over 36 independent layer
+caches (36 x 254 MB of pools, far more than the 256 MB last-level cache, so
+every layer's K/V comes from HBM).  One step = for each of the 36 layers one
+pkv_append_decode_attn launch (append + attend).  The same line carries a
+nested ``prefill`` object with the causal paged prefill at head_dim 256,
+Hq 48 / Hkv 8: the single request q_len = kv_len = 1023 and a random batch of
+8 requests (q_len U{65..4096}, kv_len = q_len + U{0..4096}), each step being
+8 layers with their own pools and inputs.
 
-One step = for each of the 36 layers: pkv_append (the new token) then
-pkv_decode_attn -- the whole decode hot path.  The step is captured once in a
-HIP graph and replayed (``--eager`` launches it from Python instead).  All
-inputs are resident in HBM before the timed region.
+Every step is captured once in a HIP graph and replayed (``--eager`` launches
+it from Python instead).  All inputs are resident in HBM before the timed
+region.  W warmup steps, then exactly K timed steps between two
+synchronisations; HIP events recorded between the steps on the launch stream
+give the per-step median and best next to the mean.
 
-Printed: one JSON line with the metric (KV-read GB/s = bytes of the attended
-K/V tokens read per step / step time), the per-layer call time, a roofline
-object for the dominant kernel (decode; its per-launch duration measured with
-HIP events on the launch stream) and the CPU oracle timed on a bounded sample
-of the same workload on the host cores.
+Each workload reports a roofline object for its dominant kernel (its
+per-launch duration from the HIP events of the timed region) and the CPU
+oracle timed on a bounded sample of the same workload on the host cores (and
+on one core).
 
-``--workload prefill`` times causal paged prefill instead (head_dim 256,
-Hq 48 / Hkv 8, the B=1 q_len = kv_len = 1023 request, or ``--batch B`` random
-requests) against the bf16 MFMA roofline.
+``--workload decode|sweep|long|prefill`` with ``--batch B`` times one
+workload only.
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
-import math
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -38,6 +43,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_MFMA_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, 2.5 PFLOP/s
+CPU_THREADS_MAX = 16           # host threads of one GPU's share of the box
 
 
 def log(*a):
@@ -49,14 +55,18 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="decode", choices=["decode", "sweep", "long", "prefill"])
+    p.add_argument("--workload", default=None, choices=["decode", "sweep", "long", "prefill"],
+                   help="time one workload only (default: decode B=64 plus the two prefill cases)")
     p.add_argument("--batch", type=int, default=None)
     p.add_argument("--layers", type=int, default=36, help="decode: layer caches per step")
     p.add_argument("--prefill-layers", type=int, default=8,
                    help="prefill: layers per step, each with its own pools and inputs")
     p.add_argument("--eager", action="store_true", help="launch from Python instead of replaying a graph")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    p.add_argument("--cpu-seconds", type=float, default=6.0,
+                   help="target CPU time of each oracle sample on all host threads")
+    p.add_argument("--cpu-seconds-1t", type=float, default=2.0,
+                   help="target CPU time of each oracle sample on one thread")
     p.add_argument("--workers", type=int, default=0, help="decode split workers (0 = library default)")
     p.add_argument("--separate", action="store_true",
                    help="decode step as pkv_append + pkv_decode_attn (two launches) instead of the fused "
@@ -109,6 +119,17 @@ def traffic_from_profile(kernel_src: str, name: str):
     return float(t.group(1))
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 # --------------------------------------------------------------------------
 # timing helpers
 # --------------------------------------------------------------------------
@@ -137,8 +158,8 @@ def events_per_call(torch, calls, reps=3):
 
 
 def time_steps(torch, step, steps, warmup, use_graph):
-    """(ms per step, graph used) over `steps` timed steps after `warmup`."""
-    graph = None
+    """Mean ms per step over exactly `steps` timed steps after `warmup`, and
+    the per-step times from events recorded between the steps."""
     if use_graph:
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -155,23 +176,30 @@ def time_steps(torch, step, steps, warmup, use_graph):
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
         run()
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps, graph
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return ev[0].elapsed_time(ev[steps]) / steps, per
+
+
+def spread(per, scale=1.0, nd=2):
+    """Median and best of per-step times, scaled."""
+    return {"median": round(statistics.median(per) * scale, nd), "best": round(min(per) * scale, nd),
+            "rounds": len(per)}
 
 
 # --------------------------------------------------------------------------
 # decode
 # --------------------------------------------------------------------------
 
-def bench_decode(args, torch, pkv, wl):
-    if args.workload == "decode":
+def bench_decode(args, torch, pkv, wl, workload):
+    if workload == "decode":
         spec = wl.decode_spec("qwen3_decode", batch=args.batch or 64)
-    elif args.workload == "sweep":
+    elif workload == "sweep":
         spec = wl.decode_spec("qwen3_sweep", batch=args.batch or 64)
     else:
         spec = wl.decode_spec("long_ragged", batch=args.batch or 256)
@@ -179,7 +207,7 @@ def bench_decode(args, torch, pkv, wl):
     L = args.layers
     fused = not args.separate and spec.dtype == "bf16"
     acc = decode_bytes(spec, fused)
-    if args.workload == "long":
+    if workload == "long":
         free = torch.cuda.mem_get_info(dev)[0]
         per_layer = 2 * spec.num_pages * spec.hkv * spec.page_size * spec.head_dim * 2
         # room for one layer's fp32 input draws on top of the pools
@@ -209,27 +237,27 @@ def bench_decode(args, torch, pkv, wl):
         out = torch.empty_like(inp.q)
         if fused:
             app = None
-            dec = pkv.api.prepare_append_decode(inp.q, kc, vc, inp.k_new, inp.v_new, bt, hist, max_kv, spec.scale, out,
-                                                workspace, seqlens_out=lens, workers=args.workers)
+            dec = pkv.api.prepare_append_decode(inp.q, kc, vc, inp.k_new, inp.v_new, bt, hist, max_kv, spec.scale,
+                                                out, workspace, seqlens_out=lens, workers=args.workers)
         else:
             app = pkv.api.prepare_append(kc, vc, inp.k_new, inp.v_new, bt, hist, lens)
             dec = pkv.api.prepare_decode(inp.q, kc, vc, bt, lens, max_kv, spec.scale, out, workspace,
                                          workers=args.workers)
-        layers.append((app, dec, None))
+        layers.append((app, dec))
         del inp
     del pools
     torch.cuda.synchronize()
 
     def step():
-        for app, dec, _ in layers:
+        for app, dec in layers:
             if app is not None:
                 app()
             dec()
 
-    ms, _ = time_steps(torch, step, args.steps, args.warmup, not args.eager)
+    ms, per = time_steps(torch, step, args.steps, args.warmup, not args.eager)
     step()  # lens is live again for the per-call brackets below
-    dec_mean, dec_med = events_per_call(torch, [d for _, d, _ in layers])
-    app_mean = None if fused else events_per_call(torch, [a for a, _, _ in layers])[0]
+    dec_mean, _ = events_per_call(torch, [d for _, d in layers])
+    app_mean = None if fused else events_per_call(torch, [a for a, _ in layers])[0]
     kv_bytes_step = acc["kv"] * L
     value = kv_bytes_step / (ms * 1e-3) / 1e9
     # the kernel's average launch duration: in the fused step the timed region
@@ -259,6 +287,9 @@ def bench_decode(args, torch, pkv, wl):
                             if fused else "per layer: pkv_append(1 token/seq) + pkv_decode_attn"),
                    "launch": "eager" if args.eager else "hip graph", "parallelism": "none (1 GPU)"},
         "us_per_call": round(ms * 1e3 / L, 2),
+        "us_per_call_over_steps": spread(per, 1e3 / L),
+        "value_over_steps": {"median": round(kv_bytes_step / (statistics.median(per) * 1e-3) / 1e9, 1),
+                             "best": round(kv_bytes_step / (min(per) * 1e-3) / 1e9, 1), "rounds": len(per)},
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "decode_us_per_call_events": round(dec_mean * 1e3, 2),
         "append_us_per_call_events": None if app_mean is None else round(app_mean * 1e3, 2),
@@ -271,13 +302,26 @@ def bench_decode(args, torch, pkv, wl):
                      "traffic": None if traffic is None else int(traffic),
                      "traffic_unit": "HBM bytes per launch", "bytes_per_launch": acc["total"]},
     }
-    return result, spec, layers
+    del layers, workspace
+    return result, spec
 
 
-def cpu_baseline_decode(args, torch, spec, layers):
+def _timed_loop(fn, seconds, min_calls=1):
+    """Call fn(i) until about `seconds` have been spent; (calls, seconds, sum of its returns)."""
+    spent, calls, total = 0.0, 0, 0
+    while spent < seconds or calls < min_calls:
+        t0 = time.perf_counter()
+        total += fn(calls)
+        spent += time.perf_counter() - t0
+        calls += 1
+    return calls, spent, total
+
+
+def cpu_baseline_decode(args, spec):
     """The oracle (as is) on a bounded sample of the same workload: whole
-    layers of the batch (host pools built by the oracle's own append), run
-    on the host cores until about --cpu-seconds have been spent."""
+    decode calls of the batch (host pools built by the oracle's own append
+    from two layers' draws), on all host threads of the GPU's share, then on
+    one thread."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import numpy as np
     import oracle
@@ -285,11 +329,11 @@ def cpu_baseline_decode(args, torch, spec, layers):
     from gpu_common import host_bits, opool
 
     orc = oracle.load()
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = max(1, min(CPU_THREADS_MAX, os.cpu_count() or 1))
     pool = opool(spec)
     zeros = np.zeros(spec.batch, np.int32)
     hosts = []
-    for layer in range(min(2, len(layers))):
+    for layer in range(2):
         inp = wl.decode_inputs(spec, device="cuda:0", seed_offset=layer).to("cpu")
         kc = host_bits(wl.empty_pool(spec, "cpu")).copy()
         vc = kc.copy()
@@ -298,32 +342,37 @@ def cpu_baseline_decode(args, torch, spec, layers):
         lens = orc.append(pool, kc, vc, host_bits(inp.k_new), host_bits(inp.v_new), spec.block_table,
                           spec.hist_lens)
         hosts.append((host_bits(inp.q), kc, vc, lens))
-    done_bytes, spent, calls = 0, 0.0, 0
-    while spent < args.cpu_seconds or calls == 0:
-        q, kc, vc, lens = hosts[calls % len(hosts)]
-        t0 = time.perf_counter()
-        orc.decode(pool, q, kc, vc, spec.block_table, lens, spec.scale, nthreads=threads)
-        spent += time.perf_counter() - t0
-        done_bytes += decode_bytes(spec)["kv"]
-        calls += 1
-    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{calls} decode calls of the same workload (all {spec.batch} sequences, layer caches "
-                      f"0..{len(hosts) - 1} in turn), fp64 oracle, {spent:.1f} s"}
+    per_call = decode_bytes(spec)["kv"]
+
+    def call(nt):
+        def f(i):
+            q, kc, vc, lens = hosts[i % len(hosts)]
+            orc.decode(pool, q, kc, vc, spec.block_table, lens, spec.scale, nthreads=nt)
+            return per_call
+        return f
+
+    calls, spent, done = _timed_loop(call(threads), args.cpu_seconds)
+    calls1, spent1, done1 = _timed_loop(call(1), args.cpu_seconds_1t)
+    return {"value": round(done / spent / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "value_1_thread": round(done1 / spent1 / 1e9, 4),
+            "host_cpu_count": os.cpu_count(), "cpu_model": cpu_model(),
+            "sample": f"{calls} decode calls of the same workload (all {spec.batch} sequences, two layers' draws "
+                      f"in turn) on {threads} threads in {spent:.1f} s; {calls1} calls on 1 thread in "
+                      f"{spent1:.1f} s; fp64 oracle, KV-read bytes per second"}
 
 
 # --------------------------------------------------------------------------
 # prefill
 # --------------------------------------------------------------------------
 
-def bench_prefill(args, torch, pkv, wl):
-    spec = wl.prefill_spec(fixed_1023=True) if args.batch is None else wl.prefill_spec(batch=args.batch)
+def bench_prefill(args, torch, pkv, wl, spec):
     dev = torch.device("cuda:0")
     flops = prefill_flops(spec)
     L = max(1, args.prefill_layers)
     log(f"[bench] {spec.name}: {flops / 1e9:.2f} GFLOP per call, {L} layers per step")
     max_q, max_kv = int(spec.q_lens.max()), int(spec.kv_lens.max())
     zeros = torch.zeros(spec.batch, dtype=torch.int32, device=dev)
-    calls, inp0, ws = [], None, None
+    calls, ws = [], None
     for layer in range(L):
         # every layer its own pools, queries and outputs, as the layers of a model
         inp = wl.prefill_inputs(spec, device=dev, seed_offset=layer)
@@ -336,8 +385,6 @@ def bench_prefill(args, torch, pkv, wl):
             ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         calls.append(pkv.api.prepare_prefill(inp.q, kc, vc, inp.block_table, kv_lens, inp.qo_indptr, max_q,
                                              max_kv, spec.scale, out, ws))
-        if layer == 0:
-            inp0 = inp
         del inp
     torch.cuda.synchronize()
 
@@ -345,7 +392,7 @@ def bench_prefill(args, torch, pkv, wl):
         for c in calls:
             c()
 
-    ms, _ = time_steps(torch, step, args.steps, args.warmup, not args.eager)
+    ms, per = time_steps(torch, step, args.steps, args.warmup, not args.eager)
     mean = ms / L  # L launches per step: the timed region's HIP events give their average duration
     tfs = flops / (mean * 1e-3) / 1e12
     traffic = traffic_from_profile(os.path.join(ROOT, "paged_kv_attention_pkv_amd", "csrc", "prefill.hip"),
@@ -358,25 +405,32 @@ def bench_prefill(args, torch, pkv, wl):
         "metric": "paged causal prefill attn: TFLOP/s (% bf16 MFMA peak), D256 Hq48/Hkv8",
         "value": round(flops * L / (ms * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": spec.name, "batch": spec.batch, "hq": spec.hq, "hkv": spec.hkv,
                    "head_dim": spec.head_dim, "q_lens_sum": int(spec.q_lens.sum()),
                    "kv_lens_sum": int(spec.kv_lens.sum()), "layers": L,
                    "step": "per layer: one pkv_prefill_attn call (own pools and inputs)",
-                   "launch": "eager" if args.eager else "hip graph", "parallelism": "none (1 GPU)"},
+                   "launch": "eager" if args.eager else "hip graph"},
         "us_per_call": round(ms * 1e3 / L, 2),
+        "us_per_call_over_steps": spread(per, 1e3 / L),
+        "value_over_steps": {"median": round(flops * L / (statistics.median(per) * 1e-3) / 1e12, 2),
+                             "best": round(flops * L / (min(per) * 1e-3) / 1e12, 2), "rounds": len(per)},
         "roofline": {"bound": "mfma", "kernel": f"prefill16_kernel<256, {waves}> (one launch per pkv_prefill_attn, "
                                                   f"{16 * waves} query rows per workgroup)", "achieved": round(tfs, 2),
                      "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s", "frac": round(tfs / BF16_MFMA_PEAK_TFS, 4),
                      "traffic": None if traffic is None else int(traffic),
                      "traffic_unit": "HBM bytes per launch", "flops_per_launch": flops},
     }
-    return result, spec, inp0
+    del calls, ws
+    return result
 
 
-def cpu_baseline_prefill(args, torch, spec, inp):
-    """Oracle on a sample of query rows of the same request(s)."""
+def cpu_baseline_prefill(args, spec):
+    """The oracle (as is) on a sample of query rows of the same request(s):
+    blocks of 32 consecutive rows of request 0, from its last row backwards,
+    each run as a chunked-prefill request over the keys it sees, on all host
+    threads of the GPU's share, then on one thread."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import numpy as np
     import oracle
@@ -384,8 +438,8 @@ def cpu_baseline_prefill(args, torch, spec, inp):
     from gpu_common import host_bits
 
     orc = oracle.load()
-    threads = max(1, min(16, os.cpu_count() or 1))
-    h = inp.to("cpu")
+    threads = max(1, min(CPU_THREADS_MAX, os.cpu_count() or 1))
+    h = wl.prefill_inputs(spec, device="cuda:0").to("cpu")
     pool = oracle.Pool.hnd(oracle.BF16, spec.num_pages, spec.page_size, spec.hkv, spec.head_dim)
     kc = host_bits(wl.empty_pool(spec, "cpu")).copy()
     vc = kc.copy()
@@ -393,30 +447,31 @@ def cpu_baseline_prefill(args, torch, spec, inp):
                np.zeros(spec.batch, np.int32), h.hist_indptr.numpy())
     kv = orc.append(pool, kc, vc, host_bits(h.k_new), host_bits(h.v_new), spec.block_table, spec.hist_lens,
                     h.qo_indptr.numpy())
-    # blocks of 32 consecutive query rows of request 0, from its last row
-    # backwards (starting over at the last row once the first is reached), each
-    # run as a chunked-prefill request over the keys it sees, until about
-    # --cpu-seconds have been spent
     r0, kvl = int(spec.q_lens[0]), int(kv[0])
     ip = h.qo_indptr.numpy()
-    fl, spent, done, blk = 0, 0.0, 0, 32
-    while spent < args.cpu_seconds or done == 0:
-        pos = done % r0
-        rows = min(blk, r0 - pos)
-        a1 = r0 - pos
-        a0 = a1 - rows
-        q = host_bits(h.q[ip[0] + a0: ip[0] + a1])
-        kv_seen = kvl - r0 + a1
-        t0 = time.perf_counter()
-        orc.prefill(pool, q, kc, vc, spec.block_table[:1], np.array([kv_seen], np.int32),
-                    np.array([0, rows], np.int32), spec.scale, causal=True, nthreads=threads)
-        spent += time.perf_counter() - t0
-        fl += 4 * spec.head_dim * spec.hq * sum(kv_seen - rows + i + 1 for i in range(rows))
-        done += rows
+    blk = 32
+
+    def block(nt):
+        def f(i):
+            pos = (i * blk) % r0
+            rows = min(blk, r0 - pos)
+            a1 = r0 - pos
+            a0 = a1 - rows
+            kv_seen = kvl - r0 + a1
+            orc.prefill(pool, host_bits(h.q[ip[0] + a0: ip[0] + a1]), kc, vc, spec.block_table[:1],
+                        np.array([kv_seen], np.int32), np.array([0, rows], np.int32), spec.scale, causal=True,
+                        nthreads=nt)
+            return 4 * spec.head_dim * spec.hq * sum(kv_seen - rows + j + 1 for j in range(rows))
+        return f
+
+    n, spent, fl = _timed_loop(block(threads), args.cpu_seconds)
+    n1, spent1, fl1 = _timed_loop(block(1), args.cpu_seconds_1t)
     return {"value": round(fl / spent / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} query rows of request 0 ({r0} rows, taken from its last row backwards, "
-                      f"cyclically) in blocks of {blk} ({fl / 1e9:.2f} GFLOP), "
-                      f"fp64 oracle, {spent:.1f} s"}
+            "value_1_thread": round(fl1 / spent1 / 1e12, 6),
+            "host_cpu_count": os.cpu_count(), "cpu_model": cpu_model(),
+            "sample": f"{n} blocks of {blk} query rows of request 0 ({r0} rows; from its last row backwards, "
+                      f"cyclically) on {threads} threads in {spent:.1f} s ({fl / 1e9:.1f} GFLOP); {n1} blocks on "
+                      f"1 thread in {spent1:.1f} s; fp64 oracle"}
 
 
 def calibrate_copy(torch):
@@ -450,15 +505,29 @@ def main():
 
     props = torch.cuda.get_device_properties(0)
     log(f"[bench] device {props.name} ({getattr(props, 'gcnArchName', '?')}), CUs {props.multi_processor_count}")
+    cpu = not args.no_cpu_baseline
     if args.workload == "prefill":
-        result, spec, inp = bench_prefill(args, torch, pkv, wl)
-        if not args.no_cpu_baseline:
-            result["cpu_baseline"] = cpu_baseline_prefill(args, torch, spec, inp)
+        spec = wl.prefill_spec(fixed_1023=True) if args.batch is None else wl.prefill_spec(batch=args.batch)
+        result = bench_prefill(args, torch, pkv, wl, spec)
+        result.update({"n_gpus": 1, "scaling": "weak", "vs_baseline": None})
+        if cpu:
+            result["cpu_baseline"] = cpu_baseline_prefill(args, spec)
     else:
-        result, spec, layers = bench_decode(args, torch, pkv, wl)
-        if not args.no_cpu_baseline:
-            result["cpu_baseline"] = cpu_baseline_decode(args, torch, spec, layers)
-    result["device"] = {"name": props.name, "cus": props.multi_processor_count}
+        result, spec = bench_decode(args, torch, pkv, wl, args.workload or "decode")
+        if cpu:
+            result["cpu_baseline"] = cpu_baseline_decode(args, spec)
+        if args.workload is None:
+            torch.cuda.empty_cache()
+            result["prefill"] = {}
+            for key, pspec in (("b1_q1023", wl.prefill_spec(fixed_1023=True)),
+                               ("b8_random", wl.prefill_spec(batch=8))):
+                sub = bench_prefill(args, torch, pkv, wl, pspec)
+                if cpu:
+                    sub["cpu_baseline"] = cpu_baseline_prefill(args, pspec)
+                result["prefill"][key] = sub
+                torch.cuda.empty_cache()
+    result["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", "?"),
+                        "cus": props.multi_processor_count}
     print(json.dumps(result), flush=True)
 
 

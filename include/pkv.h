@@ -105,6 +105,10 @@ const char *pkv_status_string(pkv_status status);
  *   seqlens_out    int32 [batch] or NULL: receives L_b + tokens appended, the
  *                  attended length for the following attention call.  Must not
  *                  alias cache_seqlens.
+ * A padding row (cache_seqlens[b] = -1, the fixed-size batch slots of a
+ * captured decode graph: unsloth scripts commit page, "Why this works" item
+ * 3) writes nothing and keeps seqlens_out[b] = -1; its new_indptr range may
+ * hold rows, which are ignored.
  * Token t of sequence b goes to logical position L_b + t; its page must be a
  * real page (1..num_pages-1) and no two appended tokens may share a slot.  The
  * copy is bit-exact; no other byte of either pool is written.
@@ -113,6 +117,39 @@ pkv_status pkv_append(const pkv_cache_desc *cache, void *k_cache, void *v_cache,
                       const void *k_new, const void *v_new, const int32_t *block_table,
                       int32_t bt_cols, const int32_t *cache_seqlens, const int32_t *new_indptr,
                       int32_t batch, int32_t total_new, int32_t *seqlens_out, void *stream);
+
+/*
+ * pkv_append_rope -- pkv_append with the rotary position embedding of the
+ * new tokens fused in: each new token's k is rotated before it is stored,
+ * and its q (when given) is rotated in place for the attention call that
+ * follows.  mini-infer 06 §3 applies this rotation to q and k right before
+ * the paged flash_attn call, and notes the two cos/sin layouts in use.
+ *
+ * A head vector's head_dim values form head_dim/2 pairs: pair i is
+ * (i, i + head_dim/2) when rope_interleaved == 0 (the half-split layout of
+ * Qwen-style rotate_half) and (2i, 2i+1) otherwise (the interleaved layout).
+ * Token t of sequence b is at position p = L_b + t, and its pair i turns by
+ * the angle of cos/sin table row p:
+ *     a' = a * rope_cos[p][i] - b * rope_sin[p][i]
+ *     b' = b * rope_cos[p][i] + a * rope_sin[p][i]
+ * evaluated in fp64 from the exact values and stored rounded to nearest
+ * (ties to even) in the pool's dtype.  V is stored unrotated.
+ *
+ *   rope_cos, rope_sin  float [rope_rows, head_dim/2], device, 16-byte aligned;
+ *                       every position L_b + t must be < rope_rows (a larger
+ *                       position reads row rope_rows - 1: stays in bounds,
+ *                       gives a wrong rotation)
+ *   q                   [total_new, num_q_heads, head_dim] or NULL: rotated in
+ *                       place, row new_indptr[b] + t by position L_b + t
+ * The other arguments, the padding-row rule (L_b = -1: nothing rotated or
+ * written) and the errors are those of pkv_append.
+ */
+pkv_status pkv_append_rope(const pkv_cache_desc *cache, void *k_cache, void *v_cache,
+                           const void *k_new, const void *v_new, void *q, int32_t num_q_heads,
+                           const float *rope_cos, const float *rope_sin, int32_t rope_rows,
+                           int32_t rope_interleaved, const int32_t *block_table, int32_t bt_cols,
+                           const int32_t *cache_seqlens, const int32_t *new_indptr, int32_t batch,
+                           int32_t total_new, int32_t *seqlens_out, void *stream);
 
 /*
  * pkv_decode_workspace_bytes -- device workspace pkv_decode_attn needs for
@@ -157,8 +194,9 @@ pkv_status pkv_decode_workspace_reset(const pkv_cache_desc *cache, int32_t batch
  *   lse            float [batch, num_q_heads] or NULL: natural-log
  *                  log-sum-exp of the scaled scores (-inf for an empty row)
  *   q              [batch, num_q_heads, head_dim], dtype of the pool
- *   cache_seqlens  int32 [batch]: ATTENDED length n_b (after append); 0 gives
- *                  out = 0 and lse = -inf for that row
+ *   cache_seqlens  int32 [batch]: ATTENDED length n_b (after append); 0 (or a
+ *                  padding row's -1) gives out = 0 and lse = -inf for that
+ *                  row, and nothing of the row (q, table) is read
  *   max_kv_len     host upper bound of cache_seqlens (no device read-back is
  *                  made to find it; mini-infer 06 §5); must satisfy
  *                  max_kv_len <= bt_cols * page_size; above 2^28 the call
@@ -213,6 +251,12 @@ pkv_status pkv_decode_attn_ex(const pkv_cache_desc *cache, void *out, float *lse
  *                     was not (see below); must not alias cache_seqlens
  *   max_kv_len        host upper bound of L_b + 1 (<= bt_cols * page_size)
  *   workspace         as for pkv_decode_attn (same size query)
+ * Padding rows: cache_seqlens[b] = -1 marks a batch slot that takes no part
+ * in the step (the fixed-size batch buckets of a captured decode graph:
+ * unsloth scripts commit page, "Why this works" item 3).  Nothing of the row
+ * is read (q, k_new, v_new, its table row may hold anything, NaN included),
+ * nothing is written to the pools, out = 0, lse = -inf and seqlens_out[b]
+ * stays -1.  No page needs to be reserved for such a slot.
  * Preconditions (checked on the host by pkv_validate_decode_step_host):
  * L_b + 1 <= max_kv_len, the slot's page is a real page (1..num_pages-1) and
  * no two sequences share a slot.  Where they are violated the call stays in
@@ -341,7 +385,8 @@ pkv_status pkv_validate_host(const pkv_cache_desc *cache, const int32_t *block_t
  * pkv_validate_decode_step_host -- host-side check of the preconditions of
  * pkv_append_decode_attn on HOST copies: 0 <= L_b and L_b + 1 <= max_kv_len
  * <= bt_cols*page_size; every block of the L_b + 1 attended keys is a page
- * in 1..num_pages-1; no two rows append into the same (page, slot).
+ * in 1..num_pages-1; no two rows append into the same (page, slot).  Padding
+ * rows (L_b = -1) are skipped.
  *   block_table  host int32 [batch, bt_cols]; cache_seqlens host int32 [batch]
  * Returns PKV_OK or PKV_EVALIDATE with a message in msg (host, may be NULL).
  */
@@ -353,7 +398,8 @@ pkv_status pkv_validate_decode_step_host(const pkv_cache_desc *cache, const int3
  * pkv_validate_append_host -- host-side check of pkv_append's preconditions
  * on HOST copies: every target position routes to a page in
  * 1..num_pages-1, the table is wide enough, new_indptr is consistent, and no
- * two appended tokens target the same (page, slot).
+ * two appended tokens target the same (page, slot).  Padding rows
+ * (cache_seqlens[b] = -1) write nothing and are skipped.
  */
 pkv_status pkv_validate_append_host(const pkv_cache_desc *cache, const int32_t *block_table,
                                     int32_t bt_cols, const int32_t *cache_seqlens,

@@ -19,6 +19,7 @@ namespace {
 
 constexpr int kPageSize = 16;
 constexpr int32_t kMaxDecodeKv = 1 << 28;  // decode: max_kv_len bound (PKV_EUNSUPPORTED above)
+constexpr int32_t kPaddingRow = -1;        // cache length of a padding row (appends and decode steps)
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -172,6 +173,34 @@ pkv_status pkv_append(const pkv_cache_desc *cache, void *k_cache, void *v_cache,
     return launch_status(pkv::launch_append(g, k_cache, v_cache, k_new, v_new, block_table, bt_cols,
                                             cache_seqlens, new_indptr, batch, total_new, seqlens_out,
                                             (hipStream_t)stream));
+}
+
+pkv_status pkv_append_rope(const pkv_cache_desc *cache, void *k_cache, void *v_cache, const void *k_new,
+                           const void *v_new, void *q, int32_t num_q_heads, const float *rope_cos,
+                           const float *rope_sin, int32_t rope_rows, int32_t rope_interleaved,
+                           const int32_t *block_table, int32_t bt_cols, const int32_t *cache_seqlens,
+                           const int32_t *new_indptr, int32_t batch, int32_t total_new, int32_t *seqlens_out,
+                           void *stream) {
+    PoolGeom g;
+    pkv_status st = check_desc(cache, &g);
+    if (st) return st;
+    if (batch < 0 || total_new < 0 || bt_cols < 0 || rope_rows < 0) return PKV_EINVAL;
+    if (q && (st = check_heads(g, num_q_heads))) return st;
+    if (batch == 0) return total_new == 0 ? PKV_OK : PKV_EINVAL;
+    if (!new_indptr && total_new != batch) return PKV_EINVAL;
+    if (!cache_seqlens) return PKV_EINVAL;
+    if (total_new > 0 && (!k_cache || !v_cache || !k_new || !v_new || !block_table || bt_cols < 1 || !rope_cos ||
+                          !rope_sin || rope_rows < 1))
+        return PKV_EINVAL;
+    if (seqlens_out && seqlens_out == cache_seqlens) return PKV_EINVAL;
+    if (total_new == 0 && !seqlens_out) return PKV_OK;
+    if (total_new > 0 && (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new) ||
+                          !aligned16(rope_cos) || !aligned16(rope_sin) || (q && !aligned16(q))))
+        return PKV_EUNSUPPORTED;
+    return launch_status(pkv::launch_append_rope(g, k_cache, v_cache, k_new, v_new, q, num_q_heads, rope_cos, rope_sin,
+                                                 rope_rows, rope_interleaved ? 1 : 0, block_table, bt_cols,
+                                                 cache_seqlens, new_indptr, batch, total_new, seqlens_out,
+                                                 (hipStream_t)stream));
 }
 
 size_t pkv_decode_workspace_bytes_ex(const pkv_cache_desc *cache, int32_t batch, int32_t num_q_heads,
@@ -484,6 +513,7 @@ pkv_status pkv_validate_decode_step_host(const pkv_cache_desc *cache, const int3
     if (batch < 0 || bt_cols < 0) return PKV_EINVAL;
     if (batch > 0 && (!cache_seqlens || !block_table)) return PKV_EINVAL;
     for (int b = 0; b < batch; ++b) {
+        if (cache_seqlens[b] == kPaddingRow) continue;
         if (cache_seqlens[b] < 0 || (int64_t)cache_seqlens[b] + 1 > max_kv_len) {
             set_msg(msg, msg_len, "row %d: cached length %d + 1 outside 1..max_kv_len (%d)", b, cache_seqlens[b],
                     max_kv_len);
@@ -493,7 +523,7 @@ pkv_status pkv_validate_decode_step_host(const pkv_cache_desc *cache, const int3
     // the attended rows (L + 1 keys each) route to real pages ...
     int32_t *attended = (int32_t *)malloc(sizeof(int32_t) * (size_t)(batch > 0 ? batch : 1));
     if (!attended) return PKV_EINVAL;
-    for (int b = 0; b < batch; ++b) attended[b] = cache_seqlens[b] + 1;
+    for (int b = 0; b < batch; ++b) attended[b] = cache_seqlens[b] == kPaddingRow ? 0 : cache_seqlens[b] + 1;
     st = pkv_validate_host(cache, block_table, bt_cols, attended, nullptr, batch, 0, 0, max_kv_len, 0, msg, msg_len);
     free(attended);
     if (st) return st;
@@ -520,6 +550,7 @@ pkv_status pkv_validate_append_host(const pkv_cache_desc *cache, const int32_t *
     pkv_status res = PKV_OK;
     for (int b = 0; b < batch && res == PKV_OK; ++b) {
         const int64_t n_new = new_indptr ? (int64_t)new_indptr[b + 1] - new_indptr[b] : 1;
+        if (cache_seqlens[b] == kPaddingRow && n_new >= 0) continue;  // writes nothing
         if (n_new < 0 || cache_seqlens[b] < 0) {
             set_msg(msg, msg_len, "row %d: negative length (%d, %lld)", b, cache_seqlens[b], (long long)n_new);
             res = PKV_EVALIDATE;

@@ -256,7 +256,7 @@ def test_validate_decode_step_paths():
     with pytest.raises(pkv.PkvError, match="max_kv_len"):
         pkv.validate_decode_step_host(kc, bt, torch.tensor([15, 40], dtype=torch.int32), 40)
     with pytest.raises(pkv.PkvError, match="max_kv_len"):
-        pkv.validate_decode_step_host(kc, bt, torch.tensor([-1, 40], dtype=torch.int32), 48)
+        pkv.validate_decode_step_host(kc, bt, torch.tensor([-3, 40], dtype=torch.int32), 48)
     # row 0's token at position 32 opens block 2, which routes to page 0
     with pytest.raises(pkv.PkvError, match="page 0"):
         pkv.validate_decode_step_host(kc, bt, torch.tensor([32, 40], dtype=torch.int32), 48)
@@ -293,3 +293,17 @@ def test_binding_requires_scale():
         pkv.prefill_attn(q, kc, kc, bt, lens, ip, 1, 16)
     with pytest.raises(TypeError, match="scale"):
         pkv.prefill_attn(q, kc, kc, bt, lens, ip, 1, 16, None)
+
+
+def test_validators_accept_padding_rows():
+    """cache length -1 marks a padding slot: it writes nothing, so the append
+    and decode-step validators skip it (other negative lengths stay errors)."""
+    kc = _cpu_pool()
+    bt = torch.tensor([[1, 2, 0], [0, 0, 0], [3, 4, 5]], dtype=torch.int32)
+    pad = torch.tensor([16, -1, 40], dtype=torch.int32)
+    pkv.validate_append_host(kc, bt, pad)
+    pkv.validate_decode_step_host(kc, bt, pad, 48)
+    with pytest.raises(pkv.PkvError, match="negative"):
+        pkv.validate_append_host(kc, bt, torch.tensor([16, -2, 40], dtype=torch.int32))
+    with pytest.raises(pkv.PkvError, match="max_kv_len"):
+        pkv.validate_decode_step_host(kc, bt, torch.tensor([16, -2, 40], dtype=torch.int32), 48)
