@@ -13,6 +13,7 @@ from .api import (  # noqa: F401
     append,
     append_decode_attn,
     append_decode_attn_noalloc,
+    append_rope,
     decode_attn,
     decode_workspace_bytes,
     decode_workspace_reset,

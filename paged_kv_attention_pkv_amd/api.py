@@ -63,6 +63,8 @@ _SIGS = {
     "pkv_abi_version": ([], ctypes.c_int32),
     "pkv_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "pkv_append": ([_DP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _VP, _VP], ctypes.c_int),
+    "pkv_append_rope": ([_DP, _VP, _VP, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _VP, _I32, _VP, _VP, _I32, _I32,
+                         _VP, _VP], ctypes.c_int),
     "pkv_decode_workspace_bytes": ([_DP, _I32, _I32, _I32], _SZ),
     "pkv_decode_workspace_bytes_ex": ([_DP, _I32, _I32, _I32, _I32], _SZ),
     "pkv_decode_workspace_reset": ([_DP, _I32, _VP, _SZ, _VP], ctypes.c_int),
@@ -255,6 +257,43 @@ def append(k_cache, v_cache, k_new, v_new, block_table, cache_seqlens, new_indpt
                           _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens), _ptr(new_indptr),
                           batch, k_new.shape[0], _ptr(seqlens_out), _stream(k_cache))
     _check("pkv_append", rc)
+    return seqlens_out
+
+
+def append_rope(k_cache, v_cache, k_new, v_new, block_table, cache_seqlens, rope_cos, rope_sin,
+                interleaved: bool = False, q=None, new_indptr=None, seqlens_out=None, layout: str = "HND"):
+    """pkv_append_rope: pkv_append with the new tokens' k rotated before it is
+    stored and q [total_new, Hq, D] (optional) rotated in place, by the
+    rotary tables rope_cos / rope_sin (float32 [rows, D/2]) at positions
+    cache_seqlens[b] + t.  Returns seqlens_out (allocated when not given)."""
+    desc = cache_desc(k_cache, v_cache, layout)
+    dev = k_cache.device
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, nm, k_cache.dtype, dev, 3)
+        _shape(t, nm, (k_new.shape[0], desc.num_kv_heads, desc.head_dim))
+    for t, nm in ((rope_cos, "rope_cos"), (rope_sin, "rope_sin")):
+        _need(t, nm, torch.float32, dev, 2)
+        _shape(t, nm, (rope_cos.shape[0], desc.head_dim // 2))
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
+    batch = cache_seqlens.shape[0]
+    hq = 0
+    if q is not None:
+        _need(q, "q", k_cache.dtype, dev, 3)
+        hq = q.shape[1]
+        _shape(q, "q", (k_new.shape[0], hq, desc.head_dim))
+    if new_indptr is not None:
+        _need(new_indptr, "new_indptr", torch.int32, dev, 1)
+        _shape(new_indptr, "new_indptr", (batch + 1,))
+    if block_table.shape[0] != batch:
+        raise ValueError("block_table rows must equal batch")
+    if seqlens_out is None:
+        seqlens_out = torch.empty_like(cache_seqlens)
+    rc = lib().pkv_append_rope(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(q),
+                               hq, _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0], int(bool(interleaved)),
+                               _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens), _ptr(new_indptr), batch,
+                               k_new.shape[0], _ptr(seqlens_out), _stream(k_cache))
+    _check("pkv_append_rope", rc)
     return seqlens_out
 
 

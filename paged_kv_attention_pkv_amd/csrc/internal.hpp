@@ -25,6 +25,14 @@ hipError_t launch_append(const PoolGeom &g, void *k_cache, void *v_cache, const 
                          const int32_t *cache_seqlens, const int32_t *new_indptr, int batch,
                          int total_new, int32_t *seqlens_out, hipStream_t stream);
 
+// Append with the rotary position embedding of the new tokens' k (stored) and,
+// when q is given, q (rotated in place).
+hipError_t launch_append_rope(const PoolGeom &g, void *k_cache, void *v_cache, const void *k_new,
+                              const void *v_new, void *q, int hq, const float *rope_cos, const float *rope_sin,
+                              int rope_rows, int interleaved, const int32_t *block_table, int bt_cols,
+                              const int32_t *cache_seqlens, const int32_t *new_indptr, int batch, int total_new,
+                              int32_t *seqlens_out, hipStream_t stream);
+
 hipError_t launch_route(const PoolGeom &g, const int32_t *block_table, int bt_cols,
                         const int32_t *seqlens, int batch, int max_len, int64_t *offsets,
                         hipStream_t stream);

@@ -328,3 +328,14 @@ def prefill_inputs(spec: PrefillSpec, device="cpu", seed_offset: int = 0) -> Pre
         torch.from_numpy(_indptr(spec.q_lens)).to(device),
         torch.from_numpy(spec.block_table.copy()).to(device),
         torch.from_numpy(spec.hist_lens.copy()).to(device))
+
+
+def rope_tables(rows: int, head_dim: int, base: float = 1_000_000.0):
+    """Rotary cos/sin tables as a model hands them to the attention call:
+    float32 [rows, head_dim/2], entry (p, i) = cos / sin of p * base^(-2i/D)
+    (angles and their cosines in fp64, rounded to fp32).  The default base
+    is Qwen3's rope_theta."""
+    half = head_dim // 2
+    inv = base ** (-np.arange(half, dtype=np.float64) * 2.0 / head_dim)
+    ang = np.arange(rows, dtype=np.float64)[:, None] * inv[None, :]
+    return (torch.from_numpy(np.cos(ang).astype(np.float32)), torch.from_numpy(np.sin(ang).astype(np.float32)))
