@@ -11,7 +11,9 @@ pkv_append_decode_attn launch (append + attend).  The same line carries a
 nested ``prefill`` object with the causal paged prefill at head_dim 256,
 Hq 48 / Hkv 8: the single request q_len = kv_len = 1023 and a random batch of
 8 requests (q_len U{65..4096}, kv_len = q_len + U{0..4096}), each step being
-8 layers with their own pools and inputs.
+8 layers with their own pools and inputs; and a nested ``mixed`` object: a
+serving step of the decode shape with 4 prompt chunks next to 64 decode rows,
+one pkv_mixed_attn launch per layer against the two separate launches.
 
 Every step is captured once in a HIP graph and replayed (``--eager`` launches
 it from Python instead).  All inputs are resident in HBM before the timed
@@ -24,7 +26,7 @@ per-launch duration from the HIP events of the timed region) and the CPU
 oracle timed on a bounded sample of the same workload on the host cores (and
 on one core).
 
-``--workload decode|sweep|long|prefill`` with ``--batch B`` times one
+``--workload decode|sweep|long|prefill|mixed`` with ``--batch B`` times one
 workload only.
 """
 from __future__ import annotations
@@ -55,7 +57,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default=None, choices=["decode", "sweep", "long", "prefill"],
+    p.add_argument("--workload", default=None, choices=["decode", "sweep", "long", "prefill", "mixed"],
                    help="time one workload only (default: decode B=64 plus the two prefill cases)")
     p.add_argument("--batch", type=int, default=None)
     p.add_argument("--layers", type=int, default=36, help="decode: layer caches per step")
@@ -426,6 +428,84 @@ def bench_prefill(args, torch, pkv, wl, spec):
     return result
 
 
+def bench_mixed(args, torch, pkv, wl):
+    """One serving step of chunked prefill next to decode (Qwen3-4B attention
+    shape: 4 prompt chunks of U{65..2048} rows continuing prompts, 64 decode
+    rows of U{512..1024} cached tokens), per layer one pkv_mixed_attn launch,
+    against the same work as two launches per layer (pkv_prefill_attn on the
+    chunks, pkv_decode_attn on the decode rows) on the same inputs."""
+    spec = wl.mixed_spec()
+    dev = torch.device("cuda:0")
+    P = int((spec.q_lens > 1).sum())
+    npf = int(spec.q_lens[:P].sum())
+    nd = spec.batch - P
+    L = 16
+    flops = 4 * spec.head_dim * spec.hq * sum(int(q) * (2 * int(kv) - int(q) + 1) // 2
+                                              for q, kv in zip(spec.q_lens[:P], spec.kv_lens[:P]))  # chunks
+    es = 2
+    kv_bytes = int(spec.kv_lens[P:].sum()) * spec.hkv * spec.head_dim * 2 * es
+    log(f"[bench] {spec.name}: {L} layers, {flops / 1e9:.1f} GFLOP and {kv_bytes / 1e6:.1f} MB decode KV per layer")
+    max_q, max_kv = int(spec.q_lens[:P].max()), int(spec.kv_lens.max())
+    zeros = torch.zeros(spec.batch, dtype=torch.int32, device=dev)
+    mixed, separate, ws_m = [], [], None
+    for layer in range(L):
+        inp = wl.prefill_inputs(spec, device=dev, seed_offset=layer)
+        kc, vc = wl.empty_pool(spec, dev), wl.empty_pool(spec, dev)
+        if ws_m is None:
+            ws_m = torch.zeros(pkv.mixed_workspace_bytes(kc, spec.batch, P, spec.hq), dtype=torch.uint8, device=dev)
+        pkv.append(kc, vc, inp.k_hist, inp.v_hist, inp.block_table, zeros, inp.hist_indptr)
+        kv = pkv.append(kc, vc, inp.k_new, inp.v_new, inp.block_table, inp.hist_lens, inp.qo_indptr)
+        out, out2 = torch.empty_like(inp.q), torch.empty_like(inp.q)
+        mixed.append(pkv.api.prepare_mixed(inp.q, kc, vc, inp.block_table, kv, inp.qo_indptr, P, max_q, max_kv,
+                                           spec.scale, out, ws_m))
+        bt_d, kv_d = inp.block_table[P:].contiguous(), kv[P:].contiguous()
+        ws_d = torch.zeros(pkv.decode_workspace_bytes(kc, nd, spec.hq, max_kv), dtype=torch.uint8, device=dev)
+        separate.append((pkv.api.prepare_prefill(inp.q[:npf], kc, vc, inp.block_table[:P], kv[:P],
+                                                 inp.qo_indptr[:P + 1], max_q, max_kv, spec.scale, out2[:npf]),
+                         pkv.api.prepare_decode(inp.q[npf:], kc, vc, bt_d, kv_d, max_kv, spec.scale, out2[npf:],
+                                                ws_d), bt_d, kv_d, ws_d))
+        del inp
+    torch.cuda.synchronize()
+
+    def step_mixed():
+        for c in mixed:
+            c()
+
+    def step_separate():
+        for pf, dc, *_ in separate:
+            pf()
+            dc()
+
+    ms_m, per_m = time_steps(torch, step_mixed, args.steps, args.warmup, not args.eager)
+    ms_s, per_s = time_steps(torch, step_separate, args.steps, args.warmup, not args.eager)
+    us_m, us_s = ms_m * 1e3 / L, ms_s * 1e3 / L
+    t_ideal = flops / (BF16_MFMA_PEAK_TFS * 1e12) + kv_bytes / (HBM_PEAK_GBS * 1e9)
+    result = {
+        "metric": "chunked prefill + decode in one launch: us per layer (lower is better)",
+        "value": round(us_m, 2), "unit": "us/layer", "higher_is_better": False,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_m, 4), "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "chunks_q": spec.q_lens[:P].tolist(), "chunks_kv": spec.kv_lens[:P].tolist(),
+                   "decode_rows": nd, "decode_mean_keys": round(float(spec.kv_lens[P:].mean()), 1), "hq": spec.hq,
+                   "hkv": spec.hkv, "head_dim": spec.head_dim, "layers": L,
+                   "step": "per layer: one pkv_mixed_attn launch (own pools and inputs)",
+                   "launch": "eager" if args.eager else "hip graph"},
+        "us_per_call_over_steps": spread(per_m, 1e3 / L),
+        "separate_us_per_layer": round(us_s, 2),
+        "separate_us_per_call_over_steps": spread(per_s, 1e3 / L),
+        "speedup_vs_separate": round(us_s / us_m, 3),
+        "roofline": {"bound": "mfma+hbm",
+                     "kernel": "mixed_kernel<128> (decode workers, then 32-row prefill tiles)",
+                     "achieved": round(flops / (us_m * 1e-6) / 1e12, 2), "unit": "TFLOP/s",
+                     "peak": BF16_MFMA_PEAK_TFS,
+                     "frac": round(t_ideal / (us_m * 1e-6), 4),
+                     "frac_definition": "(chunk flops / bf16 MFMA peak + decode KV bytes / HBM peak) / launch time",
+                     "traffic": None, "flops_per_launch": flops, "decode_kv_bytes_per_launch": kv_bytes},
+    }
+    del mixed, separate, ws_m
+    return result
+
+
 def cpu_baseline_prefill(args, spec):
     """The oracle (as is) on a sample of query rows of the same request(s):
     blocks of 32 consecutive rows of request 0, from its last row backwards,
@@ -506,7 +586,10 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log(f"[bench] device {props.name} ({getattr(props, 'gcnArchName', '?')}), CUs {props.multi_processor_count}")
     cpu = not args.no_cpu_baseline
-    if args.workload == "prefill":
+    if args.workload == "mixed":
+        result = bench_mixed(args, torch, pkv, wl)
+        result.update({"n_gpus": 1, "scaling": "weak", "vs_baseline": None})
+    elif args.workload == "prefill":
         spec = wl.prefill_spec(fixed_1023=True) if args.batch is None else wl.prefill_spec(batch=args.batch)
         result = bench_prefill(args, torch, pkv, wl, spec)
         result.update({"n_gpus": 1, "scaling": "weak", "vs_baseline": None})
@@ -526,6 +609,8 @@ def main():
                     sub["cpu_baseline"] = cpu_baseline_prefill(args, pspec)
                 result["prefill"][key] = sub
                 torch.cuda.empty_cache()
+            result["mixed"] = bench_mixed(args, torch, pkv, wl)
+            torch.cuda.empty_cache()
     result["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", "?"),
                         "cus": props.multi_processor_count}
     print(json.dumps(result), flush=True)

@@ -356,6 +356,44 @@ pkv_status pkv_prefill_attn_ex(const pkv_cache_desc *cache, void *out, float *ls
                                void *stream);
 
 /*
+ * pkv_mixed_workspace_bytes / pkv_mixed_attn -- chunked prefill and decode
+ * rows of one batch in ONE launch.
+ *
+ * The flex-vs-vLLM results page ("What's left on the table", chunked
+ * prefill) names the separate prefill pass as the main penalty left at large
+ * batch; a serving step that runs new-prompt chunks and decode rows over one
+ * pool does both here in one kernel launch, whose work list holds the decode
+ * rows' split workers first and then the chunks' query tiles.
+ *
+ * The batch is ordered: requests 0 .. num_prefill-1 are prefill chunks, the
+ * remaining batch - num_prefill requests are decode rows.
+ *   qo_indptr  int32 [batch+1], device: request r's query rows are
+ *              qo_indptr[r] .. qo_indptr[r+1]-1; a decode row has exactly one
+ *              (so the decode rows are the last batch - num_prefill query rows)
+ *   kv_lens    int32 [batch]: keys of each request, its new tokens included
+ *              (append them first, e.g. with one pkv_append over new_indptr =
+ *              qo_indptr)
+ *   max_q      host upper bound of the chunks' q_r
+ * Chunk rows are causal, end-aligned: row i of a chunk sees keys
+ * 0 .. kv_r - q_r + i (FlashInfer PR #9451 analysis, §1); a decode row sees
+ * all kv_r keys (0 keys: out = 0, lse = -inf).  The results are those of
+ * pkv_prefill_attn on the chunks and pkv_decode_attn on the decode rows.
+ * bf16, head_dim 64 or 128 only (PKV_EUNSUPPORTED otherwise).  The
+ * workspace (decode rows' partial results and counters) follows the decode
+ * workspace's rules: zero before first use, left zero by every call, sized
+ * by pkv_mixed_workspace_bytes, which depends on batch - num_prefill,
+ * num_q_heads, the descriptor and the device only.
+ */
+size_t pkv_mixed_workspace_bytes(const pkv_cache_desc *cache, int32_t batch, int32_t num_prefill,
+                                 int32_t num_q_heads);
+pkv_status pkv_mixed_attn(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
+                          int32_t num_q_heads, const void *k_cache, const void *v_cache,
+                          const int32_t *block_table, int32_t bt_cols, const int32_t *kv_lens,
+                          const int32_t *qo_indptr, int32_t batch, int32_t num_prefill,
+                          int32_t total_q, int32_t max_q, int32_t max_kv_len, float scale,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * pkv_route -- debug/test entry point, not on the hot path: the element
  * offset (kv head 0, dim 0) of every logical token, as the kernels compute it.
  *   offsets  int64 [batch, max_len]: offsets[b][j] for j < seqlens[b], -1 after

@@ -18,6 +18,8 @@ from .api import (  # noqa: F401
     decode_workspace_bytes,
     decode_workspace_reset,
     lib_path,
+    mixed_attn,
+    mixed_workspace_bytes,
     prefill_attn,
     prefill_workspace_bytes,
     route,

@@ -83,6 +83,9 @@ _SIGS = {
                           _I32, ctypes.c_float, _VP, _SZ, _VP], ctypes.c_int),
     "pkv_prefill_attn_ex": ([_DP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32,
                              _I32, ctypes.c_float, _VP, _SZ, _I32, _VP], ctypes.c_int),
+    "pkv_mixed_workspace_bytes": ([_DP, _I32, _I32, _I32], _SZ),
+    "pkv_mixed_attn": ([_DP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32, _I32,
+                        ctypes.c_float, _VP, _SZ, _VP], ctypes.c_int),
     "pkv_route": ([_DP, _VP, _I32, _VP, _I32, _I32, _VP, _VP], ctypes.c_int),
     "pkv_validate_host": ([_DP, _VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32, _I32, ctypes.c_char_p, _SZ],
                           ctypes.c_int),
@@ -463,6 +466,64 @@ def prefill_attn(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, max_q: in
             rc = lib().pkv_prefill_attn(*args, _stream(k_cache))
     _check(name, rc)
     return (out, lse) if lse is not None else out
+
+
+def mixed_workspace_bytes(k_cache, batch: int, num_prefill: int, num_q_heads: int, layout: str = "HND") -> int:
+    desc = cache_desc(k_cache, None, layout)
+    with torch.cuda.device(k_cache.device):
+        n = lib().pkv_mixed_workspace_bytes(ctypes.byref(desc), batch, num_prefill, num_q_heads)
+    if n == 0:
+        raise PkvError("pkv_mixed_workspace_bytes", 1, "invalid sizes")
+    return int(n)
+
+
+def _mixed_args(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, num_prefill, max_q, max_kv_len, scale, out,
+                lse, workspace, layout):
+    desc = cache_desc(k_cache, v_cache, layout)
+    dev = k_cache.device
+    _need(q, "q", k_cache.dtype, dev, 3)
+    _need(out, "out", q.dtype, dev, 3)
+    _prefill_operands(desc, q, out, lse, block_table, kv_lens, qo_indptr)
+    _scale(scale)
+    total_q, hq, _ = q.shape
+    batch = kv_lens.shape[0]
+    if not 0 <= num_prefill <= batch or total_q < batch - num_prefill:
+        raise ValueError("num_prefill must be in 0..batch and each decode row needs a query row")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return desc, (ctypes.byref(desc), _ptr(out), _ptr(lse), _ptr(q), hq, _ptr(k_cache), _ptr(v_cache),
+                  _ptr(block_table), block_table.shape[1], _ptr(kv_lens), _ptr(qo_indptr), batch, int(num_prefill),
+                  total_q, int(max_q), int(max_kv_len), float(scale), _ptr(workspace), nbytes)
+
+
+def mixed_attn(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, num_prefill: int, max_q: int, max_kv_len: int,
+               scale: float, out=None, lse=None, workspace=None, layout: str = "HND", return_lse: bool = False):
+    """pkv_mixed_attn: requests 0..num_prefill-1 are causal prefill chunks,
+    the others decode rows (one query row each, the last query rows), all
+    in one launch.  Returns out (and lse when return_lse or lse is given)."""
+    if out is None:
+        out = torch.empty_like(q)
+    total_q, hq, _ = q.shape
+    if lse is None and return_lse:
+        lse = torch.empty((total_q, hq), dtype=torch.float32, device=q.device)
+    batch = kv_lens.shape[0]
+    if workspace is None:
+        # the decode rows' arrival counters must start at zero
+        workspace = torch.zeros(mixed_workspace_bytes(k_cache, batch, num_prefill, hq, layout), dtype=torch.uint8,
+                                device=q.device)
+    _, args = _mixed_args(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, num_prefill, max_q, max_kv_len,
+                          scale, out, lse, workspace, layout)
+    with torch.cuda.device(q.device):
+        rc = lib().pkv_mixed_attn(*args, _stream(k_cache))
+    _check("pkv_mixed_attn", rc)
+    return (out, lse) if lse is not None else out
+
+
+def prepare_mixed(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, num_prefill: int, max_q: int,
+                  max_kv_len: int, scale: float, out, workspace, lse=None, layout: str = "HND") -> "PreparedCall":
+    desc, args = _mixed_args(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, num_prefill, max_q, max_kv_len,
+                             scale, out, lse, workspace, layout)
+    return PreparedCall("pkv_mixed_attn", args, (k_cache, v_cache, q, out, block_table, kv_lens, qo_indptr,
+                                                 workspace, lse, desc))
 
 
 def route(k_cache, block_table, seqlens, max_len: int, layout: str = "HND"):

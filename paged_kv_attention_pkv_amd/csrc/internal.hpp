@@ -78,6 +78,8 @@ size_t decode_workspace(const PoolGeom &g, int batch, int hq, int record_workers
 // here and fills args.arrivals / part_o / part_ml.
 hipError_t launch_decode(const PoolGeom &g, DecodeArgs args, void *workspace, int record_workers,
                          hipStream_t stream);
+// Fills a.arrivals / part_o / part_ml from the workspace layout.
+void decode_workspace_layout(const PoolGeom &g, DecodeArgs &a, void *workspace, int record_workers);
 // Zero `words` int32 values at p with a fill kernel (no memset node, so the
 // call can be recorded into a graph).
 hipError_t launch_zero_words(int32_t *p, int64_t words, hipStream_t stream);
@@ -109,5 +111,10 @@ struct PrefillArgs {
 };
 size_t prefill_workspace(const PoolGeom &g, int batch, int hq, int total_q, int max_q, int max_kv);
 hipError_t launch_prefill(const PoolGeom &g, const PrefillArgs &args, hipStream_t stream);
+
+// Chunked prefill (pa, bf16, head_dim 64/128) and decode rows (da, no fused
+// append) in one launch; da's workspace layout is filled here.
+hipError_t launch_mixed(const PoolGeom &g, const PrefillArgs &pa, DecodeArgs da, void *workspace, int record_workers,
+                        hipStream_t stream);
 
 }  // namespace pkv

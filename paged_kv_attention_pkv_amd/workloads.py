@@ -339,3 +339,21 @@ def rope_tables(rows: int, head_dim: int, base: float = 1_000_000.0):
     inv = base ** (-np.arange(half, dtype=np.float64) * 2.0 / head_dim)
     ang = np.arange(rows, dtype=np.float64)[:, None] * inv[None, :]
     return (torch.from_numpy(np.cos(ang).astype(np.float32)), torch.from_numpy(np.sin(ang).astype(np.float32)))
+
+
+def mixed_spec(num_decode: int = 64, num_chunks: int = 4, seed: int = 700, hq: int = 32, hkv: int = 8,
+               head_dim: int = 128, max_chunk: int = 2048, max_extra: int = 4096) -> PrefillSpec:
+    """One serving step of the Qwen3-4B attention shape with chunked prefill
+    next to decode: `num_chunks` prompt chunks first (q_len U{65..max_chunk},
+    kv_len = q_len + U{0..max_extra}: a chunk continues a prompt), then
+    `num_decode` decode rows (one new token each over a history of
+    U{512..1024} tokens, the decode workload's lengths).  A ragged prefill
+    workload whose last requests have q_len 1."""
+    rng = np.random.default_rng(seed)
+    q = rng.integers(65, max_chunk, size=num_chunks, endpoint=True)
+    kv = q + rng.integers(0, max_extra, size=num_chunks, endpoint=True)
+    dec = rng.integers(512, 1024, size=num_decode, endpoint=True) + 1
+    spec = prefill_spec(q_lens=np.concatenate([q, np.ones(num_decode, np.int64)]),
+                        kv_lens=np.concatenate([kv, dec]), hq=hq, hkv=hkv, head_dim=head_dim, seed=seed)
+    spec.name = f"mixed_c{num_chunks}_d{num_decode}"
+    return spec

@@ -1,0 +1,109 @@
+"""GPU parity of pkv_mixed_attn: chunked prefill requests and decode rows of
+one batch in one launch, against the oracle (every decode row, chunk rows
+all or tile-edge sampled) and, bit for bit, against pkv_prefill_attn on the
+chunks plus pkv_decode_attn on the decode rows (the same kernels' code)."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_attention_pkv_amd as pkv
+from paged_kv_attention_pkv_amd import workloads as wl
+from gpu_common import BF16_TOL, PrefillCase, compare, say
+from test_gpu_prefill import tile_edge_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _mixed(case, num_prefill):
+    s, i = case.spec, case.inp
+    kc, vc, kv = case.gpu_pools()
+    max_q = int(s.q_lens[:num_prefill].max()) if num_prefill else 0
+    out, lse = pkv.mixed_attn(i.q, kc, vc, i.block_table, kv, i.qo_indptr, num_prefill, max_q,
+                              int(s.kv_lens.max()), s.scale, return_lse=True)
+    torch.cuda.synchronize()
+    return kc, vc, kv, out, lse
+
+
+def _check(spec, num_prefill, sample_chunks=False):
+    say(f"[mixed] {spec.name} chunks q={spec.q_lens[:num_prefill].tolist()} kv={spec.kv_lens[:num_prefill].tolist()} "
+        f"decode rows {spec.batch - num_prefill} D={spec.head_dim}")
+    case = PrefillCase(spec, gen_device="cuda" if sample_chunks else "cpu")
+    kc, vc, kv, out, lse = _mixed(case, num_prefill)
+    okc, ovc, okv, obt, oreqs = case.oracle_pools()
+    if sample_chunks:
+        pick = lambda r, q_len: tile_edge_rows(r, q_len) if r < num_prefill else np.arange(q_len)
+        rows, ro, rl = case.oracle_row_set(okc, ovc, okv, obt, oreqs, pick)
+    else:
+        rows, ro, rl = case.oracle_rows(okc, ovc, okv, obt, oreqs)
+    s1 = compare(out.cpu()[rows], ro, *BF16_TOL, "mixed out")
+    s2 = compare(lse.cpu()[rows], rl, *BF16_TOL, "mixed lse")
+    say(f"  rows checked {len(rows)} of {out.shape[0]}; out: {s1}; lse: {s2}")
+    return case, kc, vc, kv, out, lse
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_mixed_small_all_rows(d):
+    q = [65, 300, 129, 1, 1, 1, 1, 1, 1, 1, 1]
+    kv = [200, 300, 1000, 1, 2, 16, 17, 100, 700, 1500, 2049]
+    spec = wl.prefill_spec(q_lens=q, kv_lens=kv, hq=32, hkv=8, head_dim=d, seed=d + 3)
+    _check(spec, 3)
+
+
+def test_mixed_equals_separate_calls_bitwise():
+    """The mixed launch runs the prefill tiles and decode workers of the
+    separate calls: outputs and lse bit for bit equal."""
+    spec = wl.mixed_spec(num_decode=40, num_chunks=3, seed=701, max_chunk=600, max_extra=900)
+    case, kc, vc, kv, out, lse = _check(spec, 3)
+    i, s = case.inp, spec
+    P = 3
+    npf = int(s.q_lens[:P].sum())
+    po, pl = pkv.prefill_attn(i.q[:npf], kc, vc, i.block_table[:P], kv[:P], i.qo_indptr[:P + 1],
+                              int(s.q_lens[:P].max()), int(s.kv_lens.max()), s.scale, return_lse=True)
+    do, dl = pkv.decode_attn(i.q[npf:], kc, vc, i.block_table[P:].contiguous(), kv[P:].contiguous(),
+                             int(s.kv_lens.max()), s.scale, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:npf].view(torch.int16), po.view(torch.int16)), "chunk rows differ from pkv_prefill_attn"
+    assert torch.equal(lse[:npf], pl), "chunk lse differs"
+    assert torch.equal(out[npf:].view(torch.int16), do.view(torch.int16)), "decode rows differ from pkv_decode_attn"
+    assert torch.equal(lse[npf:], dl), "decode lse differs"
+
+
+def test_mixed_full_size_qwen3():
+    """The mixed serving step of the benchmark (4 chunks of up to 2048 rows
+    continuing prompts of up to 6144 keys, 64 decode rows of 513..1025
+    keys): every decode row, tile-edge rows of every chunk."""
+    _check(wl.mixed_spec(), 4, sample_chunks=True)
+
+
+def test_mixed_chunks_up_to_4096():
+    _check(wl.mixed_spec(num_decode=32, num_chunks=3, seed=702, max_chunk=4096), 3, sample_chunks=True)
+
+
+def test_mixed_only_decode_and_only_prefill():
+    spec = wl.prefill_spec(q_lens=[1] * 9, kv_lens=[1, 5, 16, 17, 33, 300, 2000, 64, 129], hq=16, hkv=4,
+                           head_dim=128, seed=9)
+    _check(spec, 0)
+    spec = wl.prefill_spec(q_lens=[40, 1, 200], kv_lens=[40, 90, 333], hq=16, hkv=4, head_dim=128, seed=10)
+    _check(spec, 3)
+
+
+def test_mixed_empty_decode_rows():
+    """Decode rows with no keys give out = 0, lse = -inf; the other rows are
+    unchanged by them."""
+    spec = wl.prefill_spec(q_lens=[100, 1, 1, 1, 1], kv_lens=[150, 40, 40, 40, 40], hq=32, hkv=8, head_dim=128,
+                           seed=11)
+    say("[mixed] empty decode rows")
+    case = PrefillCase(spec)
+    kc, vc, kv = case.gpu_pools()
+    i, s = case.inp, spec
+    kv0 = kv.clone()
+    kv0[2] = 0
+    kv0[4] = 0
+    out, lse = pkv.mixed_attn(i.q, kc, vc, i.block_table, kv0, i.qo_indptr, 1, 100, 150, s.scale, return_lse=True)
+    ref, rlse = pkv.mixed_attn(i.q, kc, vc, i.block_table, kv, i.qo_indptr, 1, 100, 150, s.scale, return_lse=True)
+    torch.cuda.synchronize()
+    o, l = out.float().cpu(), lse.cpu()
+    for r in (101, 103):
+        assert torch.all(o[r] == 0) and torch.all(torch.isneginf(l[r])), r
+    keep = [x for x in range(104) if x not in (101, 103)]
+    assert torch.equal(out[keep].view(torch.int16), ref[keep].view(torch.int16))
