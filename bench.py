@@ -70,6 +70,8 @@ def parse():
     p.add_argument("--cpu-seconds-1t", type=float, default=2.0,
                    help="target CPU time of each oracle sample on one thread")
     p.add_argument("--workers", type=int, default=0, help="decode split workers (0 = library default)")
+    p.add_argument("--prefill-rows", type=int, default=0,
+                   help="prefill query rows per workgroup (0 = library default, 128, 192)")
     p.add_argument("--separate", action="store_true",
                    help="decode step as pkv_append + pkv_decode_attn (two launches) instead of the fused "
                         "pkv_append_decode_attn")
@@ -384,9 +386,9 @@ def bench_prefill(args, torch, pkv, wl, spec):
         out = torch.empty_like(inp.q)
         if ws is None:
             need = pkv.prefill_workspace_bytes(kc, spec.batch, spec.hq, int(spec.q_lens.sum()), max_q, max_kv)
-            ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+            ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)  # counters start at zero
         calls.append(pkv.api.prepare_prefill(inp.q, kc, vc, inp.block_table, kv_lens, inp.qo_indptr, max_q,
-                                             max_kv, spec.scale, out, ws))
+                                             max_kv, spec.scale, out, ws, rows_per_workgroup=args.prefill_rows))
         del inp
     torch.cuda.synchronize()
 
@@ -399,10 +401,13 @@ def bench_prefill(args, torch, pkv, wl, spec):
     tfs = flops / (mean * 1e-3) / 1e12
     traffic = traffic_from_profile(os.path.join(ROOT, "paged_kv_attention_pkv_amd", "csrc", "prefill.hip"),
                                    f"prefill16_kernel_{spec.name}_pmc.txt")
-    # the workgroup size the library picks for this call, by the rule stated
-    # in include/pkv.h (192 rows once ceil(total_q / 192) * Hq >= 1.5 * CUs)
+    # the tiling the library picks for this call, by the rule stated in
+    # include/pkv.h (192 rows once ceil(total_q / 192) * Hq >= 1.5 * CUs)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    waves = 12 if 2 * (-(-int(spec.q_lens.sum()) // 192) * spec.hq) >= 3 * cus else 8
+    tiling = args.prefill_rows
+    if tiling == 0:
+        tiling = 192 if 2 * (-(-int(spec.q_lens.sum()) // 192) * spec.hq) >= 3 * cus else 128
+    kernel = f"prefill16_kernel<256, {tiling // 16}> ({tiling} query rows per workgroup)"
     result = {
         "metric": "paged causal prefill attn: TFLOP/s (% bf16 MFMA peak), D256 Hq48/Hkv8",
         "value": round(flops * L / (ms * 1e-3) / 1e12, 2),
@@ -418,8 +423,7 @@ def bench_prefill(args, torch, pkv, wl, spec):
         "us_per_call_over_steps": spread(per, 1e3 / L),
         "value_over_steps": {"median": round(flops * L / (statistics.median(per) * 1e-3) / 1e12, 2),
                              "best": round(flops * L / (min(per) * 1e-3) / 1e12, 2), "rounds": len(per)},
-        "roofline": {"bound": "mfma", "kernel": f"prefill16_kernel<256, {waves}> (one launch per pkv_prefill_attn, "
-                                                  f"{16 * waves} query rows per workgroup)", "achieved": round(tfs, 2),
+        "roofline": {"bound": "mfma", "kernel": kernel + ", one launch per pkv_prefill_attn", "achieved": round(tfs, 2),
                      "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s", "frac": round(tfs / BF16_MFMA_PEAK_TFS, 4),
                      "traffic": None if traffic is None else int(traffic),
                      "traffic_unit": "HBM bytes per launch", "flops_per_launch": flops},

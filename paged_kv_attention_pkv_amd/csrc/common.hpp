@@ -110,4 +110,20 @@ __device__ __forceinline__ u32x2 ld8_stream(const void *p) {
 }
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
 
+// Partial results travel between workgroups on different XCDs (each with its
+// own L2).  They are written and read with agent-scope atomic accesses,
+// which the compiler emits as agent-coherent (sc1) loads and stores, so no
+// cache-wide write-back or invalidate (what an agent-scope fence costs on
+// this chip) is needed; the writer waits for its stores to complete before
+// it announces them with an atomic counter.
+__device__ __forceinline__ void st_agent2(float *p, float x, float y) {
+    const uint64_t v = (uint64_t)__builtin_bit_cast(uint32_t, x) | ((uint64_t)__builtin_bit_cast(uint32_t, y) << 32);
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x2 ld_agent2(const float *p) {
+    const uint64_t v =
+        __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return f32x2{__builtin_bit_cast(float, (uint32_t)v), __builtin_bit_cast(float, (uint32_t)(v >> 32))};
+}
+
 }  // namespace pkv

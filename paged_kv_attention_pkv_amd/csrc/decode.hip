@@ -166,10 +166,10 @@ struct EngF32 {
         float *o = a.part_o + rec * G * D;
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) {
-            st_shared2(o + ((2 * dc) * 4 * G + quad * G + col) * 2, acc[dc][0], acc[dc][1]);
-            st_shared2(o + ((2 * dc + 1) * 4 * G + quad * G + col) * 2, acc[dc][2], acc[dc][3]);
+            st_agent2(o + ((2 * dc) * 4 * G + quad * G + col) * 2, acc[dc][0], acc[dc][1]);
+            st_agent2(o + ((2 * dc + 1) * 4 * G + quad * G + col) * 2, acc[dc][2], acc[dc][3]);
         }
-        if (quad == 0) st_shared2(a.part_ml + (rec * G + col) * 2, m, lt);
+        if (quad == 0) st_agent2(a.part_ml + (rec * G + col) * 2, m, lt);
     }
 };
 

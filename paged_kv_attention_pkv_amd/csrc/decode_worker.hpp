@@ -83,21 +83,10 @@ __device__ __forceinline__ void seg_next(const DecodeArgs &a, Seg &s, RowLens &r
     }
 }
 
-// Partial records travel between waves on different XCDs (each with its own
-// L2).  They are written and read with agent-scope atomic accesses, which the
-// compiler emits as agent-coherent (sc1) loads and stores, so no cache-wide
-// write-back or invalidate (what an agent-scope fence costs on this chip) is
-// needed; a wave waits for its record stores to complete before it counts
-// itself in the segment's arrival counter.
-__device__ __forceinline__ void st_shared2(float *p, float x, float y) {
-    const uint64_t v = (uint64_t)__builtin_bit_cast(uint32_t, x) | ((uint64_t)__builtin_bit_cast(uint32_t, y) << 32);
-    __hip_atomic_store(reinterpret_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ f32x2 ld_shared2(const float *p) {
-    const uint64_t v =
-        __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return f32x2{__builtin_bit_cast(float, (uint32_t)v), __builtin_bit_cast(float, (uint32_t)(v >> 32))};
-}
+// Partial records travel between waves on different XCDs through
+// agent-coherent accesses (st_agent2 / ld_agent2); a wave waits for its
+// record stores to complete before it counts itself in the segment's
+// arrival counter.
 __device__ __forceinline__ void wait_stores_complete() { __builtin_amdgcn_s_waitcnt(0); }
 // LDS writes of this wave become visible to all its lanes: wait for them and
 // keep the compiler from moving LDS accesses across.
@@ -323,8 +312,8 @@ __device__ void merge_jobs(const DecodeArgs &a, const MergeJob *job, int own_job
                                                           : job[NJ - 1].wf + piece + job[NJ - 1].s;
 #pragma unroll
                         for (int k = 0; k < kPairs; ++k) {
-                            ml[j][k] = ld_shared2(a.part_ml + (rec * G + col[k]) * 2);
-                            o[j][k] = ld_shared2(a.part_o + rec * ostride + 2 * uu[k]);
+                            ml[j][k] = ld_agent2(a.part_ml + (rec * G + col[k]) * 2);
+                            o[j][k] = ld_agent2(a.part_o + rec * ostride + 2 * uu[k]);
                         }
                     }
                 }
@@ -821,8 +810,8 @@ struct Bf16 {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int jj = 0; jj < VW; ++jj)
-                st_shared2(o + ((i * VW + jj) * 4 * G + quad * G + col) * 2, o4[2 * jj][i], o4[2 * jj + 1][i]);
-        if (quad == 0) st_shared2(a.part_ml + (rec * G + col) * 2, mm, lt);
+                st_agent2(o + ((i * VW + jj) * 4 * G + quad * G + col) * 2, o4[2 * jj][i], o4[2 * jj + 1][i]);
+        if (quad == 0) st_agent2(a.part_ml + (rec * G + col) * 2, mm, lt);
     }
     __device__ __forceinline__ void store_partial(const DecodeArgs &a, int64_t rec) { store_record(a, rec, acc, m, l); }
 
