@@ -39,8 +39,12 @@
  * share one descriptor.  Page 0 is reserved: tables never need to route a
  * live token to it, and unused table entries may hold 0.
  *
- * Supported: dtype PKV_BF16 or PKV_F32; page_size 16; head_dim 64, 128 or
- * 256; a GQA ratio G = num_q_heads / num_kv_heads from 1 to 16 (this covers
+ * Supported: dtype PKV_BF16 or PKV_F32; page_size 16, 32, 64, 128 or 256
+ * (the 256-token blocks of mini-infer 06 §1 included; other sizes, and pools
+ * with num_pages * page_size above 2^31 - 1 tokens, give PKV_EUNSUPPORTED --
+ * the kernels walk every page as page_size / 16 runs of 16 consecutive
+ * slots, so the arithmetic and the results are those of 16-token pages
+ * whose table entries are expanded); head_dim 64, 128 or 256; a GQA ratio G = num_q_heads / num_kv_heads from 1 to 16 (this covers
  * the ratios {1, 2, 4, 8, 16} of the FlashInfer PR #9451 analysis, §1, and
  * the 48/8 = 6 of its D=256 workload); strides multiples of 8 elements and
  * all pointers 16-byte aligned.  Query head h reads KV head h / G.
@@ -72,7 +76,7 @@ typedef enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
 typedef struct pkv_cache_desc {
     int32_t dtype;        /* pkv_dtype of the pools, q, new K/V and out */
     int32_t num_pages;    /* physical pages per pool, page 0 included */
-    int32_t page_size;    /* tokens per page (16) */
+    int32_t page_size;    /* tokens per page: 16, 32, 64, 128 or 256 */
     int32_t num_kv_heads;
     int32_t head_dim;
     int32_t reserved;     /* must be 0 */

@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void append_kernel(
     char *__restrict__ k_cache, char *__restrict__ v_cache, const char *__restrict__ k_new,
     const char *__restrict__ v_new, const int32_t *__restrict__ block_table, int bt_cols,
     const int32_t *__restrict__ cache_seqlens, const int32_t *__restrict__ new_indptr, int batch,
-    int num_pages, int hkv, int row_bytes, int64_t s_page_b, int64_t s_head_b, int64_t s_tok_b,
+    int num_pages, int log2_page, int hkv, int row_bytes, int64_t s_page_b, int64_t s_head_b, int64_t s_tok_b,
     int64_t total_chunks, int32_t *__restrict__ seqlens_out) {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -57,11 +57,11 @@ __global__ __launch_bounds__(256) void append_kernel(
         }
         const int L = cache_seqlens[b];
         const int pos = L + t_local;
-        const int blk = pos >> 4;
+        const int blk = pos >> log2_page;
         if (L < 0 || blk >= bt_cols) continue;  // a padding row, or outside the row: write nothing
         const int page = block_table[(int64_t)b * bt_cols + blk];
         if (page < 1 || page >= num_pages) continue;  // page 0 is reserved
-        const int slot = pos & (kPage - 1);
+        const int slot = pos & ((1 << log2_page) - 1);
         const int64_t dst = page * s_page_b + g * s_head_b + slot * s_tok_b + chunk * 16;
         const int64_t src = row * row_bytes + chunk * 16;
         st16(k_cache + dst, ld16(k_new + src));
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void append_kernel(
 
 __global__ __launch_bounds__(256) void route_kernel(const int32_t *__restrict__ block_table,
                                                     int bt_cols, const int32_t *__restrict__ seqlens,
-                                                    int batch, int max_len, int64_t s_page,
+                                                    int batch, int max_len, int log2_page, int64_t s_page,
                                                     int64_t s_tok, int64_t *__restrict__ offsets) {
     const int64_t total = (int64_t)batch * max_len;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
@@ -80,8 +80,8 @@ __global__ __launch_bounds__(256) void route_kernel(const int32_t *__restrict__ 
         const int j = (int)(i - (int64_t)b * max_len);
         int64_t off = -1;
         if (j < seqlens[b]) {
-            const int page = block_table[(int64_t)b * bt_cols + (j >> 4)];
-            off = page * s_page + (j & (kPage - 1)) * s_tok;
+            const int page = block_table[(int64_t)b * bt_cols + (j >> log2_page)];
+            off = page * s_page + (j & ((1 << log2_page) - 1)) * s_tok;
         }
         offsets[i] = off;
     }
@@ -187,8 +187,8 @@ __global__ __launch_bounds__(256) void rope_append_kernel(
     const char *__restrict__ v_new, char *__restrict__ q, int hq, const float *__restrict__ rope_cos,
     const float *__restrict__ rope_sin, int rope_rows, int interleaved, const int32_t *__restrict__ block_table,
     int bt_cols, const int32_t *__restrict__ cache_seqlens, const int32_t *__restrict__ new_indptr, int batch,
-    int num_pages, int hkv, int head_dim, int64_t s_page_b, int64_t s_head_b, int64_t s_tok_b, int64_t total_units,
-    int32_t *__restrict__ seqlens_out) {
+    int num_pages, int log2_page, int hkv, int head_dim, int64_t s_page_b, int64_t s_head_b, int64_t s_tok_b,
+    int64_t total_units, int32_t *__restrict__ seqlens_out) {
     constexpr int P = RopeElems<ES>::P;
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -232,11 +232,11 @@ __global__ __launch_bounds__(256) void rope_append_kernel(
             st16(qr + offb * ES, bb);
             continue;
         }
-        const int blk = pos >> 4;
+        const int blk = pos >> log2_page;
         if (blk >= bt_cols) continue;  // outside the row: write nothing
         const int page = block_table[(int64_t)b * bt_cols + blk];
         if (page < 1 || page >= num_pages) continue;  // page 0 is reserved
-        const int slot = pos & (kPage - 1);
+        const int slot = pos & ((1 << log2_page) - 1);
         const int64_t dst = page * s_page_b + h * s_head_b + slot * s_tok_b;
         const int64_t src = ((int64_t)t * hkv + h) * row_bytes;
         u32x4 a = ld16(k_new + src + offa * ES), bb = ld16(k_new + src + offb * ES);
@@ -274,7 +274,8 @@ hipError_t launch_append(const PoolGeom &g, void *k_cache, void *v_cache, const 
     const int64_t work = total_chunks > batch ? total_chunks : batch;
     hipLaunchKernelGGL(append_kernel, dim3(grid_for(work, 256)), dim3(256), 0, stream,
                        (char *)k_cache, (char *)v_cache, (const char *)k_new, (const char *)v_new,
-                       block_table, bt_cols, cache_seqlens, new_indptr, batch, g.num_pages, g.hkv, row_bytes,
+                       block_table, bt_cols, cache_seqlens, new_indptr, batch, g.num_pages, g.page_shift + 4, g.hkv,
+                       row_bytes,
                        g.s_page * es, g.s_head * es, g.s_tok * es, total_chunks, seqlens_out);
     return hipGetLastError();
 }
@@ -283,7 +284,7 @@ hipError_t launch_route(const PoolGeom &g, const int32_t *block_table, int bt_co
                         const int32_t *seqlens, int batch, int max_len, int64_t *offsets,
                         hipStream_t stream) {
     hipLaunchKernelGGL(route_kernel, dim3(grid_for((int64_t)batch * max_len, 256)), dim3(256), 0,
-                       stream, block_table, bt_cols, seqlens, batch, max_len, g.s_page, g.s_tok,
+                       stream, block_table, bt_cols, seqlens, batch, max_len, g.page_shift + 4, g.s_page, g.s_tok,
                        offsets);
     return hipGetLastError();
 }
@@ -303,13 +304,13 @@ hipError_t launch_append_rope(const PoolGeom &g, void *k_cache, void *v_cache, c
         hipLaunchKernelGGL(rope_append_kernel<2>, dim3(grid_for(work, 256)), dim3(256), 0, stream, (char *)k_cache,
                            (char *)v_cache, (const char *)k_new, (const char *)v_new, (char *)q, hq, rope_cos,
                            rope_sin, rope_rows, interleaved, block_table, bt_cols, cache_seqlens, new_indptr, batch,
-                           g.num_pages, g.hkv, g.head_dim, g.s_page * es, g.s_head * es, g.s_tok * es, total_units,
+                           g.num_pages, g.page_shift + 4, g.hkv, g.head_dim, g.s_page * es, g.s_head * es, g.s_tok * es, total_units,
                            seqlens_out);
     else
         hipLaunchKernelGGL(rope_append_kernel<4>, dim3(grid_for(work, 256)), dim3(256), 0, stream, (char *)k_cache,
                            (char *)v_cache, (const char *)k_new, (const char *)v_new, (char *)q, hq, rope_cos,
                            rope_sin, rope_rows, interleaved, block_table, bt_cols, cache_seqlens, new_indptr, batch,
-                           g.num_pages, g.hkv, g.head_dim, g.s_page * es, g.s_head * es, g.s_tok * es, total_units,
+                           g.num_pages, g.page_shift + 4, g.hkv, g.head_dim, g.s_page * es, g.s_head * es, g.s_tok * es, total_units,
                            seqlens_out);
     return hipGetLastError();
 }

@@ -63,11 +63,12 @@ namespace pkv {
 
 namespace {
 
-template <int D>
+// SUB: pages of more than 16 tokens (page ids staged with their sub-page)
+template <int D, bool SUB>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1)))
 void decode_bf16_kernel(DecodeArgs a) {
     __shared__ __align__(16) char lds[WorkerLds<D>::kBytes];
-    decode_bf16_worker<D>(a, blockIdx.x, lds);
+    decode_bf16_worker<D, SUB>(a, blockIdx.x, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -110,9 +111,11 @@ struct EngF32 {
         const float *vbase = (const float *)a.v_cache + (int64_t)g * a.s_head;
         const float c = a.scale_log2;
         for (int p = p0; p < p1; ++p) {
-            const int phys = clamp_page(a, bt[p]);
-            const float *kp = kbase + (int64_t)phys * a.s_page;
-            const float *vp = vbase + (int64_t)phys * a.s_page;
+            // 16-token sub-page p: table column p >> page_shift, then its sub-page
+            const int phys = clamp_page(a, bt[p >> a.page_shift]);
+            const int64_t soff = (int64_t)(p & ((1 << a.page_shift) - 1)) * kPage * a.s_tok;
+            const float *kp = kbase + (int64_t)phys * a.s_page + soff;
+            const float *vp = vbase + (int64_t)phys * a.s_page + soff;
             f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc)
@@ -205,11 +208,14 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
     settle<float, Eng, D>(a, eng, pend, w, nullptr, nullptr);
 }
 
-const void *pick_kernel(int dtype, int d) {
+const void *pick_kernel(int dtype, int d, bool sub = false) {
     if (dtype == 1) {
-        if (d == 64) return reinterpret_cast<const void *>(&decode_bf16_kernel<64>);
-        if (d == 128) return reinterpret_cast<const void *>(&decode_bf16_kernel<128>);
-        if (d == 256) return reinterpret_cast<const void *>(&decode_bf16_kernel<256>);
+        if (d == 64) return sub ? reinterpret_cast<const void *>(&decode_bf16_kernel<64, true>)
+                                : reinterpret_cast<const void *>(&decode_bf16_kernel<64, false>);
+        if (d == 128) return sub ? reinterpret_cast<const void *>(&decode_bf16_kernel<128, true>)
+                                 : reinterpret_cast<const void *>(&decode_bf16_kernel<128, false>);
+        if (d == 256) return sub ? reinterpret_cast<const void *>(&decode_bf16_kernel<256, true>)
+                                 : reinterpret_cast<const void *>(&decode_bf16_kernel<256, false>);
     } else {
         if (d == 64) return reinterpret_cast<const void *>(&decode_f32_kernel<64>);
         if (d == 128) return reinterpret_cast<const void *>(&decode_f32_kernel<128>);
@@ -295,7 +301,7 @@ void decode_workspace_layout(const PoolGeom &g, DecodeArgs &a, void *workspace, 
 
 hipError_t launch_decode(const PoolGeom &g, DecodeArgs a, void *workspace, int record_workers, hipStream_t stream) {
     decode_workspace_layout(g, a, workspace, record_workers);
-    const void *k = pick_kernel(g.dtype, g.head_dim);
+    const void *k = pick_kernel(g.dtype, g.head_dim, g.page_shift > 0);
     void *args[] = {&a};
     hipError_t e = hipLaunchKernel(k, dim3(a.workers), dim3(kWave), args, 0, stream);
     if (e != hipSuccess) return e;

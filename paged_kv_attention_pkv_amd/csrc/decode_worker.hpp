@@ -494,6 +494,12 @@ struct Desc {
 // i < min(kStage, f1 - c.f()) (0 at virtual positions): one pass of coalesced
 // table reads, eight 64-entry chunks at a time with all loads of a group
 // issued before any is used.
+//
+// With pages of more than 16 tokens (SUB), position p of a segment is the
+// 16-token sub-page p of its row: table column p >> page_shift, sub-page
+// p & (2^page_shift - 1) of that page, and ids[i] holds (page << page_shift)
+// | sub-page, with entries outside the pool taken as page 0.
+template <bool SUB>
 __device__ void stage(const DecodeArgs &a, int *ids, const Cursor &c, int64_t f1, RowLens &rl) {
     const int64_t f0 = c.f();
     const int len = (int)(f1 - f0 < kStage ? f1 - f0 : kStage);
@@ -502,13 +508,21 @@ __device__ void stage(const DecodeArgs &a, int *ids, const Cursor &c, int64_t f1
     for (int c0 = 0; c0 < len; c0 += 8 * kWave) {
         const int64_t gend = f0 + (c0 + 8 * kWave < len ? c0 + 8 * kWave : len);
         int64_t off[8];
+        int sub[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) off[u] = -1;
         for (;;) {  // the segments overlapping [f0 + c0, gend)
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int64_t fl = f0 + c0 + u * kWave + l;
-                if (fl < gend && fl >= s.f && fl < s.f + s.np) off[u] = (int64_t)s.b * a.bt_cols + (fl - s.f);
+                if (fl < gend && fl >= s.f && fl < s.f + s.np) {
+                    if constexpr (SUB) {
+                        off[u] = (int64_t)s.b * a.bt_cols + ((fl - s.f) >> a.page_shift);
+                        sub[u] = (int)(fl - s.f) & ((1 << a.page_shift) - 1);
+                    } else {
+                        off[u] = (int64_t)s.b * a.bt_cols + (fl - s.f);
+                    }
+                }
             }
             if (s.f + s.np >= gend) break;
             seg_next(a, s, rl);
@@ -516,6 +530,13 @@ __device__ void stage(const DecodeArgs &a, int *ids, const Cursor &c, int64_t f1
         int v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) v[u] = off[u] >= 0 ? a.block_table[off[u]] : 0;
+        if constexpr (SUB) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int pg = v[u] >= 0 && v[u] < a.num_pages ? v[u] : 0;
+                v[u] = off[u] >= 0 ? (pg << a.page_shift) | sub[u] : 0;
+            }
+        }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int i = c0 + u * kWave + l;
@@ -526,11 +547,12 @@ __device__ void stage(const DecodeArgs &a, int *ids, const Cursor &c, int64_t f1
 
 // The next pair at the cursor, then advance.  Restages the id window when
 // the cursor has run past it.
+template <bool SUB>
 __device__ __forceinline__ void take(const DecodeArgs &a, Cursor &c, int *ids, int64_t &fbase, int64_t f1,
                                      RowLens &rl, Desc &d) {
     if (__builtin_expect(c.f() - fbase >= kStage, 0)) {
         fbase = c.f();
-        stage(a, ids, c, f1, rl);
+        stage<SUB>(a, ids, c, f1, rl);
     }
     const int64_t i = c.f() - fbase;
     d.b = c.s.b;
@@ -544,8 +566,13 @@ __device__ __forceinline__ void take(const DecodeArgs &a, Cursor &c, int *ids, i
               (c.s.fresh && c.p + npg == c.s.np ? 8 : 0);
     const int ra = uniform(ids[i]);
     const int rb = npg == 2 ? uniform(ids[i + 1]) : ra;
-    d.ida = clamp_page(a, ra);
-    d.idb = clamp_page(a, rb);
+    if constexpr (SUB) {  // staged in range
+        d.ida = ra;
+        d.idb = rb;
+    } else {
+        d.ida = clamp_page(a, ra);
+        d.idb = clamp_page(a, rb);
+    }
     d.raw_last = rb;
     c.p += npg;
     if (__builtin_expect(c.p == c.pend, 0)) {
@@ -559,7 +586,7 @@ __device__ __forceinline__ void take(const DecodeArgs &a, Cursor &c, int *ids, i
     }
 }
 
-template <int D>
+template <int D, bool SUB>
 struct Bf16 {
     using Out = __bf16;
     static constexpr bool kHolds = true;  // can hold its last piece for a merge from registers
@@ -652,13 +679,22 @@ struct Bf16 {
 
     // Loads of pair d: K and V of its pages, the query rows of (b, g) and, in
     // fused mode, the new token.
+    // Byte offset of a staged page id (with SUB: page and 16-token sub-page).
+    __device__ static __forceinline__ int64_t page_bytes(const DecodeArgs &a, int id, int64_t ps) {
+        if constexpr (SUB)
+            return (int64_t)(id >> a.page_shift) * ps + (int64_t)(id & ((1 << a.page_shift) - 1)) * kPage * a.s_tok * 2;
+        else
+            return (int64_t)id * ps;
+    }
+
     __device__ __forceinline__ void issue(const DecodeArgs &a, const Desc &d, Buf &buf) {
         const int64_t hoff = (int64_t)d.g * a.s_head * 2;
         const char *kc = (const char *)a.k_cache + hoff;
         const char *vc = (const char *)a.v_cache + hoff;
         const int64_t ps = a.s_page * 2;
-        load_page(kc + d.ida * ps, vc + d.ida * ps, buf.kA, buf.vA);
-        load_page(kc + d.idb * ps, vc + d.idb * ps, buf.kB, buf.vB);
+        const int64_t pa = page_bytes(a, d.ida, ps), pb = page_bytes(a, d.idb, ps);
+        load_page(kc + pa, vc + pa, buf.kA, buf.vA);
+        load_page(kc + pb, vc + pb, buf.kB, buf.vB);
         const int qc = col < G ? col : G - 1;  // lanes past the group read nothing
         const char *q = (const char *)a.q + ((int64_t)d.b * a.hq + (int64_t)d.g * G + qc) * D * 2;
 #pragma unroll
@@ -684,10 +720,11 @@ struct Bf16 {
         const int slot = (d.n - 1) & (kPage - 1);
         const int e = slot & 3;
         const bool inB = d.npg() == 2;
-        const bool writable = d.raw_last >= 1 && d.raw_last < a.num_pages;
+        const int last_page = SUB ? d.raw_last >> a.page_shift : d.raw_last;
+        const bool writable = last_page >= 1 && last_page < a.num_pages;
         // the new length counts the token only where it was stored
         if (d.g == 0 && lane_id() == 0 && a.seqlens_out) a.seqlens_out[d.b] = writable ? d.n : d.n - 1;
-        const int64_t base = (int64_t)d.g * a.s_head * 2 + (int64_t)d.raw_last * a.s_page * 2;
+        const int64_t base = (int64_t)d.g * a.s_head * 2 + page_bytes(a, d.raw_last, a.s_page * 2);
         if (col == slot) {
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
@@ -873,9 +910,9 @@ struct WorkerLds {
 // its range of the cost line; lds points at WorkerLds<D>::kBytes bytes of
 // this wave's own LDS (16-byte aligned).  The wave synchronises only with
 // itself, so several workers may share a workgroup.
-template <int D>
+template <int D, bool SUB>
 __device__ __forceinline__ void decode_bf16_worker(const DecodeArgs &a, int w, char *lds) {
-    using Eng = Bf16<D>;
+    using Eng = Bf16<D, SUB>;
     int *ids = reinterpret_cast<int *>(lds);
     float *own_o = reinterpret_cast<float *>(lds + WorkerLds<D>::kIdsBytes);
     float *own_ml = own_o + 16 * D;
@@ -887,7 +924,7 @@ __device__ __forceinline__ void decode_bf16_worker(const DecodeArgs &a, int w, c
     cur.pend = (int)(cur.s.np < r.f1 - cur.s.f ? cur.s.np : r.f1 - cur.s.f);
     cur.live = 1;
     int64_t fbase = r.f0;
-    stage(a, ids, cur, r.f1, rl);
+    stage<SUB>(a, ids, cur, r.f1, rl);
     Eng eng;
     eng.init(a);
     Pending pend;
@@ -895,7 +932,7 @@ __device__ __forceinline__ void decode_bf16_worker(const DecodeArgs &a, int w, c
     const float c = a.scale_log2;
     typename Eng::Buf b0, b1;
     Desc d0, d1;
-    take(a, cur, ids, fbase, r.f1, rl, d0);
+    take<SUB>(a, cur, ids, fbase, r.f1, rl, d0);
     eng.issue(a, d0, b0);
     // Two buffers in turn: the next pair's loads are issued before the
     // current pair is computed, and no load is left unconsumed at the end, so
@@ -908,7 +945,7 @@ __device__ __forceinline__ void decode_bf16_worker(const DecodeArgs &a, int w, c
     if (__builtin_expect(!cur.live && !d0.whole(), 0)) pend.check = peek_arrivals(a, (int64_t)d0.b * a.hkv + d0.g);
     for (;;) {
         if (cur.live) {
-            take(a, cur, ids, fbase, r.f1, rl, d1);
+            take<SUB>(a, cur, ids, fbase, r.f1, rl, d1);
             __builtin_amdgcn_sched_barrier(0);
             eng.issue(a, d1, b1);
             if (__builtin_expect(!cur.live && !d1.whole(), 0)) pend.check = peek_arrivals(a, (int64_t)d1.b * a.hkv + d1.g);
@@ -921,7 +958,7 @@ __device__ __forceinline__ void decode_bf16_worker(const DecodeArgs &a, int w, c
             break;
         }
         if (cur.live) {
-            take(a, cur, ids, fbase, r.f1, rl, d0);
+            take<SUB>(a, cur, ids, fbase, r.f1, rl, d0);
             __builtin_amdgcn_sched_barrier(0);
             eng.issue(a, d0, b0);
             if (__builtin_expect(!cur.live && !d0.whole(), 0)) pend.check = peek_arrivals(a, (int64_t)d0.b * a.hkv + d0.g);

@@ -11,9 +11,13 @@
 namespace pkv {
 
 // Pool geometry after the ABI checks (element strides, dim stride 1).
+// The kernels walk keys in 16-token sub-pages; a page of page_size tokens
+// holds page_size / 16 of them (page_shift = log2 of that).
 struct PoolGeom {
     int dtype;       // 0 = fp32, 1 = bf16
     int num_pages;
+    int page_size;   // 16, 32, 64, 128 or 256
+    int page_shift;  // log2(page_size / 16)
     int hkv;
     int head_dim;
     int64_t s_page, s_head, s_tok;
@@ -51,6 +55,7 @@ struct DecodeArgs {
     int32_t batch, hq, hkv;
     int32_t max_kv;     // host bound on seqlens; longer rows are cut to it
     int32_t num_pages;  // page ids are clamped into 0..num_pages-1
+    int32_t page_shift; // log2(page_size / 16): 16-token sub-page j is in table column j >> page_shift
     float scale_log2;   // softmax scale times log2(e)
     int32_t workers;    // split workers (one wave each)
     int32_t fixed_workers;  // 1: the caller fixed the count (no cap by page count)
@@ -105,6 +110,7 @@ struct PrefillArgs {
     const int32_t *qo_indptr;
     int32_t batch, hq, hkv, total_q, max_q, max_kv;
     int32_t num_pages;  // page ids are clamped into 0..num_pages-1
+    int32_t page_shift; // log2(page_size / 16)
     int32_t causal;
     float scale_log2;
     int32_t wg_rows;  // query rows per workgroup: 0 = the library's choice, else 128 or (head_dim 256) 192

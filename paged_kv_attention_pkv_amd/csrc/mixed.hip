@@ -37,7 +37,7 @@ struct MixedLds {
 // Blocks 0 .. n_dec_blocks-1: decode workers bid*4 + wave (those at or past
 // da.workers do nothing); the rest: prefill tile bid - n_dec_blocks of
 // n_pf_blocks.
-template <int D>
+template <int D, bool SUB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mixed_kernel(PrefillArgs pa, int n_qtiles, int n_pf_blocks, DecodeArgs da, int n_dec_blocks) {
     extern __shared__ __align__(16) uint16_t smem[];
@@ -46,13 +46,13 @@ void mixed_kernel(PrefillArgs pa, int n_qtiles, int n_pf_blocks, DecodeArgs da, 
         const int wave = uniform((int)threadIdx.x >> 6);
         const int w = bid * kWaves + wave;
         if (w < da.workers)
-            decode_bf16_worker<D>(da, w, reinterpret_cast<char *>(smem) + wave * WorkerLds<D>::kBytes);
+            decode_bf16_worker<D, SUB>(da, w, reinterpret_cast<char *>(smem) + wave * WorkerLds<D>::kBytes);
         return;
     }
     prefill32_block<D>(pa, n_qtiles, bid - n_dec_blocks, n_pf_blocks, smem);
 }
 
-template <int D>
+template <int D, bool SUB>
 hipError_t launch_mixed_d(const PrefillArgs &pa, const DecodeArgs &da, bool has_decode, hipStream_t stream) {
     const int n_qtiles = pa.batch > 0 ? (pa.max_q + kBM - 1) / kBM : 0;
     const int64_t n_pf = (int64_t)pa.batch * n_qtiles * pa.hq;
@@ -63,9 +63,10 @@ hipError_t launch_mixed_d(const PrefillArgs &pa, const DecodeArgs &da, bool has_
     if (n_pf + n_dec > 0x7fffffff) return hipErrorInvalidValue;
     if (n_pf + n_dec == 0) return hipSuccess;
     static std::atomic<uint64_t> attr_set{0};
-    hipError_t e = set_smem_once(reinterpret_cast<const void *>(&mixed_kernel<D>), MixedLds<D>::kBytes, attr_set);
+    hipError_t e =
+        set_smem_once(reinterpret_cast<const void *>(&mixed_kernel<D, SUB>), MixedLds<D>::kBytes, attr_set);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(mixed_kernel<D>, dim3((unsigned)(n_pf + n_dec)), dim3(kThreads), MixedLds<D>::kBytes, stream,
+    hipLaunchKernelGGL((mixed_kernel<D, SUB>), dim3((unsigned)(n_pf + n_dec)), dim3(kThreads), MixedLds<D>::kBytes, stream,
                        pa, n_qtiles, (int)n_pf, da, (int)n_dec);
     return hipGetLastError();
 }
@@ -76,9 +77,12 @@ hipError_t launch_mixed(const PoolGeom &g, const PrefillArgs &pa, DecodeArgs da,
                         hipStream_t stream) {
     const bool has_decode = da.batch > 0;
     if (has_decode) decode_workspace_layout(g, da, workspace, record_workers);
+    const bool sub = g.page_shift > 0;
     switch (g.head_dim) {
-        case 64: return launch_mixed_d<64>(pa, da, has_decode, stream);
-        case 128: return launch_mixed_d<128>(pa, da, has_decode, stream);
+        case 64: return sub ? launch_mixed_d<64, true>(pa, da, has_decode, stream)
+                            : launch_mixed_d<64, false>(pa, da, has_decode, stream);
+        case 128: return sub ? launch_mixed_d<128, true>(pa, da, has_decode, stream)
+                             : launch_mixed_d<128, false>(pa, da, has_decode, stream);
     }
     return hipErrorInvalidValue;
 }

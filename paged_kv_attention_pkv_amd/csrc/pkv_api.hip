@@ -17,7 +17,7 @@ using pkv::PoolGeom;
 
 namespace {
 
-constexpr int kPageSize = 16;
+constexpr int kSub = 16;  // tokens per sub-page, the unit the kernels walk keys in
 constexpr int32_t kMaxDecodeKv = 1 << 28;  // decode: max_kv_len bound (PKV_EUNSUPPORTED above)
 constexpr int32_t kPaddingRow = -1;        // cache length of a padding row (appends and decode steps)
 
@@ -34,7 +34,11 @@ pkv_status check_desc(const pkv_cache_desc *c, PoolGeom *out) {
         return PKV_EINVAL;
     if (c->s_page < 0 || c->s_head < 0 || c->s_tok < 0) return PKV_EINVAL;
     if (c->dtype != PKV_F32 && c->dtype != PKV_BF16) return PKV_EUNSUPPORTED;
-    if (c->page_size != kPageSize) return PKV_EUNSUPPORTED;
+    int shift = -1;
+    for (int k = 0; k <= 4; ++k)
+        if (c->page_size == (kSub << k)) shift = k;
+    if (shift < 0) return PKV_EUNSUPPORTED;  // 16, 32, 64, 128 or 256 tokens per page
+    if (((int64_t)c->num_pages << shift) > 0x7fffffff) return PKV_EUNSUPPORTED;  // page ids with their sub-page
     if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return PKV_EUNSUPPORTED;
     if (c->s_page % 8 || c->s_head % 8 || c->s_tok % 8) return PKV_EUNSUPPORTED;
     // in-page offsets are 32-bit in the kernels
@@ -42,6 +46,8 @@ pkv_status check_desc(const pkv_cache_desc *c, PoolGeom *out) {
         return PKV_EUNSUPPORTED;
     out->dtype = c->dtype == PKV_BF16 ? 1 : 0;
     out->num_pages = c->num_pages;
+    out->page_size = c->page_size;
+    out->page_shift = shift;
     out->hkv = c->num_kv_heads;
     out->head_dim = c->head_dim;
     out->s_page = c->s_page;
@@ -253,7 +259,7 @@ pkv_status decode_common(const pkv_cache_desc *cache, void *out, float *lse, con
     if (batch == 0) return PKV_OK;
     if (!out || !q || !k_cache || !v_cache || !block_table || !cache_seqlens) return PKV_EINVAL;
     if (fused && (!aligned16(k_new) || !aligned16(v_new))) return PKV_EUNSUPPORTED;
-    if ((int64_t)max_kv_len > (int64_t)bt_cols * kPageSize) return PKV_EINVAL;
+    if ((int64_t)max_kv_len > (int64_t)bt_cols * g.page_size) return PKV_EINVAL;
     if (max_kv_len > kMaxDecodeKv) return PKV_EUNSUPPORTED;  // page counts of 64 rows are summed in 32 bits
     if (!isfinite(scale)) return PKV_EINVAL;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
@@ -264,7 +270,7 @@ pkv_status decode_common(const pkv_cache_desc *cache, void *out, float *lse, con
     // waves than the call has pages
     const int w_rec = pkv::decode_workers(dev, g, num_q_heads, -1, workers);
     if (w_rec < 1) return PKV_EDEVICE;
-    const int64_t bound = (int64_t)batch * g.hkv * ceil_div64(max_kv_len, kPageSize);
+    const int64_t bound = (int64_t)batch * g.hkv * ceil_div64(max_kv_len, kSub);
     const int w = bound < w_rec ? (int)(bound > 0 ? bound : 1) : w_rec;
     const size_t need = pkv::decode_workspace(g, batch, num_q_heads, w_rec);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PKV_EWORKSPACE;
@@ -286,6 +292,7 @@ pkv_status decode_common(const pkv_cache_desc *cache, void *out, float *lse, con
     a.hkv = g.hkv;
     a.max_kv = max_kv_len;
     a.num_pages = g.num_pages;
+    a.page_shift = g.page_shift;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.workers = w;
     a.fixed_workers = workers > 0;
@@ -401,7 +408,7 @@ pkv_status pkv_prefill_attn_ex(const pkv_cache_desc *cache, void *out, float *ls
         return PKV_EINVAL;
     if (batch == 0 || total_q == 0) return batch == 0 && total_q != 0 ? PKV_EINVAL : PKV_OK;
     if (!out || !q || !k_cache || !v_cache || !block_table || !kv_lens || !qo_indptr) return PKV_EINVAL;
-    if ((int64_t)max_kv_len > (int64_t)bt_cols * kPageSize) return PKV_EINVAL;
+    if ((int64_t)max_kv_len > (int64_t)bt_cols * g.page_size) return PKV_EINVAL;
     if (!isfinite(scale)) return PKV_EINVAL;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return PKV_EUNSUPPORTED;
@@ -427,6 +434,7 @@ pkv_status pkv_prefill_attn_ex(const pkv_cache_desc *cache, void *out, float *ls
     a.max_q = max_q;
     a.max_kv = max_kv_len;
     a.num_pages = g.num_pages;
+    a.page_shift = g.page_shift;
     a.causal = causal ? 1 : 0;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.wg_rows = rows_per_workgroup;
@@ -473,7 +481,7 @@ pkv_status pkv_mixed_attn(const pkv_cache_desc *cache, void *out, float *lse, co
     if (total_q < n_dec) return PKV_EINVAL;  // every decode row has one query row
     if (batch == 0) return total_q == 0 ? PKV_OK : PKV_EINVAL;
     if (!out || !q || !k_cache || !v_cache || !block_table || !kv_lens || !qo_indptr) return PKV_EINVAL;
-    if ((int64_t)max_kv_len > (int64_t)bt_cols * kPageSize) return PKV_EINVAL;
+    if ((int64_t)max_kv_len > (int64_t)bt_cols * g.page_size) return PKV_EINVAL;
     if (max_kv_len > kMaxDecodeKv) return PKV_EUNSUPPORTED;
     if (!isfinite(scale)) return PKV_EINVAL;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_EUNSUPPORTED;
@@ -502,6 +510,7 @@ pkv_status pkv_mixed_attn(const pkv_cache_desc *cache, void *out, float *lse, co
     pa.max_q = max_q;
     pa.max_kv = max_kv_len;
     pa.num_pages = g.num_pages;
+    pa.page_shift = g.page_shift;
     pa.causal = 1;
     pa.scale_log2 = scale_log2;
     pa.wg_rows = 0;
@@ -516,7 +525,7 @@ pkv_status pkv_mixed_attn(const pkv_cache_desc *cache, void *out, float *lse, co
     if (n_dec > 0) {
         w_rec = pkv::decode_workers(dev, g, num_q_heads, -1, 0);
         if (w_rec < 1) return PKV_EDEVICE;
-        const int64_t bound = (int64_t)n_dec * g.hkv * ceil_div64(max_kv_len, kPageSize);
+        const int64_t bound = (int64_t)n_dec * g.hkv * ceil_div64(max_kv_len, kSub);
         const size_t need = pkv::decode_workspace(g, n_dec, num_q_heads, w_rec);
         if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PKV_EWORKSPACE;
         da.q = (const char *)q + pf_rows * qrow * es;
@@ -535,6 +544,7 @@ pkv_status pkv_mixed_attn(const pkv_cache_desc *cache, void *out, float *lse, co
         da.hkv = g.hkv;
         da.max_kv = max_kv_len;
         da.num_pages = g.num_pages;
+        da.page_shift = g.page_shift;
         da.scale_log2 = scale_log2;
         da.workers = bound < w_rec ? (int)(bound > 0 ? bound : 1) : w_rec;
         da.fixed_workers = 0;
@@ -551,7 +561,7 @@ pkv_status pkv_route(const pkv_cache_desc *cache, const int32_t *block_table, in
     if (batch < 0 || max_len < 0 || bt_cols < 0) return PKV_EINVAL;
     if (batch == 0 || max_len == 0) return PKV_OK;
     if (!block_table || !seqlens || !offsets) return PKV_EINVAL;
-    if ((int64_t)max_len > (int64_t)bt_cols * kPageSize) return PKV_EINVAL;
+    if ((int64_t)max_len > (int64_t)bt_cols * g.page_size) return PKV_EINVAL;
     return launch_status(
         pkv::launch_route(g, block_table, bt_cols, seqlens, batch, max_len, offsets, (hipStream_t)stream));
 }
@@ -565,9 +575,9 @@ pkv_status pkv_validate_host(const pkv_cache_desc *cache, const int32_t *block_t
     if (st) return st;
     if (batch < 0 || bt_cols < 0) return PKV_EINVAL;
     if (batch > 0 && (!kv_lens || !block_table)) return PKV_EINVAL;
-    if ((int64_t)max_kv_len > (int64_t)bt_cols * kPageSize) {
+    if ((int64_t)max_kv_len > (int64_t)bt_cols * g.page_size) {
         set_msg(msg, msg_len, "max_kv_len %d exceeds bt_cols*page_size %lld", max_kv_len,
-                (long long)bt_cols * kPageSize);
+                (long long)bt_cols * g.page_size);
         return PKV_EVALIDATE;
     }
     for (int b = 0; b < batch; ++b) {
@@ -576,7 +586,7 @@ pkv_status pkv_validate_host(const pkv_cache_desc *cache, const int32_t *block_t
             set_msg(msg, msg_len, "row %d: kv_len %lld outside 0..max_kv_len (%d)", b, (long long)kv, max_kv_len);
             return PKV_EVALIDATE;
         }
-        for (int64_t blk = 0; blk < ceil_div64(kv, kPageSize); ++blk) {
+        for (int64_t blk = 0; blk < ceil_div64(kv, g.page_size); ++blk) {
             const int32_t page = block_table[(int64_t)b * bt_cols + blk];
             if (page < 1 || page >= g.num_pages) {
                 set_msg(msg, msg_len, "row %d block %lld: page %d not in 1..num_pages-1", b, (long long)blk, page);
@@ -642,7 +652,7 @@ pkv_status pkv_validate_append_host(const pkv_cache_desc *cache, const int32_t *
         return PKV_EVALIDATE;
     }
     // (page, slot) targets must be distinct: mark them in a host bitmap
-    const size_t slots = (size_t)g.num_pages * kPageSize;
+    const size_t slots = (size_t)g.num_pages * g.page_size;
     unsigned char *seen = (unsigned char *)calloc((slots + 7) / 8, 1);
     if (!seen) return PKV_EINVAL;
     pkv_status res = PKV_OK;
@@ -656,7 +666,7 @@ pkv_status pkv_validate_append_host(const pkv_cache_desc *cache, const int32_t *
         }
         for (int64_t t = 0; t < n_new; ++t) {
             const int64_t pos = (int64_t)cache_seqlens[b] + t;
-            const int64_t blk = pos / kPageSize;
+            const int64_t blk = pos / g.page_size;
             if (blk >= bt_cols) {
                 set_msg(msg, msg_len, "row %d: position %lld beyond the table (%d blocks)", b, (long long)pos, bt_cols);
                 res = PKV_EVALIDATE;
@@ -668,7 +678,7 @@ pkv_status pkv_validate_append_host(const pkv_cache_desc *cache, const int32_t *
                 res = PKV_EVALIDATE;
                 break;
             }
-            const size_t slot = (size_t)page * kPageSize + (size_t)(pos % kPageSize);
+            const size_t slot = (size_t)page * g.page_size + (size_t)(pos % g.page_size);
             if (seen[slot >> 3] & (1u << (slot & 7))) {
                 set_msg(msg, msg_len, "row %d position %lld: slot of page %d written twice", b, (long long)pos, page);
                 res = PKV_EVALIDATE;

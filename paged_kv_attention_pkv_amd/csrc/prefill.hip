@@ -128,13 +128,16 @@ __device__ __forceinline__ int dma_block16(int tile, int wave) { return tile * (
 // stores to the table, so a table read between them would be a vector load
 // whose wait covers every transfer in flight.  Entries at or past kv read as 0.
 constexpr int kIds16 = 4096;
+// Entries are per 16-token block: block j of a row reads table column
+// j >> sh (sh = log2(page_size / 16)); its sub-page j & (2^sh - 1) is added
+// to the transfer address (dma_tile16).
 template <int NT>
-__device__ __forceinline__ void stage_ids16(const int32_t *bt, int b0, int kv, int *ids) {
+__device__ __forceinline__ void stage_ids16(const int32_t *bt, int b0, int kv, int *ids, int sh) {
     constexpr int N = (kIds16 + NT - 1) / NT;
     const int last = (kv - 1) / kPage;  // last block holding a key (kv >= 1 here)
     int v[N];
 #pragma unroll
-    for (int i = 0; i < N; ++i) v[i] = bt[min(b0 + (int)threadIdx.x + i * NT, last)];  // all in flight
+    for (int i = 0; i < N; ++i) v[i] = bt[min(b0 + (int)threadIdx.x + i * NT, last) >> sh];  // all in flight
 #pragma unroll
     for (int i = 0; i < N; ++i) {
         const int slot = (int)threadIdx.x + i * NT;
@@ -146,14 +149,14 @@ __device__ __forceinline__ void stage_ids16(const int32_t *bt, int b0, int kv, i
 // were loaded before the request's lengths were known; the rest of the
 // window is loaded here if the row has more blocks.
 template <int NT>
-__device__ __forceinline__ void stage_ids16_first(const int32_t *bt, int kv, int pre, int *ids) {
+__device__ __forceinline__ void stage_ids16_first(const int32_t *bt, int kv, int pre, int *ids, int sh) {
     const int last = (kv - 1) / kPage;  // last block holding a key (kv >= 1 here)
     ids[threadIdx.x] = (int)threadIdx.x <= last ? pre : 0;
     if (last >= NT) {
         constexpr int N = (kIds16 - NT + NT - 1) / NT;
         int v[N];
 #pragma unroll
-        for (int i = 0; i < N; ++i) v[i] = bt[min(NT + (int)threadIdx.x + i * NT, last)];
+        for (int i = 0; i < N; ++i) v[i] = bt[min(NT + (int)threadIdx.x + i * NT, last) >> sh];
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int slot = NT + (int)threadIdx.x + i * NT;
@@ -179,7 +182,8 @@ __device__ __forceinline__ void dma_tile16(const PrefillArgs &a, int entry, int 
     int pg = valid > 0 ? entry : 0;
     pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
     // scalar values, so the resources are known to be wave-uniform
-    const int64_t off = uniform64(((int64_t)pg * a.s_page + (int64_t)g * a.s_head) * 2);
+    const int64_t sub = blk & ((1 << a.page_shift) - 1);  // 16-token sub-page of a larger page
+    const int64_t off = uniform64(((int64_t)pg * a.s_page + (int64_t)g * a.s_head + sub * kPage * a.s_tok) * 2);
     const int32_t bytes = uniform((int)(valid * tok_bytes));
     const Rsrc rk = make_rsrc((const char *)a.k_cache + off, bytes);
     const Rsrc rv = make_rsrc((const char *)a.v_cache + off, bytes);
@@ -300,7 +304,7 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
     // the first page-table entries of the row (one per thread) go out before
     // the request's lengths arrive: the row depends only on r
     const int32_t *bt = a.block_table + (int64_t)r * a.bt_cols;
-    const int pre_id = (int)threadIdx.x < a.bt_cols ? bt[threadIdx.x] : 0;
+    const int pre_id = ((int)threadIdx.x >> a.page_shift) < a.bt_cols ? bt[(int)threadIdx.x >> a.page_shift] : 0;
     const int q0 = min(max(a.qo_indptr[r], 0), a.total_q);
     const int q_len = min(max(a.qo_indptr[r + 1] - q0, 0), a.total_q - q0);
     if (qt * kBM16 >= q_len) return;
@@ -364,7 +368,7 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
     const int wv = wave;
     int *ids = reinterpret_cast<int *>(smem + L::IDS);
     int window = 0;  // ids holds blocks window*kIds16 ..
-    stage_ids16_first<C::THREADS>(bt, kv, pre_id, ids);
+    stage_ids16_first<C::THREADS>(bt, kv, pre_id, ids, a.page_shift);
     // the table in LDS is complete; the Q loads may still be in flight
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     auto entry = [&](int t) { return uniform(ids[dma_block16(t, wv) - window * kIds16]); };
@@ -382,7 +386,7 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
             if (dma_block16(pre, kDmaWaves16 - 1) >= (window + 1) * kIds16) {
                 __syncthreads();
                 window = dma_block16(pre, 0) / kIds16;
-                stage_ids16<C::THREADS>(bt, window * kIds16, kv, ids);
+                stage_ids16<C::THREADS>(bt, window * kIds16, kv, ids, a.page_shift);
                 __syncthreads();
             }
             if (wv < kDmaWaves16)

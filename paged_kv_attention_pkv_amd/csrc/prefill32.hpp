@@ -66,9 +66,11 @@ __device__ __forceinline__ void load_tile(const PrefillArgs &a, const int32_t *b
     for (int u = 0; u < kBN / kPage; ++u) {
         const int blk = tile * (kBN / kPage) + u;
         const int valid = min(max(kv - blk * kPage, 0), kPage);
-        int pg = valid > 0 ? bt[blk] : 0;
+        // 16-token block blk: table column blk >> page_shift, sub-page blk & (2^page_shift - 1)
+        int pg = valid > 0 ? bt[blk >> a.page_shift] : 0;
         pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
-        const int64_t off = ((int64_t)pg * a.s_page + (int64_t)g * a.s_head) * 2;
+        const int64_t sub = blk & ((1 << a.page_shift) - 1);
+        const int64_t off = ((int64_t)pg * a.s_page + (int64_t)g * a.s_head + sub * kPage * a.s_tok) * 2;
         const int32_t bytes = (int32_t)(valid * tok_bytes);
         rk[u] = make_rsrc((const char *)a.k_cache + off, bytes);
         rv[u] = make_rsrc((const char *)a.v_cache + off, bytes);

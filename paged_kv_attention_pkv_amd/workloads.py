@@ -24,7 +24,7 @@ Workloads (sizes from the pages' Qwen3-4B / FlashInfer settings):
                             kv_len = q_len + U{0..4096}; or the fixed request
                             q_len = kv_len = 1023.
 
-Conventions: page size 16; page 0 is never dealt; the other pages are dealt
+Conventions: page size 16 unless a spec asks for another; page 0 is never dealt; the other pages are dealt
 by a seeded permutation, sequence 0 first, logical blocks in order; unused
 table entries hold 0 (the reserved page).
 """
@@ -123,32 +123,34 @@ def deal_pages(pages_per_seq: np.ndarray, usable_pages: int, bt_cols: int,
 
 
 def _decode_from_lengths(name, hist, n_new, hq, hkv, d, dtype, max_hist, slack, seed, rng,
-                         usable=None, layout="HND") -> DecodeSpec:
+                         usable=None, layout="HND", page_size=PAGE_SIZE) -> DecodeSpec:
     hist = np.asarray(hist, dtype=np.int32)
-    pages = np.array([_ceil_div(int(L) + n_new, PAGE_SIZE) for L in hist], dtype=np.int64)
-    bt_cols = _ceil_div(max_hist + n_new, PAGE_SIZE)
+    pages = np.array([_ceil_div(int(L) + n_new, page_size) for L in hist], dtype=np.int64)
+    bt_cols = _ceil_div(max_hist + n_new, page_size)
     if usable is None:
         usable = int(math.ceil(slack * int(pages.sum())))
     bt, num_pages = deal_pages(pages, usable, bt_cols, rng)
     return DecodeSpec(name, len(hist), hq, hkv, d, dtype, hist, n_new, num_pages, bt_cols, bt,
-                      seed, layout=layout)
+                      seed, page_size=page_size, layout=layout)
 
 
 def decode_spec(workload: str, batch: int | None = None, seed: int | None = None,
-                layout: str = "HND") -> DecodeSpec:
-    """Lengths, pool size and block table of one decode workload."""
+                layout: str = "HND", page_size: int = PAGE_SIZE) -> DecodeSpec:
+    """Lengths, pool size and block table of one decode workload (pages of
+    `page_size` tokens; the named workloads use 16)."""
     if workload == "tiny_f32":
         seed = 1 if seed is None else seed
         rng = np.random.default_rng(seed)
         return _decode_from_lengths("tiny_f32", [37, 80], 1, 4, 2, 64, "f32", 80, None, seed, rng,
-                                    usable=15, layout=layout)
+                                    usable=15, layout=layout, page_size=page_size)
     if workload == "qwen3_decode":
         batch = 64 if batch is None else batch
         seed = 2 if seed is None else seed
         rng = np.random.default_rng(seed)
         hist = rng.integers(512, 1024, size=batch, endpoint=True)
         return _decode_from_lengths(f"qwen3_decode_b{batch}", hist, 1, 32, 8, 128, "bf16", 1024,
-                                    1.25, seed, rng, layout=layout)
+                                    1.25, seed, rng, layout=layout,
+                                    page_size=page_size)
     if workload == "qwen3_sweep":
         if batch is None:
             raise ValueError("qwen3_sweep needs a batch size")
@@ -157,7 +159,8 @@ def decode_spec(workload: str, batch: int | None = None, seed: int | None = None
         prompt = rng.integers(64, 512, size=batch, endpoint=True)
         gen = rng.integers(0, 512, size=batch, endpoint=True)
         return _decode_from_lengths(f"qwen3_sweep_b{batch}", prompt + gen, 1, 32, 8, 128, "bf16",
-                                    1024, 1.25, seed, rng, layout=layout)
+                                    1024, 1.25, seed, rng, layout=layout,
+                                    page_size=page_size)
     if workload == "long_ragged":
         batch = 256 if batch is None else batch
         seed = 4 if seed is None else seed
@@ -165,29 +168,30 @@ def decode_spec(workload: str, batch: int | None = None, seed: int | None = None
         u = rng.uniform(math.log(16.0), math.log(32768.0), size=batch)
         hist = np.clip(np.rint(np.exp(u)), 16, 32768).astype(np.int32)
         return _decode_from_lengths(f"long_ragged_b{batch}", hist, 1, 32, 8, 128, "bf16", 32768,
-                                    1.0, seed, rng, layout=layout)
+                                    1.0, seed, rng, layout=layout,
+                                    page_size=page_size)
     raise ValueError(f"unknown decode workload {workload!r}")
 
 
 def custom_decode_spec(hist_lens, hq: int, hkv: int, head_dim: int, dtype: str, seed: int,
                        n_new: int = 1, slack: float = 1.25, extra_cols: int = 0,
-                       layout: str = "HND") -> DecodeSpec:
+                       layout: str = "HND", page_size: int = PAGE_SIZE) -> DecodeSpec:
     """Decode workload with explicit cached lengths (for edge cases)."""
     rng = np.random.default_rng(seed)
     hist = np.asarray(hist_lens, dtype=np.int32)
     max_hist = int(hist.max()) if hist.size else 0
-    pages = np.array([_ceil_div(int(L) + n_new, PAGE_SIZE) for L in hist], dtype=np.int64)
-    bt_cols = max(1, _ceil_div(max_hist + n_new, PAGE_SIZE) + extra_cols)
+    pages = np.array([_ceil_div(int(L) + n_new, page_size) for L in hist], dtype=np.int64)
+    bt_cols = max(1, _ceil_div(max_hist + n_new, page_size) + extra_cols)
     usable = max(1, int(math.ceil(slack * int(pages.sum()))))
     bt, num_pages = deal_pages(pages, usable, bt_cols, rng)
     return DecodeSpec("custom", len(hist), hq, hkv, head_dim, dtype, hist, n_new, num_pages,
-                      bt_cols, bt, seed, layout=layout)
+                      bt_cols, bt, seed, page_size=page_size, layout=layout)
 
 
 def prefill_spec(batch: int | None = None, seed: int | None = None, fixed_1023: bool = False,
                  q_lens=None, kv_lens=None, hq: int = 48, hkv: int = 8, head_dim: int = 256,
                  dtype: str = "bf16", layout: str = "HND", max_q: int = 4096,
-                 max_extra: int = 4096) -> PrefillSpec:
+                 max_extra: int = 4096, page_size: int = PAGE_SIZE) -> PrefillSpec:
     """Lengths, pool and block table of one causal prefill workload."""
     if fixed_1023:
         seed = 599 if seed is None else seed
@@ -208,11 +212,11 @@ def prefill_spec(batch: int | None = None, seed: int | None = None, fixed_1023: 
         kv = (q + rng0.integers(0, max_extra, size=batch, endpoint=True)).astype(np.int32)
         name = f"prefill_d256_b{batch}"
     rng = np.random.default_rng(seed + 1_000_003)
-    pages = np.array([_ceil_div(int(k), PAGE_SIZE) for k in kv], dtype=np.int64)
+    pages = np.array([_ceil_div(int(k), page_size) for k in kv], dtype=np.int64)
     bt_cols = max(1, int(pages.max()) if pages.size else 1)
     bt, num_pages = deal_pages(pages, max(1, int(pages.sum())), bt_cols, rng)
     return PrefillSpec(name, q, kv, num_pages, bt_cols, bt, seed, hq, hkv, head_dim, dtype,
-                       layout=layout)
+                       page_size=page_size, layout=layout)
 
 
 # --------------------------------------------------------------------------

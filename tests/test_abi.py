@@ -57,7 +57,7 @@ def _decode(desc, hq=32, batch=4, max_kv=64, bt_cols=4, out=FAKE, ws=FAKE, ws_by
 
 @pytest.mark.parametrize("kw,code", [
     (dict(head_dim=96), EUNSUPPORTED),
-    (dict(page_size=32), EUNSUPPORTED),
+    (dict(page_size=48), EUNSUPPORTED),
     (dict(dtype=7), EUNSUPPORTED),
     (dict(s_tok=127), EUNSUPPORTED),
     (dict(reserved=1), EINVAL),
@@ -307,3 +307,14 @@ def test_validators_accept_padding_rows():
         pkv.validate_append_host(kc, bt, torch.tensor([16, -2, 40], dtype=torch.int32))
     with pytest.raises(pkv.PkvError, match="max_kv_len"):
         pkv.validate_decode_step_host(kc, bt, torch.tensor([16, -2, 40], dtype=torch.int32), 48)
+
+
+def test_page_sizes_accepted():
+    """Pages of 16, 32, 64, 128 or 256 tokens; anything else is refused before
+    any launch (a zero-batch append reaches the descriptor checks only)."""
+    lib = api.lib()
+    for page, want in ((16, OK), (32, OK), (64, OK), (128, OK), (256, OK), (8, EUNSUPPORTED), (24, EUNSUPPORTED),
+                       (512, EUNSUPPORTED)):
+        d = _desc(page_size=page, s_page=8 * page * 128, s_head=page * 128, s_tok=128)
+        rc = lib.pkv_append(ctypes.byref(d), None, None, None, None, None, 0, None, None, 0, 0, None, None)
+        assert rc == want, (page, rc)

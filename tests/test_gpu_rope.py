@@ -18,9 +18,10 @@ from gpu_common import BF16_TOL, compare, host_bits, opool, say
 pytestmark = pytest.mark.gpu
 
 
-def _case(hist, new, hq, hkv, d, dtype, seed, layout="HND"):
+def _case(hist, new, hq, hkv, d, dtype, seed, layout="HND", page_size=16):
     total = [max(a, 0) + b for a, b in zip(hist, new)]
-    spec = wl.custom_decode_spec(total, hq=hq, hkv=hkv, head_dim=d, dtype=dtype, seed=seed, n_new=0, layout=layout)
+    spec = wl.custom_decode_spec(total, hq=hq, hkv=hkv, head_dim=d, dtype=dtype, seed=seed, n_new=0, layout=layout,
+                                 page_size=page_size)
     gen = torch.Generator().manual_seed(seed)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     nh = sum(max(a, 0) for a in hist)
@@ -32,11 +33,11 @@ def _case(hist, new, hq, hkv, d, dtype, seed, layout="HND"):
     return spec, kh, vh, kn, vn, q
 
 
-def _run(hist, new, hq, hkv, d, dtype, interleaved, seed, layout="HND"):
+def _run(hist, new, hq, hkv, d, dtype, interleaved, seed, layout="HND", page_size=16):
     say(f"[rope append] hist={hist} new={new} Hq={hq} Hkv={hkv} D={d} {dtype} {layout} "
-        f"{'interleaved' if interleaved else 'half-split'}")
+        f"{'interleaved' if interleaved else 'half-split'} page {page_size}")
     dev = torch.device("cuda")
-    spec, kh, vh, kn, vn, q = _case(hist, new, hq, hkv, d, dtype, seed, layout)
+    spec, kh, vh, kn, vn, q = _case(hist, new, hq, hkv, d, dtype, seed, layout, page_size)
     bt = spec.block_table
     hist_np = np.asarray(hist, np.int32)
     hist_ip = np.concatenate([[0], np.cumsum([max(a, 0) for a in hist])]).astype(np.int32)
