@@ -27,7 +27,16 @@ oracle timed on a bounded sample of the same workload on the host cores (and
 on one core).
 
 ``--workload decode|sweep|long|prefill|mixed`` with ``--batch B`` times one
-workload only.
+workload only; ``--page-size``, ``--layout`` and ``--contiguous`` change the
+pool of the decode and prefill workloads.
+
+``--workload tune`` is the tuning sweep: for the decode step (batch 64 and
+the batch-8 / batch-32 sweep shapes) it times split-worker counts, page
+sizes, the NHD layout and contiguous pages, and for prefill the two head_dim
+256 tilings, each scored on whole-step time (all layers, HIP graph) and
+timed in alternation with the library's default configuration on the same
+inputs (the control), so that drift between measurements shows up in the
+control's own spread.  It prints one JSON line per workload.
 """
 from __future__ import annotations
 
@@ -57,7 +66,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default=None, choices=["decode", "sweep", "long", "prefill", "mixed"],
+    p.add_argument("--workload", default=None, choices=["decode", "sweep", "long", "prefill", "mixed", "tune"],
                    help="time one workload only (default: decode B=64 plus the two prefill cases)")
     p.add_argument("--batch", type=int, default=None)
     p.add_argument("--layers", type=int, default=36, help="decode: layer caches per step")
@@ -75,6 +84,10 @@ def parse():
     p.add_argument("--separate", action="store_true",
                    help="decode step as pkv_append + pkv_decode_attn (two launches) instead of the fused "
                         "pkv_append_decode_attn")
+    p.add_argument("--page-size", type=int, default=16, help="decode/prefill: tokens per page (16 .. 256)")
+    p.add_argument("--layout", default="HND", choices=["HND", "NHD"], help="decode/prefill: pool layout")
+    p.add_argument("--contiguous", action="store_true",
+                   help="decode/prefill: deal every sequence a run of adjacent pages instead of shuffled pages")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (for HBM counter calibration)")
     return p.parse_args()
@@ -201,12 +214,13 @@ def spread(per, scale=1.0, nd=2):
 # --------------------------------------------------------------------------
 
 def bench_decode(args, torch, pkv, wl, workload):
+    kw = dict(page_size=args.page_size, layout=args.layout, contiguous=args.contiguous)
     if workload == "decode":
-        spec = wl.decode_spec("qwen3_decode", batch=args.batch or 64)
+        spec = wl.decode_spec("qwen3_decode", batch=args.batch or 64, **kw)
     elif workload == "sweep":
-        spec = wl.decode_spec("qwen3_sweep", batch=args.batch or 64)
+        spec = wl.decode_spec("qwen3_sweep", batch=args.batch or 64, **kw)
     else:
-        spec = wl.decode_spec("long_ragged", batch=args.batch or 256)
+        spec = wl.decode_spec("long_ragged", batch=args.batch or 256, **kw)
     dev = torch.device("cuda:0")
     L = args.layers
     fused = not args.separate and spec.dtype == "bf16"
@@ -235,18 +249,20 @@ def bench_decode(args, torch, pkv, wl, workload):
         inp = wl.decode_inputs(spec, device=dev, seed_offset=layer)
         kc, vc = pools[layer]
         if workspace is None:
-            ws_bytes = pkv.decode_workspace_bytes(kc, spec.batch, spec.hq, max_kv, workers=args.workers)
+            ws_bytes = pkv.decode_workspace_bytes(kc, spec.batch, spec.hq, max_kv, layout=spec.layout,
+                                                  workers=args.workers)
             workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
-        pkv.append(kc, vc, inp.k_hist, inp.v_hist, bt, zeros, inp.hist_indptr)
+        pkv.append(kc, vc, inp.k_hist, inp.v_hist, bt, zeros, inp.hist_indptr, layout=spec.layout)
         out = torch.empty_like(inp.q)
         if fused:
             app = None
             dec = pkv.api.prepare_append_decode(inp.q, kc, vc, inp.k_new, inp.v_new, bt, hist, max_kv, spec.scale,
-                                                out, workspace, seqlens_out=lens, workers=args.workers)
+                                                out, workspace, seqlens_out=lens, layout=spec.layout,
+                                                workers=args.workers)
         else:
-            app = pkv.api.prepare_append(kc, vc, inp.k_new, inp.v_new, bt, hist, lens)
+            app = pkv.api.prepare_append(kc, vc, inp.k_new, inp.v_new, bt, hist, lens, layout=spec.layout)
             dec = pkv.api.prepare_decode(inp.q, kc, vc, bt, lens, max_kv, spec.scale, out, workspace,
-                                         workers=args.workers)
+                                         layout=spec.layout, workers=args.workers)
         layers.append((app, dec))
         del inp
     del pools
@@ -285,7 +301,8 @@ def bench_decode(args, torch, pkv, wl, workload):
         "dtype": "bf16" if spec.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": spec.name, "batch": spec.batch, "hq": spec.hq, "hkv": spec.hkv,
-                   "head_dim": spec.head_dim, "page_size": spec.page_size, "layers": L,
+                   "head_dim": spec.head_dim, "page_size": spec.page_size, "layout": spec.layout,
+                   "pages": "contiguous" if args.contiguous else "shuffled", "layers": L,
                    "mean_attended_len": round(float(spec.hist_lens.mean()) + spec.n_new, 1),
                    "step": ("per layer: pkv_append_decode_attn (append 1 token/seq + attend, one launch)"
                             if fused else "per layer: pkv_append(1 token/seq) + pkv_decode_attn"),
@@ -381,14 +398,17 @@ def bench_prefill(args, torch, pkv, wl, spec):
         # every layer its own pools, queries and outputs, as the layers of a model
         inp = wl.prefill_inputs(spec, device=dev, seed_offset=layer)
         kc, vc = wl.empty_pool(spec, dev), wl.empty_pool(spec, dev)
-        pkv.append(kc, vc, inp.k_hist, inp.v_hist, inp.block_table, zeros, inp.hist_indptr)
-        kv_lens = pkv.append(kc, vc, inp.k_new, inp.v_new, inp.block_table, inp.hist_lens, inp.qo_indptr)
+        lay = spec.layout
+        pkv.append(kc, vc, inp.k_hist, inp.v_hist, inp.block_table, zeros, inp.hist_indptr, layout=lay)
+        kv_lens = pkv.append(kc, vc, inp.k_new, inp.v_new, inp.block_table, inp.hist_lens, inp.qo_indptr, layout=lay)
         out = torch.empty_like(inp.q)
         if ws is None:
-            need = pkv.prefill_workspace_bytes(kc, spec.batch, spec.hq, int(spec.q_lens.sum()), max_q, max_kv)
+            need = pkv.prefill_workspace_bytes(kc, spec.batch, spec.hq, int(spec.q_lens.sum()), max_q, max_kv,
+                                               layout=lay)
             ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)  # counters start at zero
         calls.append(pkv.api.prepare_prefill(inp.q, kc, vc, inp.block_table, kv_lens, inp.qo_indptr, max_q,
-                                             max_kv, spec.scale, out, ws, rows_per_workgroup=args.prefill_rows))
+                                             max_kv, spec.scale, out, ws, layout=lay,
+                                             rows_per_workgroup=args.prefill_rows))
         del inp
     torch.cuda.synchronize()
 
@@ -415,7 +435,8 @@ def bench_prefill(args, torch, pkv, wl, spec):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": spec.name, "batch": spec.batch, "hq": spec.hq, "hkv": spec.hkv,
-                   "head_dim": spec.head_dim, "q_lens_sum": int(spec.q_lens.sum()),
+                   "head_dim": spec.head_dim, "page_size": spec.page_size, "layout": spec.layout,
+                   "pages": "contiguous" if args.contiguous else "shuffled", "q_lens_sum": int(spec.q_lens.sum()),
                    "kv_lens_sum": int(spec.kv_lens.sum()), "layers": L,
                    "step": "per layer: one pkv_prefill_attn call (own pools and inputs)",
                    "launch": "eager" if args.eager else "hip graph"},
@@ -558,6 +579,150 @@ def cpu_baseline_prefill(args, spec):
                       f"1 thread in {spent1:.1f} s; fp64 oracle"}
 
 
+# --------------------------------------------------------------------------
+# tuning sweep
+# --------------------------------------------------------------------------
+
+def _median_step_ms(torch, step, args):
+    _, per = time_steps(torch, step, args.steps, args.warmup, not args.eager)
+    return statistics.median(per)
+
+
+def _decode_setup(torch, pkv, wl, spec, L, dev):
+    """L layers of pools holding the history, with each layer's q / new K/V."""
+    bt = torch.from_numpy(spec.block_table).to(dev)
+    hist = torch.from_numpy(spec.hist_lens).to(dev)
+    zeros = torch.zeros_like(hist)
+    pools = [(wl.empty_pool(spec, dev), wl.empty_pool(spec, dev)) for _ in range(L)]
+    layers = []
+    for layer in range(L):
+        inp = wl.decode_inputs(spec, device=dev, seed_offset=layer)
+        kc, vc = pools[layer]
+        pkv.append(kc, vc, inp.k_hist, inp.v_hist, bt, zeros, inp.hist_indptr, layout=spec.layout)
+        layers.append((kc, vc, inp.q, inp.k_new, inp.v_new))
+        del inp
+    torch.cuda.synchronize()
+    return {"spec": spec, "bt": bt, "hist": hist, "layers": layers,
+            "max_kv": int(spec.hist_lens.max()) + spec.n_new}
+
+
+def _decode_step(torch, pkv, setup, workers, dev):
+    """One fused append + decode launch per layer with the given worker count."""
+    spec, bt, hist, max_kv = setup["spec"], setup["bt"], setup["hist"], setup["max_kv"]
+    kc0 = setup["layers"][0][0]
+    ws = torch.zeros(pkv.decode_workspace_bytes(kc0, spec.batch, spec.hq, max_kv, layout=spec.layout,
+                                                workers=workers), dtype=torch.uint8, device=dev)
+    lens = torch.empty_like(hist)
+    calls = [pkv.api.prepare_append_decode(q, kc, vc, kn, vn, bt, hist, max_kv, spec.scale, torch.empty_like(q), ws,
+                                           seqlens_out=lens, layout=spec.layout, workers=workers)
+             for kc, vc, q, kn, vn in setup["layers"]]
+
+    def step():
+        for c in calls:
+            c()
+    step.keep = (ws, lens, calls)
+    return step
+
+
+def _alternate(torch, args, control, variant, rounds):
+    """Medians of `rounds` alternating measurements control, variant, ..."""
+    c, v = [], []
+    for _ in range(rounds):
+        c.append(_median_step_ms(torch, control, args))
+        v.append(_median_step_ms(torch, variant, args))
+    return c, v
+
+
+def bench_tune(args, torch, pkv, wl):
+    dev = torch.device("cuda:0")
+    L = args.layers
+    rounds = 3
+    lines = []
+
+    def summarise(name, control_label, per_layer, entries, controls, unit_scale):
+        all_c = [x for cs in controls for x in cs]
+        med_c = statistics.median(all_c)
+        rows = []
+        for label, cs, vs in entries:
+            mv, mc = statistics.median(vs), statistics.median(cs)
+            rows.append({"config": label, "us_per_layer": round(mv * unit_scale / per_layer, 2),
+                         "control_us_per_layer": round(mc * unit_scale / per_layer, 2),
+                         "ratio_to_control": round(mv / mc, 4)})
+        best = min(rows, key=lambda r: r["ratio_to_control"])
+        return {"metric": f"tuning sweep: {name}", "unit": "us/layer", "higher_is_better": False,
+                "control": control_label, "control_us_per_layer": round(med_c * unit_scale / per_layer, 2),
+                "control_spread": round((max(all_c) - min(all_c)) / med_c, 4), "control_runs": len(all_c),
+                "best": best["config"], "best_ratio_to_control": best["ratio_to_control"],
+                "steps_per_measurement": args.steps, "rounds": rounds, "layers": per_layer, "variants": rows}
+
+    # decode: worker counts at three batch sizes; page size, layout and page order at batch 64
+    for workload, batch in (("qwen3_decode", 64), ("qwen3_sweep", 8), ("qwen3_sweep", 32)):
+        base = wl.decode_spec(workload, batch=batch)
+        log(f"[tune] {base.name}: {L} layers")
+        ctl = _decode_setup(torch, pkv, wl, base, L, dev)
+        control = _decode_step(torch, pkv, ctl, 0, dev)
+        entries, controls = [], []
+        for w in (128, 256, 512, 768, 1280, 2048):
+            c, v = _alternate(torch, args, control, _decode_step(torch, pkv, ctl, w, dev), rounds)
+            entries.append((f"workers {w}", c, v))
+            controls.append(c)
+        if batch == 64:
+            for label, kw in (("page 64", dict(page_size=64)), ("page 256", dict(page_size=256)),
+                              ("NHD layout", dict(layout="NHD")), ("contiguous pages", dict(contiguous=True)),
+                              ("page 256, contiguous", dict(page_size=256, contiguous=True))):
+                other = _decode_setup(torch, pkv, wl, wl.decode_spec(workload, batch=batch, **kw), L, dev)
+                c, v = _alternate(torch, args, control, _decode_step(torch, pkv, other, 0, dev), rounds)
+                entries.append((label, c, v))
+                controls.append(c)
+                del other
+                torch.cuda.empty_cache()
+        lines.append(dict(summarise(f"decode {base.name} (fused append + decode per layer)",
+                                    "page 16, HND, shuffled pages, library worker count", L, entries, controls,
+                                    1e3), workload=base.name))
+        del ctl, control
+        torch.cuda.empty_cache()
+
+    # prefill: the two head_dim 256 tilings against the library's choice
+    Lp = max(1, args.prefill_layers)
+    for spec in (wl.prefill_spec(fixed_1023=True), wl.prefill_spec(batch=2), wl.prefill_spec(batch=4),
+                 wl.prefill_spec(batch=8)):
+        log(f"[tune] {spec.name}: {Lp} layers")
+        max_q, max_kv = int(spec.q_lens.max()), int(spec.kv_lens.max())
+        zeros = torch.zeros(spec.batch, dtype=torch.int32, device=dev)
+        made = []
+        for layer in range(Lp):
+            inp = wl.prefill_inputs(spec, device=dev, seed_offset=layer)
+            kc, vc = wl.empty_pool(spec, dev), wl.empty_pool(spec, dev)
+            pkv.append(kc, vc, inp.k_hist, inp.v_hist, inp.block_table, zeros, inp.hist_indptr)
+            kv = pkv.append(kc, vc, inp.k_new, inp.v_new, inp.block_table, inp.hist_lens, inp.qo_indptr)
+            made.append((inp.q, kc, vc, inp.block_table, kv, inp.qo_indptr))
+            del inp
+        need = pkv.prefill_workspace_bytes(made[0][1], spec.batch, spec.hq, int(spec.q_lens.sum()), max_q, max_kv)
+
+        def prefill_step(rows):
+            ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+            calls = [pkv.api.prepare_prefill(q, kc, vc, bt, kv, ip, max_q, max_kv, spec.scale, torch.empty_like(q), ws,
+                                             rows_per_workgroup=rows) for q, kc, vc, bt, kv, ip in made]
+
+            def step():
+                for c in calls:
+                    c()
+            step.keep = (ws, calls)
+            return step
+
+        control = prefill_step(0)
+        entries, controls = [], []
+        for rows in (128, 192):
+            c, v = _alternate(torch, args, control, prefill_step(rows), rounds)
+            entries.append((f"{rows} query rows per workgroup", c, v))
+            controls.append(c)
+        lines.append(dict(summarise(f"prefill {spec.name}", "library tiling choice", Lp, entries, controls, 1e3),
+                          workload=spec.name))
+        del made, control
+        torch.cuda.empty_cache()
+    return lines
+
+
 def calibrate_copy(torch):
     """A plain device copy of exactly 1 GiB (read 1 GiB, write 1 GiB), run 5
     times, for scaling the HBM byte counters."""
@@ -590,11 +755,19 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log(f"[bench] device {props.name} ({getattr(props, 'gcnArchName', '?')}), CUs {props.multi_processor_count}")
     cpu = not args.no_cpu_baseline
+    if args.workload == "tune":
+        for line in bench_tune(args, torch, pkv, wl):
+            line["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", "?"),
+                              "cus": props.multi_processor_count}
+            print(json.dumps(line), flush=True)
+        return
     if args.workload == "mixed":
         result = bench_mixed(args, torch, pkv, wl)
         result.update({"n_gpus": 1, "scaling": "weak", "vs_baseline": None})
     elif args.workload == "prefill":
-        spec = wl.prefill_spec(fixed_1023=True) if args.batch is None else wl.prefill_spec(batch=args.batch)
+        kw = dict(page_size=args.page_size, layout=args.layout, contiguous=args.contiguous)
+        spec = (wl.prefill_spec(fixed_1023=True, **kw) if args.batch is None
+                else wl.prefill_spec(batch=args.batch, **kw))
         result = bench_prefill(args, torch, pkv, wl, spec)
         result.update({"n_gpus": 1, "scaling": "weak", "vs_baseline": None})
         if cpu:

@@ -274,6 +274,21 @@ int decode_workers(int device, const PoolGeom &g, int hq, int64_t max_pages_boun
     return (int)w;
 }
 
+// Mid-sized calls: on the bf16 head_dim 128 kernel (one wave per SIMD, four
+// per CU) a call of fewer than 64 (page, kv head) units per CU runs faster on
+// three waves per CU than on four (measured over batch 8..64 of two length
+// mixes: up to 10% at 9000-12000 units, within 1% elsewhere); larger calls
+// keep four.  Smaller calls are cut further by the pages-per-worker floor.
+void decode_mid_cap(int device, const PoolGeom &g, int w_rec, DecodeArgs &a) {
+    a.mid_workers = 0;
+    a.mid_pages = 0;
+    if (a.fixed_workers || g.dtype != 1 || g.head_dim != 128 || device < 0 || device >= kMaxDevices) return;
+    const int cus = g_info[device].cus.load(std::memory_order_relaxed);
+    if (cus <= 0 || w_rec != 4 * cus) return;
+    a.mid_workers = 3 * cus;
+    a.mid_pages = 64 * (int64_t)cus;
+}
+
 // Workspace: one int32 arrival counter per (sequence, kv head) first, then
 // the partial records (o: G*D fp32, (m, l): 2 fp32) for up to
 // `record_workers` + batch*hkv pieces.  `record_workers` is the worker count

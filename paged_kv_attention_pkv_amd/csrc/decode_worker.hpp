@@ -212,6 +212,7 @@ __device__ __forceinline__ bool plan(const DecodeArgs &a, int w, int D, RowLens 
     const int64_t by_pages = total / kMinPagesPerWorker > 0 ? total / kMinPagesPerWorker : 1;
     int64_t wmax = by_pages < (int64_t)a.workers ? by_pages : (int64_t)a.workers;
     if (a.fixed_workers) wmax = total < (int64_t)a.workers ? total : (int64_t)a.workers;
+    else if (a.mid_workers > 0 && total < a.mid_pages && wmax > a.mid_workers) wmax = a.mid_workers;
     if ((int64_t)w >= wmax) return false;
     const int64_t len = total + (int64_t)kSegCostPages * rows * a.hkv;
     r.total = len;

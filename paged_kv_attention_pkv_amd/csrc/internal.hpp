@@ -59,6 +59,10 @@ struct DecodeArgs {
     float scale_log2;   // softmax scale times log2(e)
     int32_t workers;    // split workers (one wave each)
     int32_t fixed_workers;  // 1: the caller fixed the count (no cap by page count)
+    // Automatic count only: a call with fewer than mid_pages (page, kv head)
+    // units uses at most mid_workers waves (0: no such cap).
+    int32_t mid_workers;
+    int64_t mid_pages;
     float *part_o;      // [(record workers + batch*hkv) * group * head_dim]
     float *part_ml;     // [(record workers + batch*hkv) * group * 2]
     int32_t *arrivals;  // [batch*hkv]: pieces finished per split row; zero between calls
@@ -69,6 +73,10 @@ struct DecodeArgs {
     const void *v_new;
     int32_t *seqlens_out;  // nullable (fused mode only): L+1 where the token was stored, else L
 };
+
+// Fills a.mid_workers / a.mid_pages for an automatic worker count of
+// `w_rec` waves on `device` (zero when the caller fixed the count).
+void decode_mid_cap(int device, const PoolGeom &g, int w_rec, DecodeArgs &a);
 
 // Workers the decode kernel uses on `device` when the caller asks for
 // `requested` (0 = automatic); never more than `max_pages_bound` (< 0: no

@@ -296,6 +296,7 @@ pkv_status decode_common(const pkv_cache_desc *cache, void *out, float *lse, con
     a.scale_log2 = scale * 1.4426950408889634f;
     a.workers = w;
     a.fixed_workers = workers > 0;
+    pkv::decode_mid_cap(dev, g, w_rec, a);
     a.part_o = nullptr;  // filled by launch_decode from the workspace
     a.part_ml = nullptr;
     a.arrivals = nullptr;
@@ -548,6 +549,7 @@ pkv_status pkv_mixed_attn(const pkv_cache_desc *cache, void *out, float *lse, co
         da.scale_log2 = scale_log2;
         da.workers = bound < w_rec ? (int)(bound > 0 ? bound : 1) : w_rec;
         da.fixed_workers = 0;
+        pkv::decode_mid_cap(dev, g, w_rec, da);
     }
     return launch_status(pkv::launch_mixed(g, pa, da, workspace, w_rec, (hipStream_t)stream));
 }

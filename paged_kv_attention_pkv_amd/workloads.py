@@ -104,14 +104,19 @@ class PrefillSpec:
 
 
 def deal_pages(pages_per_seq: np.ndarray, usable_pages: int, bt_cols: int,
-               rng: np.random.Generator) -> tuple[np.ndarray, int]:
-    """Block table from a seeded permutation of pages 1..usable_pages.
+               rng: np.random.Generator, contiguous: bool = False) -> tuple[np.ndarray, int]:
+    """Block table from a seeded permutation of pages 1..usable_pages (or,
+    with ``contiguous``, pages 1, 2, 3, ... in order, so that every sequence
+    owns a run of adjacent pages; the permutation is drawn either way, so the
+    generator's state afterwards does not depend on the choice).
 
     Returns (block_table, num_pages) with num_pages = usable_pages + 1."""
     need = int(pages_per_seq.sum())
     if need > usable_pages:
         raise ValueError(f"pool of {usable_pages} usable pages cannot hold {need}")
     perm = rng.permutation(usable_pages).astype(np.int64) + 1
+    if contiguous:
+        perm = np.arange(1, usable_pages + 1, dtype=np.int64)
     bt = np.zeros((pages_per_seq.shape[0], bt_cols), dtype=np.int32)
     k = 0
     for b, n in enumerate(pages_per_seq.tolist()):
@@ -123,26 +128,28 @@ def deal_pages(pages_per_seq: np.ndarray, usable_pages: int, bt_cols: int,
 
 
 def _decode_from_lengths(name, hist, n_new, hq, hkv, d, dtype, max_hist, slack, seed, rng,
-                         usable=None, layout="HND", page_size=PAGE_SIZE) -> DecodeSpec:
+                         usable=None, layout="HND", page_size=PAGE_SIZE, contiguous=False) -> DecodeSpec:
     hist = np.asarray(hist, dtype=np.int32)
     pages = np.array([_ceil_div(int(L) + n_new, page_size) for L in hist], dtype=np.int64)
     bt_cols = _ceil_div(max_hist + n_new, page_size)
     if usable is None:
         usable = int(math.ceil(slack * int(pages.sum())))
-    bt, num_pages = deal_pages(pages, usable, bt_cols, rng)
+    bt, num_pages = deal_pages(pages, usable, bt_cols, rng, contiguous)
     return DecodeSpec(name, len(hist), hq, hkv, d, dtype, hist, n_new, num_pages, bt_cols, bt,
                       seed, page_size=page_size, layout=layout)
 
 
 def decode_spec(workload: str, batch: int | None = None, seed: int | None = None,
-                layout: str = "HND", page_size: int = PAGE_SIZE) -> DecodeSpec:
+                layout: str = "HND", page_size: int = PAGE_SIZE, contiguous: bool = False) -> DecodeSpec:
     """Lengths, pool size and block table of one decode workload (pages of
-    `page_size` tokens; the named workloads use 16)."""
+    `page_size` tokens, the named workloads use 16; pages dealt shuffled, or
+    in order with `contiguous`)."""
     if workload == "tiny_f32":
         seed = 1 if seed is None else seed
         rng = np.random.default_rng(seed)
         return _decode_from_lengths("tiny_f32", [37, 80], 1, 4, 2, 64, "f32", 80, None, seed, rng,
-                                    usable=15, layout=layout, page_size=page_size)
+                                    usable=15, layout=layout, page_size=page_size,
+                                    contiguous=contiguous)
     if workload == "qwen3_decode":
         batch = 64 if batch is None else batch
         seed = 2 if seed is None else seed
@@ -150,7 +157,7 @@ def decode_spec(workload: str, batch: int | None = None, seed: int | None = None
         hist = rng.integers(512, 1024, size=batch, endpoint=True)
         return _decode_from_lengths(f"qwen3_decode_b{batch}", hist, 1, 32, 8, 128, "bf16", 1024,
                                     1.25, seed, rng, layout=layout,
-                                    page_size=page_size)
+                                    page_size=page_size, contiguous=contiguous)
     if workload == "qwen3_sweep":
         if batch is None:
             raise ValueError("qwen3_sweep needs a batch size")
@@ -160,7 +167,7 @@ def decode_spec(workload: str, batch: int | None = None, seed: int | None = None
         gen = rng.integers(0, 512, size=batch, endpoint=True)
         return _decode_from_lengths(f"qwen3_sweep_b{batch}", prompt + gen, 1, 32, 8, 128, "bf16",
                                     1024, 1.25, seed, rng, layout=layout,
-                                    page_size=page_size)
+                                    page_size=page_size, contiguous=contiguous)
     if workload == "long_ragged":
         batch = 256 if batch is None else batch
         seed = 4 if seed is None else seed
@@ -169,13 +176,13 @@ def decode_spec(workload: str, batch: int | None = None, seed: int | None = None
         hist = np.clip(np.rint(np.exp(u)), 16, 32768).astype(np.int32)
         return _decode_from_lengths(f"long_ragged_b{batch}", hist, 1, 32, 8, 128, "bf16", 32768,
                                     1.0, seed, rng, layout=layout,
-                                    page_size=page_size)
+                                    page_size=page_size, contiguous=contiguous)
     raise ValueError(f"unknown decode workload {workload!r}")
 
 
 def custom_decode_spec(hist_lens, hq: int, hkv: int, head_dim: int, dtype: str, seed: int,
                        n_new: int = 1, slack: float = 1.25, extra_cols: int = 0,
-                       layout: str = "HND", page_size: int = PAGE_SIZE) -> DecodeSpec:
+                       layout: str = "HND", page_size: int = PAGE_SIZE, contiguous: bool = False) -> DecodeSpec:
     """Decode workload with explicit cached lengths (for edge cases)."""
     rng = np.random.default_rng(seed)
     hist = np.asarray(hist_lens, dtype=np.int32)
@@ -183,7 +190,7 @@ def custom_decode_spec(hist_lens, hq: int, hkv: int, head_dim: int, dtype: str, 
     pages = np.array([_ceil_div(int(L) + n_new, page_size) for L in hist], dtype=np.int64)
     bt_cols = max(1, _ceil_div(max_hist + n_new, page_size) + extra_cols)
     usable = max(1, int(math.ceil(slack * int(pages.sum()))))
-    bt, num_pages = deal_pages(pages, usable, bt_cols, rng)
+    bt, num_pages = deal_pages(pages, usable, bt_cols, rng, contiguous)
     return DecodeSpec("custom", len(hist), hq, hkv, head_dim, dtype, hist, n_new, num_pages,
                       bt_cols, bt, seed, page_size=page_size, layout=layout)
 
@@ -191,7 +198,7 @@ def custom_decode_spec(hist_lens, hq: int, hkv: int, head_dim: int, dtype: str, 
 def prefill_spec(batch: int | None = None, seed: int | None = None, fixed_1023: bool = False,
                  q_lens=None, kv_lens=None, hq: int = 48, hkv: int = 8, head_dim: int = 256,
                  dtype: str = "bf16", layout: str = "HND", max_q: int = 4096,
-                 max_extra: int = 4096, page_size: int = PAGE_SIZE) -> PrefillSpec:
+                 max_extra: int = 4096, page_size: int = PAGE_SIZE, contiguous: bool = False) -> PrefillSpec:
     """Lengths, pool and block table of one causal prefill workload."""
     if fixed_1023:
         seed = 599 if seed is None else seed
@@ -214,7 +221,7 @@ def prefill_spec(batch: int | None = None, seed: int | None = None, fixed_1023: 
     rng = np.random.default_rng(seed + 1_000_003)
     pages = np.array([_ceil_div(int(k), page_size) for k in kv], dtype=np.int64)
     bt_cols = max(1, int(pages.max()) if pages.size else 1)
-    bt, num_pages = deal_pages(pages, max(1, int(pages.sum())), bt_cols, rng)
+    bt, num_pages = deal_pages(pages, max(1, int(pages.sum())), bt_cols, rng, contiguous)
     return PrefillSpec(name, q, kv, num_pages, bt_cols, bt, seed, hq, hkv, head_dim, dtype,
                        page_size=page_size, layout=layout)
 

@@ -112,3 +112,16 @@ def test_seeds_reproduce_every_bit():
     # another layer's inputs differ
     a, b = wl.decode_inputs(s1), wl.decode_inputs(s1, seed_offset=1)
     assert not torch.equal(a.q, b.q)
+
+
+def test_contiguous_pages_are_runs_and_keep_the_draws():
+    a = wl.decode_spec("qwen3_decode", batch=16)
+    b = wl.decode_spec("qwen3_decode", batch=16, contiguous=True)
+    assert np.array_equal(a.hist_lens, b.hist_lens) and a.num_pages == b.num_pages
+    nxt = 1
+    for row, L in zip(b.block_table, b.hist_lens + b.n_new):
+        n = -(-int(L) // b.page_size)
+        assert row[:n].tolist() == list(range(nxt, nxt + n)) and not row[n:].any()
+        nxt += n
+    for x, y in zip(wl.decode_inputs(a).q, wl.decode_inputs(b).q):
+        assert torch.equal(x, y)
