@@ -219,7 +219,10 @@ pkv_status pkv_decode_attn(const pkv_cache_desc *cache, void *out, float *lse, c
 /*
  * Same as pkv_decode_attn with an explicit number of split workers (0 =
  * automatic: one wave per resident slot of the device, and on the device
- * fewer for small calls so that each keeps at least 8 pages).  A count > 0
+ * fewer for small calls so that each keeps at least 8 (16-token page, kv
+ * head) units; with bf16 and head_dim 128, calls of fewer than 64 such units
+ * per compute unit use at most three waves per compute unit, which measured
+ * faster than four there).  A count > 0
  * is used as given (capped at the call's page count; work is cut in equal
  * shares of pages plus a fixed charge per row and kv head, so with many
  * workers some shares hold no page and those workers do nothing).  For tests of split
