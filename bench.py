@@ -117,21 +117,33 @@ def prefill_flops(spec) -> int:
     return 4 * spec.head_dim * spec.hq * pairs
 
 
-def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+# the source files each profiled kernel is compiled from: a counter summary
+# counts only while all of them are unchanged
+KERNEL_SOURCES = {
+    "decode": ["decode.hip", "decode_worker.hpp", "common.hpp", "internal.hpp"],
+    "prefill": ["prefill.hip", "prefill32.hpp", "common.hpp", "internal.hpp"],
+    "mixed": ["mixed.hip", "decode_worker.hpp", "prefill32.hpp", "common.hpp", "internal.hpp"],
+}
 
 
-def traffic_from_profile(kernel_src: str, name: str):
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "paged_kv_attention_pkv_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kind: str, name: str):
     """HBM bytes per launch from a committed counter summary, or None when it
-    is missing or was taken on another version of the kernel source."""
+    is missing or was taken on another version of the kernel's sources."""
     path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m or not t or m.group(1) != source_hash(kernel_src):
+    if not m or not t or m.group(1) != source_hash(kind):
         return None
     return float(t.group(1))
 
@@ -285,8 +297,7 @@ def bench_decode(args, torch, pkv, wl, workload):
     # in the two-launch step, per-call event brackets of the decode launches
     launch_ms = ms / L if fused else dec_mean
     achieved = acc["total"] / (launch_ms * 1e-3) / 1e9
-    traffic = traffic_from_profile(os.path.join(ROOT, "paged_kv_attention_pkv_amd", "csrc", "decode.hip"),
-                                   f"decode_kernel_{spec.name}_pmc.txt") if fused else None
+    traffic = traffic_from_profile("decode", f"decode_kernel_{spec.name}_pmc.txt") if fused else None
     result = {
         "metric": "paged decode attn: KV-read GB/s (% HBM peak) + us/call at B=64, Hq32/Hkv8/D128",
         "value": round(value, 1),
@@ -419,8 +430,7 @@ def bench_prefill(args, torch, pkv, wl, spec):
     ms, per = time_steps(torch, step, args.steps, args.warmup, not args.eager)
     mean = ms / L  # L launches per step: the timed region's HIP events give their average duration
     tfs = flops / (mean * 1e-3) / 1e12
-    traffic = traffic_from_profile(os.path.join(ROOT, "paged_kv_attention_pkv_amd", "csrc", "prefill.hip"),
-                                   f"prefill16_kernel_{spec.name}_pmc.txt")
+    traffic = traffic_from_profile("prefill", f"prefill16_kernel_{spec.name}_pmc.txt")
     # the tiling the library picks for this call, by the rule stated in
     # include/pkv.h (192 rows once ceil(total_q / 192) * Hq >= 1.5 * CUs)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
@@ -525,7 +535,9 @@ def bench_mixed(args, torch, pkv, wl):
                      "peak": BF16_MFMA_PEAK_TFS,
                      "frac": round(t_ideal / (us_m * 1e-6), 4),
                      "frac_definition": "(chunk flops / bf16 MFMA peak + decode KV bytes / HBM peak) / launch time",
-                     "traffic": None, "flops_per_launch": flops, "decode_kv_bytes_per_launch": kv_bytes},
+                     "traffic": traffic_from_profile("mixed", f"mixed_kernel_{spec.name}_pmc.txt"),
+                     "traffic_unit": "HBM bytes per launch",
+                     "flops_per_launch": flops, "decode_kv_bytes_per_launch": kv_bytes},
     }
     del mixed, separate, ws_m
     return result
@@ -735,7 +747,103 @@ def calibrate_copy(torch):
     print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": 5}))
 
 
+# --------------------------------------------------------------------------
+# profile summaries (run on the host, from rocprofv3 CSV output)
+# --------------------------------------------------------------------------
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_trace(argv):
+    """Markdown table of the library's kernels from a rocprofv3
+    ``--kernel-trace --stats`` kernel_stats.csv."""
+    p = argparse.ArgumentParser(prog="bench.py summarize-trace")
+    p.add_argument("stats_csv")
+    p.add_argument("out")
+    p.add_argument("--title", required=True)
+    p.add_argument("--command", required=True, help="the profiled command, as run from the repository root")
+    p.add_argument("--note", default="")
+    p.add_argument("--bench-json", default=None, help="the JSON line the profiled bench.py run printed")
+    a = p.parse_args(argv)
+    lines = [f"# {a.title}", "", "Command (from the repository root, on one MI355X):", "", "```", a.command, "```",
+             ""]
+    if a.note:
+        lines += [a.note, ""]
+    lines += ["| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
+    for r in _csv_rows(a.stats_csv):
+        n = r["Name"]
+        if "pkv::" not in n:
+            continue
+        short = n.split("(anonymous namespace)::")[-1].split("(")[0].replace("pkv::", "")
+        lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
+    if a.bench_json:
+        with open(a.bench_json) as f:
+            d = [json.loads(x) for x in f.read().splitlines() if x.startswith('{"metric"')][-1]
+        keep = {k: d[k] for k in ("value", "unit", "us_per_call") if k in d}
+        keep["roofline_achieved"] = d["roofline"]["achieved"]
+        keep["roofline_frac"] = d["roofline"]["frac"]
+        lines += ["", "Line printed by the profiled run (HIP events over its timed region): " + json.dumps(keep)]
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def summarize_pmc(argv):
+    """HBM bytes per launch of one kernel from two rocprofv3 counter runs
+    (FETCH_SIZE, WRITE_SIZE), each scaled by what the same counter reads for
+    a 1 GiB device copy (``bench.py --calibrate-copy`` under the same passes)."""
+    p = argparse.ArgumentParser(prog="bench.py summarize-pmc")
+    p.add_argument("fetch_csv")
+    p.add_argument("write_csv")
+    p.add_argument("copy_fetch_csv")
+    p.add_argument("copy_write_csv")
+    p.add_argument("out")
+    p.add_argument("--kernel", required=True, help="substring of the kernel's name")
+    p.add_argument("--kind", required=True, choices=sorted(KERNEL_SOURCES))
+    p.add_argument("--command", required=True, action="append",
+                   help="each profiled command, as run from the repository root")
+    a = p.parse_args(argv)
+
+    def values(path, pat):
+        return [float(r["Counter_Value"]) for r in _csv_rows(path) if pat in r["Kernel_Name"]]
+
+    fetch, write = values(a.fetch_csv, a.kernel), values(a.write_csv, a.kernel)
+    kib = 1 << 20  # KiB in the 1 GiB copy
+    cf = [v for v in values(a.copy_fetch_csv, "copyBuffer") if v > kib / 16]
+    cw = [v for v in values(a.copy_write_csv, "copyBuffer") if v > kib / 16]
+    if not (fetch and write and cf and cw):
+        raise SystemExit("summarize-pmc: a counter file holds no matching dispatch")
+    ff, fw = kib / statistics.mean(cf), kib / statistics.mean(cw)
+    medf, medw = statistics.median(fetch), statistics.median(write)
+    read_b, write_b = medf * ff * 1024, medw * fw * 1024
+    lines = [f"# HBM counters: {a.kernel}", "", "Commands (from the repository root, one MI355X, one counter per run):",
+             ""] + [f"    {c}" for c in a.command] + [
+        "",
+        "Calibration: a 1 GiB device-to-device copy reads 1 GiB and writes 1 GiB.",
+        f"  FETCH_SIZE per copy: {statistics.mean(cf):.1f} KiB -> scale {ff:.4f}",
+        f"  WRITE_SIZE per copy: {statistics.mean(cw):.1f} KiB -> scale {fw:.4f}",
+        "",
+        f"{a.kernel} dispatches: {len(fetch)} (fetch run), {len(write)} (write run)",
+        f"  FETCH_SIZE KiB per dispatch: mean {statistics.mean(fetch):.1f}, median {medf:.1f}, "
+        f"min {min(fetch):.1f}, max {max(fetch):.1f}",
+        f"  WRITE_SIZE KiB per dispatch: mean {statistics.mean(write):.1f}, median {medw:.1f}, "
+        f"min {min(write):.1f}, max {max(write):.1f}",
+        f"  scaled HBM bytes per dispatch (medians): read {read_b:.0f}, write {write_b:.0f}",
+        "",
+        "kernel sources: " + ", ".join(f"paged_kv_attention_pkv_amd/csrc/{n}" for n in KERNEL_SOURCES[a.kind]),
+        f"source_sha256_16: {source_hash(a.kind)}",
+        f"hbm_bytes_per_launch: {read_b + write_b:.0f}",
+    ]
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] in ("summarize-trace", "summarize-pmc"):
+        (summarize_trace if sys.argv[1] == "summarize-trace" else summarize_pmc)(sys.argv[2:])
+        return
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU "
