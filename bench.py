@@ -84,6 +84,9 @@ def parse():
     p.add_argument("--separate", action="store_true",
                    help="decode step as pkv_append + pkv_decode_attn (two launches) instead of the fused "
                         "pkv_append_decode_attn")
+    p.add_argument("--head-dim", type=int, default=256, help="prefill: head_dim (64, 128 or 256)")
+    p.add_argument("--hq", type=int, default=48, help="prefill: query heads")
+    p.add_argument("--hkv", type=int, default=8, help="prefill: KV heads")
     p.add_argument("--page-size", type=int, default=16, help="decode/prefill: tokens per page (16 .. 256)")
     p.add_argument("--layout", default="HND", choices=["HND", "NHD"], help="decode/prefill: pool layout")
     p.add_argument("--contiguous", action="store_true",
@@ -121,8 +124,8 @@ def prefill_flops(spec) -> int:
 # counts only while all of them are unchanged
 KERNEL_SOURCES = {
     "decode": ["decode.hip", "decode_worker.hpp", "common.hpp", "internal.hpp"],
-    "prefill": ["prefill.hip", "prefill32.hpp", "common.hpp", "internal.hpp"],
-    "mixed": ["mixed.hip", "decode_worker.hpp", "prefill32.hpp", "common.hpp", "internal.hpp"],
+    "prefill": ["prefill.hip", "common.hpp", "internal.hpp"],
+    "mixed": ["prefill.hip", "common.hpp", "internal.hpp"],
 }
 
 
@@ -430,16 +433,17 @@ def bench_prefill(args, torch, pkv, wl, spec):
     ms, per = time_steps(torch, step, args.steps, args.warmup, not args.eager)
     mean = ms / L  # L launches per step: the timed region's HIP events give their average duration
     tfs = flops / (mean * 1e-3) / 1e12
-    traffic = traffic_from_profile("prefill", f"prefill16_kernel_{spec.name}_pmc.txt")
+    traffic = traffic_from_profile("prefill", f"prefill16{'' if spec.head_dim == 256 else 'r'}_kernel_{spec.name}_pmc.txt")
     # the tiling the library picks for this call, by the rule stated in
     # include/pkv.h (192 rows once ceil(total_q / 192) * Hq >= 1.5 * CUs)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     tiling = args.prefill_rows
     if tiling == 0:
         tiling = 192 if 2 * (-(-int(spec.q_lens.sum()) // 192) * spec.hq) >= 3 * cus else 128
-    kernel = f"prefill16_kernel<256, {tiling // 16}> ({tiling} query rows per workgroup)"
+    kname = "prefill16_kernel" if spec.head_dim == 256 else "prefill16r_kernel"
+    kernel = f"{kname}<{spec.head_dim}, {tiling // 16}> ({tiling} query rows per workgroup)"
     result = {
-        "metric": "paged causal prefill attn: TFLOP/s (% bf16 MFMA peak), D256 Hq48/Hkv8",
+        "metric": f"paged causal prefill attn: TFLOP/s (% bf16 MFMA peak), D{spec.head_dim} Hq{spec.hq}/Hkv{spec.hkv}",
         "value": round(flops * L / (ms * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -530,12 +534,12 @@ def bench_mixed(args, torch, pkv, wl):
         "separate_us_per_call_over_steps": spread(per_s, 1e3 / L),
         "speedup_vs_separate": round(us_s / us_m, 3),
         "roofline": {"bound": "mfma+hbm",
-                     "kernel": "mixed_kernel<128> (decode workers, then 32-row prefill tiles)",
+                     "kernel": "prefill16r_kernel<128, 12> (decode rows packed by KV head, then the chunks' query tiles)",
                      "achieved": round(flops / (us_m * 1e-6) / 1e12, 2), "unit": "TFLOP/s",
                      "peak": BF16_MFMA_PEAK_TFS,
                      "frac": round(t_ideal / (us_m * 1e-6), 4),
                      "frac_definition": "(chunk flops / bf16 MFMA peak + decode KV bytes / HBM peak) / launch time",
-                     "traffic": traffic_from_profile("mixed", f"mixed_kernel_{spec.name}_pmc.txt"),
+                     "traffic": traffic_from_profile("mixed", f"prefill16r_kernel_{spec.name}_pmc.txt"),
                      "traffic_unit": "HBM bytes per launch",
                      "flops_per_launch": flops, "decode_kv_bytes_per_launch": kv_bytes},
     }
@@ -873,7 +877,8 @@ def main():
         result = bench_mixed(args, torch, pkv, wl)
         result.update({"n_gpus": 1, "scaling": "weak", "vs_baseline": None})
     elif args.workload == "prefill":
-        kw = dict(page_size=args.page_size, layout=args.layout, contiguous=args.contiguous)
+        kw = dict(page_size=args.page_size, layout=args.layout, contiguous=args.contiguous, head_dim=args.head_dim,
+                  hq=args.hq, hkv=args.hkv)
         spec = (wl.prefill_spec(fixed_1023=True, **kw) if args.batch is None
                 else wl.prefill_spec(batch=args.batch, **kw))
         result = bench_prefill(args, torch, pkv, wl, spec)

@@ -348,11 +348,11 @@ pkv_status pkv_prefill_attn(const pkv_cache_desc *cache, void *out, float *lse, 
  * As pkv_prefill_attn, with the query rows per workgroup chosen by the caller
  * (the outputs are the same; only the speed differs):
  *   rows_per_workgroup  0: the library's choice (what pkv_prefill_attn does);
- *                       128: 8 waves of 16 rows (head_dim 256) or 4 of 32 (64, 128);
- *                       192: 12 waves of 16 rows, head_dim 256 only.
- * Any other value, or 192 with another head_dim, gives PKV_EINVAL.  The
- * library takes 192 once the call has work for about one and a half rounds of
- * 192-row workgroups on every CU, else 128.
+ *                       128: 8 waves of 16 rows;
+ *                       192: 12 waves of 16 rows.
+ * Any other value gives PKV_EINVAL.  At head_dim 256 the library takes 192
+ * once the call has work for about one and a half rounds of 192-row
+ * workgroups on every CU, else 128; at head_dim 64 and 128 it takes 192.
  */
 pkv_status pkv_prefill_attn_ex(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
                                int32_t num_q_heads, const void *k_cache, const void *v_cache,
@@ -370,7 +370,8 @@ pkv_status pkv_prefill_attn_ex(const pkv_cache_desc *cache, void *out, float *ls
  * prefill) names the separate prefill pass as the main penalty left at large
  * batch; a serving step that runs new-prompt chunks and decode rows over one
  * pool does both here in one kernel launch, whose work list holds the decode
- * rows' split workers first and then the chunks' query tiles.
+ * rows first (one workgroup per decode row and KV head, that KV head's query
+ * heads computed together) and then the chunks' query tiles.
  *
  * The batch is ordered: requests 0 .. num_prefill-1 are prefill chunks, the
  * remaining batch - num_prefill requests are decode rows.
@@ -383,13 +384,12 @@ pkv_status pkv_prefill_attn_ex(const pkv_cache_desc *cache, void *out, float *ls
  *   max_q      host upper bound of the chunks' q_r
  * Chunk rows are causal, end-aligned: row i of a chunk sees keys
  * 0 .. kv_r - q_r + i (FlashInfer PR #9451 analysis, §1); a decode row sees
- * all kv_r keys (0 keys: out = 0, lse = -inf).  The results are those of
- * pkv_prefill_attn on the chunks and pkv_decode_attn on the decode rows.
- * bf16, head_dim 64 or 128 only (PKV_EUNSUPPORTED otherwise).  The
- * workspace (decode rows' partial results and counters) follows the decode
- * workspace's rules: zero before first use, left zero by every call, sized
- * by pkv_mixed_workspace_bytes, which depends on batch - num_prefill,
- * num_q_heads, the descriptor and the device only.
+ * all kv_r keys (0 keys: out = 0, lse = -inf).  The chunk rows are bit for
+ * bit those of pkv_prefill_attn on the chunks; the decode rows equal
+ * pkv_decode_attn's up to rounding order.  bf16, head_dim 64 or 128 only
+ * (PKV_EUNSUPPORTED otherwise).  No workspace is used: pkv_mixed_workspace_bytes
+ * returns a token size for valid arguments (0 otherwise), and the workspace
+ * arguments of pkv_mixed_attn are ignored (NULL and 0 are accepted).
  */
 size_t pkv_mixed_workspace_bytes(const pkv_cache_desc *cache, int32_t batch, int32_t num_prefill,
                                  int32_t num_q_heads);

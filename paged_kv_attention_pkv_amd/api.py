@@ -499,17 +499,13 @@ def mixed_attn(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, num_prefill
                scale: float, out=None, lse=None, workspace=None, layout: str = "HND", return_lse: bool = False):
     """pkv_mixed_attn: requests 0..num_prefill-1 are causal prefill chunks,
     the others decode rows (one query row each, the last query rows), all
-    in one launch.  Returns out (and lse when return_lse or lse is given)."""
+    in one launch (no workspace is used; one may still be passed).  Returns
+    out (and lse when return_lse or lse is given)."""
     if out is None:
         out = torch.empty_like(q)
     total_q, hq, _ = q.shape
     if lse is None and return_lse:
         lse = torch.empty((total_q, hq), dtype=torch.float32, device=q.device)
-    batch = kv_lens.shape[0]
-    if workspace is None:
-        # the decode rows' arrival counters must start at zero
-        workspace = torch.zeros(mixed_workspace_bytes(k_cache, batch, num_prefill, hq, layout), dtype=torch.uint8,
-                                device=q.device)
     _, args = _mixed_args(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, num_prefill, max_q, max_kv_len,
                           scale, out, lse, workspace, layout)
     with torch.cuda.device(q.device):
@@ -519,7 +515,7 @@ def mixed_attn(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, num_prefill
 
 
 def prepare_mixed(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, num_prefill: int, max_q: int,
-                  max_kv_len: int, scale: float, out, workspace, lse=None, layout: str = "HND") -> "PreparedCall":
+                  max_kv_len: int, scale: float, out, workspace=None, lse=None, layout: str = "HND") -> "PreparedCall":
     desc, args = _mixed_args(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, num_prefill, max_q, max_kv_len,
                              scale, out, lse, workspace, layout)
     return PreparedCall("pkv_mixed_attn", args, (k_cache, v_cache, q, out, block_table, kv_lens, qo_indptr,

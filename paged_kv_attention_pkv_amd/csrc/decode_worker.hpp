@@ -1,5 +1,5 @@
 // decode_worker.hpp -- device code of the bf16 split decode worker (included
-// by decode.hip and mixed.hip).  What it computes and how the work is cut is
+// by decode.hip).  What it computes and how the work is cut is
 // described at the top of decode.hip.
 #pragma once
 

@@ -126,9 +126,10 @@ struct PrefillArgs {
 size_t prefill_workspace(const PoolGeom &g, int batch, int hq, int total_q, int max_q, int max_kv);
 hipError_t launch_prefill(const PoolGeom &g, const PrefillArgs &args, hipStream_t stream);
 
-// Chunked prefill (pa, bf16, head_dim 64/128) and decode rows (da, no fused
-// append) in one launch; da's workspace layout is filled here.
-hipError_t launch_mixed(const PoolGeom &g, const PrefillArgs &pa, DecodeArgs da, void *workspace, int record_workers,
-                        hipStream_t stream);
+// Chunked prefill and one-row requests in one launch (bf16, head_dim 64 or
+// 128): a's requests 0 .. a.batch-1 as query tiles, then n_rows1 one-row
+// requests first_row1 .. first_row1+n_rows1-1 (a.total_q counts the rows of
+// both) packed by KV head.
+hipError_t launch_mixed(const PoolGeom &g, const PrefillArgs &a, int n_rows1, int first_row1, hipStream_t stream);
 
 }  // namespace pkv

@@ -405,7 +405,7 @@ pkv_status pkv_prefill_attn_ex(const pkv_cache_desc *cache, void *out, float *ls
     if ((st = check_heads(g, num_q_heads))) return st;
     if (g.dtype != 1) return PKV_EUNSUPPORTED;
     if (batch < 0 || total_q < 0 || max_q < 0 || max_kv_len < 0 || bt_cols < 0) return PKV_EINVAL;
-    if (rows_per_workgroup != 0 && rows_per_workgroup != 128 && !(rows_per_workgroup == 192 && g.head_dim == 256))
+    if (rows_per_workgroup != 0 && rows_per_workgroup != 128 && rows_per_workgroup != 192)
         return PKV_EINVAL;
     if (batch == 0 || total_q == 0) return batch == 0 && total_q != 0 ? PKV_EINVAL : PKV_OK;
     if (!out || !q || !k_cache || !v_cache || !block_table || !kv_lens || !qo_indptr) return PKV_EINVAL;
@@ -458,11 +458,7 @@ size_t pkv_mixed_workspace_bytes(const pkv_cache_desc *cache, int32_t batch, int
     PoolGeom g;
     if (check_desc(cache, &g) || check_heads(g, num_q_heads) || batch < 1 || num_prefill < 0 || num_prefill > batch)
         return 0;
-    const int n_dec = batch - num_prefill;
-    if (n_dec == 0) return 256;  // no decode rows: nothing is used; a token size keeps the query non-zero
-    const int w = pkv::decode_workers(current_device(), g, num_q_heads, -1, 0);
-    if (w < 1) return 0;
-    return pkv::decode_workspace(g, n_dec, num_q_heads, w);
+    return 256;  // nothing is used; a token size keeps the query non-zero for valid arguments
 }
 
 pkv_status pkv_mixed_attn(const pkv_cache_desc *cache, void *out, float *lse, const void *q, int32_t num_q_heads,
@@ -470,6 +466,8 @@ pkv_status pkv_mixed_attn(const pkv_cache_desc *cache, void *out, float *lse, co
                           const int32_t *kv_lens, const int32_t *qo_indptr, int32_t batch, int32_t num_prefill,
                           int32_t total_q, int32_t max_q, int32_t max_kv_len, float scale, void *workspace,
                           size_t workspace_bytes, void *stream) {
+    (void)workspace;  // the launch keeps no state between its workgroups
+    (void)workspace_bytes;
     PoolGeom g;
     pkv_status st = check_desc(cache, &g);
     if (st) return st;
@@ -483,12 +481,9 @@ pkv_status pkv_mixed_attn(const pkv_cache_desc *cache, void *out, float *lse, co
     if (batch == 0) return total_q == 0 ? PKV_OK : PKV_EINVAL;
     if (!out || !q || !k_cache || !v_cache || !block_table || !kv_lens || !qo_indptr) return PKV_EINVAL;
     if ((int64_t)max_kv_len > (int64_t)bt_cols * g.page_size) return PKV_EINVAL;
-    if (max_kv_len > kMaxDecodeKv) return PKV_EUNSUPPORTED;
     if (!isfinite(scale)) return PKV_EINVAL;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_EUNSUPPORTED;
-    const int dev = current_device();
-    if (dev < 0) return PKV_EDEVICE;
-    const float scale_log2 = scale * 1.4426950408889634f;
+    if (current_device() < 0) return PKV_EDEVICE;
     const int64_t pf_rows = (int64_t)total_q - n_dec;
 
     pkv::PrefillArgs pa;
@@ -504,54 +499,19 @@ pkv_status pkv_mixed_attn(const pkv_cache_desc *cache, void *out, float *lse, co
     pa.bt_cols = bt_cols;
     pa.kv_lens = kv_lens;
     pa.qo_indptr = qo_indptr;
-    pa.batch = pf_rows > 0 ? num_prefill : 0;
+    pa.batch = pf_rows > 0 ? num_prefill : 0;  // the chunks, as query tiles
     pa.hq = num_q_heads;
     pa.hkv = g.hkv;
-    pa.total_q = (int32_t)pf_rows;
+    pa.total_q = total_q;  // chunk rows, then the decode rows' one row each
     pa.max_q = max_q;
     pa.max_kv = max_kv_len;
     pa.num_pages = g.num_pages;
     pa.page_shift = g.page_shift;
     pa.causal = 1;
-    pa.scale_log2 = scale_log2;
+    pa.scale_log2 = scale * 1.4426950408889634f;
     pa.wg_rows = 0;
-
-    // decode rows: the last n_dec requests, one query row each, at query rows
-    // total_q - n_dec .. total_q - 1
-    const size_t es = 2;
-    const int64_t qrow = (int64_t)num_q_heads * g.head_dim;
-    pkv::DecodeArgs da;
-    memset(&da, 0, sizeof(da));
-    int w_rec = 0;
-    if (n_dec > 0) {
-        w_rec = pkv::decode_workers(dev, g, num_q_heads, -1, 0);
-        if (w_rec < 1) return PKV_EDEVICE;
-        const int64_t bound = (int64_t)n_dec * g.hkv * ceil_div64(max_kv_len, kSub);
-        const size_t need = pkv::decode_workspace(g, n_dec, num_q_heads, w_rec);
-        if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PKV_EWORKSPACE;
-        da.q = (const char *)q + pf_rows * qrow * es;
-        da.out = (char *)out + pf_rows * qrow * es;
-        da.lse = lse ? lse + pf_rows * num_q_heads : nullptr;
-        da.k_cache = k_cache;
-        da.v_cache = v_cache;
-        da.s_page = g.s_page;
-        da.s_head = g.s_head;
-        da.s_tok = g.s_tok;
-        da.block_table = block_table + (int64_t)num_prefill * bt_cols;
-        da.bt_cols = bt_cols;
-        da.seqlens = kv_lens + num_prefill;
-        da.batch = n_dec;
-        da.hq = num_q_heads;
-        da.hkv = g.hkv;
-        da.max_kv = max_kv_len;
-        da.num_pages = g.num_pages;
-        da.page_shift = g.page_shift;
-        da.scale_log2 = scale_log2;
-        da.workers = bound < w_rec ? (int)(bound > 0 ? bound : 1) : w_rec;
-        da.fixed_workers = 0;
-        pkv::decode_mid_cap(dev, g, w_rec, da);
-    }
-    return launch_status(pkv::launch_mixed(g, pa, da, workspace, w_rec, (hipStream_t)stream));
+    // decode rows: requests num_prefill .. batch-1, one query row each
+    return launch_status(pkv::launch_mixed(g, pa, n_dec, num_prefill, (hipStream_t)stream));
 }
 
 pkv_status pkv_route(const pkv_cache_desc *cache, const int32_t *block_table, int32_t bt_cols,

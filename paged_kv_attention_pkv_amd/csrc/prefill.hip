@@ -9,55 +9,56 @@
 // attention over the visible keys read through block_table, query head h
 // reading KV head h / G.
 //
-// Two kernels.  head_dim 256 runs prefill16_kernel (below: 16 query rows
-// per wave, 8 or 12 waves by call size, two or three per SIMD, K/V tiles
-// moved from HBM to LDS by buffer-to-LDS transfers, output rows written
-// through LDS); head_dim 64 and 128 run prefill_kernel:
+// Kernels: one workgroup per (request, tile of 128 or 192 query rows,
+// query head); each wave owns 16 query rows of the tile.  Keys are walked in
+// tiles of 64 (four 16-token blocks), staged in LDS as [key][dim] rows,
+// double-buffered, the next tile's loads in flight during the current one.
+// head_dim 256 runs prefill16_kernel, whose tiles move from HBM to LDS by
+// buffer-to-LDS transfers; head_dim 64 and 128 run prefill16r_kernel, whose
+// tiles pass through registers (their rows need a padded layout that whole
+// 1 KB transfers cannot write).  Scores carry the softmax scale folded into
+// log2 units and use exp2; Q stays in registers for the whole walk; the V^T
+// operand comes straight from the [key][dim] rows through gfx950's
+// transposing LDS read.  Keys at or past kv_r (tail slots of the last page,
+// which may hold anything) load as zeros and masked scores get -inf; tiles
+// that no row of a wave needs are skipped and tiles no row's limit cuts are
+// not masked.  Tiles are scheduled longest first (causal rows late in a
+// request see the most keys), and whole groups of the G query heads of one
+// KV head, which read the same K/V tiles, are dealt to one XCD.
 //
-// One workgroup (4 waves) per (request, tile of 128 query rows,
-// query head); wave w owns query rows 32w .. 32w+31 of the tile.  Keys are
-// walked in tiles of 64 (four pages).  Per 32 keys, for every wave:
-//   S^T[32 key x 32 q]  = K[32 x D] . Q^T[D x 32]        (D/16 MFMA 32x32x16)
-//   O^T[D x 32 q]      += V^T[D x 32 key] . P^T[32 key x 32 q]  (D/16 MFMA)
-// Query rows sit on lanes (lane % 32) so the softmax statistics of a row live
-// in two lanes (lane and lane ^ 32); scores carry the softmax scale folded
-// into log2 units and use exp2.  Q stays in registers for the whole walk.
-// K and V tiles are staged in LDS as [key][dim] rows (padded against bank
-// conflicts, double-buffered, next tile's global loads in flight during the
-// current one); the V^T operand comes straight from the [key][dim] rows
-// through gfx950's transposing LDS read.  Keys at or past kv_r (tail slots
-// of the last page, which may hold anything) are written to LDS as zeros
-// and masked scores get -inf; tiles that no row of a wave needs are skipped
-// and tiles no row's limit cuts are not masked.  Tiles are scheduled
-// longest first (causal rows late in a request see the most keys).
+// The mixed launch (pkv_mixed_attn) runs prefill16r_kernel over one work
+// list: the chunks' (request, tile, head) workgroups, then the one-row
+// (decode) requests, one workgroup per (request, KV head) computing that KV
+// head's G query heads as the rows of one 16-row block.
 #include <math.h>
 
-#include "prefill32.hpp"
+#include "common.hpp"
+#include "internal.hpp"
 
 namespace pkv {
 
 namespace {
 
-template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void prefill_kernel(PrefillArgs a, int n_qtiles) {
-    extern __shared__ __align__(16) uint16_t smem[];
-    prefill32_block<D>(a, n_qtiles, blockIdx.x, gridDim.x, smem);
-}
+constexpr float kLn2f = 0.6931471805599453f;
+constexpr float kNegInff = -__builtin_inff();
+// A row's running max is raised only when a tile's scores exceed it by more
+// than this (log2 units); weights relative to a stale max stay below 2^8, so
+// the output (normalised by the same max) is unchanged and the rescale of the
+// accumulators is skipped for most tiles.
+constexpr float kRescaleSlack = 8.f;
 
 // ---------------------------------------------------------------------------
 // 16 query rows per wave, 8 or 12 waves per workgroup
 // ---------------------------------------------------------------------------
 //
-// The same walk as prefill_kernel with v_mfma_f32_16x16x32_bf16 blocks:
+// Per 64-key tile, with v_mfma_f32_16x16x32_bf16 blocks:
 //   S^T[16 key x 16 q]  = K[16 x 32] . Q^T[32 x 16]       (D/32 k-steps per 16 keys)
 //   O^T[16 dim x 16 q] += V^T[16 dim x 32 key] . P^T[32 key x 16 q]
 // Lane (g = lane/16, c = lane%16) owns query row c of its wave; the softmax
 // statistics of a row live in lanes c, c+16, c+32, c+48 (row-swap permutes).
-// With half the rows per wave the accumulators take half the registers, so
-// several waves share each SIMD and one wave's softmax, barrier wait and LDS
-// reads overlap another's MFMAs; each K/V byte read from LDS feeds half as
-// many rows as in prefill_kernel.
+// With 16 rows per wave the accumulators take few registers, so several
+// waves share each SIMD and one wave's softmax, barrier wait and LDS reads
+// overlap another's MFMAs.
 //
 // Key order inside a 32-key PV step: lane group g takes keys 4g..4g+3 of the
 // first 16-key score block and 4g..4g+3 of the second, which is exactly where
@@ -199,7 +200,10 @@ __device__ __forceinline__ void dma_tile16(const PrefillArgs &a, int entry, int 
     }
 }
 
-// The transposing LDS read of ld_tr, written out: for the intrinsic the
+// The transposing LDS read (ds_read_b64_tr_b16: in each group of 16 lanes,
+// lane 4a+b names V[key0 + a][dim0 + 4b .. +3] and lane i of the group
+// receives dims dim0 + i at keys key0 .. key0+3, one column of V), written
+// out: for the intrinsic the
 // compiler has no alias information, so while buffer-to-LDS transfers are in
 // flight it waits for all of them (vmcnt 0) before the read, which would
 // drain the transfers running ahead.  Here the read is opaque to the
@@ -287,9 +291,13 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
     constexpr int TPW = 2 * Dma16<D>::PPW;  // transfers per wave per tile
     extern __shared__ __align__(16) uint16_t smem[];
 
-    // grid: (request, tile, head), longest tiles first, heads fastest; whole
-    // groups of the G heads of one KV head are dealt to one XCD (see
-    // prefill_kernel)
+    // grid: (request, tile, head) with tiles reversed (longest first) and
+    // heads fastest, so the G heads of one KV head, which read the same K/V
+    // tiles, are G neighbours in that order.  Workgroups are dealt to the 8
+    // XCDs round-robin by blockIdx; the remap hands each XCD whole groups of
+    // G (groups in order, round-robin over the XCDs), so a group's heads run
+    // side by side on one XCD and share its L2, and the order stays longest
+    // first.  The last partial round keeps the identity.
     const int G = a.hq / a.hkv;
     int idx = blockIdx.x;
     if (idx < (int)(gridDim.x / (8 * G)) * 8 * G) {
@@ -418,9 +426,9 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
             for (int k = 0; k < KD; ++k) read_k(k, kb[k]);
 #pragma unroll
             for (int k = 0; k < KS; ++k) {
-                // k-step k's reads are done once only the r later k-steps issued remain
-                const int r = KD - 1 < KS - 1 - k ? KD - 1 : KS - 1 - k;
-                lgkm_wait_n(NB * r, kb[k % (KD + 1)]);
+                // k-step k's reads are done once only the rr later k-steps issued remain
+                const int rr = KD - 1 < KS - 1 - k ? KD - 1 : KS - 1 - k;
+                lgkm_wait_n(NB * rr, kb[k % (KD + 1)]);
                 if (k + KD < KS) read_k(k + KD, kb[(k + KD) % (KD + 1)]);
 #pragma unroll
                 for (int u = 0; u < NB; ++u)
@@ -493,9 +501,9 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
             for (int gi = 0; gi < VD && gi < NVG; ++gi) read_v(gi, vb[gi]);
 #pragma unroll
             for (int gi = 0; gi < NVG; ++gi) {
-                // group gi's reads are done once only the r later groups issued remain
-                const int r = VD - 1 < NVG - 1 - gi ? VD - 1 : NVG - 1 - gi;
-                lgkm_wait_n(2 * VG * r, vb[gi % (VD + 1)]);
+                // group gi's reads are done once only the rr later groups issued remain
+                const int rr = VD - 1 < NVG - 1 - gi ? VD - 1 : NVG - 1 - gi;
+                lgkm_wait_n(2 * VG * rr, vb[gi % (VD + 1)]);
                 if (gi + VD < NVG) read_v(gi + VD, vb[(gi + VD) % (VD + 1)]);
                 const int t = gi / (DB / VG), db0 = (gi % (DB / VG)) * VG;
 #pragma unroll
@@ -547,6 +555,353 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// 16 query rows per wave for head_dim 64 and 128: tiles through registers
+// ---------------------------------------------------------------------------
+//
+// prefill16_kernel's walk (the same MFMA blocks, lane roles, softmax, P^T key
+// order and output path) for head_dims whose rows are too short for its
+// row-pair transfer layout.  The first 8 waves load each 64-key tile from HBM
+// into registers (16-byte chunks, each wave-instruction within one page, so
+// one buffer resource per instruction zero-fills keys at or past kv) while the
+// tile before is computed, and then write it into the other LDS stage; one
+// barrier per tile.  The page-table entries a loading wave needs are read one
+// tile earlier still, so no table read waits in front of a tile's loads.
+//
+// LDS rows are padded to D + 16 elements (288 or 160 bytes).  Measured on the
+// device with a probe of the kernel's two read patterns (16 rows x 16 bytes
+// per K operand read, 4 rows x 32 bytes per group of a transposing V^T read):
+// both run at the conflict-free rate when the row stride is 32 mod 64 bytes,
+// and at half that rate or less for strides of 0, 16 or 48 mod 64 and for
+// shifted or XOR-swizzled variants of them.
+template <int D>
+struct Reg16 {
+    static_assert(D == 64 || D == 128, "the register-staged 16-row kernel is for head_dim 64 and 128");
+    static_assert(((D + 16) * 2) % 64 == 32, "row stride 32 mod 64 bytes");
+    static constexpr int RS = D + 16;              // LDS elements per K or V row
+    static constexpr int TILE = kBN16 * RS;        // one of K or V
+    static constexpr int BUF = 2 * TILE;           // K then V, one stage
+    static constexpr int BYTES = kNST16 * BUF * 2;  // kNST16 stages of bf16
+    static constexpr int CPK = D / 8;              // 16-byte chunks per key row
+    static constexpr int LOADERS = 8;              // waves that load the tiles
+    static constexpr int CHUNKS = kBN16 * CPK / (LOADERS * kWave);  // per loading lane, of K and of V
+    static constexpr int PAGES = CHUNKS;           // one page per load instruction of a wave
+    static_assert(CHUNKS >= 1 && kBN16 * CPK == CHUNKS * LOADERS * kWave, "tile split");
+    static_assert(kWave / CPK <= kPage, "a load instruction stays within one page");
+};
+
+__device__ __forceinline__ int reg16_row(int r, int rs) { return r * rs; }
+
+template <int D>
+struct Reg16Tile {
+    u32x4 k[Reg16<D>::CHUNKS], v[Reg16<D>::CHUNKS];
+};
+
+// 16-token block of key tile `tile` that load instruction i of loading wave w reads
+template <int D>
+__device__ __forceinline__ int reg16_block(int tile, int wave, int i) {
+    using R = Reg16<D>;
+    return tile * (kBN16 / kPage) + ((kWave * wave + R::LOADERS * kWave * i) / R::CPK) / kPage;
+}
+
+template <int D>
+__device__ __forceinline__ void reg16_load(const PrefillArgs &a, const int (&pg_ids)[Reg16<D>::PAGES], int g,
+                                           int tile, int wave, int kv, Reg16Tile<D> &t) {
+    using R = Reg16<D>;
+    const int lane = threadIdx.x & 63;
+    const int64_t tok_bytes = a.s_tok * 2;
+#pragma unroll
+    for (int i = 0; i < R::CHUNKS; ++i) {
+        const int blk = reg16_block<D>(tile, wave, i);
+        const int valid = min(max(kv - blk * kPage, 0), kPage);
+        int pg = valid > 0 ? pg_ids[i] : 0;
+        pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+        const int64_t sub = blk & ((1 << a.page_shift) - 1);
+        const int64_t off = uniform64(((int64_t)pg * a.s_page + (int64_t)g * a.s_head + sub * kPage * a.s_tok) * 2);
+        const int32_t bytes = uniform((int)(valid * tok_bytes));
+        const Rsrc rk = make_rsrc((const char *)a.k_cache + off, bytes);
+        const Rsrc rv = make_rsrc((const char *)a.v_cache + off, bytes);
+        const int c = kWave * wave + R::LOADERS * kWave * i + lane;  // chunk of the tile
+        const int key = c / R::CPK;
+        const uint32_t voff = (uint32_t)((key & (kPage - 1)) * tok_bytes) + (uint32_t)(c % R::CPK) * 16u;
+        t.k[i] = bld16(rk, voff);
+        t.v[i] = bld16(rv, voff);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void reg16_store(uint16_t *buf, const Reg16Tile<D> &t, int wave) {
+    using R = Reg16<D>;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < R::CHUNKS; ++i) {
+        const int c = kWave * wave + R::LOADERS * kWave * i + lane;
+        const int key = c / R::CPK;
+        const int e = reg16_row(key, R::RS) + 8 * (c % R::CPK);
+        *reinterpret_cast<u32x4 *>(buf + e) = t.k[i];
+        *reinterpret_cast<u32x4 *>(buf + R::TILE + e) = t.v[i];
+    }
+}
+
+// the raw table entries of key tile `tile` for loading wave w (0 past the row's last block)
+template <int D>
+__device__ __forceinline__ void reg16_ids(const PrefillArgs &a, const int32_t *bt, int tile, int wave, int kv,
+                                          int (&ids)[Reg16<D>::PAGES]) {
+    const int last = (kv - 1) / kPage;
+#pragma unroll
+    for (int i = 0; i < Reg16<D>::PAGES; ++i) {
+        const int blk = reg16_block<D>(tile, wave, i);
+        ids[i] = blk <= last ? bt[blk >> a.page_shift] : 0;
+    }
+}
+
+template <int D, int W>
+__global__ __launch_bounds__(Cfg16<W>::THREADS) __attribute__((amdgpu_waves_per_eu(Cfg16<W>::PER_SIMD,
+                                                                                   Cfg16<W>::PER_SIMD)))
+void prefill16r_kernel(PrefillArgs a, int n_qtiles, int n_packed, int packed_first) {
+    using R = Reg16<D>;
+    using C = Cfg16<W>;
+    constexpr int kBM16 = C::BM;
+    constexpr int KS = D / 32;      // k-steps of the QK contraction
+    constexpr int DB = D / 16;      // 16-dim blocks of the output
+    constexpr int NB = kBN16 / 16;  // 16-key score blocks per tile
+    extern __shared__ __align__(16) uint16_t smem[];
+
+    // The last n_packed workgroups serve one-row requests packed by KV head:
+    // packed workgroup p takes request packed_first + p / Hkv and KV head
+    // p % Hkv, and its wave 0 computes the G query heads of that KV head as
+    // the rows of its 16-row block (lane row c is head g*G + c; every head of
+    // a one-row request sees the same keys), the other waves only load tiles.
+    // They come after the query tiles (ordered longest first), whose ragged
+    // end they fill.  The others: grid as in prefill16_kernel, over requests
+    // 0 .. batch-1.
+    const int G = a.hq / a.hkv;
+    const int n = (int)gridDim.x - n_packed;  // query-tile workgroups
+    const bool packed = (int)blockIdx.x >= n;
+    int r, qt, h, g;
+    if (packed) {
+        const int pk = (int)blockIdx.x - n;
+        r = packed_first + pk / a.hkv;
+        g = pk - (r - packed_first) * a.hkv;
+        qt = 0;
+        h = g * G;
+    } else {
+        int idx = (int)blockIdx.x;
+        if (idx < (n / (8 * G)) * 8 * G) {
+            const int k = idx >> 3;
+            idx = ((k / G) * 8 + (idx & 7)) * G + k % G;
+        }
+        const int per_req = n_qtiles * a.hq;
+        r = idx / per_req;
+        const int rem = idx - r * per_req;
+        qt = n_qtiles - 1 - rem / a.hq;
+        h = rem - (rem / a.hq) * a.hq;
+        g = h / G;
+    }
+    const int32_t *bt = a.block_table + (int64_t)r * a.bt_cols;
+    const int q0 = min(max(a.qo_indptr[r], 0), a.total_q);
+    const int q_len = min(max(a.qo_indptr[r + 1] - q0, 0), a.total_q - q0);
+    if (qt * kBM16 >= q_len) return;
+    const int kv = min(max(a.kv_lens[r], 0), a.max_kv);
+
+    const int wave = uniform(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int grp = lane >> 4;
+    const int col = lane & 15;
+    // packed: row c of wave 0 is query position 0 of head g*G + c; the other
+    // waves hold no row (their first row lies past the request)
+    const int head = packed ? h + min(col, G - 1) : h;
+    const int i_row = packed ? (wave == 0 && col < G ? 0 : q_len) : qt * kBM16 + wave * kRows16 + col;
+    const bool row_ok = i_row < q_len;
+    const int i_eff = row_ok ? i_row : q_len - 1;
+    const int limit = a.causal ? kv - q_len + i_eff : kv - 1;
+
+    const int i_last_wg = packed ? 0 : min(qt * kBM16 + kBM16, q_len) - 1;
+    const int last_key_wg = a.causal ? kv - q_len + i_last_wg : kv - 1;
+    const int n_tiles = last_key_wg / kBN16 + 1;
+    const int wave_first = packed ? (wave == 0 ? 0 : q_len) : qt * kBM16 + wave * kRows16;
+    const int i_last_wave = packed ? 0 : min(wave_first + kRows16, q_len) - 1;
+    const int last_key_wave = wave_first >= q_len ? -1 : (a.causal ? kv - q_len + i_last_wave : kv - 1);
+    const int common_keys = wave_first >= q_len ? -1 : (a.causal ? kv - q_len + wave_first : kv - 1);
+    if (kv == 0 || (a.causal && kv < q_len)) {
+        if (row_ok) {
+            uint16_t *orow = (uint16_t *)a.out + ((int64_t)(q0 + i_row) * a.hq + head) * D;
+            for (int d = grp; d < D; d += 4) orow[d] = 0;
+            if (grp == 0 && a.lse) a.lse[(int64_t)(q0 + i_row) * a.hq + head] = kNegInff;
+        }
+        return;
+    }
+
+    const bool loader = wave < R::LOADERS;
+    int ids[R::PAGES];
+    Reg16Tile<D> regs;
+    if (loader) {
+        reg16_ids<D>(a, bt, 0, wave, kv, ids);
+        reg16_load<D>(a, ids, g, 0, wave, kv, regs);
+        if (n_tiles > 1) reg16_ids<D>(a, bt, 1, wave, kv, ids);
+    }
+    // Q^T operand: lane holds Q[row][32ks + 8grp .. +7] for every k-step
+    u32x4 qop[KS];
+    {
+        const uint16_t *qrow = (const uint16_t *)a.q + ((int64_t)(q0 + i_eff) * a.hq + head) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qop[ks] = ld16(qrow + 32 * ks + 8 * grp);
+    }
+    f32x4 acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = kNegInff, l = 0.f;  // l: this lane's part of the row sum
+    const float c = a.scale_log2;
+    // K operand: row 16u + col, dims 32k + 8grp; V^T transposing reads: lane
+    // 4a+b of its group names key 32t + 4grp + a (and +16), dims 16db + 4b
+    const int k_base = reg16_row(col, R::RS) + 8 * grp;
+    const int v_base = reg16_row(4 * grp + (col >> 2), R::RS) + 4 * (col & 3);
+    if (loader) reg16_store<D>(smem, regs, wave);
+    __syncthreads();
+    for (int tile = 0; tile < n_tiles; ++tile) {
+        uint16_t *cur = smem + (tile & 1) * R::BUF;
+        uint16_t *nxt = smem + ((tile + 1) & 1) * R::BUF;
+        const bool more = tile + 1 < n_tiles;
+        if (loader && more) {
+            reg16_load<D>(a, ids, g, tile + 1, wave, kv, regs);
+            if (tile + 2 < n_tiles) reg16_ids<D>(a, bt, tile + 2, wave, kv, ids);
+        }
+
+        if (tile * kBN16 <= last_key_wave) {
+            const uint16_t *ks = cur;
+            const uint16_t *vs = cur + R::TILE;
+            constexpr int KD = C::KD < KS ? C::KD : KS;
+            static_assert(NB * KD <= 15, "LDS read counter");
+            f32x4 sc[NB];
+#pragma unroll
+            for (int u = 0; u < NB; ++u) sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            u32x4 kb[KD + 1][NB];
+            __builtin_amdgcn_s_setprio(1);
+            const uint32_t ka = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t *)ks +
+                                2u * (uint32_t)k_base;
+            auto read_k = [&](int k, u32x4 (&dst)[NB]) {
+#pragma unroll
+                for (int u = 0; u < NB; ++u) dst[u] = ld_lds128(ka, 2u * (uint32_t)(16 * u * R::RS + 32 * k));
+            };
+#pragma unroll
+            for (int k = 0; k < KD; ++k) read_k(k, kb[k]);
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                const int rr = KD - 1 < KS - 1 - k ? KD - 1 : KS - 1 - k;
+                lgkm_wait_n(NB * rr, kb[k % (KD + 1)]);
+                if (k + KD < KS) read_k(k + KD, kb[(k + KD) % (KD + 1)]);
+#pragma unroll
+                for (int u = 0; u < NB; ++u)
+                    sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[k % (KD + 1)][u]),
+                                                                    __builtin_bit_cast(bf16x8, qop[k]), sc[u], 0, 0, 0);
+            }
+            __builtin_amdgcn_s_setprio(0);
+            // scores in log2 units; element i of block u is key tile*64 + 16u + 4grp + i
+            const bool need_mask = tile * kBN16 + kBN16 - 1 > common_keys;
+            float mx = kNegInff;
+#pragma unroll
+            for (int u = 0; u < NB; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float x = sc[u][i] * c;
+                    if (need_mask) {
+                        const int j = tile * kBN16 + 16 * u + 4 * grp + i;
+                        x = j <= limit ? x : kNegInff;
+                    }
+                    sc[u][i] = x;
+                    mx = fmaxf(mx, x);
+                }
+            mx = rows4_max(mx);
+            const bool raise = mx > m + kRescaleSlack;
+            if (__any(raise)) {
+                const float mn = raise ? mx : m;
+                const float alpha = fast_exp2(m - mn);
+                l *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+                m = mn;
+            }
+            u32x4 pop[NB / 2];
+#pragma unroll
+            for (int t = 0; t < NB / 2; ++t) {
+                float p[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[i] = fast_exp2(sc[2 * t][i] - m);
+                    p[4 + i] = fast_exp2(sc[2 * t + 1][i] - m);
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) l += p[i];
+                pop[t] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                               pack_bf16x2(p[6], p[7])};
+            }
+            constexpr int VG = C::VG, VD = C::VD;
+            static_assert(DB % VG == 0 && 2 * VG * VD <= 15, "LDS read counter");
+            constexpr int NVG = (NB / 2) * (DB / VG);
+            u32x4 vb[VD + 1][VG];
+            __builtin_amdgcn_s_setprio(1);
+            const uint32_t va = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint16_t *)vs +
+                                2u * (uint32_t)v_base;
+            auto read_v = [&](int gi, u32x4 (&dst)[VG]) {
+                const int t = gi / (DB / VG), db0 = (gi % (DB / VG)) * VG;
+#pragma unroll
+                for (int j = 0; j < VG; ++j) {
+                    const uint32_t off = 2u * (uint32_t)(32 * t * R::RS + 16 * (db0 + j));
+                    const u32x2 lo = ld_tr_lds(va, off);
+                    const u32x2 hi = ld_tr_lds(va, off + 2u * 16u * R::RS);
+                    dst[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                }
+            };
+#pragma unroll
+            for (int gi = 0; gi < VD && gi < NVG; ++gi) read_v(gi, vb[gi]);
+#pragma unroll
+            for (int gi = 0; gi < NVG; ++gi) {
+                const int rr = VD - 1 < NVG - 1 - gi ? VD - 1 : NVG - 1 - gi;
+                lgkm_wait_n(2 * VG * rr, vb[gi % (VD + 1)]);
+                if (gi + VD < NVG) read_v(gi + VD, vb[(gi + VD) % (VD + 1)]);
+                const int t = gi / (DB / VG), db0 = (gi % (DB / VG)) * VG;
+#pragma unroll
+                for (int j = 0; j < VG; ++j)
+                    acc[db0 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, vb[gi % (VD + 1)][j]), __builtin_bit_cast(bf16x8, pop[t]),
+                        acc[db0 + j], 0, 0, 0);
+            }
+            __builtin_amdgcn_s_setprio(0);
+        }
+        if (more) {
+            if (loader) reg16_store<D>(nxt, regs, wave);
+            __syncthreads();
+        }
+    }
+
+    // normalise and write through LDS, as prefill16_kernel
+    const float lt = rows4_sum(l);
+    const float inv = 1.f / lt;
+    constexpr int OS = D + 8;
+    static_assert(kWaves16Max * kRows16 * OS * 2 <= Reg16<D>::BYTES, "output block fits the stages");
+    __syncthreads();
+    uint16_t *ob = smem + wave * kRows16 * OS;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        const u32x2 v = {pack_bf16x2(acc[db][0] * inv, acc[db][1] * inv),
+                         pack_bf16x2(acc[db][2] * inv, acc[db][3] * inv)};
+        *reinterpret_cast<u32x2 *>(ob + col * OS + 16 * db + 4 * grp) = v;
+    }
+    if (row_ok && grp == 0 && a.lse) a.lse[(int64_t)(q0 + i_row) * a.hq + head] = (m + log2f(lt)) * kLn2f;
+    constexpr int LPR = D / 8;
+    constexpr int RPI = kWave / LPR;
+#pragma unroll
+    for (int j = 0; j < kRows16 / RPI; ++j) {
+        const int rr = RPI * j + lane / LPR;
+        const int ch = lane % LPR;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(ob + rr * OS + 8 * ch);
+        // packed: block row rr is head h + rr of query position 0
+        const bool keep = packed ? (wave == 0 && rr < G) : wave_first + rr < q_len;
+        const int64_t orow = packed ? (int64_t)q0 * a.hq + h + rr : (int64_t)(q0 + wave_first + rr) * a.hq + h;
+        if (keep) __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>((uint16_t *)a.out + orow * D + 8 * ch));
+    }
+}
+
 template <int D, int W>
 hipError_t launch16_d(const PrefillArgs &a, hipStream_t stream) {
     constexpr int kSmem16 = Dma16<D>::BYTES + kIds16 * 4;
@@ -562,45 +917,69 @@ hipError_t launch16_d(const PrefillArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Query rows per workgroup of the 16-row kernel when the caller leaves the
-// choice to the library: 192 once the call has work for about one and a half
-// rounds of 192-row workgroups on every CU (counted from total_q, which
-// ragged tails only raise), else 128, whose finer tiles end closer together.
-// Measured: the single 1023-row request (1.1 rounds) runs faster at 128, two
-// requests of 910 and 627 rows (1.7 rounds) already at 192.
-int auto_wg_rows16(const PrefillArgs &a) {
+// Query rows per workgroup of the 16-row kernels when the caller leaves the
+// choice to the library.  head_dim 256: 192 once the call has work for about
+// one and a half rounds of 192-row workgroups on every CU (counted from
+// total_q, which ragged tails only raise), else 128, whose finer tiles end
+// closer together (measured: the single 1023-row request, 1.1 rounds, runs
+// faster at 128; two requests of 910 and 627 rows, 1.7 rounds, already at
+// 192).  head_dim 64 and 128: always 192 (measured faster on every workload
+// timed, the single 1023-row request included: 34.1 vs 36.0 us at 128).
+int auto_wg_rows16(const PrefillArgs &a, int head_dim) {
+    if (head_dim != 256) return Cfg16<12>::BM;
     const int cus = current_device_cus();
     if (cus <= 0) return -1;
     const int64_t wgs192 = ((int64_t)a.total_q + Cfg16<12>::BM - 1) / Cfg16<12>::BM * a.hq;
     return 2 * wgs192 >= 3 * (int64_t)cus ? Cfg16<12>::BM : Cfg16<8>::BM;
 }
 
-// head_dim 256 runs the 16-row kernel, 64 and 128 the 32-row kernel
+// a.batch requests as (request, tile, head) workgroups, after n_packed_rows
+// one-row requests (packed_first ..) as (request, KV head) workgroups
+template <int D, int W>
+hipError_t launch16r_d(const PrefillArgs &a, hipStream_t stream, int n_packed_rows = 0, int packed_first = 0) {
+    constexpr int kSmem = Reg16<D>::BYTES;
+    constexpr int BM = Cfg16<W>::BM;
+    const int n_qtiles = a.batch > 0 ? (a.max_q + BM - 1) / BM : 0;
+    const int64_t n_packed = (int64_t)n_packed_rows * a.hkv;
+    const int64_t grid = (int64_t)a.batch * n_qtiles * a.hq + n_packed;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    if (grid == 0) return hipSuccess;
+    static std::atomic<uint64_t> attr_set{0};
+    hipError_t e = set_smem_once(reinterpret_cast<const void *>(&prefill16r_kernel<D, W>), kSmem, attr_set);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((prefill16r_kernel<D, W>), dim3((unsigned)grid), dim3(Cfg16<W>::THREADS), kSmem, stream, a,
+                       n_qtiles, (int)n_packed, packed_first);
+    return hipGetLastError();
+}
+
+// every head_dim runs a 16-row kernel: 256 with its transfer layout, 64 and
+// 128 with register-staged tiles
 template <int D>
 hipError_t launch_d(const PrefillArgs &a, hipStream_t stream) {
+    const int rows = a.wg_rows > 0 ? a.wg_rows : auto_wg_rows16(a, D);
+    if (rows < 0) return hipErrorInvalidDevice;
     if constexpr (D == 256) {
-        const int rows = a.wg_rows > 0 ? a.wg_rows : auto_wg_rows16(a);
-        if (rows < 0) return hipErrorInvalidDevice;
         if (rows == Cfg16<12>::BM) return launch16_d<D, 12>(a, stream);
         if (rows == Cfg16<8>::BM) return launch16_d<D, 8>(a, stream);
         return hipErrorInvalidValue;
     } else {
-        if (a.wg_rows != 0 && a.wg_rows != kBM) return hipErrorInvalidValue;
-        const int n_qtiles = (a.max_q + kBM - 1) / kBM;
-        const int64_t grid = (int64_t)a.batch * n_qtiles * a.hq;
-        if (grid > 0x7fffffff) return hipErrorInvalidValue;
-        static std::atomic<uint64_t> attr_set{0};
-        hipError_t e = set_smem_once(reinterpret_cast<const void *>(&prefill_kernel<D>), Smem<D>::BYTES, attr_set);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(prefill_kernel<D>, dim3((unsigned)grid), dim3(kThreads), Smem<D>::BYTES, stream, a,
-                           n_qtiles);
-        return hipGetLastError();
+        if (rows == Cfg16<12>::BM) return launch16r_d<D, 12>(a, stream);
+        if (rows == Cfg16<8>::BM) return launch16r_d<D, 8>(a, stream);
+        return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
 size_t prefill_workspace(const PoolGeom &, int, int, int, int, int) { return 0; }
+
+hipError_t launch_mixed(const PoolGeom &g, const PrefillArgs &a, int n_rows1, int first_row1, hipStream_t stream) {
+    switch (g.head_dim) {
+        case 64: return launch16r_d<64, 12>(a, stream, n_rows1, first_row1);
+        case 128: return launch16r_d<128, 12>(a, stream, n_rows1, first_row1);
+    }
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_prefill(const PoolGeom &g, const PrefillArgs &a, hipStream_t stream) {
     if (a.max_q <= 0 || a.batch <= 0) return hipSuccess;

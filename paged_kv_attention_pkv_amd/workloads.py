@@ -204,7 +204,7 @@ def prefill_spec(batch: int | None = None, seed: int | None = None, fixed_1023: 
         seed = 599 if seed is None else seed
         q = np.array([1023], dtype=np.int32)
         kv = np.array([1023], dtype=np.int32)
-        name = "prefill_d256_b1_q1023"
+        name = f"prefill_d{head_dim}_b1_q1023"
     elif q_lens is not None:
         seed = 0 if seed is None else seed
         q = np.asarray(q_lens, dtype=np.int32)
@@ -217,7 +217,7 @@ def prefill_spec(batch: int | None = None, seed: int | None = None, fixed_1023: 
         rng0 = np.random.default_rng(seed)
         q = rng0.integers(65, max_q, size=batch, endpoint=True).astype(np.int32)
         kv = (q + rng0.integers(0, max_extra, size=batch, endpoint=True)).astype(np.int32)
-        name = f"prefill_d256_b{batch}"
+        name = f"prefill_d{head_dim}_b{batch}"
     rng = np.random.default_rng(seed + 1_000_003)
     pages = np.array([_ceil_div(int(k), page_size) for k in kv], dtype=np.int64)
     bt_cols = max(1, int(pages.max()) if pages.size else 1)

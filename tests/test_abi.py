@@ -124,7 +124,7 @@ def test_prefill_rejects_scalars():
 
 
 def test_prefill_ex_rejects_tilings():
-    """rows_per_workgroup is 0, 128, or 192 at head_dim 256 only."""
+    """rows_per_workgroup is 0, 128 or 192 (any head_dim)."""
     lib = api.lib()
     call = lambda desc, rows: lib.pkv_prefill_attn_ex(
         ctypes.byref(desc), FAKE, None, FAKE, 48, FAKE, FAKE, FAKE, 300, FAKE, FAKE, 2, 10, 8, 4096, 1, 0.0625,
@@ -133,7 +133,7 @@ def test_prefill_ex_rejects_tilings():
     d128 = _desc(head_dim=128, s_page=8 * 16 * 128, s_head=16 * 128, s_tok=128)
     for rows in (-1, 1, 64, 127, 256, 384):
         assert call(d256, rows) == EINVAL, rows
-    assert call(d128, 192) == EINVAL
+        assert call(d128, rows) == EINVAL, rows
 
 
 def _cpu_pool(num_pages=10):

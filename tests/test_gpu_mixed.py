@@ -1,7 +1,8 @@
 """GPU parity of pkv_mixed_attn: chunked prefill requests and decode rows of
 one batch in one launch, against the oracle (every decode row, chunk rows
-all or tile-edge sampled) and, bit for bit, against pkv_prefill_attn on the
-chunks plus pkv_decode_attn on the decode rows (the same kernels' code)."""
+all or tile-edge sampled) and against the separate calls: bit for bit with
+pkv_prefill_attn on the chunks (the same query tiles), within the bf16 bar
+of pkv_decode_attn on the decode rows (the same sums cut another way)."""
 import numpy as np
 import pytest
 import torch
@@ -49,9 +50,12 @@ def test_mixed_small_all_rows(d):
     _check(spec, 3)
 
 
-def test_mixed_equals_separate_calls_bitwise():
-    """The mixed launch runs the prefill tiles and decode workers of the
-    separate calls: outputs and lse bit for bit equal."""
+def test_mixed_equals_separate_calls():
+    """Chunk rows and their lse bit for bit equal to pkv_prefill_attn on the
+    chunks (the launch runs the same query tiles); decode rows within the
+    bf16 bar of pkv_decode_attn (a KV head's query heads as one 16-row block
+    walking the keys in 64-key tiles, against the decode kernel's split
+    workers)."""
     spec = wl.mixed_spec(num_decode=40, num_chunks=3, seed=701, max_chunk=600, max_extra=900)
     case, kc, vc, kv, out, lse = _check(spec, 3)
     i, s = case.inp, spec
@@ -64,8 +68,8 @@ def test_mixed_equals_separate_calls_bitwise():
     torch.cuda.synchronize()
     assert torch.equal(out[:npf].view(torch.int16), po.view(torch.int16)), "chunk rows differ from pkv_prefill_attn"
     assert torch.equal(lse[:npf], pl), "chunk lse differs"
-    assert torch.equal(out[npf:].view(torch.int16), do.view(torch.int16)), "decode rows differ from pkv_decode_attn"
-    assert torch.equal(lse[npf:], dl), "decode lse differs"
+    compare(out[npf:].cpu(), do.float().cpu().double().numpy(), *BF16_TOL, "decode rows vs pkv_decode_attn")
+    compare(lse[npf:].cpu(), dl.cpu().double().numpy(), *BF16_TOL, "decode lse vs pkv_decode_attn")
 
 
 def test_mixed_full_size_qwen3():

@@ -56,7 +56,19 @@ def test_d256_tilings_ragged(rows, hq, hkv):
     _parity(spec, rows=rows)
 
 
-@pytest.mark.parametrize("d,rows", [(128, 0), (256, 128), (256, 192)])
+@pytest.mark.parametrize("rows", [128, 192])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (32, 8)])
+def test_d64_d128_tilings_ragged(d, rows, hq, hkv):
+    """Both workgroup tilings of head_dim 64 and 128 (8 and 12 waves of 16
+    rows), with requests ending inside, at and just past the tiles."""
+    q = [1, 17, 191, 192, 193, 255, 256, 257, 400, 129]
+    kv = [1, 17, 300, 192, 611, 255, 700, 257, 900, 129]
+    spec = wl.prefill_spec(q_lens=q, kv_lens=kv, hq=hq, hkv=hkv, head_dim=d, seed=rows + hq + d)
+    _parity(spec, rows=rows)
+
+
+@pytest.mark.parametrize("d,rows", [(128, 0), (128, 128), (64, 192), (256, 128), (256, 192)])
 def test_non_causal(d, rows):
     spec = wl.prefill_spec(q_lens=[3, 64, 130], kv_lens=[50, 64, 400], hq=12, hkv=4, head_dim=d, seed=7)
     _parity(spec, causal=False, rows=rows)
