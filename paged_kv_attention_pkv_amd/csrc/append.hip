@@ -109,23 +109,7 @@ __global__ __launch_bounds__(256) void route_kernel(const int32_t *__restrict__ 
 // of the 2P values A:B.  Either way the pairs are i = P*c + e, whose table
 // entries are contiguous.
 
-// fp64 -> bf16 bits, nearest with ties to even: scale the value so that its
-// quantum (8 significant bits, subnormal quantum 2^-133 below 2^-126) is 1,
-// round to the nearest integer (ties to even) and scale back (exact powers
-// of two); magnitudes from 2^128 on are infinities.
-__device__ __forceinline__ uint32_t bf16_bits_rne(double v) {
-    float f;
-    if (__builtin_isnan(v) || v == 0.0 || __builtin_isinf(v)) {
-        f = (float)v;
-    } else {
-        int e;
-        (void)frexp(v, &e);
-        const int qexp = (e < -125 ? -125 : e) - 8;
-        const double r = ldexp(rint(ldexp(v, -qexp)), qexp);
-        f = fabs(r) >= 0x1p128 ? (r > 0 ? __builtin_inff() : -__builtin_inff()) : (float)r;  // exact
-    }
-    return __float_as_uint(f) >> 16;
-}
+// (bf16_bits_rne, the rounding, is in common.hpp.)
 
 template <int ES>
 struct RopeElems;

@@ -2,12 +2,13 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 namespace pkv {
 
 constexpr int kWave = 64;
-constexpr int kPage = 16;  // tokens per page (the only page size supported)
+constexpr int kPage = 16;  // tokens per block: pages of 32..256 tokens are walked as runs of 16
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -109,6 +110,27 @@ __device__ __forceinline__ u32x2 ld8_stream(const void *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
 }
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+
+// fp64 -> bf16 bits, nearest with ties to even, without library calls: the
+// value is first rounded to fp32 toward zero with the last bit set when that
+// step is inexact (round to odd: fp32 keeps 16 more bits than bf16, so the
+// second rounding cannot create a tie or move one), then the fp32 bits are
+// rounded to nearest even at bit 16.  Both steps act on bit patterns, so
+// fp32 subnormals, overflow to infinity and signed zeros come out as the
+// correctly rounded bf16; a NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t bf16_bits_rne(double v) {
+    float f = (float)v;  // nearest
+    double back = (double)f;
+    if (fabs(back) > fabs(v)) {  // rounded away from zero: one step back (|f| > 0 here)
+        f = __uint_as_float(__float_as_uint(f) - 1u);
+        back = (double)f;
+    }
+    uint32_t u = __float_as_uint(f);
+    if (v != v) return (u >> 16) | 0x40u;
+    if (back != v) u |= 1u;  // inexact: round to odd
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
 
 // Partial results travel between workgroups on different XCDs (each with its
 // own L2).  They are written and read with agent-scope atomic accesses,
