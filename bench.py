@@ -771,18 +771,31 @@ def summarize_trace(argv):
     p.add_argument("--command", required=True, help="the profiled command, as run from the repository root")
     p.add_argument("--note", default="")
     p.add_argument("--bench-json", default=None, help="the JSON line the profiled bench.py run printed")
+    p.add_argument("--trace-csv", default=None,
+                   help="kernel_trace.csv of the same run: rows per (kernel, grid size) instead of per kernel")
     a = p.parse_args(argv)
     lines = [f"# {a.title}", "", "Command (from the repository root, on one MI355X):", "", "```", a.command, "```",
              ""]
     if a.note:
         lines += [a.note, ""]
-    lines += ["| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
-    for r in _csv_rows(a.stats_csv):
-        n = r["Name"]
-        if "pkv::" not in n:
-            continue
-        short = n.split("(anonymous namespace)::")[-1].split("(")[0].replace("pkv::", "")
-        lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
+    shorten = lambda n: n.split("(anonymous namespace)::")[-1].split("(")[0].replace("pkv::", "")
+    if a.trace_csv:
+        groups = {}
+        for r in _csv_rows(a.trace_csv):
+            if "pkv::" not in r["Kernel_Name"]:
+                continue
+            key = (shorten(r["Kernel_Name"]), int(r["Grid_Size_X"]))
+            groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        lines += ["| kernel | grid (work-items) | calls | average ns | min ns | max ns |", "|---|---|---|---|---|---|"]
+        for (k, grid), d in sorted(groups.items()):
+            lines.append(f"| {k} | {grid} | {len(d)} | {sum(d) / len(d):.0f} | {min(d)} | {max(d)} |")
+    else:
+        lines += ["| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
+        for r in _csv_rows(a.stats_csv):
+            n = r["Name"]
+            if "pkv::" not in n:
+                continue
+            lines.append(f"| {shorten(n)} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
     if a.bench_json:
         with open(a.bench_json) as f:
             d = [json.loads(x) for x in f.read().splitlines() if x.startswith('{"metric"')][-1]
@@ -808,12 +821,20 @@ def summarize_pmc(argv):
     p.add_argument("--kind", required=True, choices=sorted(KERNEL_SOURCES))
     p.add_argument("--command", required=True, action="append",
                    help="each profiled command, as run from the repository root")
+    p.add_argument("--largest-grid", action="store_true",
+                   help="only the dispatches of the kernel with the largest grid (another launch of the same "
+                        "kernel in the run, with a smaller grid, is left out)")
     a = p.parse_args(argv)
 
-    def values(path, pat):
-        return [float(r["Counter_Value"]) for r in _csv_rows(path) if pat in r["Kernel_Name"]]
+    def values(path, pat, largest=False):
+        rows = [r for r in _csv_rows(path) if pat in r["Kernel_Name"]]
+        if largest and rows:
+            top = max(int(r["Grid_Size"]) for r in rows)
+            rows = [r for r in rows if int(r["Grid_Size"]) == top]
+        return [float(r["Counter_Value"]) for r in rows]
 
-    fetch, write = values(a.fetch_csv, a.kernel), values(a.write_csv, a.kernel)
+    fetch = values(a.fetch_csv, a.kernel, a.largest_grid)
+    write = values(a.write_csv, a.kernel, a.largest_grid)
     kib = 1 << 20  # KiB in the 1 GiB copy
     cf = [v for v in values(a.copy_fetch_csv, "copyBuffer") if v > kib / 16]
     cw = [v for v in values(a.copy_write_csv, "copyBuffer") if v > kib / 16]
@@ -822,7 +843,8 @@ def summarize_pmc(argv):
     ff, fw = kib / statistics.mean(cf), kib / statistics.mean(cw)
     medf, medw = statistics.median(fetch), statistics.median(write)
     read_b, write_b = medf * ff * 1024, medw * fw * 1024
-    lines = [f"# HBM counters: {a.kernel}", "", "Commands (from the repository root, one MI355X, one counter per run):",
+    what = a.kernel + (" (largest grid of the run)" if a.largest_grid else "")
+    lines = [f"# HBM counters: {what}", "", "Commands (from the repository root, one MI355X, one counter per run):",
              ""] + [f"    {c}" for c in a.command] + [
         "",
         "Calibration: a 1 GiB device-to-device copy reads 1 GiB and writes 1 GiB.",
@@ -844,9 +866,72 @@ def summarize_pmc(argv):
         f.write("\n".join(lines) + "\n")
 
 
+def summarize_mfma(argv):
+    """MFMA and LDS utilisation of one kernel from a rocprofv3 counter pass of
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_VALU_MFMA_COEXEC_CYCLES, SQ_ACTIVE_INST_VALU,
+    SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_LDS_IDX_ACTIVE, SQ_LDS_BANK_CONFLICT and
+    GRBM_GUI_ACTIVE (the last summed over the 8 XCDs; 256 CUs, 1024 SIMDs)."""
+    import collections
+    p = argparse.ArgumentParser(prog="bench.py summarize-mfma")
+    p.add_argument("csv")
+    p.add_argument("out")
+    p.add_argument("--kernel", required=True)
+    p.add_argument("--kind", required=True, choices=sorted(KERNEL_SOURCES))
+    p.add_argument("--command", required=True)
+    p.add_argument("--flops", type=float, required=True, help="algorithmic flops per dispatch")
+    p.add_argument("--largest-grid", action="store_true", help="only the dispatches with the kernel's largest grid")
+    a = p.parse_args(argv)
+    per = collections.defaultdict(dict)
+    name = a.kernel
+    rows_k = [r for r in _csv_rows(a.csv) if a.kernel in r["Kernel_Name"]]
+    if a.largest_grid and rows_k:
+        top = max(int(r["Grid_Size"]) for r in rows_k)
+        rows_k = [r for r in rows_k if int(r["Grid_Size"]) == top]
+    for r in rows_k:
+        name = r["Kernel_Name"]
+        per[r["Dispatch_Id"]][r["Counter_Name"]] = float(r["Counter_Value"])
+    ks = sorted(per, key=int)
+    if not ks:
+        raise SystemExit("summarize-mfma: no matching dispatch")
+    rows = []
+    for k in ks:
+        c = per[k]
+        act = c["GRBM_GUI_ACTIVE"] / 8
+        rows.append({"mfma": c["SQ_VALU_MFMA_BUSY_CYCLES"] / (act * 1024),
+                     "coexec": c.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0.0) / (act * 1024),
+                     "valu": 4 * c.get("SQ_ACTIVE_INST_VALU", 0.0) / (act * 1024),
+                     "lds": c["SQ_LDS_IDX_ACTIVE"] / (act * 256),
+                     "conf": c["SQ_LDS_BANK_CONFLICT"] / max(1.0, c["SQ_LDS_IDX_ACTIVE"]),
+                     "flops": c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512, "act": act})
+    med = lambda key: statistics.median(r[key] for r in rows)
+    short = name.split("(anonymous namespace)::")[-1].split("(")[0].replace("pkv::", "")
+    last = per[ks[-1]]
+    lines = [f"# MFMA and LDS counters: {short}", "", "Command (from the repository root, one MI355X, one counter pass):",
+             "", f"    {a.command}", "",
+             "Per dispatch (GRBM_GUI_ACTIVE is summed over the 8 XCDs: one XCD's active cycles are the sum / 8):",
+             "  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (active cycles x 1024 SIMDs)",
+             "  MFMA and VALU at once = SQ_VALU_MFMA_COEXEC_CYCLES / (active cycles x 1024 SIMDs)",
+             "  VALU issuing = 4 x SQ_ACTIVE_INST_VALU (quad-cycles) / (active cycles x 1024 SIMDs)",
+             "  LDS active = SQ_LDS_IDX_ACTIVE / (active cycles x 256 CUs)",
+             "  MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512", "",
+             f"{short} dispatches: {len(ks)} (medians)",
+             f"  MFMA busy {100 * med('mfma'):.1f}%, VALU issuing {100 * med('valu'):.1f}%, both at once "
+             f"{100 * med('coexec'):.1f}%",
+             f"  LDS active {100 * med('lds'):.1f}%, bank-conflict cycles {100 * med('conf'):.2f}% of LDS-active cycles",
+             f"  MFMA flops per dispatch {med('flops') / 1e9:.2f} GFLOP against {a.flops / 1e9:.2f} GFLOP of causal pairs "
+             f"({100 * (med('flops') / a.flops - 1):.1f}% more: the masked part of diagonal tiles)",
+             f"  active cycles per XCD {med('act'):.0f}", "", "Raw counters of the last dispatch:"]
+    lines += [f"  {n}: {int(last[n])}" for n in sorted(last)]
+    lines += ["", "kernel sources: " + ", ".join(f"paged_kv_attention_pkv_amd/csrc/{n}" for n in KERNEL_SOURCES[a.kind]),
+              f"source_sha256_16: {source_hash(a.kind)}"]
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main():
-    if len(sys.argv) > 1 and sys.argv[1] in ("summarize-trace", "summarize-pmc"):
-        (summarize_trace if sys.argv[1] == "summarize-trace" else summarize_pmc)(sys.argv[2:])
+    if len(sys.argv) > 1 and sys.argv[1] in ("summarize-trace", "summarize-pmc", "summarize-mfma"):
+        {"summarize-trace": summarize_trace, "summarize-pmc": summarize_pmc,
+         "summarize-mfma": summarize_mfma}[sys.argv[1]](sys.argv[2:])
         return
     args = parse()
     if args.gpus != 1:
