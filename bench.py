@@ -6,8 +6,11 @@ Qwen3-4B-shaped decode step at batch 64 (Hq 32 / Hkv 8 / head_dim 128, bf16,
 page size 16, cached lengths U{512..1024}, pages shuffled over a pool 1.25x
 the pages needed), one appended token per sequence, over 36 independent layer
 caches (36 x 254 MB of pools, far more than the 256 MB last-level cache, so
-every layer's K/V comes from HBM).  One step = for each of the 36 layers one
-pkv_append_decode_attn launch (append + attend).  The same line carries a
+every layer's K/V comes from HBM).  One step = one pkv_decode_plan launch
+(the cut of the step's work, shared by its layers), then for each of the 36
+layers one pkv_append_decode_attn launch (append + attend); ``--no-plan``
+leaves the plan out, so that every layer's launch cuts the work itself.  The
+same line carries a
 nested ``prefill`` object with the causal paged prefill at head_dim 256,
 Hq 48 / Hkv 8: the single request q_len = kv_len = 1023 and a random batch of
 8 requests (q_len U{65..4096}, kv_len = q_len + U{0..4096}), each step being
@@ -31,8 +34,9 @@ workload only; ``--page-size``, ``--layout`` and ``--contiguous`` change the
 pool of the decode and prefill workloads.
 
 ``--workload tune`` is the tuning sweep: for the decode step (batch 64 and
-the batch-8 / batch-32 sweep shapes) it times split-worker counts, page
-sizes, the NHD layout and contiguous pages, and for prefill the two head_dim
+the batch-8 / batch-32 sweep shapes) it times the step with one
+pkv_decode_plan, split-worker counts, page sizes, the NHD layout and
+contiguous pages, and for prefill the two head_dim
 256 tilings, each scored on whole-step time (all layers, HIP graph) and
 timed in alternation with the library's default configuration on the same
 inputs (the control), so that drift between measurements shows up in the
@@ -84,6 +88,8 @@ def parse():
     p.add_argument("--separate", action="store_true",
                    help="decode step as pkv_append + pkv_decode_attn (two launches) instead of the fused "
                         "pkv_append_decode_attn")
+    p.add_argument("--no-plan", action="store_true",
+                   help="decode: no pkv_decode_plan per step (every call cuts the work itself)")
     p.add_argument("--head-dim", type=int, default=256, help="prefill: head_dim (64, 128 or 256)")
     p.add_argument("--hq", type=int, default=48, help="prefill: query heads")
     p.add_argument("--hkv", type=int, default=8, help="prefill: KV heads")
@@ -280,25 +286,36 @@ def bench_decode(args, torch, pkv, wl, workload):
                                          layout=spec.layout, workers=args.workers)
         layers.append((app, dec))
         del inp
+    # the cut of the step's work, computed once for all its layers (the
+    # lengths every decode call sees: pre-append when fused, else those the
+    # first append writes)
+    plan = None
+    if not args.no_plan:
+        plan = pkv.api.prepare_decode_plan(pools[0][0], hist if fused else lens, spec.hq, max_kv, workspace,
+                                           fused=fused, layout=spec.layout, workers=args.workers)
     del pools
     torch.cuda.synchronize()
 
     def step():
-        for app, dec in layers:
+        for n, (app, dec) in enumerate(layers):
             if app is not None:
                 app()
+            if n == 0 and plan is not None:
+                plan()
             dec()
 
     ms, per = time_steps(torch, step, args.steps, args.warmup, not args.eager)
     step()  # lens is live again for the per-call brackets below
     dec_mean, _ = events_per_call(torch, [d for _, d in layers])
     app_mean = None if fused else events_per_call(torch, [a for a, _ in layers])[0]
+    plan_ms = 0.0 if plan is None else events_per_call(torch, [plan])[0]
     kv_bytes_step = acc["kv"] * L
     value = kv_bytes_step / (ms * 1e-3) / 1e9
     # the kernel's average launch duration: in the fused step the timed region
-    # holds exactly L launches of it (HIP events around the graph replays);
-    # in the two-launch step, per-call event brackets of the decode launches
-    launch_ms = ms / L if fused else dec_mean
+    # holds exactly L launches of it and the plan launch (HIP events around
+    # the graph replays, less the plan launch's own event bracket); in the
+    # two-launch step, per-call event brackets of the decode launches
+    launch_ms = (ms - plan_ms) / L if fused else dec_mean
     achieved = acc["total"] / (launch_ms * 1e-3) / 1e9
     traffic = traffic_from_profile("decode", f"decode_kernel_{spec.name}_pmc.txt") if fused else None
     result = {
@@ -319,7 +336,8 @@ def bench_decode(args, torch, pkv, wl, workload):
                    "pages": "contiguous" if args.contiguous else "shuffled", "layers": L,
                    "mean_attended_len": round(float(spec.hist_lens.mean()) + spec.n_new, 1),
                    "step": ("per layer: pkv_append_decode_attn (append 1 token/seq + attend, one launch)"
-                            if fused else "per layer: pkv_append(1 token/seq) + pkv_decode_attn"),
+                            if fused else "per layer: pkv_append(1 token/seq) + pkv_decode_attn")
+                   + ("; once per step: pkv_decode_plan" if plan is not None else ""),
                    "launch": "eager" if args.eager else "hip graph", "parallelism": "none (1 GPU)"},
         "us_per_call": round(ms * 1e3 / L, 2),
         "us_per_call_over_steps": spread(per, 1e3 / L),
@@ -328,6 +346,7 @@ def bench_decode(args, torch, pkv, wl, workload):
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "decode_us_per_call_events": round(dec_mean * 1e3, 2),
         "append_us_per_call_events": None if app_mean is None else round(app_mean * 1e3, 2),
+        "plan_us_per_step_events": None if plan is None else round(plan_ms * 1e3, 2),
         "kernel_us_per_launch": round(launch_ms * 1e3, 2),
         "roofline": {"bound": "hbm",
                      "kernel": "decode_bf16_kernel (one launch per pkv_append_decode_attn)" if fused
@@ -622,8 +641,9 @@ def _decode_setup(torch, pkv, wl, spec, L, dev):
             "max_kv": int(spec.hist_lens.max()) + spec.n_new}
 
 
-def _decode_step(torch, pkv, setup, workers, dev):
-    """One fused append + decode launch per layer with the given worker count."""
+def _decode_step(torch, pkv, setup, workers, dev, plan=False):
+    """One fused append + decode launch per layer with the given worker
+    count (with plan: after one pkv_decode_plan for the step)."""
     spec, bt, hist, max_kv = setup["spec"], setup["bt"], setup["hist"], setup["max_kv"]
     kc0 = setup["layers"][0][0]
     ws = torch.zeros(pkv.decode_workspace_bytes(kc0, spec.batch, spec.hq, max_kv, layout=spec.layout,
@@ -632,6 +652,9 @@ def _decode_step(torch, pkv, setup, workers, dev):
     calls = [pkv.api.prepare_append_decode(q, kc, vc, kn, vn, bt, hist, max_kv, spec.scale, torch.empty_like(q), ws,
                                            seqlens_out=lens, layout=spec.layout, workers=workers)
              for kc, vc, q, kn, vn in setup["layers"]]
+    if plan:
+        calls.insert(0, pkv.api.prepare_decode_plan(kc0, hist, spec.hq, max_kv, ws, fused=True,
+                                                    layout=spec.layout, workers=workers))
 
     def step():
         for c in calls:
@@ -678,6 +701,9 @@ def bench_tune(args, torch, pkv, wl):
         ctl = _decode_setup(torch, pkv, wl, base, L, dev)
         control = _decode_step(torch, pkv, ctl, 0, dev)
         entries, controls = [], []
+        c, v = _alternate(torch, args, control, _decode_step(torch, pkv, ctl, 0, dev, plan=True), rounds)
+        entries.append(("pkv_decode_plan once per step", c, v))
+        controls.append(c)
         for w in (128, 256, 512, 768, 1280, 2048):
             c, v = _alternate(torch, args, control, _decode_step(torch, pkv, ctl, w, dev), rounds)
             entries.append((f"workers {w}", c, v))
@@ -693,7 +719,8 @@ def bench_tune(args, torch, pkv, wl):
                 del other
                 torch.cuda.empty_cache()
         lines.append(dict(summarise(f"decode {base.name} (fused append + decode per layer)",
-                                    "page 16, HND, shuffled pages, library worker count", L, entries, controls,
+                                    "page 16, HND, shuffled pages, library worker count, no plan", L, entries,
+                                    controls,
                                     1e3), workload=base.name))
         del ctl, control
         torch.cuda.empty_cache()

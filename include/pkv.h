@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 3
 
 typedef enum pkv_status {
     PKV_OK = 0,
@@ -164,8 +164,9 @@ pkv_status pkv_append_rope(const pkv_cache_desc *cache, void *k_cache, void *v_c
  * however the lengths grow or shrink.
  *
  * Layout: one int32 arrival counter per (sequence, kv head) at the start,
- * then the partial results of rows split across workers.  The counter
- * region must be zero before a call: zero-fill the workspace before its
+ * then the partial results of rows split across workers, then the plan
+ * region that pkv_decode_plan writes.  The counter region must be zero
+ * before a call: zero-fill the workspace before its
  * first use (pkv_decode_workspace_reset, or any fill of zeros), and again
  * when it is reused for a different batch or kv-head count.  Every call that
  * completes leaves it zero.  A launch that did not complete (an aborted or
@@ -185,6 +186,43 @@ size_t pkv_decode_workspace_bytes(const pkv_cache_desc *cache, int32_t batch, in
  */
 pkv_status pkv_decode_workspace_reset(const pkv_cache_desc *cache, int32_t batch, void *workspace,
                                       size_t workspace_bytes, void *stream);
+
+/*
+ * pkv_decode_plan -- the split of a decode step's work, computed once for
+ * all the decode calls of the step.
+ *
+ * Every layer of a decode step attends over the same block_table and
+ * cache_seqlens, so how the (row, kv head, page) units are cut across the
+ * split workers is the same for each layer's call; mini-infer 06 §5 makes
+ * the same point for its per-step metadata (computed once, shared by every
+ * layer).  This call enqueues one small kernel on `stream` that reads
+ * cache_seqlens and writes that cut into the plan region of `workspace`.
+ * A later pkv_decode_attn / _ex or pkv_append_decode_attn / _ex call given
+ * the same workspace reads the plan together with its own lengths, and uses
+ * it only if the plan was made for the same descriptor head count, batch,
+ * max_kv_len, worker count and mode (`fused`) and every row's
+ * cache_seqlens value still equals the planned one; otherwise the call plans
+ * on its own, as it does without this call.  Results are bit-identical
+ * either way: the plan only saves the calls the work of cutting (the table
+ * is read by each call, so it may change freely).
+ *
+ *   cache_seqlens  int32 [batch] on the device, as the calls will get it
+ *                  (pre-append lengths when fused = 1)
+ *   max_kv_len     as the calls will pass it
+ *   fused          1: plan pkv_append_decode_attn calls; 0: pkv_decode_attn
+ *   workers        as the calls will pass it (0 = automatic)
+ *   workspace      a decode workspace of pkv_decode_workspace_bytes_ex(...,
+ *                  workers) bytes; only its plan region is written
+ * Only bf16 pools use a plan: for fp32 pools the call checks its arguments
+ * and enqueues nothing.  pkv_append_decode_attn_noalloc never uses one.  A
+ * plan stays in the workspace until the next pkv_decode_plan on it
+ * (pkv_decode_workspace_reset does not clear it).  The plan call must be
+ * ordered before the calls that use it (same stream), like every use of a
+ * workspace.
+ */
+pkv_status pkv_decode_plan(const pkv_cache_desc *cache, int32_t num_q_heads, const int32_t *cache_seqlens,
+                           int32_t batch, int32_t max_kv_len, int32_t fused, void *workspace,
+                           size_t workspace_bytes, int32_t workers, void *stream);
 
 /*
  * pkv_decode_attn -- GQA decode attention, one query token per sequence.

@@ -15,6 +15,7 @@ from .api import (  # noqa: F401
     append_decode_attn_noalloc,
     append_rope,
     decode_attn,
+    decode_plan,
     decode_workspace_bytes,
     decode_workspace_reset,
     lib_path,

@@ -24,7 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # The in-tree build (python -m paged_kv_attention_pkv_amd.build).
 _LIB_PATH = os.path.join(_HERE, "libpkv.so")
 # PKV_ABI_VERSION of include/pkv.h that these bindings are written against.
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 PKV_F32, PKV_BF16 = 0, 1
 _STATUS = {
@@ -68,6 +68,7 @@ _SIGS = {
     "pkv_decode_workspace_bytes": ([_DP, _I32, _I32, _I32], _SZ),
     "pkv_decode_workspace_bytes_ex": ([_DP, _I32, _I32, _I32, _I32], _SZ),
     "pkv_decode_workspace_reset": ([_DP, _I32, _VP, _SZ, _VP], ctypes.c_int),
+    "pkv_decode_plan": ([_DP, _I32, _VP, _I32, _I32, _I32, _VP, _SZ, _I32, _VP], ctypes.c_int),
     "pkv_decode_attn": ([_DP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _VP, _I32, _I32, ctypes.c_float,
                          _VP, _SZ, _VP], ctypes.c_int),
     "pkv_decode_attn_ex": ([_DP, _VP, _VP, _VP, _I32, _VP, _VP, _VP, _I32, _VP, _I32, _I32, ctypes.c_float,
@@ -317,6 +318,37 @@ def decode_workspace_reset(k_cache, batch: int, workspace, layout: str = "HND") 
     rc = lib().pkv_decode_workspace_reset(ctypes.byref(desc), int(batch), _ptr(workspace),
                                           workspace.numel() * workspace.element_size(), _stream(workspace))
     _check("pkv_decode_workspace_reset", rc)
+
+
+def _decode_plan_args(k_cache, cache_seqlens, num_q_heads: int, max_kv_len: int, workspace, fused: bool,
+                      layout: str, workers: int):
+    desc = cache_desc(k_cache, None, layout)
+    dev = k_cache.device
+    _need(cache_seqlens, "cache_seqlens", torch.int32, dev, 1)
+    _need(workspace, "workspace", None, dev)
+    batch = cache_seqlens.shape[0]
+    with torch.cuda.device(dev):
+        need = lib().pkv_decode_workspace_bytes_ex(ctypes.byref(desc), batch, int(num_q_heads), int(max_kv_len),
+                                                   int(workers))
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise PkvError("pkv_decode_plan", 3, f"workspace {nbytes} < {need} bytes")
+    args = (ctypes.byref(desc), int(num_q_heads), _ptr(cache_seqlens), batch, int(max_kv_len), int(bool(fused)),
+            _ptr(workspace), nbytes, int(workers))
+    return args, (k_cache, cache_seqlens, workspace, desc)
+
+
+def decode_plan(k_cache, cache_seqlens, num_q_heads: int, max_kv_len: int, workspace, fused: bool,
+                layout: str = "HND", workers: int = 0) -> None:
+    """pkv_decode_plan: enqueue, on the current stream, the cut of the
+    decode calls of one step (same lengths, shape, max_kv_len, workers and
+    mode) into the workspace's plan region.  Later calls with this workspace
+    use it where it matches them and give the same bits either way."""
+    args, keep = _decode_plan_args(k_cache, cache_seqlens, num_q_heads, max_kv_len, workspace, fused, layout,
+                                   workers)
+    with torch.cuda.device(k_cache.device):
+        rc = lib().pkv_decode_plan(*args, _stream(workspace))
+    _check("pkv_decode_plan", rc)
 
 
 def decode_attn(q, k_cache, v_cache, block_table, cache_seqlens, max_kv_len: int, scale: float,
@@ -676,6 +708,13 @@ def prepare_append_decode(q, k_cache, v_cache, k_new, v_new, block_table, cache_
             int(max_kv_len), float(scale), _ptr(workspace), nbytes, int(workers))
     return PreparedCall("pkv_append_decode_attn_ex", args, (k_cache, v_cache, q, out, k_new, v_new, block_table,
                                                             cache_seqlens, seqlens_out, workspace, lse, desc))
+
+
+def prepare_decode_plan(k_cache, cache_seqlens, num_q_heads: int, max_kv_len: int, workspace, fused: bool,
+                        layout: str = "HND", workers: int = 0) -> PreparedCall:
+    args, keep = _decode_plan_args(k_cache, cache_seqlens, num_q_heads, max_kv_len, workspace, fused, layout,
+                                   workers)
+    return PreparedCall("pkv_decode_plan", args, keep)
 
 
 def prepare_prefill(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, max_q: int, max_kv_len: int,

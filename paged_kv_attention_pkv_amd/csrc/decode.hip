@@ -176,6 +176,9 @@ struct EngF32 {
     }
 };
 
+// The plan of a call shaped as `a` (see write_plan).
+__global__ __launch_bounds__(64) void decode_plan_kernel(DecodeArgs a) { write_plan(a, blockIdx.x); }
+
 template <int D>
 __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
     using Eng = EngF32<D>;
@@ -291,16 +294,25 @@ void decode_mid_cap(int device, const PoolGeom &g, int w_rec, DecodeArgs &a) {
 
 // Workspace: one int32 arrival counter per (sequence, kv head) first, then
 // the partial records (o: G*D fp32, (m, l): 2 fp32) for up to
-// `record_workers` + batch*hkv pieces.  `record_workers` is the worker count
-// before any cap by the call's page count, so the size and the layout depend
-// on the batch shape and the device only, never on the lengths.  The
-// counters must be zero before a call; every call that completes leaves them
-// zero.
-size_t decode_workspace(const PoolGeom &g, int batch, int hq, int record_workers) {
+// `record_workers` + batch*hkv pieces, then the plan region (header, the
+// planned length of every row, one record per worker; decode_worker.hpp).
+// `record_workers` is the worker count before any cap by the call's page
+// count, so the size and the layout depend on the batch shape and the device
+// only, never on the lengths.  The counters must be zero before a call; every
+// call that completes leaves them zero.
+static size_t decode_records_end(const PoolGeom &g, int batch, int hq, int record_workers) {
     const int G = hq / g.hkv;
     const size_t recs = (size_t)record_workers + (size_t)batch * g.hkv;
     return decode_counter_bytes(g, batch) + align256(recs * G * g.head_dim * sizeof(float)) +
            align256(recs * G * 2 * sizeof(float));
+}
+
+static size_t decode_plan_bytes(int batch, int record_workers) {
+    return (size_t)kPlanHdr * 4 + align256((size_t)batch * 4) + align256((size_t)record_workers * kPlanRec * 4);
+}
+
+size_t decode_workspace(const PoolGeom &g, int batch, int hq, int record_workers) {
+    return decode_records_end(g, batch, hq, record_workers) + decode_plan_bytes(batch, record_workers);
 }
 
 size_t decode_counter_bytes(const PoolGeom &g, int batch) { return align256((size_t)batch * g.hkv * sizeof(int32_t)); }
@@ -312,13 +324,26 @@ void decode_workspace_layout(const PoolGeom &g, DecodeArgs &a, void *workspace, 
     a.arrivals = (int32_t *)ws;
     a.part_o = (float *)(ws + decode_counter_bytes(g, a.batch));
     a.part_ml = (float *)((char *)a.part_o + align256(recs * G * g.head_dim * sizeof(float)));
+    a.plan = (int32_t *)(ws + decode_records_end(g, a.batch, a.hq, record_workers));
 }
 
-hipError_t launch_decode(const PoolGeom &g, DecodeArgs a, void *workspace, int record_workers, hipStream_t stream) {
+hipError_t launch_decode(const PoolGeom &g, DecodeArgs a, void *workspace, int record_workers, bool use_plan,
+                         hipStream_t stream) {
     decode_workspace_layout(g, a, workspace, record_workers);
+    if (!use_plan) a.plan = nullptr;
     const void *k = pick_kernel(g.dtype, g.head_dim, g.page_shift > 0);
     void *args[] = {&a};
     hipError_t e = hipLaunchKernel(k, dim3(a.workers), dim3(kWave), args, 0, stream);
+    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_plan(const PoolGeom &g, DecodeArgs a, void *workspace, int record_workers,
+                              hipStream_t stream) {
+    decode_workspace_layout(g, a, workspace, record_workers);
+    void *args[] = {&a};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&decode_plan_kernel), dim3(a.workers), dim3(kWave),
+                                   args, 0, stream);
     if (e != hipSuccess) return e;
     return hipGetLastError();
 }

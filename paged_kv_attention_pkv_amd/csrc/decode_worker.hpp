@@ -30,13 +30,13 @@ constexpr int kStage = 2048;  // page ids of its range a wave keeps in LDS at a 
 // on the host).  In fused-append mode the raw length is the pre-append one.
 __device__ __forceinline__ int attended(const DecodeArgs &a, int raw) {
     if (raw < 0) return 0;
-    if (a.k_new) return raw >= a.max_kv ? a.max_kv : raw + 1;
+    if (a.fused) return raw >= a.max_kv ? a.max_kv : raw + 1;
     return raw > a.max_kv ? a.max_kv : raw;
 }
 
 // Fused mode: the row's last attended key is the new token (not cut away).
 __device__ __forceinline__ int fresh_token(const DecodeArgs &a, int raw) {
-    return a.k_new && raw >= 0 && raw < a.max_kv;
+    return a.fused && raw >= 0 && raw < a.max_kv;
 }
 
 __device__ __forceinline__ int raw_len(const DecodeArgs &a, int b) { return b < a.batch ? a.seqlens[b] : -1; }
@@ -170,21 +170,34 @@ __device__ __forceinline__ void locate2(const DecodeArgs &a, int64_t x0, int64_t
     }
 }
 
-// Line length and this wave's share, with the segment its range starts in.
-// The range is [f0, f1) with f0 and f1 the first page positions at or after
-// the two cuts, so a walk stops where the next segment would start at or past
-// f1.  Rows are handed out round-robin (row b to worker b mod workers) for
-// the per-row chores: zero fill of rows without keys, and in fused mode the
-// new lengths.  The first 64 raw lengths stay in `rl`.  False when the wave
-// has no pages.
+// The per-row chores of worker w for the 64 rows from `base` (raw lengths one
+// per lane): rows are handed out round-robin (row b to worker b mod workers);
+// a row without keys gets zero output and -inf lse, and in fused mode a row
+// whose token is not stored keeps its length (the others get theirs from the
+// wave that writes the token, in the splice).
 template <typename OutT>
-__device__ __forceinline__ bool plan(const DecodeArgs &a, int w, int D, RowLens &rl, Range &r, Seg &s) {
-    const int l = lane_id();
-    int64_t pages = 0;  // pages of all rows, one kv head
-    int rows = 0;       // rows with pages
+__device__ __forceinline__ void row_chores(const DecodeArgs &a, int w, int D, int base, int raw) {
+    const int b = base + lane_id();
+    const bool mine = b < a.batch && b % a.workers == w;
+    if (mine && a.seqlens_out && !fresh_token(a, raw)) a.seqlens_out[b] = raw;
+    uint64_t empty = __ballot(mine && attended(a, raw) == 0);
+    while (empty) {
+        const int e = uniform((int)__builtin_ctzll(empty));
+        empty &= empty - 1;
+        zero_row<OutT>(a, base + e, D);
+    }
+}
+
+// Pages of all rows (one kv head) and the number of rows with pages, with
+// the chores of worker w when kChores.  The first 64 raw lengths and their
+// page prefix sums stay in `rl`.
+template <typename OutT, bool kChores>
+__device__ __forceinline__ void count_rows(const DecodeArgs &a, int w, int D, RowLens &rl, int64_t &pages,
+                                           int &rows) {
+    pages = 0;
+    rows = 0;
     for (int base = 0; base < a.batch; base += kWave) {
-        const int b = base + l;
-        const int raw = raw_len(a, b);
+        const int raw = raw_len(a, base + lane_id());
         const int n = attended(a, raw);
         const int incl = wave_incl_scan32(ceil_div(n, kPage));
         if (base == 0) {
@@ -194,17 +207,16 @@ __device__ __forceinline__ bool plan(const DecodeArgs &a, int w, int D, RowLens 
         }
         pages += __builtin_amdgcn_readlane(incl, kWave - 1);
         rows += __builtin_popcountll(__ballot(n > 0));
-        const bool mine = b < a.batch && b % a.workers == w;
-        // a row whose token is not appended keeps its length; the others get
-        // theirs from the wave that writes the token (splice)
-        if (mine && a.seqlens_out && !fresh_token(a, raw)) a.seqlens_out[b] = raw;
-        uint64_t empty = __ballot(mine && n == 0);
-        while (empty) {
-            const int e = uniform((int)__builtin_ctzll(empty));
-            empty &= empty - 1;
-            zero_row<OutT>(a, base + e, D);
-        }
+        if constexpr (kChores) row_chores<OutT>(a, w, D, base, raw);
     }
+}
+
+// Line length and the share of wave w, with the segment its range starts in.
+// The range is [f0, f1) with f0 and f1 the first page positions at or after
+// the two cuts, so a walk stops where the next segment would start at or past
+// f1.  False when the wave has no pages.
+__device__ __forceinline__ bool cut_range(const DecodeArgs &a, int w, int64_t pages, int rows, const RowLens &rl,
+                                          Range &r, Seg &s) {
     const int64_t total = pages * a.hkv;
     // Small calls use fewer waves, so each keeps at least kMinPagesPerWorker
     // pages (a segment cut into many tiny pieces costs more in merges than
@@ -219,6 +231,143 @@ __device__ __forceinline__ bool plan(const DecodeArgs &a, int w, int D, RowLens 
     r.workers = (int)wmax;
     locate2(a, (int64_t)w * len / wmax, (int64_t)(w + 1) * len / wmax, rl, s, r.f0, r.f1);
     return r.f0 < r.f1;
+}
+
+// Everything a wave needs before its first page: the chores, the line and
+// its range.  The first 64 raw lengths stay in `rl`.  False when the wave has
+// no pages.
+template <typename OutT>
+__device__ __forceinline__ bool plan(const DecodeArgs &a, int w, int D, RowLens &rl, Range &r, Seg &s) {
+    int64_t pages;
+    int rows;
+    count_rows<OutT, true>(a, w, D, rl, pages, rows);
+    return cut_range(a, w, pages, rows, rl, r, s);
+}
+
+// ---------------------------------------------------------------------------
+// a plan computed once for several calls
+// ---------------------------------------------------------------------------
+//
+// The cut depends only on the row lengths and on the call's shape (batch, kv
+// heads, max_kv, fused mode, worker counts), so the decode calls of one step
+// (one per layer, all on the same table and lengths) share it.
+// decode_plan_kernel writes it to the plan region of a workspace:
+//   words 0..15            header: kPlanMagic and the shape (plan_word)
+//   kPlanHdr ..            the raw length of every row, as planned
+//   kPlanHdr + lens_words  one record of kPlanRec words per worker: has
+//                          pages, workers, line length, f0, f1, and the
+//                          first segment (b, g, n, np, fresh, f)
+// A call given a plan reads the header, its record and every row's length
+// and planned length together (one round trip), and takes the record only if
+// every header word and every length agree with its own; otherwise it plans
+// as without one.  Either way it walks the same range.
+constexpr int kPlanMagic = 0x504b5650;
+constexpr int kPlanHdr = 64;  // words (256 bytes)
+constexpr int kPlanRec = 16;  // words per worker
+
+__device__ __forceinline__ int plan_lens_words(int batch) { return (batch + 63) & ~63; }
+
+// Header word k (0..15) of a plan for the call `a`.
+__device__ __forceinline__ int plan_word(const DecodeArgs &a, int k) {
+    switch (k) {
+        case 0: return kPlanMagic;
+        case 1: return a.batch;
+        case 2: return a.hkv;
+        case 3: return a.max_kv;
+        case 4: return a.fused;
+        case 5: return a.workers;
+        case 6: return a.fixed_workers;
+        case 7: return a.mid_workers;
+        case 8: return (int)(uint32_t)a.mid_pages;
+        case 9: return (int)(a.mid_pages >> 32);
+        default: return 0;
+    }
+}
+
+__device__ __forceinline__ int64_t lanes64(int v, int k) {
+    return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(v, k + 1) << 32) |
+                     (uint32_t)__builtin_amdgcn_readlane(v, k));
+}
+
+// plan() through the plan at a.plan when it matches the call (see above).
+template <typename OutT>
+__device__ __forceinline__ bool plan_or_load(const DecodeArgs &a, int w, int D, RowLens &rl, Range &r, Seg &s) {
+    if (!a.plan) return plan<OutT>(a, w, D, rl, r, s);
+    const int l = lane_id();
+    const int32_t *lens = a.plan + kPlanHdr;
+    const int32_t *recs = lens + plan_lens_words(a.batch);
+    const int hv = a.plan[l & 15];
+    const int rv = recs[(int64_t)w * kPlanRec + (l & 15)];
+    const int raw = raw_len(a, l);
+    const int cp = l < a.batch ? lens[l] : -1;
+    bool ok = __ballot((l < 16 && hv != plan_word(a, l)) || raw != cp) == 0;
+    for (int base = kWave; ok && base < a.batch; base += kWave) {
+        const int b = base + l;
+        ok = __ballot(raw_len(a, b) != (b < a.batch ? lens[b] : -1)) == 0;
+    }
+    if (!ok) return plan<OutT>(a, w, D, rl, r, s);
+    rl.base = 0;
+    rl.raw = raw;
+    rl.incl = 0;  // read by the cut only
+    row_chores<OutT>(a, w, D, 0, raw);
+    for (int base = kWave; base < a.batch; base += kWave) row_chores<OutT>(a, w, D, base, raw_len(a, base + l));
+    if (!__builtin_amdgcn_readlane(rv, 0)) return false;
+    r.workers = __builtin_amdgcn_readlane(rv, 1);
+    r.total = lanes64(rv, 2);
+    r.f0 = lanes64(rv, 4);
+    r.f1 = lanes64(rv, 6);
+    s.b = __builtin_amdgcn_readlane(rv, 8);
+    s.g = __builtin_amdgcn_readlane(rv, 9);
+    s.n = __builtin_amdgcn_readlane(rv, 10);
+    s.np = __builtin_amdgcn_readlane(rv, 11);
+    s.fresh = __builtin_amdgcn_readlane(rv, 12);
+    s.f = lanes64(rv, 13);
+    return true;
+}
+
+// Writes the plan of a call shaped as `a` (one wave per worker, w = its
+// index): its record, the lengths of rows 64w.. (and every further
+// 64*workers), and from wave 0 the header.
+__device__ __forceinline__ void write_plan(const DecodeArgs &a, int w) {
+    RowLens rl;
+    int64_t pages;
+    int rows;
+    count_rows<float, false>(a, w, 0, rl, pages, rows);
+    Range r;
+    Seg s;
+    const bool has = cut_range(a, w, pages, rows, rl, r, s);
+    const int l = lane_id();
+    int32_t *lens = a.plan + kPlanHdr;
+    int32_t *recs = lens + plan_lens_words(a.batch);
+    if (l < 16) {
+        int v = 0;
+        if (has) {
+            switch (l) {
+                case 0: v = 1; break;
+                case 1: v = r.workers; break;
+                case 2: v = (int)(uint32_t)r.total; break;
+                case 3: v = (int)(r.total >> 32); break;
+                case 4: v = (int)(uint32_t)r.f0; break;
+                case 5: v = (int)(r.f0 >> 32); break;
+                case 6: v = (int)(uint32_t)r.f1; break;
+                case 7: v = (int)(r.f1 >> 32); break;
+                case 8: v = s.b; break;
+                case 9: v = s.g; break;
+                case 10: v = s.n; break;
+                case 11: v = s.np; break;
+                case 12: v = s.fresh; break;
+                case 13: v = (int)(uint32_t)s.f; break;
+                case 14: v = (int)(s.f >> 32); break;
+                default: v = 0;
+            }
+        }
+        recs[(int64_t)w * kPlanRec + l] = v;
+    }
+    for (int64_t base = (int64_t)w * kWave; base < a.batch; base += (int64_t)a.workers * kWave) {
+        const int b = (int)base + l;
+        if (b < a.batch) lens[b] = a.seqlens[b];
+    }
+    if (w == 0 && l < 16) a.plan[l] = plan_word(a, l);
 }
 
 // Worker whose range holds the page at position x.
@@ -920,7 +1069,7 @@ __device__ __forceinline__ void decode_bf16_worker(const DecodeArgs &a, int w, c
     RowLens rl;
     Range r;
     Cursor cur;
-    if (!plan<__bf16>(a, w, D, rl, r, cur.s)) return;
+    if (!plan_or_load<__bf16>(a, w, D, rl, r, cur.s)) return;
     cur.p = cur.pstart = (int)(r.f0 - cur.s.f);
     cur.pend = (int)(cur.s.np < r.f1 - cur.s.f ? cur.s.np : r.f1 - cur.s.f);
     cur.live = 1;

@@ -66,12 +66,16 @@ struct DecodeArgs {
     float *part_o;      // [(record workers + batch*hkv) * group * head_dim]
     float *part_ml;     // [(record workers + batch*hkv) * group * 2]
     int32_t *arrivals;  // [batch*hkv]: pieces finished per split row; zero between calls
-    // Fused append (bf16 only): when k_new is set, seqlens holds the pre-append
+    // Fused append (bf16 only): when fused is 1, seqlens holds the pre-append
     // lengths L, each row attends L+1 keys, and the token at position L is taken
     // from k_new / v_new [batch, hkv, head_dim] and written into the pool.
+    int32_t fused;
     const void *k_new;
     const void *v_new;
     int32_t *seqlens_out;  // nullable (fused mode only): L+1 where the token was stored, else L
+    // Nullable: a plan of the cut for calls of this shape (written by
+    // launch_decode_plan, taken only where it matches the call's lengths).
+    int32_t *plan;
 };
 
 // Fills a.mid_workers / a.mid_pages for an automatic worker count of
@@ -87,11 +91,16 @@ size_t decode_counter_bytes(const PoolGeom &g, int batch);
 // Whole decode workspace for `record_workers` (the uncapped worker count).
 size_t decode_workspace(const PoolGeom &g, int batch, int hq, int record_workers);
 // Launches the decode kernel on args.workers waves; the workspace layout
-// (counters, then records for record_workers + batch*hkv pieces) is derived
-// here and fills args.arrivals / part_o / part_ml.
-hipError_t launch_decode(const PoolGeom &g, DecodeArgs args, void *workspace, int record_workers,
+// (counters, then records for record_workers + batch*hkv pieces, then the
+// plan region) is derived here and fills args.arrivals / part_o / part_ml,
+// and args.plan when use_plan.
+hipError_t launch_decode(const PoolGeom &g, DecodeArgs args, void *workspace, int record_workers, bool use_plan,
                          hipStream_t stream);
-// Fills a.arrivals / part_o / part_ml from the workspace layout.
+// Writes the plan of calls shaped as args into the workspace's plan region
+// (one wave per worker; args.workers of them).
+hipError_t launch_decode_plan(const PoolGeom &g, DecodeArgs args, void *workspace, int record_workers,
+                              hipStream_t stream);
+// Fills a.arrivals / part_o / part_ml / plan from the workspace layout.
 void decode_workspace_layout(const PoolGeom &g, DecodeArgs &a, void *workspace, int record_workers);
 // Zero `words` int32 values at p with a fill kernel (no memset node, so the
 // call can be recorded into a graph).

@@ -240,30 +240,44 @@ pkv_status pkv_decode_workspace_reset(const pkv_cache_desc *cache, int32_t batch
 
 namespace {
 
+// What a decode_common call enqueues.
+enum class DecodeRun {
+    kCall,        // the decode launch, taking a matching plan from the workspace
+    kCallNoPlan,  // the decode launch after a clear of the counters, no plan (allocation-free entry)
+    kPlan,        // only the plan kernel (q, out, pools, table and new tokens are not used)
+};
+
 // Decode, optionally with the step's token appended in the same launch
-// (k_new != NULL).
+// (k_new != NULL), or the plan of such calls.
 pkv_status decode_common(const pkv_cache_desc *cache, void *out, float *lse, const void *q, int32_t num_q_heads,
                          const void *k_cache, const void *v_cache, const void *k_new, const void *v_new,
                          const int32_t *block_table, int32_t bt_cols, const int32_t *cache_seqlens,
                          int32_t *seqlens_out, int32_t batch, int32_t max_kv_len, float scale, void *workspace,
-                         size_t workspace_bytes, int32_t workers, void *stream, bool clear_counters = false) {
+                         size_t workspace_bytes, int32_t workers, void *stream, DecodeRun run = DecodeRun::kCall,
+                         bool plan_fused = false) {
     PoolGeom g;
     pkv_status st = check_desc(cache, &g);
     if (st) return st;
     if ((st = check_heads(g, num_q_heads))) return st;
-    const bool fused = k_new != nullptr || v_new != nullptr;
+    const bool planning = run == DecodeRun::kPlan;
+    const bool fused = planning ? plan_fused : (k_new != nullptr || v_new != nullptr);
     if (fused && g.dtype != 1) return PKV_EUNSUPPORTED;
     if (batch < 0 || max_kv_len < 0 || bt_cols < 0 || workers < 0) return PKV_EINVAL;
-    if (fused && (!k_new || !v_new)) return PKV_EINVAL;
+    if (!planning && fused && (!k_new || !v_new)) return PKV_EINVAL;
     if (seqlens_out && (!fused || seqlens_out == cache_seqlens)) return PKV_EINVAL;
     if (batch == 0) return PKV_OK;
-    if (!out || !q || !k_cache || !v_cache || !block_table || !cache_seqlens) return PKV_EINVAL;
-    if (fused && (!aligned16(k_new) || !aligned16(v_new))) return PKV_EUNSUPPORTED;
-    if ((int64_t)max_kv_len > (int64_t)bt_cols * g.page_size) return PKV_EINVAL;
+    if (!cache_seqlens) return PKV_EINVAL;
+    if (!planning) {
+        if (!out || !q || !k_cache || !v_cache || !block_table) return PKV_EINVAL;
+        if (fused && (!aligned16(k_new) || !aligned16(v_new))) return PKV_EUNSUPPORTED;
+        if ((int64_t)max_kv_len > (int64_t)bt_cols * g.page_size) return PKV_EINVAL;
+    }
     if (max_kv_len > kMaxDecodeKv) return PKV_EUNSUPPORTED;  // page counts of 64 rows are summed in 32 bits
-    if (!isfinite(scale)) return PKV_EINVAL;
-    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
-        return PKV_EUNSUPPORTED;
+    if (!planning) {
+        if (!isfinite(scale)) return PKV_EINVAL;
+        if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+            return PKV_EUNSUPPORTED;
+    }
     const int dev = current_device();
     if (dev < 0) return PKV_EDEVICE;
     // records are laid out for the uncapped count; the launch never has more
@@ -274,6 +288,8 @@ pkv_status decode_common(const pkv_cache_desc *cache, void *out, float *lse, con
     const int w = bound < w_rec ? (int)(bound > 0 ? bound : 1) : w_rec;
     const size_t need = pkv::decode_workspace(g, batch, num_q_heads, w_rec);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PKV_EWORKSPACE;
+    // the fp32 kernel plans at every call: nothing to write
+    if (planning && g.dtype != 1) return PKV_OK;
 
     pkv::DecodeArgs a;
     a.q = q;
@@ -297,23 +313,36 @@ pkv_status decode_common(const pkv_cache_desc *cache, void *out, float *lse, con
     a.workers = w;
     a.fixed_workers = workers > 0;
     pkv::decode_mid_cap(dev, g, w_rec, a);
-    a.part_o = nullptr;  // filled by launch_decode from the workspace
+    a.part_o = nullptr;  // filled from the workspace layout at launch
     a.part_ml = nullptr;
     a.arrivals = nullptr;
+    a.plan = nullptr;
+    a.fused = fused ? 1 : 0;
     a.k_new = k_new;
     a.v_new = v_new;
     a.seqlens_out = seqlens_out;
-    if (clear_counters) {
+    if (planning) return launch_status(pkv::launch_decode_plan(g, a, workspace, w_rec, (hipStream_t)stream));
+    if (run == DecodeRun::kCallNoPlan) {
         const pkv_status zs = launch_status(pkv::launch_zero_words(
             (int32_t *)workspace, (int64_t)(pkv::decode_counter_bytes(g, batch) / 4), (hipStream_t)stream));
         if (zs) return zs;
     }
-    return launch_status(pkv::launch_decode(g, a, workspace, w_rec, (hipStream_t)stream));
+    return launch_status(
+        pkv::launch_decode(g, a, workspace, w_rec, run == DecodeRun::kCall, (hipStream_t)stream));
 }
 
 }  // namespace
 
 extern "C" {
+
+pkv_status pkv_decode_plan(const pkv_cache_desc *cache, int32_t num_q_heads, const int32_t *cache_seqlens,
+                           int32_t batch, int32_t max_kv_len, int32_t fused, void *workspace, size_t workspace_bytes,
+                           int32_t workers, void *stream) {
+    if (fused != 0 && fused != 1) return PKV_EINVAL;
+    return decode_common(cache, nullptr, nullptr, nullptr, num_q_heads, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+                         cache_seqlens, nullptr, batch, max_kv_len, 1.f, workspace, workspace_bytes, workers, stream,
+                         DecodeRun::kPlan, fused == 1);
+}
 
 pkv_status pkv_decode_attn_ex(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
                               int32_t num_q_heads, const void *k_cache, const void *v_cache,
@@ -371,7 +400,8 @@ pkv_status pkv_append_decode_attn_noalloc(const pkv_cache_desc *cache, void *out
     // The array keeps the last call's contents: its arrival counters are
     // cleared by a fill kernel on the call's stream before the decode launch.
     return decode_common(cache, out, lse, q, num_q_heads, k_cache, v_cache, k_new, v_new, block_table, bt_cols,
-                         cache_seqlens, seqlens_out, batch, max_kv_len, scale, ws, kScratchBytes, 0, stream, true);
+                         cache_seqlens, seqlens_out, batch, max_kv_len, scale, ws, kScratchBytes, 0, stream,
+                         DecodeRun::kCallNoPlan);
 }
 
 pkv_status pkv_decode_attn(const pkv_cache_desc *cache, void *out, float *lse, const void *q,

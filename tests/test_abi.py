@@ -278,6 +278,24 @@ def test_workspace_reset_rejects_bad_buffers():
     assert reset(4, ctypes.c_void_p((1 << 20) + 4), 1 << 20) == EWORKSPACE  # misaligned
 
 
+def test_decode_plan_rejects_scalars():
+    lib = api.lib()
+    d = _desc()
+    plan = lambda **kw: lib.pkv_decode_plan(ctypes.byref(kw.get("desc", d)), kw.get("hq", 32),
+                                            kw.get("seqlens", FAKE), kw.get("batch", 4), kw.get("max_kv", 64),
+                                            kw.get("fused", 1), FAKE, 1 << 30, kw.get("workers", 0), None)
+    assert plan(fused=2) == EINVAL
+    assert plan(batch=-1) == EINVAL
+    assert plan(batch=0) == OK                       # nothing to plan
+    assert plan(seqlens=None) == EINVAL
+    assert plan(hq=30) == EINVAL                     # Hq % Hkv != 0
+    assert plan(workers=-1) == EINVAL
+    assert plan(max_kv=-1) == EINVAL
+    assert plan(max_kv=(1 << 28) + 1) == EUNSUPPORTED
+    assert plan(desc=_desc(dtype=api.PKV_F32)) == EUNSUPPORTED  # fused calls are bf16 only
+    assert plan(desc=_desc(head_dim=96)) == EUNSUPPORTED
+
+
 def test_binding_requires_scale():
     """The softmax scale is the caller's: the binding computes no default."""
     kc = _cpu_pool()
