@@ -220,3 +220,26 @@ def test_plan_in_graph_replays():
         torch.cuda.synchronize()
         for k in range(2):
             _same(outs[k], refs[k], f"replay {rep} layer {k}")
+
+
+@pytest.mark.parametrize("page,layout,d,hq,hkv", [(64, "HND", 128, 32, 8), (256, "HND", 256, 48, 8),
+                                                  (16, "NHD", 128, 32, 8), (16, "HND", 64, 16, 2),
+                                                  (32, "NHD", 64, 8, 8)])
+def test_planned_calls_every_kernel(page, layout, d, hq, hkv):
+    """Planned fused calls on the other kernel instances (head_dim 64 / 256,
+    pages of 32..256 tokens, NHD) give the bits of unplanned ones."""
+    rng = np.random.default_rng(page + d)
+    hist = np.exp(rng.uniform(0, np.log(3000), 40)).astype(np.int32)
+    spec = wl.custom_decode_spec(hist, hq, hkv, d, "bf16", page + d, layout=layout, page_size=page)
+    say(f"[plan] page={page} {layout} D={d} Hq={hq} Hkv={hkv} B=40")
+    case = DecodeCase(spec)
+    kc, vc = _history(case)
+    lens = case.inp.hist_lens
+    max_kv = int(hist.max()) + 1
+    ref = _fused(case, kc, vc, lens, max_kv, _ws(kc, 40, hq, max_kv, layout))
+    ws = _ws(kc, 40, hq, max_kv, layout)
+    pkv.decode_plan(kc, lens, hq, max_kv, ws, fused=True, layout=layout)
+    for call in range(2):
+        got = _fused(case, kc, vc, lens, max_kv, ws)
+        torch.cuda.synchronize()
+        _same(got, ref, f"planned call {call}")
