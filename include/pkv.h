@@ -199,12 +199,13 @@ pkv_status pkv_decode_workspace_reset(const pkv_cache_desc *cache, int32_t batch
  * cache_seqlens and writes that cut into the plan region of `workspace`.
  * A later pkv_decode_attn / _ex or pkv_append_decode_attn / _ex call given
  * the same workspace reads the plan together with its own lengths, and uses
- * it only if the plan was made for the same descriptor head count, batch,
+ * it only if the plan was made for the same number of KV heads, batch,
  * max_kv_len, worker count and mode (`fused`) and every row's
  * cache_seqlens value still equals the planned one; otherwise the call plans
- * on its own, as it does without this call.  Results are bit-identical
- * either way: the plan only saves the calls the work of cutting (the table
- * is read by each call, so it may change freely).
+ * on its own, as it does without this call.  The cut depends on nothing
+ * else, so results are bit-identical either way: the plan only saves the
+ * calls the work of cutting.  It holds no page ids (each call reads the
+ * table it is given, which may change freely between plan and call).
  *
  *   cache_seqlens  int32 [batch] on the device, as the calls will get it
  *                  (pre-append lengths when fused = 1)
@@ -213,12 +214,18 @@ pkv_status pkv_decode_workspace_reset(const pkv_cache_desc *cache, int32_t batch
  *   workers        as the calls will pass it (0 = automatic)
  *   workspace      a decode workspace of pkv_decode_workspace_bytes_ex(...,
  *                  workers) bytes; only its plan region is written
- * Only bf16 pools use a plan: for fp32 pools the call checks its arguments
- * and enqueues nothing.  pkv_append_decode_attn_noalloc never uses one.  A
- * plan stays in the workspace until the next pkv_decode_plan on it
+ * Only bf16 pools use a plan: for fp32 pools (fused = 0) the call checks its
+ * arguments and enqueues nothing.  pkv_append_decode_attn_noalloc never uses
+ * one.  A plan stays in the workspace until the next pkv_decode_plan on it
  * (pkv_decode_workspace_reset does not clear it).  The plan call must be
  * ordered before the calls that use it (same stream), like every use of a
  * workspace.
+ * Errors: PKV_EINVAL (fused not 0 or 1, negative sizes, NULL cache_seqlens,
+ * num_q_heads not a multiple of the KV heads), PKV_EUNSUPPORTED (descriptor,
+ * more than 16 query heads per KV head, fused = 1 on fp32 pools, max_kv_len
+ * above 2^28), PKV_EWORKSPACE (workspace
+ * missing, misaligned or smaller than the query for this worker count),
+ * PKV_ELAUNCH, PKV_EDEVICE; batch = 0 returns PKV_OK and enqueues nothing.
  */
 pkv_status pkv_decode_plan(const pkv_cache_desc *cache, int32_t num_q_heads, const int32_t *cache_seqlens,
                            int32_t batch, int32_t max_kv_len, int32_t fused, void *workspace,
