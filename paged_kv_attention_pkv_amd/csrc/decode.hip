@@ -16,6 +16,10 @@
 // and cut into ranges of equal cost, one per wavefront: `workers` of them, or
 // fewer on small calls (each wave keeps at least kMinPagesPerWorker pages; the
 // count is decided on the device from the lengths, with no host read-back).
+// The cut depends only on the lengths and the call's shape, so the calls of
+// one decode step (one per layer) may share it: decode_plan_kernel writes it
+// to the workspace once, and a call takes its range from there when the
+// plan matches it exactly (decode_worker.hpp, plan_or_load).
 // A segment costs its pages plus a few virtual ones for the work its start
 // brings, so a range that starts a segment holds fewer pages.  A wave walks its
 // range as one stream of page pairs that crosses segment boundaries without
