@@ -157,6 +157,18 @@ def traffic_from_profile(kind: str, name: str):
     return float(t.group(1))
 
 
+def device_info(torch, props) -> dict:
+    """The GPU the line was measured on: name, ISA, CU count, HIP runtime of
+    the torch build, and the clock and L2 size where torch reports them."""
+    d = {"name": props.name, "arch": getattr(props, "gcnArchName", "?"), "cus": props.multi_processor_count,
+         "hip": getattr(torch.version, "hip", None)}
+    for key in ("clock_rate", "L2_cache_size", "total_memory"):
+        v = getattr(props, key, None)
+        if v is not None:
+            d[key] = v
+    return d
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -981,8 +993,7 @@ def main():
     cpu = not args.no_cpu_baseline
     if args.workload == "tune":
         for line in bench_tune(args, torch, pkv, wl):
-            line["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", "?"),
-                              "cus": props.multi_processor_count}
+            line["device"] = device_info(torch, props)
             print(json.dumps(line), flush=True)
         return
     if args.workload == "mixed":
@@ -1013,8 +1024,7 @@ def main():
                 torch.cuda.empty_cache()
             result["mixed"] = bench_mixed(args, torch, pkv, wl)
             torch.cuda.empty_cache()
-    result["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", "?"),
-                        "cus": props.multi_processor_count}
+    result["device"] = device_info(torch, props)
     print(json.dumps(result), flush=True)
 
 
