@@ -101,3 +101,60 @@ def test_random_prefill(seed):
     r, ro, rl = case.oracle_rows(okc, ovc, okv, obt, oreqs, causal=causal)
     compare(out.cpu()[r], ro, *BF16_TOL, "out")
     compare(lse.cpu()[r], rl, *BF16_TOL, "lse")
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_decode_planned(seed):
+    """bf16 decode steps with the step's plan (pkv_decode_plan) on random
+    shapes: batch 1..300, GQA ratios, head dims, pages of 16..256 tokens,
+    HND or NHD, fused or separate calls, automatic or forced worker counts.
+    Every row against the oracle, and bit for bit against the same call
+    without a plan."""
+    rng = np.random.default_rng(9000 + seed)
+    b = int(rng.integers(1, 301))
+    hq, hkv = HEADS[rng.integers(len(HEADS))]
+    d = int(rng.choice([64, 128, 256]))
+    page = int(rng.choice([16, 16, 32, 64, 128, 256]))
+    layout = "NHD" if rng.random() < 0.3 else "HND"
+    fused = rng.random() < 0.6
+    workers = 0 if rng.random() < 0.6 else int(rng.integers(1, 2000))
+    lens = np.minimum(np.exp(rng.uniform(0, np.log(3000), size=b)).astype(np.int32) - 1, 2999)
+    lens[rng.random(b) < 0.1] = 0
+    say(f"[random planned decode {seed}] B={b} Hq={hq} Hkv={hkv} D={d} page={page} {layout} fused={fused} "
+        f"workers={workers}")
+    spec = wl.custom_decode_spec(lens, hq=hq, hkv=hkv, head_dim=d, dtype="bf16", seed=9500 + seed,
+                                 layout=layout, page_size=page)
+    case = DecodeCase(spec)
+    i = case.inp
+    max_kv = int(spec.hist_lens.max()) + 1
+    if fused:
+        kc, vc = wl.empty_pool(spec, case.dev), wl.empty_pool(spec, case.dev)
+        pkv.append(kc, vc, i.k_hist, i.v_hist, i.block_table, torch.zeros(b, dtype=torch.int32, device=case.dev),
+                   i.hist_indptr, layout=layout)
+        lens_in = i.hist_lens
+    else:
+        kc, vc, lens_in = case.gpu_pools()
+    nbytes = pkv.decode_workspace_bytes(kc, b, hq, max_kv, layout=layout, workers=workers)
+    results = []
+    for planned in (False, True):
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=case.dev)
+        if planned:
+            pkv.decode_plan(kc, lens_in, hq, max_kv, ws, fused=fused, layout=layout, workers=workers)
+        if fused:
+            res = pkv.append_decode_attn(i.q, kc, vc, i.k_new, i.v_new, i.block_table, lens_in, max_kv,
+                                         scale=spec.scale, workspace=ws, layout=layout, workers=workers,
+                                         return_lse=True)
+        else:
+            res = pkv.decode_attn(i.q, kc, vc, i.block_table, lens_in, max_kv, scale=spec.scale, workspace=ws,
+                                  layout=layout, workers=workers, return_lse=True)
+        torch.cuda.synchronize()
+        results.append([t.clone() for t in res])
+    for x, y in zip(*results):
+        assert torch.equal(x.contiguous().view(torch.uint8), y.contiguous().view(torch.uint8)), "plan changed bits"
+    okc, ovc, olens, obt = case.oracle_pools()
+    if fused:
+        assert np.array_equal(results[1][2].cpu().numpy(), olens), "seqlens_out differs"
+        assert np.array_equal(host_bits(kc).view(np.uint8), okc.view(np.uint8)), "K pool not bit-exact"
+    ro, rl = case.oracle_decode(okc, ovc, olens, obt)
+    compare(results[1][0].cpu(), ro, *tol(spec), "out")
+    compare(results[1][1].cpu(), rl, *tol(spec), "lse")
