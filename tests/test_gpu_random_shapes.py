@@ -1,7 +1,8 @@
 """GPU parity on seeded random small shapes, decode and prefill, against the
-oracle: head counts and GQA ratios, head dims, dtypes, layouts, ragged and
-empty rows, forced split-worker counts and prefill tilings drawn at random
-(fixed seeds), every output row compared.  Bar as in the other parity tests."""
+oracle: head counts and GQA ratios, head dims, dtypes, layouts, page sizes,
+ragged and empty rows, forced split-worker counts, planned decode steps and
+prefill tilings drawn at random (fixed seeds), every output row compared.
+Bar as in the other parity tests."""
 import numpy as np
 import pytest
 import torch
@@ -89,10 +90,12 @@ def test_random_prefill(seed):
     q = rng.integers(1, 401, size=b).astype(np.int32)
     kv = (q + rng.integers(0, 601, size=b)).astype(np.int32)
     causal = bool(rng.random() < 0.8)
-    rows = int(rng.choice([0, 128] + ([192] if d == 256 else [])))
-    say(f"[random prefill {seed}] B={b} Hq={hq} Hkv={hkv} D={d} {layout} causal={causal} rows/wg={rows} "
-        f"q={q.tolist()} kv={kv.tolist()}")
-    spec = wl.prefill_spec(q_lens=q, kv_lens=kv, hq=hq, hkv=hkv, head_dim=d, seed=4000 + seed, layout=layout)
+    rows = int(rng.choice([0, 128, 192]))
+    page = int(rng.choice([16, 16, 32, 64, 128, 256]))
+    say(f"[random prefill {seed}] B={b} Hq={hq} Hkv={hkv} D={d} {layout} page={page} causal={causal} "
+        f"rows/wg={rows} q={q.tolist()} kv={kv.tolist()}")
+    spec = wl.prefill_spec(q_lens=q, kv_lens=kv, hq=hq, hkv=hkv, head_dim=d, seed=4000 + seed, layout=layout,
+                           page_size=page)
     case = PrefillCase(spec)
     kc, vc, kvl = case.gpu_pools()
     out, lse = case.gpu_prefill(kc, vc, kvl, causal=causal, rows=rows)
