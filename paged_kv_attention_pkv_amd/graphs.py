@@ -6,7 +6,8 @@ one CUDA graph per batch-size bucket and pads the live batch up to the
 bucket.  ``DecodeStepGraphs`` does the same over this library: for every
 bucket size it owns static buffers (per layer q, k_new, v_new, out, lse; per
 step the block table, cache lengths and new lengths) and one graph holding
-the ``pkv_append_decode_attn`` launch of every layer.  ``stage`` copies the
+one ``pkv_decode_plan`` launch (the cut of the step's work, shared by its
+layers) and the ``pkv_append_decode_attn`` launch of every layer.  ``stage`` copies the
 live rows of a step into the bucket's buffers and marks the other slots as
 padding rows (cache length -1: nothing is read or written for them, their
 output is 0 / -inf and their new length stays -1), ``replay`` runs the graph.
@@ -65,6 +66,9 @@ class DecodeStepGraphs:
                                           buf["out"][i], buf["workspace"], seqlens_out=buf["seqlens_out"],
                                           lse=buf["lse"][i], layout=layout)
                 for i, (kc, vc) in enumerate(self.layers)]
+            if len(self.layers) > 1:
+                buf["calls"].insert(0, api.prepare_decode_plan(k0, buf["cache_seqlens"], self.hq, self.max_kv_len,
+                                                               buf["workspace"], fused=True, layout=layout))
             self._buf[b] = buf
         torch.cuda.synchronize(self.dev)
         for b in self.buckets:
