@@ -278,6 +278,33 @@ __device__ __forceinline__ void wait_transfers(int ahead) {
     }
 }
 
+// Scores of a 64-key tile to log2 units, the causal mask, and the lane's
+// maximum.  Element i of block u is key key0 + 16u + i (key0 = the tile's first
+// key plus 4 * the lane's group).  The mask runs only on tiles that reach past
+// the keys every row of the workgroup sees: as one block behind a uniform
+// branch, it stays a branch, where a test per score would be turned into index
+// compares and selects on every tile.
+template <int NB>
+__device__ __forceinline__ float scale_mask_max(f32x4 (&sc)[NB], float c, bool need_mask, int key0, int limit) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[u][i] *= c;
+    if (need_mask) {
+#pragma unroll
+        for (int u = 0; u < NB; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (key0 + 16 * u + i > limit) sc[u][i] = kNegInff;
+    }
+    float mx = kNegInff;
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[u][i]);
+    return mx;
+}
+
 template <int D, int W>
 __global__ __launch_bounds__(Cfg16<W>::THREADS) __attribute__((amdgpu_waves_per_eu(Cfg16<W>::PER_SIMD,
                                                                                    Cfg16<W>::PER_SIMD)))
@@ -438,19 +465,7 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
             __builtin_amdgcn_s_setprio(0);
             // scores in log2 units; element i of block u is key tile*64 + 16u + 4grp + i
             const bool need_mask = tile * kBN16 + kBN16 - 1 > common_keys;
-            float mx = kNegInff;
-#pragma unroll
-            for (int u = 0; u < NB; ++u)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float x = sc[u][i] * c;
-                    if (need_mask) {
-                        const int j = tile * kBN16 + 16 * u + 4 * grp + i;
-                        x = j <= limit ? x : kNegInff;
-                    }
-                    sc[u][i] = x;
-                    mx = fmaxf(mx, x);
-                }
+            float mx = scale_mask_max<NB>(sc, c, need_mask, tile * kBN16 + 4 * grp, limit);
             mx = rows4_max(mx);
             const bool raise = mx > m + kRescaleSlack;
             if (__any(raise)) {
@@ -798,19 +813,7 @@ void prefill16r_kernel(PrefillArgs a, int n_qtiles, int n_packed, int packed_fir
             __builtin_amdgcn_s_setprio(0);
             // scores in log2 units; element i of block u is key tile*64 + 16u + 4grp + i
             const bool need_mask = tile * kBN16 + kBN16 - 1 > common_keys;
-            float mx = kNegInff;
-#pragma unroll
-            for (int u = 0; u < NB; ++u)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float x = sc[u][i] * c;
-                    if (need_mask) {
-                        const int j = tile * kBN16 + 16 * u + 4 * grp + i;
-                        x = j <= limit ? x : kNegInff;
-                    }
-                    sc[u][i] = x;
-                    mx = fmaxf(mx, x);
-                }
+            float mx = scale_mask_max<NB>(sc, c, need_mask, tile * kBN16 + 4 * grp, limit);
             mx = rows4_max(mx);
             const bool raise = mx > m + kRescaleSlack;
             if (__any(raise)) {
