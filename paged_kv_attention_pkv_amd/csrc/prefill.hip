@@ -16,8 +16,8 @@
 // head_dim 256 runs prefill16_kernel, whose tiles move from HBM to LDS by
 // buffer-to-LDS transfers; head_dim 64 and 128 run prefill16r_kernel, whose
 // tiles pass through registers (their rows need a padded layout that whole
-// 1 KB transfers cannot write).  Scores carry the softmax scale folded into
-// log2 units and use exp2; Q stays in registers for the whole walk; the V^T
+// 1 KB transfers cannot write).  The softmax scale, in log2 units, is applied
+// inside exp2 (one fma per score with the max subtracted); Q stays in registers for the whole walk; the V^T
 // operand comes straight from the [key][dim] rows through gfx950's
 // transposing LDS read.  Keys at or past kv_r (tail slots of the last page,
 // which may hold anything) load as zeros and masked scores get -inf; tiles
@@ -278,18 +278,30 @@ __device__ __forceinline__ void wait_transfers(int ahead) {
     }
 }
 
-// Scores of a 64-key tile to log2 units, the causal mask, and the lane's
-// maximum.  Element i of block u is key key0 + 16u + i (key0 = the tile's first
-// key plus 4 * the lane's group).  The mask runs only on tiles that reach past
-// the keys every row of the workgroup sees: as one block behind a uniform
-// branch, it stays a branch, where a test per score would be turned into index
-// compares and selects on every tile.
+// The scores of a tile enter exp2 as fma(s, c, -m), scaled there, which keeps
+// their order only for c > 0.  A negative scale is applied as the negated
+// query (bf16 sign bits flipped: every product, and so every score, exactly
+// negated) times |c|.  A zero scale is taken as the smallest normal float:
+// every weight exp2(s * 2^-126 - m) is then 1 up to rounding for any score
+// below 2^100, as with a zero scale.
+template <int KS>
+__device__ __forceinline__ float positive_scale(float c, u32x4 (&qop)[KS]) {
+    if (c < 0.f) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qop[ks] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+        return -c;
+    }
+    return c > 0.f ? c : 1.17549435e-38f;
+}
+
+// The causal mask on the raw scores of a 64-key tile, and the row's scaled
+// maximum on this lane (c > 0).  Element i of block u is key key0 + 16u + i
+// (key0 = the tile's first key plus 4 * the lane's group).  The mask runs only
+// on tiles that reach past the keys every row of the workgroup sees: as one
+// block behind a uniform branch, it stays a branch, where a test per score
+// would be turned into index compares and selects on every tile.
 template <int NB>
-__device__ __forceinline__ float scale_mask_max(f32x4 (&sc)[NB], float c, bool need_mask, int key0, int limit) {
-#pragma unroll
-    for (int u = 0; u < NB; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[u][i] *= c;
+__device__ __forceinline__ float mask_max(f32x4 (&sc)[NB], float c, bool need_mask, int key0, int limit) {
     if (need_mask) {
 #pragma unroll
         for (int u = 0; u < NB; ++u)
@@ -302,7 +314,7 @@ __device__ __forceinline__ float scale_mask_max(f32x4 (&sc)[NB], float c, bool n
     for (int u = 0; u < NB; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[u][i]);
-    return mx;
+    return mx * c;
 }
 
 template <int D, int W>
@@ -382,7 +394,7 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = kNegInff, l = 0.f;  // l: this lane's part of the row sum
-    const float c = a.scale_log2;
+    const float c = positive_scale<KS>(a.scale_log2, qop);
     // Lane offsets in the row-pair layout.  A chunk index's bit 3 flips in
     // odd rows, so each pattern has two lane bases: one for reads whose
     // chunk has bit 3 clear (the odd rows' chunk moves up 8) and one for the
@@ -463,9 +475,9 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
                                                                     __builtin_bit_cast(bf16x8, qop[k]), sc[u], 0, 0, 0);
             }
             __builtin_amdgcn_s_setprio(0);
-            // scores in log2 units; element i of block u is key tile*64 + 16u + 4grp + i
+            // raw scores (scaled inside exp2); element i of block u is key tile*64 + 16u + 4grp + i
             const bool need_mask = tile * kBN16 + kBN16 - 1 > common_keys;
-            float mx = scale_mask_max<NB>(sc, c, need_mask, tile * kBN16 + 4 * grp, limit);
+            float mx = mask_max<NB>(sc, c, need_mask, tile * kBN16 + 4 * grp, limit);
             mx = rows4_max(mx);
             const bool raise = mx > m + kRescaleSlack;
             if (__any(raise)) {
@@ -483,8 +495,8 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
                 float p[8];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    p[i] = fast_exp2(sc[2 * t][i] - m);
-                    p[4 + i] = fast_exp2(sc[2 * t + 1][i] - m);
+                    p[i] = fast_exp2(fmaf(sc[2 * t][i], c, -m));
+                    p[4 + i] = fast_exp2(fmaf(sc[2 * t + 1][i], c, -m));
                 }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) l += p[i];
@@ -766,7 +778,7 @@ void prefill16r_kernel(PrefillArgs a, int n_qtiles, int n_packed, int packed_fir
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = kNegInff, l = 0.f;  // l: this lane's part of the row sum
-    const float c = a.scale_log2;
+    const float c = positive_scale<KS>(a.scale_log2, qop);
     // K operand: row 16u + col, dims 32k + 8grp; V^T transposing reads: lane
     // 4a+b of its group names key 32t + 4grp + a (and +16), dims 16db + 4b
     const int k_base = reg16_row(col, R::RS) + 8 * grp;
@@ -811,9 +823,9 @@ void prefill16r_kernel(PrefillArgs a, int n_qtiles, int n_packed, int packed_fir
                                                                     __builtin_bit_cast(bf16x8, qop[k]), sc[u], 0, 0, 0);
             }
             __builtin_amdgcn_s_setprio(0);
-            // scores in log2 units; element i of block u is key tile*64 + 16u + 4grp + i
+            // raw scores (scaled inside exp2); element i of block u is key tile*64 + 16u + 4grp + i
             const bool need_mask = tile * kBN16 + kBN16 - 1 > common_keys;
-            float mx = scale_mask_max<NB>(sc, c, need_mask, tile * kBN16 + 4 * grp, limit);
+            float mx = mask_max<NB>(sc, c, need_mask, tile * kBN16 + 4 * grp, limit);
             mx = rows4_max(mx);
             const bool raise = mx > m + kRescaleSlack;
             if (__any(raise)) {
@@ -830,8 +842,8 @@ void prefill16r_kernel(PrefillArgs a, int n_qtiles, int n_packed, int packed_fir
                 float p[8];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    p[i] = fast_exp2(sc[2 * t][i] - m);
-                    p[4 + i] = fast_exp2(sc[2 * t + 1][i] - m);
+                    p[i] = fast_exp2(fmaf(sc[2 * t][i], c, -m));
+                    p[4 + i] = fast_exp2(fmaf(sc[2 * t + 1][i], c, -m));
                 }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) l += p[i];

@@ -134,6 +134,22 @@ class DecodeCase:
                                     nthreads=nthreads or min(16, os.cpu_count() or 1))
 
 
+def with_scale(spec, scale: float):
+    """The same workload with another softmax scale (the specs derive theirs
+    from head_dim)."""
+    import dataclasses
+
+    @dataclasses.dataclass
+    class Scaled(type(spec)):
+        scale_value: float = 0.0
+
+        @property
+        def scale(self):
+            return self.scale_value
+
+    return Scaled(**{f.name: getattr(spec, f.name) for f in dataclasses.fields(spec)}, scale_value=float(scale))
+
+
 def scale_of(d):
     return float(np.float32(1.0 / math.sqrt(d)))
 

@@ -9,7 +9,7 @@ import torch
 
 import paged_kv_attention_pkv_amd as pkv
 from paged_kv_attention_pkv_amd import workloads as wl
-from gpu_common import BF16_TOL, PrefillCase, compare, say
+from gpu_common import BF16_TOL, PrefillCase, compare, say, with_scale
 from test_gpu_prefill import tile_edge_rows
 
 pytestmark = pytest.mark.gpu
@@ -111,3 +111,12 @@ def test_mixed_empty_decode_rows():
         assert torch.all(o[r] == 0) and torch.all(torch.isneginf(l[r])), r
     keep = [x for x in range(104) if x not in (101, 103)]
     assert torch.equal(out[keep].view(torch.int16), ref[keep].view(torch.int16))
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+def test_mixed_negative_and_zero_scale(scale):
+    """Chunks and packed decode rows with a negative and a zero softmax
+    scale (applied as the negated query, and as the smallest normal float)."""
+    q = [65, 129, 1, 1, 1, 1]
+    kv = [200, 1000, 1, 17, 700, 2049]
+    _check(with_scale(wl.prefill_spec(q_lens=q, kv_lens=kv, hq=32, hkv=8, head_dim=128, seed=31), scale), 2)

@@ -11,7 +11,7 @@ import torch
 
 import paged_kv_attention_pkv_amd as pkv
 from paged_kv_attention_pkv_amd import workloads as wl
-from gpu_common import BF16_TOL, PrefillCase, compare, say
+from gpu_common import BF16_TOL, PrefillCase, compare, say, with_scale
 
 pytestmark = pytest.mark.gpu
 
@@ -209,3 +209,24 @@ def test_long_kv_restages_table_window(rows):
     see every key) are checked."""
     spec = wl.prefill_spec(q_lens=[40], kv_lens=[70000], hq=8, hkv=8, head_dim=256, seed=11)
     _parity(spec, sample=4, gen_device="cuda", rows=rows)
+
+
+@pytest.mark.parametrize("scale", [-0.0625, 0.0, 1e-3, 0.5])
+@pytest.mark.parametrize("d", [128, 256])
+def test_prefill_any_scale(d, scale):
+    """The scale is applied inside exp2 by an fma that needs it positive:
+    a negative scale runs as the negated query times |scale|, a zero scale as
+    the smallest normal float.  Every row against the oracle, which takes the
+    scale as given."""
+    base = wl.prefill_spec(q_lens=[200, 65, 1], kv_lens=[450, 300, 90], hq=32 if d == 128 else 48, hkv=8,
+                           head_dim=d, seed=17)
+    spec = with_scale(base, scale)
+    say(f"[prefill scale] D={d} scale={scale}")
+    case = PrefillCase(spec)
+    kc, vc, kv = case.gpu_pools()
+    out, lse = case.gpu_prefill(kc, vc, kv)
+    torch.cuda.synchronize()
+    okc, ovc, okv, obt, oreqs = case.oracle_pools()
+    rows, ro, rl = case.oracle_rows(okc, ovc, okv, obt, oreqs)
+    say("  out:", compare(out.cpu()[rows], ro, *BF16_TOL, "out"))
+    compare(lse.cpu()[rows], rl, *BF16_TOL, "lse")
