@@ -88,6 +88,8 @@ def parse():
     p.add_argument("--separate", action="store_true",
                    help="decode step as pkv_append + pkv_decode_attn (two launches) instead of the fused "
                         "pkv_append_decode_attn")
+    p.add_argument("--decode-heads", default=None,
+                   help="decode/sweep/long: HQ,HKV,D in place of the Qwen3 shape 32,8,128 (same lengths and pages)")
     p.add_argument("--no-plan", action="store_true",
                    help="decode: no pkv_decode_plan per step (every call cuts the work itself)")
     p.add_argument("--head-dim", type=int, default=256, help="prefill: head_dim (64, 128 or 256)")
@@ -247,7 +249,8 @@ def spread(per, scale=1.0, nd=2):
 # --------------------------------------------------------------------------
 
 def bench_decode(args, torch, pkv, wl, workload):
-    kw = dict(page_size=args.page_size, layout=args.layout, contiguous=args.contiguous)
+    kw = dict(page_size=args.page_size, layout=args.layout, contiguous=args.contiguous,
+              heads=tuple(int(x) for x in args.decode_heads.split(",")) if args.decode_heads else None)
     if workload == "decode":
         spec = wl.decode_spec("qwen3_decode", batch=args.batch or 64, **kw)
     elif workload == "sweep":

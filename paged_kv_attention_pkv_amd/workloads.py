@@ -140,10 +140,15 @@ def _decode_from_lengths(name, hist, n_new, hq, hkv, d, dtype, max_hist, slack, 
 
 
 def decode_spec(workload: str, batch: int | None = None, seed: int | None = None,
-                layout: str = "HND", page_size: int = PAGE_SIZE, contiguous: bool = False) -> DecodeSpec:
+                layout: str = "HND", page_size: int = PAGE_SIZE, contiguous: bool = False,
+                heads: tuple | None = None) -> DecodeSpec:
     """Lengths, pool size and block table of one decode workload (pages of
     `page_size` tokens, the named workloads use 16; pages dealt shuffled, or
-    in order with `contiguous`)."""
+    in order with `contiguous`).  `heads` = (Hq, Hkv, head_dim) replaces the
+    Qwen3 shape (32, 8, 128) of the bf16 workloads, with the same lengths
+    and pages; the name then carries the shape."""
+    hq, hkv, d = (32, 8, 128) if heads is None else (int(heads[0]), int(heads[1]), int(heads[2]))
+    tag = "" if heads is None else f"_hq{hq}_hkv{hkv}_d{d}"
     if workload == "tiny_f32":
         seed = 1 if seed is None else seed
         rng = np.random.default_rng(seed)
@@ -155,7 +160,7 @@ def decode_spec(workload: str, batch: int | None = None, seed: int | None = None
         seed = 2 if seed is None else seed
         rng = np.random.default_rng(seed)
         hist = rng.integers(512, 1024, size=batch, endpoint=True)
-        return _decode_from_lengths(f"qwen3_decode_b{batch}", hist, 1, 32, 8, 128, "bf16", 1024,
+        return _decode_from_lengths(f"qwen3_decode_b{batch}{tag}", hist, 1, hq, hkv, d, "bf16", 1024,
                                     1.25, seed, rng, layout=layout,
                                     page_size=page_size, contiguous=contiguous)
     if workload == "qwen3_sweep":
@@ -165,7 +170,7 @@ def decode_spec(workload: str, batch: int | None = None, seed: int | None = None
         rng = np.random.default_rng(seed)
         prompt = rng.integers(64, 512, size=batch, endpoint=True)
         gen = rng.integers(0, 512, size=batch, endpoint=True)
-        return _decode_from_lengths(f"qwen3_sweep_b{batch}", prompt + gen, 1, 32, 8, 128, "bf16",
+        return _decode_from_lengths(f"qwen3_sweep_b{batch}{tag}", prompt + gen, 1, hq, hkv, d, "bf16",
                                     1024, 1.25, seed, rng, layout=layout,
                                     page_size=page_size, contiguous=contiguous)
     if workload == "long_ragged":
@@ -174,7 +179,7 @@ def decode_spec(workload: str, batch: int | None = None, seed: int | None = None
         rng = np.random.default_rng(seed)
         u = rng.uniform(math.log(16.0), math.log(32768.0), size=batch)
         hist = np.clip(np.rint(np.exp(u)), 16, 32768).astype(np.int32)
-        return _decode_from_lengths(f"long_ragged_b{batch}", hist, 1, 32, 8, 128, "bf16", 32768,
+        return _decode_from_lengths(f"long_ragged_b{batch}{tag}", hist, 1, hq, hkv, d, "bf16", 32768,
                                     1.0, seed, rng, layout=layout,
                                     page_size=page_size, contiguous=contiguous)
     raise ValueError(f"unknown decode workload {workload!r}")

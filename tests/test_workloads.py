@@ -125,3 +125,14 @@ def test_contiguous_pages_are_runs_and_keep_the_draws():
         nxt += n
     for x, y in zip(wl.decode_inputs(a).q, wl.decode_inputs(b).q):
         assert torch.equal(x, y)
+
+
+def test_decode_heads_keep_lengths_and_pages():
+    """Another head shape for a named decode workload changes only the
+    shape: the lengths, the pool size and the dealt pages stay."""
+    for name, batch in (("qwen3_decode", 64), ("qwen3_sweep", 8), ("long_ragged", 16)):
+        a = wl.decode_spec(name, batch=batch)
+        b = wl.decode_spec(name, batch=batch, heads=(16, 8, 256))
+        assert (b.hq, b.hkv, b.head_dim) == (16, 8, 256) and (a.hq, a.hkv, a.head_dim) == (32, 8, 128)
+        assert np.array_equal(a.hist_lens, b.hist_lens) and np.array_equal(a.block_table, b.block_table)
+        assert a.num_pages == b.num_pages and b.name == a.name + "_hq16_hkv8_d256"
