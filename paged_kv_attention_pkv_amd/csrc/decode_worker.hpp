@@ -265,7 +265,7 @@ constexpr int kPlanMagic = 0x504b5650;
 constexpr int kPlanHdr = 64;  // words (256 bytes)
 constexpr int kPlanRec = 16;  // words per worker
 
-__device__ __forceinline__ int plan_lens_words(int batch) { return (batch + 63) & ~63; }
+__device__ __forceinline__ int64_t plan_lens_words(int batch) { return ((int64_t)batch + 63) & ~(int64_t)63; }
 
 // Header word k (0..15) of a plan for the call `a`.
 __device__ __forceinline__ int plan_word(const DecodeArgs &a, int k) {

@@ -17,14 +17,15 @@
 // buffer-to-LDS transfers; head_dim 64 and 128 run prefill16r_kernel, whose
 // tiles pass through registers (their rows need a padded layout that whole
 // 1 KB transfers cannot write).  The softmax scale, in log2 units, is applied
-// inside exp2 (one fma per score with the max subtracted); Q stays in registers for the whole walk; the V^T
-// operand comes straight from the [key][dim] rows through gfx950's
-// transposing LDS read.  Keys at or past kv_r (tail slots of the last page,
-// which may hold anything) load as zeros and masked scores get -inf; tiles
-// that no row of a wave needs are skipped and tiles no row's limit cuts are
-// not masked.  Tiles are scheduled longest first (causal rows late in a
-// request see the most keys), and whole groups of the G query heads of one
-// KV head, which read the same K/V tiles, are dealt to one XCD.
+// inside exp2 (one fma per score with the max subtracted); Q stays in
+// registers for the whole walk; the V^T operand comes straight from the
+// [key][dim] rows through gfx950's transposing LDS read.  Keys at or past
+// kv_r (tail slots of the last page, which may hold anything) load as zeros
+// and masked scores get -inf; tiles that no row of a wave needs are skipped
+// and tiles no row's limit cuts are not masked.  Tiles are scheduled longest
+// first (causal rows late in a request see the most keys), and whole groups
+// of the G query heads of one KV head, which read the same K/V tiles, are
+// dealt to one XCD.
 //
 // The mixed launch (pkv_mixed_attn) runs prefill16r_kernel over one work
 // list: the chunks' (request, tile, head) workgroups, then the one-row
