@@ -414,9 +414,9 @@ pkv_status pkv_prefill_attn_ex(const pkv_cache_desc *cache, void *out, float *ls
  * The flex-vs-vLLM results page ("What's left on the table", chunked
  * prefill) names the separate prefill pass as the main penalty left at large
  * batch; a serving step that runs new-prompt chunks and decode rows over one
- * pool does both here in one kernel launch, whose work list holds the decode
- * rows first (one workgroup per decode row and KV head, that KV head's query
- * heads computed together) and then the chunks' query tiles.
+ * pool does both here in one kernel launch, whose work list holds the
+ * chunks' query tiles and then the decode rows (one workgroup per decode row
+ * and KV head, that KV head's query heads computed together).
  *
  * The batch is ordered: requests 0 .. num_prefill-1 are prefill chunks, the
  * remaining batch - num_prefill requests are decode rows.
@@ -432,9 +432,18 @@ pkv_status pkv_prefill_attn_ex(const pkv_cache_desc *cache, void *out, float *ls
  * all kv_r keys (0 keys: out = 0, lse = -inf).  The chunk rows are bit for
  * bit those of pkv_prefill_attn on the chunks; the decode rows equal
  * pkv_decode_attn's up to rounding order.  bf16, head_dim 64 or 128 only
- * (PKV_EUNSUPPORTED otherwise).  No workspace is used: pkv_mixed_workspace_bytes
- * returns a token size for valid arguments (0 otherwise), and the workspace
- * arguments of pkv_mixed_attn are ignored (NULL and 0 are accepted).
+ * (PKV_EUNSUPPORTED otherwise).
+ * Long decode rows: a decode row in that launch is not split across
+ * workgroups, so a row of many keys would hold the launch.  With max_kv_len
+ * above 8192 the call therefore enqueues two launches instead: the chunks as
+ * pkv_prefill_attn and the decode rows as pkv_decode_attn (bit for bit
+ * those calls' results), and only then is the workspace used.
+ *   workspace  device buffer of pkv_mixed_workspace_bytes(...) bytes (the
+ *              decode rows' pkv_decode_attn workspace; a token size when
+ *              every request is a chunk; 0 for invalid arguments), zero-filled
+ *              before its first use like a decode workspace.  Calls with
+ *              max_kv_len <= 8192 use none (NULL and 0 are accepted there);
+ *              the others return PKV_EWORKSPACE without one.
  */
 size_t pkv_mixed_workspace_bytes(const pkv_cache_desc *cache, int32_t batch, int32_t num_prefill,
                                  int32_t num_q_heads);

@@ -500,6 +500,11 @@ def prefill_attn(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, max_q: in
     return (out, lse) if lse is not None else out
 
 
+# max_kv_len above which pkv_mixed_attn runs its decode rows as a split
+# decode launch (and needs its workspace); include/pkv.h states the same.
+MIXED_PACKED_MAX_KV = 8192
+
+
 def mixed_workspace_bytes(k_cache, batch: int, num_prefill: int, num_q_heads: int, layout: str = "HND") -> int:
     desc = cache_desc(k_cache, None, layout)
     with torch.cuda.device(k_cache.device):
@@ -530,14 +535,18 @@ def _mixed_args(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, num_prefil
 def mixed_attn(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, num_prefill: int, max_q: int, max_kv_len: int,
                scale: float, out=None, lse=None, workspace=None, layout: str = "HND", return_lse: bool = False):
     """pkv_mixed_attn: requests 0..num_prefill-1 are causal prefill chunks,
-    the others decode rows (one query row each, the last query rows), all
-    in one launch (no workspace is used; one may still be passed).  Returns
+    the others decode rows (one query row each, the last query rows), in one
+    launch (two when max_kv_len exceeds 8192: then a zeroed workspace of
+    pkv_mixed_workspace_bytes is allocated here when none is given).  Returns
     out (and lse when return_lse or lse is given)."""
     if out is None:
         out = torch.empty_like(q)
     total_q, hq, _ = q.shape
     if lse is None and return_lse:
         lse = torch.empty((total_q, hq), dtype=torch.float32, device=q.device)
+    if workspace is None and max_kv_len > MIXED_PACKED_MAX_KV:
+        workspace = torch.zeros(mixed_workspace_bytes(k_cache, kv_lens.shape[0], num_prefill, hq, layout=layout),
+                                dtype=torch.uint8, device=q.device)
     _, args = _mixed_args(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, num_prefill, max_q, max_kv_len,
                           scale, out, lse, workspace, layout)
     with torch.cuda.device(q.device):
@@ -550,6 +559,11 @@ def prepare_mixed(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, num_pref
                   max_kv_len: int, scale: float, out, workspace=None, lse=None, layout: str = "HND") -> "PreparedCall":
     desc, args = _mixed_args(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, num_prefill, max_q, max_kv_len,
                              scale, out, lse, workspace, layout)
+    if max_kv_len > MIXED_PACKED_MAX_KV and num_prefill < kv_lens.shape[0]:
+        need = mixed_workspace_bytes(k_cache, kv_lens.shape[0], num_prefill, q.shape[1], layout=layout)
+        have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        if have < need:
+            raise PkvError("pkv_mixed_attn", 3, f"workspace {have} < {need} bytes (max_kv_len > {MIXED_PACKED_MAX_KV})")
     return PreparedCall("pkv_mixed_attn", args, (k_cache, v_cache, q, out, block_table, kv_lens, qo_indptr,
                                                  workspace, lse, desc))
 

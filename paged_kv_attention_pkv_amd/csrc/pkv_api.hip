@@ -19,6 +19,12 @@ namespace {
 
 constexpr int kSub = 16;  // tokens per sub-page, the unit the kernels walk keys in
 constexpr int32_t kMaxDecodeKv = 1 << 28;  // decode: max_kv_len bound (PKV_EUNSUPPORTED above)
+// Above this max_kv_len the decode rows of a mixed call run as a split decode
+// launch beside the chunks' prefill launch.  Packed into one workgroup per
+// row and KV head, a decode row walks all its keys alone: with decode rows of
+// up to 32768 keys the one launch took 741 us per layer against 331 us for the
+// two; with rows of up to 4096 keys the one launch is still faster (244 vs 252).
+constexpr int32_t kMixedPackedMaxKv = 8192;
 constexpr int32_t kPaddingRow = -1;        // cache length of a padding row (appends and decode steps)
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -488,7 +494,12 @@ size_t pkv_mixed_workspace_bytes(const pkv_cache_desc *cache, int32_t batch, int
     PoolGeom g;
     if (check_desc(cache, &g) || check_heads(g, num_q_heads) || batch < 1 || num_prefill < 0 || num_prefill > batch)
         return 0;
-    return 256;  // nothing is used; a token size keeps the query non-zero for valid arguments
+    const int n_dec = batch - num_prefill;
+    if (n_dec == 0) return 256;  // nothing is used; a token size keeps the query non-zero for valid arguments
+    // the decode rows' workspace, for calls whose decode rows run split (max_kv_len above kMixedPackedMaxKv)
+    const int w = pkv::decode_workers(current_device(), g, num_q_heads, -1, 0);
+    if (w < 1) return 0;
+    return pkv::decode_workspace(g, n_dec, num_q_heads, w);
 }
 
 pkv_status pkv_mixed_attn(const pkv_cache_desc *cache, void *out, float *lse, const void *q, int32_t num_q_heads,
@@ -496,8 +507,6 @@ pkv_status pkv_mixed_attn(const pkv_cache_desc *cache, void *out, float *lse, co
                           const int32_t *kv_lens, const int32_t *qo_indptr, int32_t batch, int32_t num_prefill,
                           int32_t total_q, int32_t max_q, int32_t max_kv_len, float scale, void *workspace,
                           size_t workspace_bytes, void *stream) {
-    (void)workspace;  // the launch keeps no state between its workgroups
-    (void)workspace_bytes;
     PoolGeom g;
     pkv_status st = check_desc(cache, &g);
     if (st) return st;
@@ -540,6 +549,21 @@ pkv_status pkv_mixed_attn(const pkv_cache_desc *cache, void *out, float *lse, co
     pa.causal = 1;
     pa.scale_log2 = scale * 1.4426950408889634f;
     pa.wg_rows = 0;
+    if (n_dec > 0 && max_kv_len > kMixedPackedMaxKv) {
+        // long decode rows: the chunks as pkv_prefill_attn, the decode rows (the
+        // last n_dec query rows, one each) as pkv_decode_attn, split across workers
+        if (pf_rows > 0) {
+            pa.batch = num_prefill;
+            pa.total_q = (int)pf_rows;
+            const pkv_status ps = launch_status(pkv::launch_prefill(g, pa, (hipStream_t)stream));
+            if (ps) return ps;
+        }
+        const int64_t off = pf_rows * num_q_heads * g.head_dim * 2;  // bytes (bf16)
+        return decode_common(cache, (char *)out + off, lse ? lse + pf_rows * num_q_heads : nullptr,
+                             (const char *)q + off, num_q_heads, k_cache, v_cache, nullptr, nullptr,
+                             block_table + (int64_t)num_prefill * bt_cols, bt_cols, kv_lens + num_prefill, nullptr,
+                             n_dec, max_kv_len, scale, workspace, workspace_bytes, 0, stream);
+    }
     // decode rows: requests num_prefill .. batch-1, one query row each
     return launch_status(pkv::launch_mixed(g, pa, n_dec, num_prefill, (hipStream_t)stream));
 }

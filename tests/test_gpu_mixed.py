@@ -120,3 +120,34 @@ def test_mixed_negative_and_zero_scale(scale):
     q = [65, 129, 1, 1, 1, 1]
     kv = [200, 1000, 1, 17, 700, 2049]
     _check(with_scale(wl.prefill_spec(q_lens=q, kv_lens=kv, hq=32, hkv=8, head_dim=128, seed=31), scale), 2)
+
+
+def test_mixed_long_decode_rows_split():
+    """With max_kv_len above 8192 the decode rows run as a split decode
+    launch beside the chunks' prefill launch: every row against the oracle,
+    chunk rows bit-equal to pkv_prefill_attn and decode rows to
+    pkv_decode_attn; without a workspace the call reports PKV_EWORKSPACE."""
+    rng = np.random.default_rng(41)
+    q = [130, 65, 1, 1, 1, 1, 1, 1, 1, 1]
+    dec = np.clip(np.rint(np.exp(rng.uniform(np.log(16), np.log(20000), size=8))), 16, 20000).astype(int) + 1
+    kv = [400, 2000] + dec.tolist()
+    spec = wl.prefill_spec(q_lens=q, kv_lens=kv, hq=32, hkv=8, head_dim=128, seed=41)
+    assert int(spec.kv_lens.max()) > pkv.api.MIXED_PACKED_MAX_KV
+    case, kc, vc, kv_d, out, lse = _check(spec, 2)
+    i, s = case.inp, spec
+    P, npf = 2, int(spec.q_lens[:2].sum())
+    max_kv = int(s.kv_lens.max())
+    ref_p, ref_pl = pkv.prefill_attn(i.q[:npf], kc, vc, i.block_table[:P], kv_d[:P], i.qo_indptr[:P + 1],
+                                     int(s.q_lens[:P].max()), max_kv, scale=s.scale, return_lse=True)
+    ref_d, ref_dl = pkv.decode_attn(i.q[npf:].contiguous(), kc, vc, i.block_table[P:].contiguous(),
+                                    kv_d[P:].contiguous(), max_kv, scale=s.scale, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:npf].view(torch.int16), ref_p.view(torch.int16)), "chunk rows differ from prefill_attn"
+    assert torch.equal(lse[:npf].view(torch.int32), ref_pl.view(torch.int32))
+    assert torch.equal(out[npf:].view(torch.int16), ref_d.view(torch.int16)), "decode rows differ from decode_attn"
+    assert torch.equal(lse[npf:].view(torch.int32), ref_dl.view(torch.int32))
+    # the raw call without a workspace
+    desc, args = pkv.api._mixed_args(i.q, kc, vc, i.block_table, kv_d, i.qo_indptr, P, int(s.q_lens[:P].max()),
+                                     max_kv, s.scale, torch.empty_like(i.q), None, None, "HND")
+    rc = pkv.api.lib().pkv_mixed_attn(*args, pkv.api._stream(kc))
+    assert rc == 3, rc
