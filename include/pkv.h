@@ -378,7 +378,24 @@ pkv_status pkv_append_decode_attn_noalloc(const pkv_cache_desc *cache, void *out
  *   qo_indptr  int32 [batch+1], device: ragged query offsets, qo_indptr[0] = 0,
  *              qo_indptr[batch] = total_q, 0 <= q_r (<= kv_r when causal)
  *   max_q      host upper bound of q_r; max_kv_len host upper bound of kv_r
+ *   workspace  NULL, or device memory of at least pkv_prefill_workspace_bytes
+ *              (same arguments, same current device), 16-byte aligned and
+ *              zero-filled before its first use; each call leaves it ready
+ *              for the next.  Calls that share one must not overlap.
  * Only PKV_BF16 is supported by this entry point.
+ *
+ * Key splits: a call whose (request, 128-row query tile, query head)
+ * workgroups number at most half the device's CUs, and whose longest request
+ * has more than 960 keys, cuts each workgroup's keys into S pieces when it is
+ * given a workspace: S = CUs / workgroups (rounded down), at most one piece
+ * per 512 keys of the longest request and at most 16.  The pieces' partial
+ * rows meet in the workspace and are merged in a fixed piece order, so
+ * results are deterministic.  They equal the unsplit results up to rounding
+ * (the online softmax rescales at other points), not bit for bit.
+ * pkv_prefill_workspace_bytes returns 0 when the call would not split; the
+ * workspace may then be NULL.  Without a workspace (NULL) the keys are never
+ * split and no error is returned; a workspace smaller than needed gives
+ * PKV_EWORKSPACE.
  */
 size_t pkv_prefill_workspace_bytes(const pkv_cache_desc *cache, int32_t batch,
                                    int32_t num_q_heads, int32_t total_q, int32_t max_q,
@@ -391,13 +408,15 @@ pkv_status pkv_prefill_attn(const pkv_cache_desc *cache, void *out, float *lse, 
                             void *workspace, size_t workspace_bytes, void *stream);
 /*
  * As pkv_prefill_attn, with the query rows per workgroup chosen by the caller
- * (the outputs are the same; only the speed differs):
+ * (the outputs of 128 and 192 are the same; only the speed differs):
  *   rows_per_workgroup  0: the library's choice (what pkv_prefill_attn does);
  *                       128: 8 waves of 16 rows;
  *                       192: 12 waves of 16 rows.
  * Any other value gives PKV_EINVAL.  At head_dim 256 the library takes 192
  * once the call has work for about one and a half rounds of 192-row
- * workgroups on every CU, else 128; at head_dim 64 and 128 it takes 192.
+ * workgroups on every CU, else 128; at head_dim 64 and 128 it takes 192.  A
+ * call that splits its keys (see above) runs 128.  With 128 or 192 the keys
+ * are never split and the workspace is not used.
  */
 pkv_status pkv_prefill_attn_ex(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
                                int32_t num_q_heads, const void *k_cache, const void *v_cache,
@@ -430,14 +449,16 @@ pkv_status pkv_prefill_attn_ex(const pkv_cache_desc *cache, void *out, float *ls
  * Chunk rows are causal, end-aligned: row i of a chunk sees keys
  * 0 .. kv_r - q_r + i (FlashInfer PR #9451 analysis, §1); a decode row sees
  * all kv_r keys (0 keys: out = 0, lse = -inf).  The chunk rows are bit for
- * bit those of pkv_prefill_attn on the chunks; the decode rows equal
+ * bit those of pkv_prefill_attn on the chunks without a workspace (the
+ * chunks' keys are never split here); the decode rows equal
  * pkv_decode_attn's up to rounding order.  bf16, head_dim 64 or 128 only
  * (PKV_EUNSUPPORTED otherwise).
  * Long decode rows: a decode row in that launch is not split across
  * workgroups, so a row of many keys would hold the launch.  With max_kv_len
  * above 8192 the call therefore enqueues two launches instead: the chunks as
- * pkv_prefill_attn and the decode rows as pkv_decode_attn (bit for bit
- * those calls' results), and only then is the workspace used.
+ * pkv_prefill_attn without a workspace and the decode rows as
+ * pkv_decode_attn (bit for bit those calls' results), and only then is the
+ * workspace used.
  *   workspace  device buffer of pkv_mixed_workspace_bytes(...) bytes (the
  *              decode rows' pkv_decode_attn workspace; a token size when
  *              every request is a chunk; 0 for invalid arguments), zero-filled

@@ -460,16 +460,21 @@ def append_decode_attn_noalloc(q, k_cache, v_cache, k_new, v_new, block_table, c
 
 def prefill_workspace_bytes(k_cache, batch, num_q_heads, total_q, max_q, max_kv_len, layout="HND") -> int:
     desc = cache_desc(k_cache, None, layout)
-    return int(lib().pkv_prefill_workspace_bytes(ctypes.byref(desc), batch, num_q_heads, total_q, max_q,
-                                                 max_kv_len))
+    with torch.cuda.device(k_cache.device):  # the size depends on the device's CU count
+        return int(lib().pkv_prefill_workspace_bytes(ctypes.byref(desc), batch, num_q_heads, total_q, max_q,
+                                                     max_kv_len))
 
 
 def prefill_attn(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, max_q: int, max_kv_len: int,
                  scale: float, causal: bool = True, out=None, lse=None, workspace=None,
-                 layout: str = "HND", return_lse: bool = False, rows_per_workgroup: int = 0):
+                 layout: str = "HND", return_lse: bool = False, rows_per_workgroup: int = 0,
+                 split: bool = True):
     """pkv_prefill_attn: ragged queries q [total_q, Hq, D] (offsets qo_indptr)
     against kv_lens[r] keys of each request, end-aligned causal mask.
-    rows_per_workgroup != 0 calls pkv_prefill_attn_ex with that tiling."""
+    rows_per_workgroup != 0 calls pkv_prefill_attn_ex with that tiling.
+    A call that may split its keys gets a zero-filled workspace of
+    pkv_prefill_workspace_bytes (allocated here unless given); split=False
+    passes none, so the keys are never split."""
     desc = cache_desc(k_cache, v_cache, layout)
     dev = k_cache.device
     _need(q, "q", k_cache.dtype, dev, 3)
@@ -483,9 +488,13 @@ def prefill_attn(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, max_q: in
         lse = torch.empty((total_q, hq), dtype=torch.float32, device=dev)
     _prefill_operands(desc, q, out, lse, block_table, kv_lens, qo_indptr)
     with torch.cuda.device(dev):
-        need = lib().pkv_prefill_workspace_bytes(ctypes.byref(desc), batch, hq, total_q, max_q, max_kv_len)
-        if workspace is None and need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        need = 0
+        if split and not rows_per_workgroup:
+            need = lib().pkv_prefill_workspace_bytes(ctypes.byref(desc), batch, hq, total_q, max_q, max_kv_len)
+        if not need:
+            workspace = None
+        elif workspace is None:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
         args = (ctypes.byref(desc), _ptr(out), _ptr(lse), _ptr(q), hq, _ptr(k_cache), _ptr(v_cache),
                 _ptr(block_table), block_table.shape[1], _ptr(kv_lens), _ptr(qo_indptr), batch, total_q,
                 int(max_q), int(max_kv_len), int(bool(causal)), float(scale), _ptr(workspace),
@@ -742,7 +751,11 @@ def prepare_prefill(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, max_q:
     total_q, hq, d = q.shape
     batch = kv_lens.shape[0]
     _scale(scale)
-    need = lib().pkv_prefill_workspace_bytes(ctypes.byref(desc), batch, hq, total_q, max_q, max_kv_len)
+    # without a workspace (or with a tiling fixed by the caller) the keys are never split
+    need = 0
+    if workspace is not None and not rows_per_workgroup:
+        with torch.cuda.device(dev):
+            need = lib().pkv_prefill_workspace_bytes(ctypes.byref(desc), batch, hq, total_q, max_q, max_kv_len)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if nbytes < need:
         raise PkvError("pkv_prefill_attn", 3, f"workspace {nbytes} < {need} bytes")

@@ -131,9 +131,23 @@ struct PrefillArgs {
     int32_t causal;
     float scale_log2;
     int32_t wg_rows;  // query rows per workgroup: 0 = the library's choice, else 128 or (head_dim 256) 192
+    // Key splits (set by launch_prefill; 1 = none): each (request, query tile,
+    // head) workgroup's key tiles are cut into `splits` pieces, whose partial
+    // rows meet as fp32 records in `part` and are merged by the piece that
+    // counts last in `arrivals` (one counter per workgroup; zero between calls).
+    int32_t splits;
+    float *part;
+    int32_t *arrivals;
 };
+// Workspace of a prefill call with the library's tiling: the key-split
+// records and counters when the call splits (see launch_prefill), else 0.
 size_t prefill_workspace(const PoolGeom &g, int batch, int hq, int total_q, int max_q, int max_kv);
-hipError_t launch_prefill(const PoolGeom &g, const PrefillArgs &args, hipStream_t stream);
+// Launches the prefill kernel.  With the library's tiling (args.wg_rows 0) and
+// a workspace of prefill_workspace bytes, a call whose workgroups fill the
+// chip less than once runs with its keys split (args' split fields are set
+// here); without one it runs unsplit.
+hipError_t launch_prefill(const PoolGeom &g, const PrefillArgs &args, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
 
 // Chunked prefill and one-row requests in one launch (bf16, head_dim 64 or
 // 128): a's requests 0 .. a.batch-1 as query tiles, then n_rows1 one-row

@@ -449,8 +449,11 @@ pkv_status pkv_prefill_attn_ex(const pkv_cache_desc *cache, void *out, float *ls
     if (!isfinite(scale)) return PKV_EINVAL;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return PKV_EUNSUPPORTED;
-    const size_t need = pkv::prefill_workspace(g, batch, num_q_heads, total_q, max_q, max_kv_len);
-    if (need && (!workspace || workspace_bytes < need || !aligned16(workspace))) return PKV_EWORKSPACE;
+    // a tiling the caller fixed never splits the keys, nor does a call
+    // without a workspace; both need none
+    const size_t need =
+        rows_per_workgroup || !workspace ? 0 : pkv::prefill_workspace(g, batch, num_q_heads, total_q, max_q, max_kv_len);
+    if (need && (workspace_bytes < need || !aligned16(workspace))) return PKV_EWORKSPACE;
     pkv::PrefillArgs a;
     a.q = q;
     a.out = out;
@@ -475,7 +478,11 @@ pkv_status pkv_prefill_attn_ex(const pkv_cache_desc *cache, void *out, float *ls
     a.causal = causal ? 1 : 0;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.wg_rows = rows_per_workgroup;
-    return launch_status(pkv::launch_prefill(g, a, (hipStream_t)stream));
+    a.splits = 1;
+    a.part = nullptr;
+    a.arrivals = nullptr;
+    return launch_status(pkv::launch_prefill(g, a, need ? workspace : nullptr, need ? workspace_bytes : 0,
+                                             (hipStream_t)stream));
 }
 
 pkv_status pkv_prefill_attn(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
@@ -549,13 +556,16 @@ pkv_status pkv_mixed_attn(const pkv_cache_desc *cache, void *out, float *lse, co
     pa.causal = 1;
     pa.scale_log2 = scale * 1.4426950408889634f;
     pa.wg_rows = 0;
+    pa.splits = 1;  // the chunks never split their keys here
+    pa.part = nullptr;
+    pa.arrivals = nullptr;
     if (n_dec > 0 && max_kv_len > kMixedPackedMaxKv) {
         // long decode rows: the chunks as pkv_prefill_attn, the decode rows (the
         // last n_dec query rows, one each) as pkv_decode_attn, split across workers
         if (pf_rows > 0) {
             pa.batch = num_prefill;
             pa.total_q = (int)pf_rows;
-            const pkv_status ps = launch_status(pkv::launch_prefill(g, pa, (hipStream_t)stream));
+            const pkv_status ps = launch_status(pkv::launch_prefill(g, pa, nullptr, 0, (hipStream_t)stream));
             if (ps) return ps;
         }
         const int64_t off = pf_rows * num_q_heads * g.head_dim * 2;  // bytes (bf16)

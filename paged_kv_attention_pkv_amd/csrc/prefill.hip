@@ -33,6 +33,8 @@
 // head's G query heads as the rows of one 16-row block.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -318,6 +320,108 @@ __device__ __forceinline__ float mask_max(f32x4 (&sc)[NB], float c, bool need_ma
     return mx * c;
 }
 
+// ---------------------------------------------------------------------------
+// key splits
+// ---------------------------------------------------------------------------
+//
+// A call whose (request, query tile, head) workgroups fill the chip less than
+// once (few query rows over many keys) runs each of them as S pieces, one
+// 8-wave workgroup each.  Piece s walks key tiles [s*T/S, (s+1)*T/S) of the
+// workgroup's T, writes its rows' unnormalised output and (max, sum) as an
+// fp32 record and counts itself; the piece that counts last folds the S
+// records, its own read back like the others, in piece order and writes the
+// rows.  The arithmetic is the same whichever piece is last, so results do
+// not depend on the order of arrival.  Records travel between XCDs with
+// agent-coherent accesses, like the decode merge's.  A piece's running max
+// starts at kSplitFloor instead of -inf: a row whose keys all lie in other
+// pieces then gets weights 2^(-inf) = 0, not 2^(-inf + inf).
+constexpr float kSplitFloor = -3.0e38f;
+constexpr int kMaxSplits = 16;
+
+// Record of piece s of workgroup `unit`: BM rows of D fp32 (row-major), then
+// BM (max, sum) pairs.
+template <int D, int BM>
+__device__ __forceinline__ float *split_record(const PrefillArgs &a, int64_t unit, int s) {
+    return a.part + (unit * a.splits + s) * ((int64_t)BM * (D + 2));
+}
+
+// After the walk of piece s of workgroup `unit` (every wave of it calls this;
+// it synchronises the workgroup): true when this workgroup now holds the
+// merged rows (acc, m and lt then cover all the keys), false when another
+// piece merges them.  rows: the wave holds query rows of the request (waves
+// past its last row neither write nor merge a record); rr: the lane's row in
+// the workgroup; lt: the row sum.
+//
+// The merge's loads go out together, so that it waits for a few round trips
+// to memory rather than one per record: first every piece's (max, sum), then
+// the records NR at a time (NR * D/4 registers of them in flight).  Indices
+// past the last piece load piece S-1 again and take weight 0, which keeps
+// every register index static and the sums' order fixed.
+template <int D, int BM>
+__device__ bool split_settle(const PrefillArgs &a, int64_t unit, int s, bool rows, int rr, int grp,
+                             f32x4 (&acc)[D / 16], float &m, float &lt, int *prior_lds) {
+    constexpr int DB = D / 16;
+    constexpr int NR = D == 64 ? 4 : 128 / (4 * DB);  // head_dim 64 stays within 128 registers
+    const int S = a.splits;
+    if (rows) {
+        float *own = split_record<D, BM>(a, unit, s);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            float *p = own + rr * D + 16 * db + 4 * grp;
+            st_agent2(p, acc[db][0], acc[db][1]);
+            st_agent2(p + 2, acc[db][2], acc[db][3]);
+        }
+        if (grp == 0) st_agent2(own + BM * D + rr * 2, m, lt);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the record is complete before the piece counts
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *prior_lds = __hip_atomic_fetch_add(a.arrivals + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (*prior_lds != S - 1) return false;
+    if (threadIdx.x == 0) __hip_atomic_store(a.arrivals + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!rows) return true;
+    float M = kSplitFloor;
+    {
+        float mt[kMaxSplits];
+#pragma unroll
+        for (int t = 0; t < kMaxSplits; ++t)
+            mt[t] = ld_agent2(split_record<D, BM>(a, unit, min(t, S - 1)) + BM * D + rr * 2)[0];
+#pragma unroll
+        for (int t = 0; t < kMaxSplits; ++t) M = fmaxf(M, mt[t]);
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+    for (int t0 = 0; t0 < S; t0 += NR) {
+        f32x4 v[NR][DB];
+        f32x2 ml[NR];
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+            const float *rec = split_record<D, BM>(a, unit, min(t0 + j, S - 1));
+            ml[j] = ld_agent2(rec + BM * D + rr * 2);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const f32x2 lo = ld_agent2(rec + rr * D + 16 * db + 4 * grp);
+                const f32x2 hi = ld_agent2(rec + rr * D + 16 * db + 4 * grp + 2);
+                v[j][db] = f32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+            const float w = t0 + j < S ? fast_exp2(ml[j][0] - M) : 0.f;
+            L = fmaf(w, ml[j][1], L);
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[db][i] = fmaf(w, v[j][db][i], acc[db][i]);
+        }
+    }
+    m = M;
+    lt = L;
+    return true;
+}
+
 template <int D, int W>
 __global__ __launch_bounds__(Cfg16<W>::THREADS) __attribute__((amdgpu_waves_per_eu(Cfg16<W>::PER_SIMD,
                                                                                    Cfg16<W>::PER_SIMD)))
@@ -338,9 +442,17 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
     // G (groups in order, round-robin over the XCDs), so a group's heads run
     // side by side on one XCD and share its L2, and the order stays longest
     // first.  The last partial round keeps the identity.
+    // With key splits (8-wave instances only) the grid is S copies of that
+    // order, piece s of every workgroup in copy s.
     const int G = a.hq / a.hkv;
-    int idx = blockIdx.x;
-    if (idx < (int)(gridDim.x / (8 * G)) * 8 * G) {
+    int idx = blockIdx.x, nwg = gridDim.x, S = 1, s = 0;
+    if constexpr (W == 8) {
+        S = a.splits;
+        nwg /= S;
+        s = idx / nwg;
+        idx -= s * nwg;
+    }
+    if (idx < (nwg / (8 * G)) * 8 * G) {
         const int k = idx >> 3;
         idx = ((k / G) * 8 + (idx & 7)) * G + k % G;
     }
@@ -371,6 +483,7 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
     const int i_last_wg = min(qt * kBM16 + kBM16, q_len) - 1;
     const int last_key_wg = a.causal ? kv - q_len + i_last_wg : kv - 1;
     const int n_tiles = last_key_wg / kBN16 + 1;
+    const int t0 = (int)((int64_t)s * n_tiles / S), t1 = (int)((int64_t)(s + 1) * n_tiles / S);  // this piece
     const int wave_first = qt * kBM16 + wave * kRows16;
     const int i_last_wave = min(wave_first + kRows16, q_len) - 1;
     const int last_key_wave = wave_first >= q_len ? -1 : (a.causal ? kv - q_len + i_last_wave : kv - 1);
@@ -394,7 +507,7 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
     f32x4 acc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = kNegInff, l = 0.f;  // l: this lane's part of the row sum
+    float m = S > 1 ? kSplitFloor : kNegInff, l = 0.f;  // l: this lane's part of the row sum
     const float c = positive_scale<KS>(a.scale_log2, qop);
     // Lane offsets in the row-pair layout.  A chunk index's bit 3 flips in
     // odd rows, so each pattern has two lane bases: one for reads whose
@@ -410,25 +523,30 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
     const int v_base = (2 * grp + (col >> 3)) * L::PAIR + v_odd * D + 8 * ((col & 3) >> 1) + 4 * (col & 1);
     const int v_lo = v_base + 64 * v_odd, v_hi = v_base - 64 * v_odd;
 
-    // table entries of blocks 0 .. kIds16-1, then tiles 0 .. kNST16-2 in
-    // flight, then wait for tile 0
+    // table entries of the window holding tile t0 (blocks 0 .. kIds16-1
+    // unless a piece starts further on), then tiles t0 .. t0+kNST16-2 in
+    // flight, then wait for tile t0
     // waves 0 .. kDmaWaves16-1 issue the transfers
     const int wv = wave;
     int *ids = reinterpret_cast<int *>(smem + L::IDS);
-    int window = 0;  // ids holds blocks window*kIds16 ..
-    stage_ids16_first<C::THREADS>(bt, kv, pre_id, ids, a.page_shift);
+    int window = dma_block16(t0, 0) / kIds16;  // ids holds blocks window*kIds16 ..
+    if (window == 0)
+        stage_ids16_first<C::THREADS>(bt, kv, pre_id, ids, a.page_shift);
+    else
+        stage_ids16<C::THREADS>(bt, window * kIds16, kv, ids, a.page_shift);
     // the table in LDS is complete; the Q loads may still be in flight
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     auto entry = [&](int t) { return uniform(ids[dma_block16(t, wv) - window * kIds16]); };
-    const int pro = min(kNST16 - 1, n_tiles);
+    const int pro = min(kNST16 - 1, t1 - t0);
     if (wv < kDmaWaves16)
-        for (int t = 0; t < pro; ++t) dma_tile16<D>(a, entry(t), g, t, wv, kv, smem + t * L::BUF);
+        for (int t = t0; t < t0 + pro; ++t)
+            dma_tile16<D>(a, entry(t), g, t, wv, kv, smem + (t & (kNST16 - 1)) * L::BUF);
     wait_transfers<TPW>(pro - 1);
     __syncthreads();
-    for (int tile = 0; tile < n_tiles; ++tile) {
+    for (int tile = t0; tile < t1; ++tile) {
         uint16_t *cur = smem + (tile & (kNST16 - 1)) * L::BUF;
         const int pre = tile + kNST16 - 1;  // into the stage read in the tile before
-        if (pre < n_tiles) {
+        if (pre < t1) {
             // past the staged entries (rows of more than 2 * kIds16 * 16 / (kBN16 / 16) keys): restage,
             // every wave at the same tile; its loads' wait also drains the transfers in flight
             if (dma_block16(pre, kDmaWaves16 - 1) >= (window + 1) * kIds16) {
@@ -542,9 +660,9 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
             }
             __builtin_amdgcn_s_setprio(0);
         }
-        if (tile + 1 < n_tiles) {
+        if (tile + 1 < t1) {
             // this wave's transfers of the next tile have landed, then every wave's
-            wait_transfers<TPW>(min(tile + kNST16 - 1, n_tiles - 1) - (tile + 1));
+            wait_transfers<TPW>(min(tile + kNST16 - 1, t1 - 1) - (tile + 1));
             __syncthreads();
         }
     }
@@ -557,7 +675,13 @@ void prefill16_kernel(PrefillArgs a, int n_qtiles) {
     // output again, and with the hint a launch that writes 25 MB of it ends
     // ~3 us sooner (measured; the dirty lines otherwise drain from the L2s
     // when the launch ends).
-    const float lt = rows4_sum(l);
+    float lt = rows4_sum(l);
+    if constexpr (W == 8) {
+        __shared__ int prior;
+        if (S > 1 && !split_settle<D, kBM16>(a, ((int64_t)r * n_qtiles + qt) * a.hq + h, s, wave_first < q_len,
+                                             wave * kRows16 + col, grp, acc, m, lt, &prior))
+            return;
+    }
     const float inv = 1.f / lt;
     constexpr int OS = D + 8;  // LDS row stride of the output block (elements)
     static_assert(kWaves16Max * kRows16 * OS * 2 <= Dma16<D>::BYTES, "output block fits the stages");
@@ -703,18 +827,27 @@ void prefill16r_kernel(PrefillArgs a, int n_qtiles, int n_packed, int packed_fir
     // They come after the query tiles (ordered longest first), whose ragged
     // end they fill.  The others: grid as in prefill16_kernel, over requests
     // 0 .. batch-1.
+    // With key splits (8-wave instances, which pack no rows) the grid is S
+    // copies of the query-tile order, piece s of every workgroup in copy s.
     const int G = a.hq / a.hkv;
-    const int n = (int)gridDim.x - n_packed;  // query-tile workgroups
-    const bool packed = (int)blockIdx.x >= n;
+    int n = (int)gridDim.x - n_packed;  // query-tile workgroups
+    int bid = (int)blockIdx.x, S = 1, s = 0;
+    if constexpr (W == 8) {
+        S = a.splits;
+        n = (int)gridDim.x / S;
+        s = bid / n;
+        bid -= s * n;
+    }
+    const bool packed = bid >= n;
     int r, qt, h, g;
     if (packed) {
-        const int pk = (int)blockIdx.x - n;
+        const int pk = bid - n;
         r = packed_first + pk / a.hkv;
         g = pk - (r - packed_first) * a.hkv;
         qt = 0;
         h = g * G;
     } else {
-        int idx = (int)blockIdx.x;
+        int idx = bid;
         if (idx < (n / (8 * G)) * 8 * G) {
             const int k = idx >> 3;
             idx = ((k / G) * 8 + (idx & 7)) * G + k % G;
@@ -747,6 +880,7 @@ void prefill16r_kernel(PrefillArgs a, int n_qtiles, int n_packed, int packed_fir
     const int i_last_wg = packed ? 0 : min(qt * kBM16 + kBM16, q_len) - 1;
     const int last_key_wg = a.causal ? kv - q_len + i_last_wg : kv - 1;
     const int n_tiles = last_key_wg / kBN16 + 1;
+    const int t0 = (int)((int64_t)s * n_tiles / S), t1 = (int)((int64_t)(s + 1) * n_tiles / S);  // this piece
     const int wave_first = packed ? (wave == 0 ? 0 : q_len) : qt * kBM16 + wave * kRows16;
     const int i_last_wave = packed ? 0 : min(wave_first + kRows16, q_len) - 1;
     const int last_key_wave = wave_first >= q_len ? -1 : (a.causal ? kv - q_len + i_last_wave : kv - 1);
@@ -763,10 +897,10 @@ void prefill16r_kernel(PrefillArgs a, int n_qtiles, int n_packed, int packed_fir
     const bool loader = wave < R::LOADERS;
     int ids[R::PAGES];
     Reg16Tile<D> regs;
-    if (loader) {
-        reg16_ids<D>(a, bt, 0, wave, kv, ids);
-        reg16_load<D>(a, ids, g, 0, wave, kv, regs);
-        if (n_tiles > 1) reg16_ids<D>(a, bt, 1, wave, kv, ids);
+    if (loader && t0 < t1) {
+        reg16_ids<D>(a, bt, t0, wave, kv, ids);
+        reg16_load<D>(a, ids, g, t0, wave, kv, regs);
+        if (t0 + 1 < t1) reg16_ids<D>(a, bt, t0 + 1, wave, kv, ids);
     }
     // Q^T operand: lane holds Q[row][32ks + 8grp .. +7] for every k-step
     u32x4 qop[KS];
@@ -778,21 +912,21 @@ void prefill16r_kernel(PrefillArgs a, int n_qtiles, int n_packed, int packed_fir
     f32x4 acc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = kNegInff, l = 0.f;  // l: this lane's part of the row sum
+    float m = S > 1 ? kSplitFloor : kNegInff, l = 0.f;  // l: this lane's part of the row sum
     const float c = positive_scale<KS>(a.scale_log2, qop);
     // K operand: row 16u + col, dims 32k + 8grp; V^T transposing reads: lane
     // 4a+b of its group names key 32t + 4grp + a (and +16), dims 16db + 4b
     const int k_base = reg16_row(col, R::RS) + 8 * grp;
     const int v_base = reg16_row(4 * grp + (col >> 2), R::RS) + 4 * (col & 3);
-    if (loader) reg16_store<D>(smem, regs, wave);
+    if (loader && t0 < t1) reg16_store<D>(smem + (t0 & 1) * R::BUF, regs, wave);
     __syncthreads();
-    for (int tile = 0; tile < n_tiles; ++tile) {
+    for (int tile = t0; tile < t1; ++tile) {
         uint16_t *cur = smem + (tile & 1) * R::BUF;
         uint16_t *nxt = smem + ((tile + 1) & 1) * R::BUF;
-        const bool more = tile + 1 < n_tiles;
+        const bool more = tile + 1 < t1;
         if (loader && more) {
             reg16_load<D>(a, ids, g, tile + 1, wave, kv, regs);
-            if (tile + 2 < n_tiles) reg16_ids<D>(a, bt, tile + 2, wave, kv, ids);
+            if (tile + 2 < t1) reg16_ids<D>(a, bt, tile + 2, wave, kv, ids);
         }
 
         if (tile * kBN16 <= last_key_wave) {
@@ -891,7 +1025,13 @@ void prefill16r_kernel(PrefillArgs a, int n_qtiles, int n_packed, int packed_fir
     }
 
     // normalise and write through LDS, as prefill16_kernel
-    const float lt = rows4_sum(l);
+    float lt = rows4_sum(l);
+    if constexpr (W == 8) {
+        __shared__ int prior;
+        if (S > 1 && !split_settle<D, kBM16>(a, ((int64_t)r * n_qtiles + qt) * a.hq + h, s, wave_first < q_len,
+                                             wave * kRows16 + col, grp, acc, m, lt, &prior))
+            return;
+    }
     const float inv = 1.f / lt;
     constexpr int OS = D + 8;
     static_assert(kWaves16Max * kRows16 * OS * 2 <= Reg16<D>::BYTES, "output block fits the stages");
@@ -923,7 +1063,8 @@ hipError_t launch16_d(const PrefillArgs &a, hipStream_t stream) {
     constexpr int kSmem16 = Dma16<D>::BYTES + kIds16 * 4;
     constexpr int BM = Cfg16<W>::BM;
     const int n_qtiles = (a.max_q + BM - 1) / BM;
-    const int64_t grid = (int64_t)a.batch * n_qtiles * a.hq;
+    if (W != 8 && a.splits != 1) return hipErrorInvalidValue;
+    const int64_t grid = (int64_t)a.batch * n_qtiles * a.hq * a.splits;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     static std::atomic<uint64_t> attr_set{0};
     hipError_t e = set_smem_once(reinterpret_cast<const void *>(&prefill16_kernel<D, W>), kSmem16, attr_set);
@@ -957,7 +1098,9 @@ hipError_t launch16r_d(const PrefillArgs &a, hipStream_t stream, int n_packed_ro
     constexpr int BM = Cfg16<W>::BM;
     const int n_qtiles = a.batch > 0 ? (a.max_q + BM - 1) / BM : 0;
     const int64_t n_packed = (int64_t)n_packed_rows * a.hkv;
-    const int64_t grid = (int64_t)a.batch * n_qtiles * a.hq + n_packed;
+    if (W != 8 && a.splits != 1) return hipErrorInvalidValue;
+    if (a.splits != 1 && n_packed) return hipErrorInvalidValue;
+    const int64_t grid = (int64_t)a.batch * n_qtiles * a.hq * a.splits + n_packed;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     if (grid == 0) return hipSuccess;
     static std::atomic<uint64_t> attr_set{0};
@@ -987,7 +1130,51 @@ hipError_t launch_d(const PrefillArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-size_t prefill_workspace(const PoolGeom &, int, int, int, int, int) { return 0; }
+namespace {
+
+// Key splits.  A call whose (request, 128-row query tile, head) workgroups,
+// one per CU at a time, fill the chip less than once leaves CUs idle for its
+// whole length; with many keys per row it runs 8-wave workgroups with each
+// one's key tiles cut into S pieces: as many as still fit in one round over
+// the CUs (S = CUs / workgroups, rounded down), at most one piece per 8 key
+// tiles of the longest row (a piece's first tile is not hidden behind
+// compute) and at most kMaxSplits.  Measured over S = 1 .. 16 on 12 shapes
+// (head_dim 64, 128 and 256, 16 to 1023 query rows, 4000 to 32768 keys):
+// time falls with S while the pieces fit in one round and jumps as soon as
+// they spill into a second (each piece also slows as more CUs run at once),
+// so the one-round S was the fastest or within 10% of it on every shape that
+// splits, and 1.6 to 4 times faster than no split.
+constexpr int kSplitRows = Cfg16<8>::BM;
+
+int64_t split_units(int batch, int hq, int max_q) {
+    return (int64_t)batch * ((max_q + kSplitRows - 1) / kSplitRows) * hq;
+}
+
+int split_count(int batch, int hq, int max_q, int max_kv) {
+    const int cus = current_device_cus();
+    const int64_t units = split_units(batch, hq, max_q);
+    if (cus <= 0 || units <= 0 || units >= cus) return 1;
+    const int64_t by_cus = cus / units;
+    const int64_t by_keys = ((int64_t)max_kv + kBN16 - 1) / kBN16 / 8;
+    const int64_t n = std::min<int64_t>(std::min<int64_t>(by_cus, by_keys), kMaxSplits);
+    return n > 1 ? (int)n : 1;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// bytes: counters (int32 per workgroup), then S records of BM rows x (D + 2) fp32 per workgroup
+size_t split_bytes(int head_dim, int64_t units, int splits) {
+    return align256((size_t)units * 4) + (size_t)units * splits * kSplitRows * (head_dim + 2) * 4;
+}
+
+}  // namespace
+
+size_t prefill_workspace(const PoolGeom &g, int batch, int hq, int total_q, int max_q, int max_kv) {
+    (void)total_q;
+    if (batch <= 0 || hq <= 0 || max_q <= 0 || max_kv <= 0) return 0;
+    const int S = split_count(batch, hq, max_q, max_kv);
+    return S > 1 ? split_bytes(g.head_dim, split_units(batch, hq, max_q), S) : 0;
+}
 
 hipError_t launch_mixed(const PoolGeom &g, const PrefillArgs &a, int n_rows1, int first_row1, hipStream_t stream) {
     switch (g.head_dim) {
@@ -997,8 +1184,23 @@ hipError_t launch_mixed(const PoolGeom &g, const PrefillArgs &a, int n_rows1, in
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_prefill(const PoolGeom &g, const PrefillArgs &a, hipStream_t stream) {
-    if (a.max_q <= 0 || a.batch <= 0) return hipSuccess;
+hipError_t launch_prefill(const PoolGeom &g, const PrefillArgs &args, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+    if (args.max_q <= 0 || args.batch <= 0) return hipSuccess;
+    PrefillArgs a = args;
+    a.splits = 1;
+    a.part = nullptr;
+    a.arrivals = nullptr;
+    if (a.wg_rows == 0 && workspace && a.max_kv > 0) {
+        const int S = split_count(a.batch, a.hq, a.max_q, a.max_kv);
+        const int64_t units = split_units(a.batch, a.hq, a.max_q);
+        if (S > 1 && workspace_bytes >= split_bytes(g.head_dim, units, S)) {
+            a.splits = std::min(S, kMaxSplits);  // the merge reads at most kMaxSplits records
+            a.arrivals = static_cast<int32_t *>(workspace);
+            a.part = reinterpret_cast<float *>(static_cast<char *>(workspace) + align256((size_t)units * 4));
+            a.wg_rows = kSplitRows;
+        }
+    }
     switch (g.head_dim) {
         case 64: return launch_d<64>(a, stream);
         case 128: return launch_d<128>(a, stream);

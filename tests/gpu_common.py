@@ -175,11 +175,12 @@ class PrefillCase:
         kv = pkv.append(kc, vc, i.k_new, i.v_new, i.block_table, i.hist_lens, i.qo_indptr, layout=s.layout)
         return kc, vc, kv
 
-    def gpu_prefill(self, kc, vc, kv, causal=True, rows=0):
+    def gpu_prefill(self, kc, vc, kv, causal=True, rows=0, split=True, workspace=None):
         s = self.spec
         return pkv.prefill_attn(self.inp.q, kc, vc, self.inp.block_table, kv, self.inp.qo_indptr,
                                 int(s.q_lens.max()), int(s.kv_lens.max()), causal=causal, scale=s.scale,
-                                layout=s.layout, return_lse=True, rows_per_workgroup=rows)
+                                layout=s.layout, return_lse=True, rows_per_workgroup=rows, split=split,
+                                workspace=workspace)
 
     def oracle_pools(self, requests=None):
         """Host pools holding the history and chunk of `requests` (all by default)."""

@@ -62,7 +62,7 @@ def test_mixed_equals_separate_calls():
     P = 3
     npf = int(s.q_lens[:P].sum())
     po, pl = pkv.prefill_attn(i.q[:npf], kc, vc, i.block_table[:P], kv[:P], i.qo_indptr[:P + 1],
-                              int(s.q_lens[:P].max()), int(s.kv_lens.max()), s.scale, return_lse=True)
+                              int(s.q_lens[:P].max()), int(s.kv_lens.max()), s.scale, return_lse=True, split=False)
     do, dl = pkv.decode_attn(i.q[npf:], kc, vc, i.block_table[P:].contiguous(), kv[P:].contiguous(),
                              int(s.kv_lens.max()), s.scale, return_lse=True)
     torch.cuda.synchronize()
@@ -138,7 +138,8 @@ def test_mixed_long_decode_rows_split():
     P, npf = 2, int(spec.q_lens[:2].sum())
     max_kv = int(s.kv_lens.max())
     ref_p, ref_pl = pkv.prefill_attn(i.q[:npf], kc, vc, i.block_table[:P], kv_d[:P], i.qo_indptr[:P + 1],
-                                     int(s.q_lens[:P].max()), max_kv, scale=s.scale, return_lse=True)
+                                     int(s.q_lens[:P].max()), max_kv, scale=s.scale, return_lse=True,
+                                     split=False)
     ref_d, ref_dl = pkv.decode_attn(i.q[npf:].contiguous(), kc, vc, i.block_table[P:].contiguous(),
                                     kv_d[P:].contiguous(), max_kv, scale=s.scale, return_lse=True)
     torch.cuda.synchronize()
