@@ -92,6 +92,10 @@ def parse():
                    help="decode/sweep/long: HQ,HKV,D in place of the Qwen3 shape 32,8,128 (same lengths and pages)")
     p.add_argument("--no-plan", action="store_true",
                    help="decode: no pkv_decode_plan per step (every call cuts the work itself)")
+    p.add_argument("--q-len", default=None,
+                   help="prefill: query rows of each request (comma list; with --kv-len) instead of the "
+                        "q = kv = 1023 request or a random batch")
+    p.add_argument("--kv-len", default=None, help="prefill: keys of each request (comma list, kv >= q)")
     p.add_argument("--head-dim", type=int, default=256, help="prefill: head_dim (64, 128 or 256)")
     p.add_argument("--hq", type=int, default=48, help="prefill: query heads")
     p.add_argument("--hkv", type=int, default=8, help="prefill: KV heads")
@@ -441,7 +445,7 @@ def bench_prefill(args, torch, pkv, wl, spec):
     log(f"[bench] {spec.name}: {flops / 1e9:.2f} GFLOP per call, {L} layers per step")
     max_q, max_kv = int(spec.q_lens.max()), int(spec.kv_lens.max())
     zeros = torch.zeros(spec.batch, dtype=torch.int32, device=dev)
-    calls, ws = [], None
+    calls, ws, need = [], None, 0
     for layer in range(L):
         # every layer its own pools, queries and outputs, as the layers of a model
         inp = wl.prefill_inputs(spec, device=dev, seed_offset=layer)
@@ -469,13 +473,23 @@ def bench_prefill(args, torch, pkv, wl, spec):
     tfs = flops / (mean * 1e-3) / 1e12
     traffic = traffic_from_profile("prefill", f"prefill16{'' if spec.head_dim == 256 else 'r'}_kernel_{spec.name}_pmc.txt")
     # the tiling the library picks for this call, by the rule stated in
-    # include/pkv.h (192 rows once ceil(total_q / 192) * Hq >= 1.5 * CUs)
+    # include/pkv.h (head_dim 256: 192 rows once ceil(total_q / 192) * Hq >=
+    # 1.5 * CUs; 64 and 128: 192), and its key splits: a workspace of
+    # counters (256-byte aligned) then S records of 128 x (D + 2) fp32 per
+    # (request, 128-row tile, head) workgroup
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    tiling = args.prefill_rows
+    tiling, splits = args.prefill_rows, 1
     if tiling == 0:
-        tiling = 192 if 2 * (-(-int(spec.q_lens.sum()) // 192) * spec.hq) >= 3 * cus else 128
+        units = spec.batch * (-(-max_q // 128)) * spec.hq
+        if need:
+            tiling, splits = 128, (need - (-(-units * 4 // 256)) * 256) // (units * 128 * (spec.head_dim + 2) * 4)
+        elif spec.head_dim != 256:
+            tiling = 192
+        else:
+            tiling = 192 if 2 * (-(-int(spec.q_lens.sum()) // 192) * spec.hq) >= 3 * cus else 128
     kname = "prefill16_kernel" if spec.head_dim == 256 else "prefill16r_kernel"
-    kernel = f"{kname}<{spec.head_dim}, {tiling // 16}> ({tiling} query rows per workgroup)"
+    kernel = f"{kname}<{spec.head_dim}, {tiling // 16}> ({tiling} query rows per workgroup" + (
+        f", keys split in {splits} pieces)" if splits > 1 else ")")
     result = {
         "metric": f"paged causal prefill attn: TFLOP/s (% bf16 MFMA peak), D{spec.head_dim} Hq{spec.hq}/Hkv{spec.hkv}",
         "value": round(flops * L / (ms * 1e-3) / 1e12, 2),
@@ -1005,8 +1019,17 @@ def main():
     elif args.workload == "prefill":
         kw = dict(page_size=args.page_size, layout=args.layout, contiguous=args.contiguous, head_dim=args.head_dim,
                   hq=args.hq, hkv=args.hkv)
-        spec = (wl.prefill_spec(fixed_1023=True, **kw) if args.batch is None
-                else wl.prefill_spec(batch=args.batch, **kw))
+        if args.q_len is not None or args.kv_len is not None:
+            q = [int(x) for x in (args.q_len or "").split(",") if x]
+            kv = [int(x) for x in (args.kv_len or "").split(",") if x]
+            if not q or len(q) != len(kv) or any(a < 1 or a > b for a, b in zip(q, kv)):
+                raise SystemExit("--q-len and --kv-len: equal-length lists with 1 <= q <= kv")
+            spec = wl.prefill_spec(q_lens=q, kv_lens=kv, seed=9, **kw)
+            spec.name = f"prefill_d{args.head_dim}_q{'-'.join(map(str, q))}_kv{'-'.join(map(str, kv))}"
+        elif args.batch is None:
+            spec = wl.prefill_spec(fixed_1023=True, **kw)
+        else:
+            spec = wl.prefill_spec(batch=args.batch, **kw)
         result = bench_prefill(args, torch, pkv, wl, spec)
         result.update({"n_gpus": 1, "scaling": "weak", "vs_baseline": None})
         if cpu:
