@@ -123,6 +123,18 @@ def test_prefill_rejects_scalars():
     assert call(d, max_kv=300 * 16 + 1) == EINVAL
 
 
+def test_prefill_workspace_sizes():
+    """Invalid sizes need no workspace; without a device (CU count unknown)
+    no call splits its keys, so none needs one either."""
+    lib = api.lib()
+    d = _desc(head_dim=256, s_page=8 * 16 * 256, s_head=16 * 256, s_tok=256)
+    size = lambda *a: lib.pkv_prefill_workspace_bytes(ctypes.byref(d), *a)
+    for args in ((0, 48, 64, 64, 4096), (1, 0, 64, 64, 4096), (1, 48, 64, 0, 4096), (1, 48, 64, 64, 0)):
+        assert size(*args) == 0, args
+    if not torch.cuda.is_available():
+        assert size(1, 48, 64, 64, 32768) == 0
+
+
 def test_prefill_ex_rejects_tilings():
     """rows_per_workgroup is 0, 128 or 192 (any head_dim)."""
     lib = api.lib()

@@ -107,6 +107,37 @@ def test_random_prefill(seed):
 
 
 @pytest.mark.parametrize("seed", range(10))
+def test_random_prefill_split(seed):
+    """Few query rows over thousands of keys, so that the library splits the
+    keys (asserted through the workspace size): head counts, head dims,
+    layouts, page sizes, causal or full mask drawn at random, every row
+    against the oracle."""
+    rng = np.random.default_rng(7000 + seed)
+    b = int(rng.integers(1, 4))
+    hq, hkv = HEADS[rng.integers(len(HEADS))]
+    d = int(rng.choice([64, 128, 256]))
+    layout = "NHD" if rng.random() < 0.3 else "HND"
+    q = rng.integers(1, 97, size=b).astype(np.int32)
+    kv = (q + rng.integers(1000, 3001, size=b)).astype(np.int32)
+    causal = bool(rng.random() < 0.7)
+    page = int(rng.choice([16, 32, 64, 128, 256]))
+    say(f"[random split prefill {seed}] B={b} Hq={hq} Hkv={hkv} D={d} {layout} page={page} causal={causal} "
+        f"q={q.tolist()} kv={kv.tolist()}")
+    spec = wl.prefill_spec(q_lens=q, kv_lens=kv, hq=hq, hkv=hkv, head_dim=d, seed=7500 + seed, layout=layout,
+                           page_size=page)
+    case = PrefillCase(spec)
+    kc, vc, kvl = case.gpu_pools()
+    need = pkv.prefill_workspace_bytes(kc, b, hq, int(q.sum()), int(q.max()), int(kv.max()), layout=layout)
+    assert need > 0, "expected a key split"
+    out, lse = case.gpu_prefill(kc, vc, kvl, causal=causal)
+    torch.cuda.synchronize()
+    okc, ovc, okv, obt, oreqs = case.oracle_pools(None)
+    r, ro, rl = case.oracle_rows(okc, ovc, okv, obt, oreqs, causal=causal)
+    compare(out.cpu()[r], ro, *BF16_TOL, "out")
+    compare(lse.cpu()[r], rl, *BF16_TOL, "lse")
+
+
+@pytest.mark.parametrize("seed", range(10))
 def test_random_decode_planned(seed):
     """bf16 decode steps with the step's plan (pkv_decode_plan) on random
     shapes: batch 1..300, GQA ratios, head dims, pages of 16..256 tokens,
