@@ -473,20 +473,21 @@ def bench_prefill(args, torch, pkv, wl, spec):
     tfs = flops / (mean * 1e-3) / 1e12
     traffic = traffic_from_profile("prefill", f"prefill16{'' if spec.head_dim == 256 else 'r'}_kernel_{spec.name}_pmc.txt")
     # the tiling the library picks for this call, by the rule stated in
-    # include/pkv.h (head_dim 256: 192 rows once ceil(total_q / 192) * Hq >=
-    # 1.5 * CUs; 64 and 128: 192), and its key splits: a workspace of
+    # include/pkv.h (192 rows once ceil(total_q / 192) * Hq >= 1.5 * CUs at
+    # head_dim 256, > CUs at 64 and 128), and its key splits: a workspace of
     # counters (256-byte aligned) then S records of 128 x (D + 2) fp32 per
     # (request, 128-row tile, head) workgroup
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     tiling, splits = args.prefill_rows, 1
     if tiling == 0:
         units = spec.batch * (-(-max_q // 128)) * spec.hq
+        wgs192 = -(-int(spec.q_lens.sum()) // 192) * spec.hq
         if need:
             tiling, splits = 128, (need - (-(-units * 4 // 256)) * 256) // (units * 128 * (spec.head_dim + 2) * 4)
         elif spec.head_dim != 256:
-            tiling = 192
+            tiling = 192 if wgs192 > cus else 128
         else:
-            tiling = 192 if 2 * (-(-int(spec.q_lens.sum()) // 192) * spec.hq) >= 3 * cus else 128
+            tiling = 192 if 2 * wgs192 >= 3 * cus else 128
     kname = "prefill16_kernel" if spec.head_dim == 256 else "prefill16r_kernel"
     kernel = f"{kname}<{spec.head_dim}, {tiling // 16}> ({tiling} query rows per workgroup" + (
         f", keys split in {splits} pieces)" if splits > 1 else ")")

@@ -412,11 +412,12 @@ pkv_status pkv_prefill_attn(const pkv_cache_desc *cache, void *out, float *lse, 
  *   rows_per_workgroup  0: the library's choice (what pkv_prefill_attn does);
  *                       128: 8 waves of 16 rows;
  *                       192: 12 waves of 16 rows.
- * Any other value gives PKV_EINVAL.  At head_dim 256 the library takes 192
- * once the call has work for about one and a half rounds of 192-row
- * workgroups on every CU, else 128; at head_dim 64 and 128 it takes 192.  A
- * call that splits its keys (see above) runs 128.  With 128 or 192 the keys
- * are never split and the workspace is not used.
+ * Any other value gives PKV_EINVAL.  The library takes 192 once the call has
+ * enough 192-row workgroups (ceil(total_q / 192) * num_q_heads of them): at
+ * least one and a half per CU at head_dim 256, more than one per CU at
+ * head_dim 64 and 128; else 128.  A call that splits its keys (see above)
+ * runs 128.  With 128 or 192 the keys are never split and the workspace is
+ * not used.
  */
 pkv_status pkv_prefill_attn_ex(const pkv_cache_desc *cache, void *out, float *lse, const void *q,
                                int32_t num_q_heads, const void *k_cache, const void *v_cache,

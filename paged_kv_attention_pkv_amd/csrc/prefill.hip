@@ -1075,18 +1075,20 @@ hipError_t launch16_d(const PrefillArgs &a, hipStream_t stream) {
 }
 
 // Query rows per workgroup of the 16-row kernels when the caller leaves the
-// choice to the library.  head_dim 256: 192 once the call has work for about
-// one and a half rounds of 192-row workgroups on every CU (counted from
-// total_q, which ragged tails only raise), else 128, whose finer tiles end
-// closer together (measured: the single 1023-row request, 1.1 rounds, runs
-// faster at 128; two requests of 910 and 627 rows, 1.7 rounds, already at
-// 192).  head_dim 64 and 128: always 192 (measured faster on every workload
-// timed, the single 1023-row request included: 34.1 vs 36.0 us at 128).
+// choice to the library: 192 once the call has enough 192-row workgroups
+// (counted from total_q, which ragged tails only raise), else 128, whose
+// finer tiles fill more CUs and end closer together.  head_dim 256: 192 from
+// about one and a half rounds on every CU (measured: the single 1023-row
+// request, 1.1 rounds, runs faster at 128; two requests of 910 and 627 rows,
+// 1.7 rounds, already at 192).  head_dim 64 and 128: 192 above one round
+// (measured over 14 shapes: at or under one round 128 is 0-19% faster, e.g.
+// one request of 1500 rows 46.8 vs 51.0 us; at 1.1 rounds the two are within
+// 1-5%; from 1.4 rounds up 192 is 5-27% faster).
 int auto_wg_rows16(const PrefillArgs &a, int head_dim) {
-    if (head_dim != 256) return Cfg16<12>::BM;
     const int cus = current_device_cus();
     if (cus <= 0) return -1;
     const int64_t wgs192 = ((int64_t)a.total_q + Cfg16<12>::BM - 1) / Cfg16<12>::BM * a.hq;
+    if (head_dim != 256) return wgs192 > (int64_t)cus ? Cfg16<12>::BM : Cfg16<8>::BM;
     return 2 * wgs192 >= 3 * (int64_t)cus ? Cfg16<12>::BM : Cfg16<8>::BM;
 }
 

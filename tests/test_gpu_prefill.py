@@ -131,6 +131,25 @@ def test_random_batches_forced_tiling(batch, rows):
     _parity(spec, sample=4, reqs=reqs, gen_device="cuda", rows=rows)
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_tilings_give_the_same_bits(d):
+    """The 128- and 192-row tilings (and the library's own unsplit choice)
+    compute every row with the same operations in the same order, so their
+    outputs are equal bit for bit; ragged requests, causal and full mask."""
+    spec = wl.prefill_spec(q_lens=[1, 100, 300, 191], kv_lens=[500, 100, 900, 700], hq=12, hkv=4, head_dim=d,
+                           seed=61 + d)
+    say(f"[prefill] tilings bit-equal, D={d}")
+    case = PrefillCase(spec)
+    kc, vc, kv = case.gpu_pools()
+    for causal in (True, False):
+        ref = case.gpu_prefill(kc, vc, kv, causal=causal, split=False)
+        for rows in (128, 192):
+            o, l = case.gpu_prefill(kc, vc, kv, causal=causal, rows=rows)
+            torch.cuda.synchronize()
+            assert torch.equal(o.view(torch.int16), ref[0].view(torch.int16)), (causal, rows)
+            assert torch.equal(l.view(torch.int32), ref[1].view(torch.int32)), (causal, rows)
+
+
 @pytest.mark.parametrize("rows", [128, 192])
 def test_permutation_invariance_and_determinism(rows):
     spec1 = wl.prefill_spec(q_lens=[100, 257], kv_lens=[300, 257], hq=12, hkv=2, head_dim=256, seed=21)
