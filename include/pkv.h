@@ -449,23 +449,29 @@ pkv_status pkv_prefill_attn_ex(const pkv_cache_desc *cache, void *out, float *ls
  *   max_q      host upper bound of the chunks' q_r
  * Chunk rows are causal, end-aligned: row i of a chunk sees keys
  * 0 .. kv_r - q_r + i (FlashInfer PR #9451 analysis, §1); a decode row sees
- * all kv_r keys (0 keys: out = 0, lse = -inf).  The chunk rows are bit for
- * bit those of pkv_prefill_attn on the chunks without a workspace (the
- * chunks' keys are never split here); the decode rows equal
- * pkv_decode_attn's up to rounding order.  bf16, head_dim 64 or 128 only
- * (PKV_EUNSUPPORTED otherwise).
- * Long decode rows: a decode row in that launch is not split across
- * workgroups, so a row of many keys would hold the launch.  With max_kv_len
- * above 8192 the call therefore enqueues two launches instead: the chunks as
- * pkv_prefill_attn without a workspace and the decode rows as
- * pkv_decode_attn (bit for bit those calls' results), and only then is the
- * workspace used.
- *   workspace  device buffer of pkv_mixed_workspace_bytes(...) bytes (the
- *              decode rows' pkv_decode_attn workspace; a token size when
- *              every request is a chunk; 0 for invalid arguments), zero-filled
- *              before its first use like a decode workspace.  Calls with
- *              max_kv_len <= 8192 use none (NULL and 0 are accepted there);
- *              the others return PKV_EWORKSPACE without one.
+ * all kv_r keys (0 keys: out = 0, lse = -inf).  The chunks take
+ * pkv_prefill_attn's tiling and, given a workspace, its key splits: the
+ * chunk rows are bit for bit those of pkv_prefill_attn on the chunks (same
+ * max_q and max_kv_len) called with a workspace exactly when this call gets
+ * one.  The decode rows equal pkv_decode_attn's up to rounding order.  bf16,
+ * head_dim 64 or 128 only (PKV_EUNSUPPORTED otherwise).
+ * Two launches: a decode row in that launch is one workgroup per KV head,
+ * not split across workgroups, so a row of many keys would hold the launch,
+ * and many rows queue for the CUs.  With max_kv_len above 8192, or (given a
+ * workspace) with more than 2 x CUs decode-row workgroups (decode rows x
+ * Hkv), the call therefore enqueues two launches instead: the chunks as
+ * pkv_prefill_attn and the decode rows as pkv_decode_attn (bit for bit those
+ * calls' results).
+ *   workspace  NULL, or a device buffer of pkv_mixed_workspace_bytes(...)
+ *              bytes, 16-byte aligned, zero-filled before its first use like a
+ *              decode workspace (each call leaves it ready for the next; calls
+ *              sharing one must not overlap): the decode rows'
+ *              pkv_decode_attn workspace, then room for any key split of the
+ *              chunks (at most one record of 128 rows per CU).  The size
+ *              depends on the current device; 0 for invalid arguments.
+ *              Without one the chunks never split, and calls with decode rows
+ *              and max_kv_len above 8192 return PKV_EWORKSPACE; one smaller
+ *              than the size gives PKV_EWORKSPACE.
  */
 size_t pkv_mixed_workspace_bytes(const pkv_cache_desc *cache, int32_t batch, int32_t num_prefill,
                                  int32_t num_q_heads);

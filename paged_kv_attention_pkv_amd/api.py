@@ -542,20 +542,32 @@ def _mixed_args(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, num_prefil
 
 
 def mixed_attn(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, num_prefill: int, max_q: int, max_kv_len: int,
-               scale: float, out=None, lse=None, workspace=None, layout: str = "HND", return_lse: bool = False):
+               scale: float, out=None, lse=None, workspace=None, layout: str = "HND", return_lse: bool = False,
+               split: bool = True):
     """pkv_mixed_attn: requests 0..num_prefill-1 are causal prefill chunks,
     the others decode rows (one query row each, the last query rows), in one
-    launch (two when max_kv_len exceeds 8192: then a zeroed workspace of
-    pkv_mixed_workspace_bytes is allocated here when none is given).  Returns
-    out (and lse when return_lse or lse is given)."""
+    launch (two for decode rows over more than 8192 keys or more than 2 x CUs
+    of them per KV head).  A zeroed workspace of pkv_mixed_workspace_bytes is
+    allocated here when none is given and the call uses one: in those two
+    cases, or for chunks that split their keys (split=False passes none where
+    it can).  Returns out (and lse when return_lse or lse is given)."""
     if out is None:
         out = torch.empty_like(q)
     total_q, hq, _ = q.shape
+    batch = kv_lens.shape[0]
     if lse is None and return_lse:
         lse = torch.empty((total_q, hq), dtype=torch.float32, device=q.device)
-    if workspace is None and max_kv_len > MIXED_PACKED_MAX_KV:
-        workspace = torch.zeros(mixed_workspace_bytes(k_cache, kv_lens.shape[0], num_prefill, hq, layout=layout),
-                                dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        n_dec = batch - num_prefill
+        cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+        use = n_dec > 0 and (max_kv_len > MIXED_PACKED_MAX_KV or n_dec * k_cache.shape[1 if layout == "HND" else 2]
+                             > 2 * cus)
+        if split and not use and num_prefill > 0 and max_q > 0:
+            use = prefill_workspace_bytes(k_cache, num_prefill, hq, total_q - (batch - num_prefill), max_q,
+                                          max_kv_len, layout=layout) > 0
+        if use:
+            workspace = torch.zeros(mixed_workspace_bytes(k_cache, batch, num_prefill, hq, layout=layout),
+                                    dtype=torch.uint8, device=q.device)
     _, args = _mixed_args(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, num_prefill, max_q, max_kv_len,
                           scale, out, lse, workspace, layout)
     with torch.cuda.device(q.device):
@@ -568,11 +580,13 @@ def prepare_mixed(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, num_pref
                   max_kv_len: int, scale: float, out, workspace=None, lse=None, layout: str = "HND") -> "PreparedCall":
     desc, args = _mixed_args(q, k_cache, v_cache, block_table, kv_lens, qo_indptr, num_prefill, max_q, max_kv_len,
                              scale, out, lse, workspace, layout)
-    if max_kv_len > MIXED_PACKED_MAX_KV and num_prefill < kv_lens.shape[0]:
+    # a workspace is needed for decode rows over more than 8192 keys, and
+    # optional otherwise (with one, the chunks may split their keys)
+    if workspace is not None or (max_kv_len > MIXED_PACKED_MAX_KV and num_prefill < kv_lens.shape[0]):
         need = mixed_workspace_bytes(k_cache, kv_lens.shape[0], num_prefill, q.shape[1], layout=layout)
         have = 0 if workspace is None else workspace.numel() * workspace.element_size()
         if have < need:
-            raise PkvError("pkv_mixed_attn", 3, f"workspace {have} < {need} bytes (max_kv_len > {MIXED_PACKED_MAX_KV})")
+            raise PkvError("pkv_mixed_attn", 3, f"workspace {have} < {need} bytes")
     return PreparedCall("pkv_mixed_attn", args, (k_cache, v_cache, q, out, block_table, kv_lens, qo_indptr,
                                                  workspace, lse, desc))
 

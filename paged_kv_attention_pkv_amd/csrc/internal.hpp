@@ -142,9 +142,13 @@ struct PrefillArgs {
 // Workspace of a prefill call with the library's tiling: the key-split
 // records and counters when the call splits (see launch_prefill), else 0.
 size_t prefill_workspace(const PoolGeom &g, int batch, int hq, int total_q, int max_q, int max_kv);
+// Bytes that hold the key split of any call on the current device (at most
+// one record per CU, and counters): what a caller that cannot size its
+// workspace from max_q and max_kv reserves.
+size_t prefill_split_region_max(int head_dim);
 // Launches the prefill kernel.  With the library's tiling (args.wg_rows 0) and
 // a workspace of prefill_workspace bytes, a call whose workgroups fill the
-// chip less than once runs with its keys split (args' split fields are set
+// chip at most half way runs with its keys split (args' split fields are set
 // here); without one it runs unsplit.
 hipError_t launch_prefill(const PoolGeom &g, const PrefillArgs &args, void *workspace, size_t workspace_bytes,
                           hipStream_t stream);
@@ -152,7 +156,9 @@ hipError_t launch_prefill(const PoolGeom &g, const PrefillArgs &args, void *work
 // Chunked prefill and one-row requests in one launch (bf16, head_dim 64 or
 // 128): a's requests 0 .. a.batch-1 as query tiles, then n_rows1 one-row
 // requests first_row1 .. first_row1+n_rows1-1 (a.total_q counts the rows of
-// both) packed by KV head.
-hipError_t launch_mixed(const PoolGeom &g, const PrefillArgs &a, int n_rows1, int first_row1, hipStream_t stream);
+// both) packed by KV head.  The chunks take launch_prefill's tiling and, with
+// a workspace, its key splits.
+hipError_t launch_mixed(const PoolGeom &g, const PrefillArgs &a, int n_rows1, int first_row1, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream);
 
 }  // namespace pkv

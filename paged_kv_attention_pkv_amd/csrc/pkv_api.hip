@@ -496,17 +496,31 @@ pkv_status pkv_prefill_attn(const pkv_cache_desc *cache, void *out, float *lse, 
                                workspace_bytes, 0, stream);
 }
 
+namespace {
+
+// The mixed workspace: the decode rows' pkv_decode_attn workspace (used when
+// they run as their own launch, max_kv_len above kMixedPackedMaxKv), then,
+// 256-byte aligned, room for any key split of the chunks.  0: invalid.
+size_t mixed_decode_part(const PoolGeom &g, int batch, int num_prefill, int num_q_heads) {
+    const int n_dec = batch - num_prefill;
+    if (n_dec == 0) return 0;
+    const int w = pkv::decode_workers(current_device(), g, num_q_heads, -1, 0);
+    if (w < 1) return 0;
+    return (pkv::decode_workspace(g, n_dec, num_q_heads, w) + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
 size_t pkv_mixed_workspace_bytes(const pkv_cache_desc *cache, int32_t batch, int32_t num_prefill,
                                  int32_t num_q_heads) {
     PoolGeom g;
     if (check_desc(cache, &g) || check_heads(g, num_q_heads) || batch < 1 || num_prefill < 0 || num_prefill > batch)
         return 0;
-    const int n_dec = batch - num_prefill;
-    if (n_dec == 0) return 256;  // nothing is used; a token size keeps the query non-zero for valid arguments
-    // the decode rows' workspace, for calls whose decode rows run split (max_kv_len above kMixedPackedMaxKv)
-    const int w = pkv::decode_workers(current_device(), g, num_q_heads, -1, 0);
-    if (w < 1) return 0;
-    return pkv::decode_workspace(g, n_dec, num_q_heads, w);
+    const size_t split = pkv::prefill_split_region_max(g.head_dim);
+    if (split == 0) return 0;
+    if (batch == num_prefill) return split;
+    const size_t dec = mixed_decode_part(g, batch, num_prefill, num_q_heads);
+    return dec ? dec + split : 0;
 }
 
 pkv_status pkv_mixed_attn(const pkv_cache_desc *cache, void *out, float *lse, const void *q, int32_t num_q_heads,
@@ -556,26 +570,50 @@ pkv_status pkv_mixed_attn(const pkv_cache_desc *cache, void *out, float *lse, co
     pa.causal = 1;
     pa.scale_log2 = scale * 1.4426950408889634f;
     pa.wg_rows = 0;
-    pa.splits = 1;  // the chunks never split their keys here
+    pa.splits = 1;
     pa.part = nullptr;
     pa.arrivals = nullptr;
-    if (n_dec > 0 && max_kv_len > kMixedPackedMaxKv) {
-        // long decode rows: the chunks as pkv_prefill_attn, the decode rows (the
-        // last n_dec query rows, one each) as pkv_decode_attn, split across workers
+    // with a workspace: the decode rows' part, then the chunks' key-split region
+    size_t dec_bytes = 0;
+    void *split_ws = nullptr;
+    size_t split_bytes = 0;
+    if (workspace) {
+        const size_t need = pkv_mixed_workspace_bytes(cache, batch, num_prefill, num_q_heads);
+        if (need == 0) return PKV_EDEVICE;
+        if (workspace_bytes < need || !aligned16(workspace)) return PKV_EWORKSPACE;
+        dec_bytes = mixed_decode_part(g, batch, num_prefill, num_q_heads);
+        split_ws = (char *)workspace + dec_bytes;
+        split_bytes = workspace_bytes - dec_bytes;
+    }
+    // Two launches instead of one: the chunks as pkv_prefill_attn, the decode
+    // rows (the last n_dec query rows, one each) as pkv_decode_attn, split
+    // across workers.  Always for decode rows over more than
+    // kMixedPackedMaxKv keys (a packed row is one workgroup per KV head,
+    // however long); and, given a workspace, once the packed rows' workgroups
+    // (one per row and KV head, each holding a CU for its whole walk) exceed
+    // two rounds over the CUs, where the decode kernel's streaming waves
+    // finish them sooner (measured over 14 mixes: 128 decode rows at Hkv 8
+    // 7-8% faster as two launches, 256 rows 15-18%, 16-64 rows 1-30% slower).
+    const int cus = pkv::current_device_cus();
+    const bool long_rows = n_dec > 0 && max_kv_len > kMixedPackedMaxKv;
+    const bool many_rows = workspace && n_dec > 0 && cus > 0 && (int64_t)n_dec * g.hkv > 2 * (int64_t)cus;
+    if (long_rows || many_rows) {
+        if (!workspace) return PKV_EWORKSPACE;
         if (pf_rows > 0) {
             pa.batch = num_prefill;
             pa.total_q = (int)pf_rows;
-            const pkv_status ps = launch_status(pkv::launch_prefill(g, pa, nullptr, 0, (hipStream_t)stream));
+            const pkv_status ps =
+                launch_status(pkv::launch_prefill(g, pa, split_ws, split_bytes, (hipStream_t)stream));
             if (ps) return ps;
         }
         const int64_t off = pf_rows * num_q_heads * g.head_dim * 2;  // bytes (bf16)
         return decode_common(cache, (char *)out + off, lse ? lse + pf_rows * num_q_heads : nullptr,
                              (const char *)q + off, num_q_heads, k_cache, v_cache, nullptr, nullptr,
                              block_table + (int64_t)num_prefill * bt_cols, bt_cols, kv_lens + num_prefill, nullptr,
-                             n_dec, max_kv_len, scale, workspace, workspace_bytes, 0, stream);
+                             n_dec, max_kv_len, scale, workspace, dec_bytes, 0, stream);
     }
     // decode rows: requests num_prefill .. batch-1, one query row each
-    return launch_status(pkv::launch_mixed(g, pa, n_dec, num_prefill, (hipStream_t)stream));
+    return launch_status(pkv::launch_mixed(g, pa, n_dec, num_prefill, split_ws, split_bytes, (hipStream_t)stream));
 }
 
 pkv_status pkv_route(const pkv_cache_desc *cache, const int32_t *block_table, int32_t bt_cols,

@@ -827,18 +827,26 @@ void prefill16r_kernel(PrefillArgs a, int n_qtiles, int n_packed, int packed_fir
     // They come after the query tiles (ordered longest first), whose ragged
     // end they fill.  The others: grid as in prefill16_kernel, over requests
     // 0 .. batch-1.
-    // With key splits (8-wave instances, which pack no rows) the grid is S
-    // copies of the query-tile order, piece s of every workgroup in copy s.
+    // With key splits (8-wave instances only) the query-tile part of the
+    // grid is S copies of that order, piece s of every workgroup in copy s,
+    // and the packed rows follow the last copy.
     const int G = a.hq / a.hkv;
     int n = (int)gridDim.x - n_packed;  // query-tile workgroups
     int bid = (int)blockIdx.x, S = 1, s = 0;
     if constexpr (W == 8) {
         S = a.splits;
-        n = (int)gridDim.x / S;
-        s = bid / n;
-        bid -= s * n;
+        if (S > 1) {
+            n /= S;
+            if (bid < n * S) {
+                s = bid / n;
+                bid -= s * n;
+            } else {
+                bid -= n * (S - 1);
+            }
+        }
     }
     const bool packed = bid >= n;
+    if (packed) S = 1;  // a packed workgroup walks all its keys
     int r, qt, h, g;
     if (packed) {
         const int pk = bid - n;
@@ -1101,7 +1109,6 @@ hipError_t launch16r_d(const PrefillArgs &a, hipStream_t stream, int n_packed_ro
     const int n_qtiles = a.batch > 0 ? (a.max_q + BM - 1) / BM : 0;
     const int64_t n_packed = (int64_t)n_packed_rows * a.hkv;
     if (W != 8 && a.splits != 1) return hipErrorInvalidValue;
-    if (a.splits != 1 && n_packed) return hipErrorInvalidValue;
     const int64_t grid = (int64_t)a.batch * n_qtiles * a.hq * a.splits + n_packed;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     if (grid == 0) return hipSuccess;
@@ -1178,31 +1185,64 @@ size_t prefill_workspace(const PoolGeom &g, int batch, int hq, int total_q, int 
     return S > 1 ? split_bytes(g.head_dim, split_units(batch, hq, max_q), S) : 0;
 }
 
-hipError_t launch_mixed(const PoolGeom &g, const PrefillArgs &a, int n_rows1, int first_row1, hipStream_t stream) {
-    switch (g.head_dim) {
-        case 64: return launch16r_d<64, 12>(a, stream, n_rows1, first_row1);
-        case 128: return launch16r_d<128, 12>(a, stream, n_rows1, first_row1);
-    }
-    return hipErrorInvalidValue;
+size_t prefill_split_region_max(int head_dim) {
+    // a split call has at most CUs / 2 workgroups and S x workgroups <= CUs pieces
+    const int cus = current_device_cus();
+    if (cus <= 0) return 0;
+    return align256((size_t)(cus / 2) * 4) + (size_t)cus * kSplitRows * (head_dim + 2) * 4;
+}
+
+namespace {
+
+// Sets a's key-split fields and its 128-row tiling when the call splits its
+// keys and `workspace` (zero-filled counters, then records) is large enough;
+// otherwise leaves a unsplit and returns false.
+bool set_split(const PoolGeom &g, PrefillArgs &a, void *workspace, size_t workspace_bytes) {
+    a.splits = 1;
+    a.part = nullptr;
+    a.arrivals = nullptr;
+    if (!workspace || a.batch <= 0 || a.max_q <= 0 || a.max_kv <= 0) return false;
+    const int S = std::min(split_count(a.batch, a.hq, a.max_q, a.max_kv), kMaxSplits);
+    const int64_t units = split_units(a.batch, a.hq, a.max_q);
+    if (S <= 1 || workspace_bytes < split_bytes(g.head_dim, units, S)) return false;
+    a.splits = S;
+    a.arrivals = static_cast<int32_t *>(workspace);
+    a.part = reinterpret_cast<float *>(static_cast<char *>(workspace) + align256((size_t)units * 4));
+    a.wg_rows = kSplitRows;
+    return true;
+}
+
+template <int D>
+hipError_t launch_mixed_d(const PrefillArgs &a, int rows, int n_rows1, int first_row1, hipStream_t stream) {
+    if (rows == Cfg16<8>::BM) return launch16r_d<D, 8>(a, stream, n_rows1, first_row1);
+    return launch16r_d<D, 12>(a, stream, n_rows1, first_row1);
+}
+
+}  // namespace
+
+hipError_t launch_mixed(const PoolGeom &g, const PrefillArgs &args, int n_rows1, int first_row1, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+    if (g.head_dim != 64 && g.head_dim != 128) return hipErrorInvalidValue;
+    PrefillArgs a = args;
+    // the chunks' tiling by pkv_prefill_attn's rule over their own rows, and
+    // their key splits as there
+    PrefillArgs chunks = a;
+    chunks.total_q = a.total_q - n_rows1;
+    int rows = auto_wg_rows16(chunks, g.head_dim);
+    if (rows < 0) return hipErrorInvalidDevice;
+    if (set_split(g, a, workspace, workspace_bytes)) rows = kSplitRows;
+    return g.head_dim == 64 ? launch_mixed_d<64>(a, rows, n_rows1, first_row1, stream)
+                            : launch_mixed_d<128>(a, rows, n_rows1, first_row1, stream);
 }
 
 hipError_t launch_prefill(const PoolGeom &g, const PrefillArgs &args, void *workspace, size_t workspace_bytes,
                           hipStream_t stream) {
     if (args.max_q <= 0 || args.batch <= 0) return hipSuccess;
     PrefillArgs a = args;
-    a.splits = 1;
-    a.part = nullptr;
-    a.arrivals = nullptr;
-    if (a.wg_rows == 0 && workspace && a.max_kv > 0) {
-        const int S = split_count(a.batch, a.hq, a.max_q, a.max_kv);
-        const int64_t units = split_units(a.batch, a.hq, a.max_q);
-        if (S > 1 && workspace_bytes >= split_bytes(g.head_dim, units, S)) {
-            a.splits = std::min(S, kMaxSplits);  // the merge reads at most kMaxSplits records
-            a.arrivals = static_cast<int32_t *>(workspace);
-            a.part = reinterpret_cast<float *>(static_cast<char *>(workspace) + align256((size_t)units * 4));
-            a.wg_rows = kSplitRows;
-        }
-    }
+    if (a.wg_rows == 0)
+        set_split(g, a, workspace, workspace_bytes);
+    else
+        set_split(g, a, nullptr, 0);
     switch (g.head_dim) {
         case 64: return launch_d<64>(a, stream);
         case 128: return launch_d<128>(a, stream);

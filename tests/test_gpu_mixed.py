@@ -1,8 +1,9 @@
 """GPU parity of pkv_mixed_attn: chunked prefill requests and decode rows of
 one batch in one launch, against the oracle (every decode row, chunk rows
 all or tile-edge sampled) and against the separate calls: bit for bit with
-pkv_prefill_attn on the chunks (the same query tiles), within the bf16 bar
-of pkv_decode_attn on the decode rows (the same sums cut another way)."""
+pkv_prefill_attn on the chunks (the same query tiles and key splits), within
+the bf16 bar of pkv_decode_attn on the decode rows (the same sums cut
+another way)."""
 import numpy as np
 import pytest
 import torch
@@ -62,7 +63,7 @@ def test_mixed_equals_separate_calls():
     P = 3
     npf = int(s.q_lens[:P].sum())
     po, pl = pkv.prefill_attn(i.q[:npf], kc, vc, i.block_table[:P], kv[:P], i.qo_indptr[:P + 1],
-                              int(s.q_lens[:P].max()), int(s.kv_lens.max()), s.scale, return_lse=True, split=False)
+                              int(s.q_lens[:P].max()), int(s.kv_lens.max()), s.scale, return_lse=True)
     do, dl = pkv.decode_attn(i.q[npf:], kc, vc, i.block_table[P:].contiguous(), kv[P:].contiguous(),
                              int(s.kv_lens.max()), s.scale, return_lse=True)
     torch.cuda.synchronize()
@@ -138,8 +139,7 @@ def test_mixed_long_decode_rows_split():
     P, npf = 2, int(spec.q_lens[:2].sum())
     max_kv = int(s.kv_lens.max())
     ref_p, ref_pl = pkv.prefill_attn(i.q[:npf], kc, vc, i.block_table[:P], kv_d[:P], i.qo_indptr[:P + 1],
-                                     int(s.q_lens[:P].max()), max_kv, scale=s.scale, return_lse=True,
-                                     split=False)
+                                     int(s.q_lens[:P].max()), max_kv, scale=s.scale, return_lse=True)
     ref_d, ref_dl = pkv.decode_attn(i.q[npf:].contiguous(), kc, vc, i.block_table[P:].contiguous(),
                                     kv_d[P:].contiguous(), max_kv, scale=s.scale, return_lse=True)
     torch.cuda.synchronize()
@@ -152,3 +152,63 @@ def test_mixed_long_decode_rows_split():
                                      max_kv, s.scale, torch.empty_like(i.q), None, None, "HND")
     rc = pkv.api.lib().pkv_mixed_attn(*args, pkv.api._stream(kc))
     assert rc == 3, rc
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_mixed_short_chunk_over_long_keys(d):
+    """A chunk of few rows continuing a long prompt next to decode rows: with
+    a workspace its keys split as in pkv_prefill_attn (chunk rows bit-equal
+    to pkv_prefill_attn given a workspace, every row against the oracle);
+    without one (split=False) the chunk runs unsplit, bit-equal to
+    pkv_prefill_attn without one."""
+    rng = np.random.default_rng(50 + d)
+    dec = rng.integers(512, 1025, size=48).tolist()
+    spec = wl.prefill_spec(q_lens=[99] + [1] * 48, kv_lens=[3879] + dec, hq=32, hkv=8, head_dim=d, seed=51 + d)
+    case, kc, vc, kv, out, lse = _check(spec, 1)
+    i, s = case.inp, spec
+    assert pkv.prefill_workspace_bytes(kc, 1, 32, 99, 99, int(s.kv_lens.max())) > 0, "expected a key split"
+    max_kv = int(s.kv_lens.max())
+    for split in (True, False):
+        o, l = (out, lse) if split else pkv.mixed_attn(i.q, kc, vc, i.block_table, kv, i.qo_indptr, 1, 99, max_kv,
+                                                       s.scale, return_lse=True, split=False)
+        ref_p, ref_pl = pkv.prefill_attn(i.q[:99], kc, vc, i.block_table[:1], kv[:1], i.qo_indptr[:2], 99, max_kv,
+                                         scale=s.scale, return_lse=True, split=split)
+        torch.cuda.synchronize()
+        assert torch.equal(o[:99].view(torch.int16), ref_p.view(torch.int16)), f"chunk rows, split={split}"
+        assert torch.equal(l[:99].view(torch.int32), ref_pl.view(torch.int32)), f"chunk lse, split={split}"
+    compare(out[:99].cpu(), o[:99].cpu().double().numpy(), *BF16_TOL, "split vs unsplit chunk rows")
+    assert torch.equal(out[99:].view(torch.int16), o[99:].view(torch.int16)), "decode rows depend on the chunk split"
+
+
+def test_mixed_many_decode_rows_two_launches():
+    """More decode-row workgroups (rows x Hkv) than two rounds over the CUs:
+    with a workspace the call runs the chunks as pkv_prefill_attn and the
+    decode rows as pkv_decode_attn (both bit for bit); without one it stays
+    one launch (decode rows within the bar). Every row against the oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n_dec = 2 * cus // 8 + 16
+    rng = np.random.default_rng(77)
+    dec = rng.integers(16, 1025, size=n_dec).tolist()
+    spec = wl.prefill_spec(q_lens=[300, 70] + [1] * n_dec, kv_lens=[900, 2500] + dec, hq=32, hkv=8, head_dim=128,
+                           seed=78)
+    case, kc, vc, kv, out, lse = _check(spec, 2)
+    i, s = case.inp, spec
+    P, npf, max_kv = 2, 370, int(s.kv_lens.max())
+    ref_p, ref_pl = pkv.prefill_attn(i.q[:npf], kc, vc, i.block_table[:P], kv[:P], i.qo_indptr[:P + 1], 300, max_kv,
+                                     scale=s.scale, return_lse=True)
+    ref_d, ref_dl = pkv.decode_attn(i.q[npf:].contiguous(), kc, vc, i.block_table[P:].contiguous(),
+                                    kv[P:].contiguous(), max_kv, scale=s.scale, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:npf].view(torch.int16), ref_p.view(torch.int16)), "chunk rows differ from prefill_attn"
+    assert torch.equal(lse[:npf].view(torch.int32), ref_pl.view(torch.int32))
+    assert torch.equal(out[npf:].view(torch.int16), ref_d.view(torch.int16)), "decode rows differ from decode_attn"
+    assert torch.equal(lse[npf:].view(torch.int32), ref_dl.view(torch.int32))
+    # the raw call without a workspace: one launch
+    o1 = torch.empty_like(i.q)
+    l1 = torch.empty((o1.shape[0], s.hq), dtype=torch.float32, device=o1.device)
+    desc, args = pkv.api._mixed_args(i.q, kc, vc, i.block_table, kv, i.qo_indptr, P, 300, max_kv, s.scale, o1, l1,
+                                     None, "HND")
+    assert pkv.api.lib().pkv_mixed_attn(*args, pkv.api._stream(kc)) == 0
+    torch.cuda.synchronize()
+    compare(o1[npf:].cpu(), ref_d.cpu().double().numpy(), *BF16_TOL, "one-launch decode rows")
+    compare(l1[npf:].cpu(), ref_dl.cpu().double().numpy(), *BF16_TOL, "one-launch decode lse")
