@@ -385,13 +385,16 @@ pkv_status pkv_append_decode_attn_noalloc(const pkv_cache_desc *cache, void *out
  * Only PKV_BF16 is supported by this entry point.
  *
  * Key splits: a call whose (request, 128-row query tile, query head)
- * workgroups number at most half the device's CUs, and whose longest request
- * has more than 960 keys, cuts each workgroup's keys into S pieces when it is
- * given a workspace: S = CUs / workgroups (rounded down), at most one piece
- * per 512 keys of the longest request and at most 16.  The pieces' partial
- * rows meet in the workspace and are merged in a fixed piece order, so
- * results are deterministic.  They equal the unsplit results up to rounding
- * (the online softmax rescales at other points), not bit for bit.
+ * workgroups number at most the device's CUs, and whose longest request has
+ * more than 960 keys, may cut each workgroup's keys into S pieces when it is
+ * given a workspace.  S (at most 16, at most one piece per 512 keys, at most
+ * three rounds of pieces over the CUs) minimises rounds x piece length, with
+ * 1024 keys added to each piece for its start-up and merge.  The pieces'
+ * partial rows meet in the workspace (one 128 x (head_dim + 2) fp32 record
+ * per piece: up to ~100 MB at head_dim 256 on 256 CUs) and are merged in a
+ * fixed piece order, so results are deterministic.  They equal the unsplit
+ * results up to rounding (the online softmax rescales at other points), not
+ * bit for bit.
  * pkv_prefill_workspace_bytes returns 0 when the call would not split; the
  * workspace may then be NULL.  Without a workspace (NULL) the keys are never
  * split and no error is returned; a workspace smaller than needed gives
@@ -467,8 +470,9 @@ pkv_status pkv_prefill_attn_ex(const pkv_cache_desc *cache, void *out, float *ls
  *              decode workspace (each call leaves it ready for the next; calls
  *              sharing one must not overlap): the decode rows'
  *              pkv_decode_attn workspace, then room for any key split of the
- *              chunks (at most one record of 128 rows per CU).  The size
- *              depends on the current device; 0 for invalid arguments.
+ *              chunks (three records of 128 rows per CU: ~51 MB at head_dim
+ *              128 on 256 CUs).  The size depends on the current device; 0
+ *              for invalid arguments.
  *              Without one the chunks never split, and calls with decode rows
  *              and max_kv_len above 8192 return PKV_EWORKSPACE; one smaller
  *              than the size gives PKV_EWORKSPACE.

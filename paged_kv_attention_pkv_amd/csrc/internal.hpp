@@ -143,13 +143,14 @@ struct PrefillArgs {
 // records and counters when the call splits (see launch_prefill), else 0.
 size_t prefill_workspace(const PoolGeom &g, int batch, int hq, int total_q, int max_q, int max_kv);
 // Bytes that hold the key split of any call on the current device (at most
-// one record per CU, and counters): what a caller that cannot size its
+// three records per CU, and counters): what a caller that cannot size its
 // workspace from max_q and max_kv reserves.
 size_t prefill_split_region_max(int head_dim);
 // Launches the prefill kernel.  With the library's tiling (args.wg_rows 0) and
-// a workspace of prefill_workspace bytes, a call whose workgroups fill the
-// chip at most half way runs with its keys split (args' split fields are set
-// here); without one it runs unsplit.
+// a workspace, a call of at most one round of workgroups over long keys runs
+// with its keys split (args' split fields are set here), as far as the
+// workspace holds the records (prefill_workspace bytes hold the best split);
+// without one it runs unsplit.
 hipError_t launch_prefill(const PoolGeom &g, const PrefillArgs &args, void *workspace, size_t workspace_bytes,
                           hipStream_t stream);
 

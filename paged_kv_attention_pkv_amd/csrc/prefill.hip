@@ -33,6 +33,8 @@
 // head's G query heads as the rows of one 16-row block.
 #include <math.h>
 
+#include <stdint.h>
+
 #include <algorithm>
 
 #include "common.hpp"
@@ -1142,31 +1144,46 @@ hipError_t launch_d(const PrefillArgs &a, hipStream_t stream) {
 namespace {
 
 // Key splits.  A call whose (request, 128-row query tile, head) workgroups,
-// one per CU at a time, fill the chip less than once leaves CUs idle for its
-// whole length; with many keys per row it runs 8-wave workgroups with each
-// one's key tiles cut into S pieces: as many as still fit in one round over
-// the CUs (S = CUs / workgroups, rounded down), at most one piece per 8 key
-// tiles of the longest row (a piece's first tile is not hidden behind
-// compute) and at most kMaxSplits.  Measured over S = 1 .. 16 on 12 shapes
-// (head_dim 64, 128 and 256, 16 to 1023 query rows, 4000 to 32768 keys):
-// time falls with S while the pieces fit in one round and jumps as soon as
-// they spill into a second (each piece also slows as more CUs run at once),
-// so the one-round S was the fastest or within 10% of it on every shape that
-// splits, and 1.6 to 4 times faster than no split.
+// one per CU at a time, fill the chip at most once leaves CUs idle for its
+// whole length when it has few of them; with many keys per row it runs
+// 8-wave workgroups with each one's key tiles cut into S pieces.  S minimises
+// a cost of rounds x piece length: ceil(S x workgroups / CUs) x (ceil(T / S)
+// + 16), T = key tiles of the longest row, the 16 tiles standing for a
+// piece's start-up and merge; S <= kMaxSplits, S <= T / 8, at most three
+// rounds of pieces (kSplitRounds), ties to the smaller S.  The model was
+// fitted to sweeps of S = 1 .. 16 on 21 shapes (head_dim 64, 128 and 256, 16
+// to 1023 query rows, 4000 to 32768 keys, 32 to 384 workgroups): its S was
+// the fastest or within 5% of it on each, 1.3 to 5.8 times faster than no
+// split where it splits.  Time falls with S while the pieces fill whole
+// rounds and jumps when a round is left part-empty, and each piece slows as
+// more CUs run at once; calls of more than one round of workgroups lost with
+// every S measured.
 constexpr int kSplitRows = Cfg16<8>::BM;
+constexpr int kSplitRounds = 3;
+constexpr int kSplitPieceCost = 16;  // tiles
 
 int64_t split_units(int batch, int hq, int max_q) {
     return (int64_t)batch * ((max_q + kSplitRows - 1) / kSplitRows) * hq;
 }
 
-int split_count(int batch, int hq, int max_q, int max_kv) {
+// The split count for the call, with at most max_pieces pieces in all.
+int split_count(int batch, int hq, int max_q, int max_kv, int64_t max_pieces) {
     const int cus = current_device_cus();
     const int64_t units = split_units(batch, hq, max_q);
-    if (cus <= 0 || units <= 0 || units >= cus) return 1;
-    const int64_t by_cus = cus / units;
-    const int64_t by_keys = ((int64_t)max_kv + kBN16 - 1) / kBN16 / 8;
-    const int64_t n = std::min<int64_t>(std::min<int64_t>(by_cus, by_keys), kMaxSplits);
-    return n > 1 ? (int)n : 1;
+    if (cus <= 0 || units <= 0 || units > cus) return 1;
+    const int64_t tiles = ((int64_t)max_kv + kBN16 - 1) / kBN16;
+    const int64_t top = std::min<int64_t>(std::min<int64_t>(tiles / 8, kMaxSplits),
+                                          std::min<int64_t>(max_pieces, (int64_t)kSplitRounds * cus) / units);
+    int best = 1;
+    int64_t best_cost = tiles + kSplitPieceCost;  // S = 1: one round
+    for (int64_t S = 2; S <= top; ++S) {
+        const int64_t cost = ((S * units + cus - 1) / cus) * ((tiles + S - 1) / S + kSplitPieceCost);
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = (int)S;
+        }
+    }
+    return best;
 }
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -1181,15 +1198,15 @@ size_t split_bytes(int head_dim, int64_t units, int splits) {
 size_t prefill_workspace(const PoolGeom &g, int batch, int hq, int total_q, int max_q, int max_kv) {
     (void)total_q;
     if (batch <= 0 || hq <= 0 || max_q <= 0 || max_kv <= 0) return 0;
-    const int S = split_count(batch, hq, max_q, max_kv);
+    const int S = split_count(batch, hq, max_q, max_kv, INT64_MAX);
     return S > 1 ? split_bytes(g.head_dim, split_units(batch, hq, max_q), S) : 0;
 }
 
 size_t prefill_split_region_max(int head_dim) {
-    // a split call has at most CUs / 2 workgroups and S x workgroups <= CUs pieces
+    // a split call has at most CUs workgroups and kSplitRounds x CUs pieces
     const int cus = current_device_cus();
     if (cus <= 0) return 0;
-    return align256((size_t)(cus / 2) * 4) + (size_t)cus * kSplitRows * (head_dim + 2) * 4;
+    return align256((size_t)cus * 4) + (size_t)kSplitRounds * cus * kSplitRows * (head_dim + 2) * 4;
 }
 
 namespace {
@@ -1202,8 +1219,12 @@ bool set_split(const PoolGeom &g, PrefillArgs &a, void *workspace, size_t worksp
     a.part = nullptr;
     a.arrivals = nullptr;
     if (!workspace || a.batch <= 0 || a.max_q <= 0 || a.max_kv <= 0) return false;
-    const int S = std::min(split_count(a.batch, a.hq, a.max_q, a.max_kv), kMaxSplits);
     const int64_t units = split_units(a.batch, a.hq, a.max_q);
+    const size_t counters = align256((size_t)units * 4), record = (size_t)kSplitRows * (g.head_dim + 2) * 4;
+    if (workspace_bytes < counters + record) return false;
+    // the best split whose records fit in the workspace
+    const int S = std::min(split_count(a.batch, a.hq, a.max_q, a.max_kv, (workspace_bytes - counters) / record),
+                           kMaxSplits);
     if (S <= 1 || workspace_bytes < split_bytes(g.head_dim, units, S)) return false;
     a.splits = S;
     a.arrivals = static_cast<int32_t *>(workspace);

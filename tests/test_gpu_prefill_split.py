@@ -1,7 +1,7 @@
 """GPU parity of pkv_prefill_attn's key splits against the oracle.
 
 A call whose (request, 128-row query tile, head) workgroups number at most
-half the CUs, over more than 960 keys, runs with each workgroup's keys cut
+the CUs, over more than 960 keys, may run with each workgroup's keys cut
 into pieces that are merged through the workspace.  The cases below take every
 path of that: each head_dim's kernel, pieces with no key tiles at all (short
 requests beside long ones), waves past a request's last row, requests with
@@ -192,3 +192,26 @@ def test_split_graph_replays():
     okc, ovc, okv, obt, oreqs = case.oracle_pools()
     rows, ro, rl = case.oracle_rows(okc, ovc, okv, obt, oreqs)
     compare(out.cpu()[rows], ro, *BF16_TOL, "graph out")
+
+
+@pytest.mark.parametrize("d,hq,q,kv,pieces", [(128, 32, 600, 4096, 3), (64, 32, 700, 16384, 4), (256, 48, 256, 32768, 5)])
+def test_split_over_several_rounds(d, hq, q, kv, pieces):
+    """Splits whose pieces take two or three rounds over the CUs (the cost
+    model's choice on 256 CUs), checked on the tile-edge rows, every 53rd and
+    the last row, each against the oracle over exactly the keys it sees."""
+    from test_gpu_prefill import tile_edge_rows
+    spec = wl.prefill_spec(q_lens=[q], kv_lens=[kv], hq=hq, hkv=8, head_dim=d, seed=90 + d)
+    say(f"[prefill split] several rounds D={d} Hq={hq} q={q} kv={kv}")
+    case = PrefillCase(spec, gen_device="cuda")
+    need = _need(case)
+    units = -(-q // 128) * hq
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert need == -(-units * 4 // 256) * 256 + units * pieces * 128 * (d + 2) * 4, need
+    assert need > 0
+    kc, vc, kv_t = case.gpu_pools()
+    out, lse = case.gpu_prefill(kc, vc, kv_t)
+    torch.cuda.synchronize()
+    okc, ovc, okv, obt, oreqs = case.oracle_pools()
+    rows, ro, rl = case.oracle_row_set(okc, ovc, okv, obt, oreqs, lambda r, q_len: tile_edge_rows(r, q_len))
+    compare(out.cpu()[rows], ro, *BF16_TOL, "out")
+    compare(lse.cpu()[rows], rl, *BF16_TOL, "lse")
