@@ -340,8 +340,8 @@ __device__ __forceinline__ float mask_max(f32x4 (&sc)[NB], float c, bool need_ma
 constexpr float kSplitFloor = -3.0e38f;
 constexpr int kMaxSplits = 16;
 
-// Record of piece s of workgroup `unit`: BM rows of D fp32 (row-major), then
-// BM (max, sum) pairs.
+// Record of piece s of workgroup `unit`: BM x D fp32 output values (in wave
+// and lane order, see split_settle), then BM (max, sum) pairs by row.
 template <int D, int BM>
 __device__ __forceinline__ float *split_record(const PrefillArgs &a, int64_t unit, int s) {
     return a.part + (unit * a.splits + s) * ((int64_t)BM * (D + 2));
@@ -354,24 +354,30 @@ __device__ __forceinline__ float *split_record(const PrefillArgs &a, int64_t uni
 // past its last row neither write nor merge a record); rr: the lane's row in
 // the workgroup; lt: the row sum.
 //
-// The merge's loads go out together, so that it waits for a few round trips
-// to memory rather than one per record: first every piece's (max, sum), then
-// the records NR at a time (NR * D/4 registers of them in flight).  Indices
-// past the last piece load piece S-1 again and take weight 0, which keeps
-// every register index static and the sums' order fixed.
+// The merge's loads go out NR records at a time (NR * D/4 registers of them
+// in flight), so that it waits for one round trip to memory per group rather
+// than per record; a record is read in the order it was written, each
+// instruction 512 contiguous bytes (stored with 16-byte row runs instead,
+// the records took 4.7 us to write and 16 us to merge at 8 pieces, against
+// 1.4 and 5.5 us in this order; measured per workgroup).  Indices past the
+// last piece load piece S-1 again and take weight 0, which keeps every
+// register index static and the sums' order fixed.
 template <int D, int BM>
 __device__ bool split_settle(const PrefillArgs &a, int64_t unit, int s, bool rows, int rr, int grp,
                              f32x4 (&acc)[D / 16], float &m, float &lt, int *prior_lds) {
     constexpr int DB = D / 16;
     constexpr int NR = D == 64 ? 4 : 128 / (4 * DB);  // head_dim 64 stays within 128 registers
     const int S = a.splits;
+    // record values in wave and lane order: element pair i of dim block db of
+    // wave w's lane at ((w * DB + db) * 2 + i) * 128 + 2 * lane, so that each
+    // 8-byte store or load instruction covers 512 contiguous bytes
+    const int vo = (int)(threadIdx.x >> 6) * DB * 256 + 2 * (int)(threadIdx.x & 63);
     if (rows) {
         float *own = split_record<D, BM>(a, unit, s);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            float *p = own + rr * D + 16 * db + 4 * grp;
-            st_agent2(p, acc[db][0], acc[db][1]);
-            st_agent2(p + 2, acc[db][2], acc[db][3]);
+            st_agent2(own + vo + db * 256, acc[db][0], acc[db][1]);
+            st_agent2(own + vo + db * 256 + 128, acc[db][2], acc[db][3]);
         }
         if (grp == 0) st_agent2(own + BM * D + rr * 2, m, lt);
     }
@@ -383,18 +389,11 @@ __device__ bool split_settle(const PrefillArgs &a, int64_t unit, int s, bool row
     if (*prior_lds != S - 1) return false;
     if (threadIdx.x == 0) __hip_atomic_store(a.arrivals + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (!rows) return true;
-    float M = kSplitFloor;
-    {
-        float mt[kMaxSplits];
-#pragma unroll
-        for (int t = 0; t < kMaxSplits; ++t)
-            mt[t] = ld_agent2(split_record<D, BM>(a, unit, min(t, S - 1)) + BM * D + rr * 2)[0];
-#pragma unroll
-        for (int t = 0; t < kMaxSplits; ++t) M = fmaxf(M, mt[t]);
-    }
+    // fold the records in piece order, NR per round trip, rescaling the sum
+    // so far whenever a group raises the running max
+    float M = kSplitFloor, L = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float L = 0.f;
     for (int t0 = 0; t0 < S; t0 += NR) {
         f32x4 v[NR][DB];
         f32x2 ml[NR];
@@ -404,11 +403,19 @@ __device__ bool split_settle(const PrefillArgs &a, int64_t unit, int s, bool row
             ml[j] = ld_agent2(rec + BM * D + rr * 2);
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const f32x2 lo = ld_agent2(rec + rr * D + 16 * db + 4 * grp);
-                const f32x2 hi = ld_agent2(rec + rr * D + 16 * db + 4 * grp + 2);
+                const f32x2 lo = ld_agent2(rec + vo + db * 256);
+                const f32x2 hi = ld_agent2(rec + vo + db * 256 + 128);
                 v[j][db] = f32x4{lo[0], lo[1], hi[0], hi[1]};
             }
         }
+        float Mn = M;
+#pragma unroll
+        for (int j = 0; j < NR; ++j) Mn = fmaxf(Mn, ml[j][0]);
+        const float r = fast_exp2(M - Mn);  // 1 when the max holds, 0 on the first group
+        L *= r;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] *= r;
+        M = Mn;
 #pragma unroll
         for (int j = 0; j < NR; ++j) {
             const float w = t0 + j < S ? fast_exp2(ml[j][0] - M) : 0.f;
