@@ -389,7 +389,7 @@ pkv_status pkv_append_decode_attn_noalloc(const pkv_cache_desc *cache, void *out
  * more than 960 keys, may cut each workgroup's keys into S pieces when it is
  * given a workspace.  S (at most 16, at most one piece per 512 keys, at most
  * three rounds of pieces over the CUs) minimises rounds x piece length, with
- * 1024 keys added to each piece for its start-up and merge.  The pieces'
+ * 512 keys added to each piece for its start-up and merge.  The pieces'
  * partial rows meet in the workspace (one 128 x (head_dim + 2) fp32 record
  * per piece: up to ~100 MB at head_dim 256 on 256 CUs) and are merged in a
  * fixed piece order, so results are deterministic.  They equal the unsplit

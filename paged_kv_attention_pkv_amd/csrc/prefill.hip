@@ -1155,19 +1155,21 @@ namespace {
 // whole length when it has few of them; with many keys per row it runs
 // 8-wave workgroups with each one's key tiles cut into S pieces.  S minimises
 // a cost of rounds x piece length: ceil(S x workgroups / CUs) x (ceil(T / S)
-// + 16), T = key tiles of the longest row, the 16 tiles standing for a
-// piece's start-up and merge; S <= kMaxSplits, S <= T / 8, at most three
-// rounds of pieces (kSplitRounds), ties to the smaller S.  The model was
-// fitted to sweeps of S = 1 .. 16 on 21 shapes (head_dim 64, 128 and 256, 16
-// to 1023 query rows, 4000 to 32768 keys, 32 to 384 workgroups): its S was
-// the fastest or within 5% of it on each, 1.3 to 5.8 times faster than no
-// split where it splits.  Time falls with S while the pieces fill whole
-// rounds and jumps when a round is left part-empty, and each piece slows as
-// more CUs run at once; calls of more than one round of workgroups lost with
-// every S measured.
+// + 8), T = key tiles of the longest row, the 8 tiles standing for a piece's
+// start-up, record and merge (~3 + 2 + 5 us, measured per workgroup);
+// S <= kMaxSplits, S <= T / 8, at most three rounds of pieces
+// (kSplitRounds), ties to the smaller S.  Fitted to sweeps of S = 1 .. 16 on
+// 24 shapes (head_dim 64, 128 and 256, 16 to 1023 query rows, 2000 to 32768
+// keys, 32 to 384 workgroups): the model's S was within 1.6% of the fastest
+// on average and 11% at worst, and 1.3 to 6.7 times faster than no split
+// where it splits.  Time falls with S while the pieces fill whole rounds and
+// jumps when a round is left part-empty, and each piece slows as more CUs
+// run at once; calls of more than one round of workgroups lost with most S
+// (the causal q = kv = 1023 request at head_dim 256: 44 us unsplit, 72 at
+// S = 2).
 constexpr int kSplitRows = Cfg16<8>::BM;
 constexpr int kSplitRounds = 3;
-constexpr int kSplitPieceCost = 16;  // tiles
+constexpr int kSplitPieceCost = 8;  // tiles
 
 int64_t split_units(int batch, int hq, int max_q) {
     return (int64_t)batch * ((max_q + kSplitRows - 1) / kSplitRows) * hq;

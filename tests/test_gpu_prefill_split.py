@@ -194,7 +194,7 @@ def test_split_graph_replays():
     compare(out.cpu()[rows], ro, *BF16_TOL, "graph out")
 
 
-@pytest.mark.parametrize("d,hq,q,kv,pieces", [(128, 32, 600, 4096, 3), (64, 32, 700, 16384, 4), (256, 48, 256, 32768, 5)])
+@pytest.mark.parametrize("d,hq,q,kv,pieces", [(128, 32, 600, 4096, 3), (64, 32, 700, 16384, 4), (256, 48, 256, 32768, 8)])
 def test_split_over_several_rounds(d, hq, q, kv, pieces):
     """Splits whose pieces take two or three rounds over the CUs (the cost
     model's choice on 256 CUs), checked on the tile-edge rows, every 53rd and
