@@ -21,7 +21,7 @@ def _mixed(case, num_prefill):
     kc, vc, kv = case.gpu_pools()
     max_q = int(s.q_lens[:num_prefill].max()) if num_prefill else 0
     out, lse = pkv.mixed_attn(i.q, kc, vc, i.block_table, kv, i.qo_indptr, num_prefill, max_q,
-                              int(s.kv_lens.max()), s.scale, return_lse=True)
+                              int(s.kv_lens.max()), s.scale, return_lse=True, layout=s.layout)
     torch.cuda.synchronize()
     return kc, vc, kv, out, lse
 
@@ -212,3 +212,26 @@ def test_mixed_many_decode_rows_two_launches():
     torch.cuda.synchronize()
     compare(o1[npf:].cpu(), ref_d.cpu().double().numpy(), *BF16_TOL, "one-launch decode rows")
     compare(l1[npf:].cpu(), ref_dl.cpu().double().numpy(), *BF16_TOL, "one-launch decode lse")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_mixed(seed):
+    """Random serving steps: 0-3 chunks (1-400 rows over up to 3000 more keys,
+    so that some split their keys), 0-120 decode rows (enough, with 8 KV heads,
+    for the two-launch route), head counts, head dims 64/128, HND or NHD,
+    pages of 16-256 tokens; every row against the oracle."""
+    rng = np.random.default_rng(8800 + seed)
+    hq, hkv = [(32, 8), (16, 4), (8, 8), (12, 2)][int(rng.integers(4))]
+    d = int(rng.choice([64, 128]))
+    nc = int(rng.integers(0, 4))
+    nd = int(rng.integers(0 if nc else 1, 121))
+    q = rng.integers(1, 401, size=nc).tolist()
+    kv = [x + int(rng.integers(0, 3001)) for x in q]
+    dec = rng.integers(0, 3001, size=nd).tolist()
+    layout = "NHD" if rng.random() < 0.4 else "HND"
+    page = int(rng.choice([16, 16, 32, 64, 128, 256]))
+    say(f"[random mixed {seed}] Hq={hq} Hkv={hkv} D={d} {layout} page={page} chunks q={q} kv={kv} decode rows {nd}")
+    dec_kv = [max(x, 1) for x in dec]
+    spec = wl.prefill_spec(q_lens=q + [1] * nd, kv_lens=kv + dec_kv, hq=hq, hkv=hkv, head_dim=d, seed=8900 + seed,
+                           layout=layout, page_size=page)
+    _check(spec, nc)
