@@ -326,9 +326,9 @@ __device__ __forceinline__ float mask_max(f32x4 (&sc)[NB], float c, bool need_ma
 // key splits
 // ---------------------------------------------------------------------------
 //
-// A call whose (request, query tile, head) workgroups fill the chip less than
-// once (few query rows over many keys) runs each of them as S pieces, one
-// 8-wave workgroup each.  Piece s walks key tiles [s*T/S, (s+1)*T/S) of the
+// A call whose (request, query tile, head) workgroups fill the chip at most
+// once (few query rows over many keys) may run each of them as S pieces, one
+// 8-wave workgroup each (the choice of S is with the launch code below).  Piece s walks key tiles [s*T/S, (s+1)*T/S) of the
 // workgroup's T, writes its rows' unnormalised output and (max, sum) as an
 // fp32 record and counts itself; the piece that counts last folds the S
 // records, its own read back like the others, in piece order and writes the
@@ -357,9 +357,10 @@ __device__ __forceinline__ float *split_record(const PrefillArgs &a, int64_t uni
 // The merge's loads go out NR records at a time (NR * D/4 registers of them
 // in flight), so that it waits for one round trip to memory per group rather
 // than per record; a record is read in the order it was written, each
-// instruction 512 contiguous bytes (stored with 16-byte row runs instead,
-// the records took 4.7 us to write and 16 us to merge at 8 pieces, against
-// 1.4 and 5.5 us in this order; measured per workgroup).  Indices past the
+// instruction 512 contiguous bytes (stored row by row instead, each
+// instruction touching 16 rows, the records took 4.7 us to write and 16 us
+// to merge at 8 pieces, against 1.4 and 5.5 us in this order; measured per
+// workgroup).  Indices past the
 // last piece load piece S-1 again and take weight 0, which keeps every
 // register index static and the sums' order fixed.
 template <int D, int BM>
