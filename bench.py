@@ -175,6 +175,23 @@ def device_info(torch, props) -> dict:
     return d
 
 
+def parity(gpu, ref, dtype: str, what: str) -> dict:
+    """Element-wise |gpu - ref| <= atol + rtol |ref| of a GPU output (widened
+    exactly) against the oracle's fp64 result, at the bar of the output dtype
+    (bf16: 2e-2 / 2e-2, fp32: 1e-5 / 1e-5)."""
+    import numpy as np
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_common import BF16_TOL, F32_TOL
+
+    atol, rtol = BF16_TOL if dtype == "bf16" else F32_TOL
+    g = gpu.float().double().numpy()
+    r = np.asarray(ref, dtype=np.float64).reshape(g.shape)
+    err = np.abs(g - r)
+    return {"what": what, "elements": int(g.size), "max_abs_err": float(np.max(err)),
+            "max_rel_err": float(np.max(err / np.maximum(np.abs(r), 1e-30))), "atol": atol, "rtol": rtol,
+            "pass": bool(np.all(err <= atol + rtol * np.abs(r)))}
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -294,6 +311,8 @@ def bench_decode(args, torch, pkv, wl, workload):
             workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
         pkv.append(kc, vc, inp.k_hist, inp.v_hist, bt, zeros, inp.hist_indptr, layout=spec.layout)
         out = torch.empty_like(inp.q)
+        if layer == 0:
+            out0 = out
         if fused:
             app = None
             dec = pkv.api.prepare_append_decode(inp.q, kc, vc, inp.k_new, inp.v_new, bt, hist, max_kv, spec.scale,
@@ -375,8 +394,9 @@ def bench_decode(args, torch, pkv, wl, workload):
                      "traffic": None if traffic is None else int(traffic),
                      "traffic_unit": "HBM bytes per launch", "bytes_per_launch": acc["total"]},
     }
-    del layers, workspace
-    return result, spec
+    gpu_out0 = out0.cpu()  # layer 0's output after the timed steps (every step computes the same)
+    del layers, workspace, out0
+    return result, spec, gpu_out0
 
 
 def _timed_loop(fn, seconds, min_calls=1):
@@ -390,11 +410,12 @@ def _timed_loop(fn, seconds, min_calls=1):
     return calls, spent, total
 
 
-def cpu_baseline_decode(args, spec):
+def cpu_baseline_decode(args, spec, gpu_out0=None):
     """The oracle (as is) on a bounded sample of the same workload: whole
     decode calls of the batch (host pools built by the oracle's own append
     from two layers' draws), on all host threads of the GPU's share, then on
-    one thread."""
+    one thread.  With gpu_out0 (layer 0's output of the timed GPU step) the
+    oracle's layer-0 call is also compared with it, every element."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import numpy as np
     import oracle
@@ -426,12 +447,17 @@ def cpu_baseline_decode(args, spec):
 
     calls, spent, done = _timed_loop(call(threads), args.cpu_seconds)
     calls1, spent1, done1 = _timed_loop(call(1), args.cpu_seconds_1t)
-    return {"value": round(done / spent / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "value_1_thread": round(done1 / spent1 / 1e9, 4),
-            "host_cpu_count": os.cpu_count(), "cpu_model": cpu_model(),
-            "sample": f"{calls} decode calls of the same workload (all {spec.batch} sequences, two layers' draws "
-                      f"in turn) on {threads} threads in {spent:.1f} s; {calls1} calls on 1 thread in "
-                      f"{spent1:.1f} s; fp64 oracle, KV-read bytes per second"}
+    res = {"value": round(done / spent / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "value_1_thread": round(done1 / spent1 / 1e9, 4),
+           "host_cpu_count": os.cpu_count(), "cpu_model": cpu_model(),
+           "sample": f"{calls} decode calls of the same workload (all {spec.batch} sequences, two layers' draws "
+                     f"in turn) on {threads} threads in {spent:.1f} s; {calls1} calls on 1 thread in "
+                     f"{spent1:.1f} s; fp64 oracle, KV-read bytes per second"}
+    if gpu_out0 is not None:
+        q, kc, vc, lens = hosts[0]
+        ref, _ = orc.decode(pool, q, kc, vc, spec.block_table, lens, spec.scale, nthreads=threads)
+        res["parity"] = parity(gpu_out0, ref, spec.dtype, f"layer 0, all {spec.batch} x {spec.hq} output rows")
+    return res
 
 
 # --------------------------------------------------------------------------
@@ -454,6 +480,8 @@ def bench_prefill(args, torch, pkv, wl, spec):
         pkv.append(kc, vc, inp.k_hist, inp.v_hist, inp.block_table, zeros, inp.hist_indptr, layout=lay)
         kv_lens = pkv.append(kc, vc, inp.k_new, inp.v_new, inp.block_table, inp.hist_lens, inp.qo_indptr, layout=lay)
         out = torch.empty_like(inp.q)
+        if layer == 0:
+            out0 = out
         if ws is None:
             need = pkv.prefill_workspace_bytes(kc, spec.batch, spec.hq, int(spec.q_lens.sum()), max_q, max_kv,
                                                layout=lay)
@@ -512,8 +540,9 @@ def bench_prefill(args, torch, pkv, wl, spec):
                      "traffic": None if traffic is None else int(traffic),
                      "traffic_unit": "HBM bytes per launch", "flops_per_launch": flops},
     }
-    del calls, ws
-    return result
+    gpu_out0 = out0.cpu()
+    del calls, ws, out0
+    return result, gpu_out0
 
 
 def bench_mixed(args, torch, pkv, wl):
@@ -596,11 +625,13 @@ def bench_mixed(args, torch, pkv, wl):
     return result
 
 
-def cpu_baseline_prefill(args, spec):
+def cpu_baseline_prefill(args, spec, gpu_out0=None):
     """The oracle (as is) on a sample of query rows of the same request(s):
     blocks of 32 consecutive rows of request 0, from its last row backwards,
     each run as a chunked-prefill request over the keys it sees, on all host
-    threads of the GPU's share, then on one thread."""
+    threads of the GPU's share, then on one thread.  With gpu_out0 (layer 0's
+    output of the timed GPU step) the oracle's first and last blocks of
+    request 0 are also compared with it, all heads."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import numpy as np
     import oracle
@@ -636,12 +667,25 @@ def cpu_baseline_prefill(args, spec):
 
     n, spent, fl = _timed_loop(block(threads), args.cpu_seconds)
     n1, spent1, fl1 = _timed_loop(block(1), args.cpu_seconds_1t)
-    return {"value": round(fl / spent / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "value_1_thread": round(fl1 / spent1 / 1e12, 6),
-            "host_cpu_count": os.cpu_count(), "cpu_model": cpu_model(),
-            "sample": f"{n} blocks of {blk} query rows of request 0 ({r0} rows; from its last row backwards, "
-                      f"cyclically) on {threads} threads in {spent:.1f} s ({fl / 1e9:.1f} GFLOP); {n1} blocks on "
-                      f"1 thread in {spent1:.1f} s; fp64 oracle"}
+    res = {"value": round(fl / spent / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "value_1_thread": round(fl1 / spent1 / 1e12, 6),
+           "host_cpu_count": os.cpu_count(), "cpu_model": cpu_model(),
+           "sample": f"{n} blocks of {blk} query rows of request 0 ({r0} rows; from its last row backwards, "
+                     f"cyclically) on {threads} threads in {spent:.1f} s ({fl / 1e9:.1f} GFLOP); {n1} blocks on "
+                     f"1 thread in {spent1:.1f} s; fp64 oracle"}
+    if gpu_out0 is not None:
+        gpu, ref = [], []
+        for a0 in sorted({0, max(0, r0 - blk)}):
+            a1 = min(a0 + blk, r0)
+            o, _ = orc.prefill(pool, host_bits(h.q[ip[0] + a0: ip[0] + a1]), kc, vc, spec.block_table[:1],
+                               np.array([kvl - r0 + a1], np.int32), np.array([0, a1 - a0], np.int32), spec.scale,
+                               causal=True, nthreads=threads)
+            gpu.append(gpu_out0[ip[0] + a0: ip[0] + a1])
+            ref.append(o)
+        import torch
+        res["parity"] = parity(torch.cat(gpu), np.concatenate(ref), spec.dtype,
+                               f"layer 0, request 0: its first and last {blk} query rows, all {spec.hq} heads")
+    return res
 
 
 # --------------------------------------------------------------------------
@@ -1031,22 +1075,24 @@ def main():
             spec = wl.prefill_spec(fixed_1023=True, **kw)
         else:
             spec = wl.prefill_spec(batch=args.batch, **kw)
-        result = bench_prefill(args, torch, pkv, wl, spec)
+        result, out0 = bench_prefill(args, torch, pkv, wl, spec)
         result.update({"n_gpus": 1, "scaling": "weak", "vs_baseline": None})
         if cpu:
-            result["cpu_baseline"] = cpu_baseline_prefill(args, spec)
+            result["cpu_baseline"] = cpu_baseline_prefill(args, spec, out0)
     else:
-        result, spec = bench_decode(args, torch, pkv, wl, args.workload or "decode")
+        result, spec, out0 = bench_decode(args, torch, pkv, wl, args.workload or "decode")
         if cpu:
-            result["cpu_baseline"] = cpu_baseline_decode(args, spec)
+            result["cpu_baseline"] = cpu_baseline_decode(args, spec, out0)
+        del out0
         if args.workload is None:
             torch.cuda.empty_cache()
             result["prefill"] = {}
             for key, pspec in (("b1_q1023", wl.prefill_spec(fixed_1023=True)),
                                ("b8_random", wl.prefill_spec(batch=8))):
-                sub = bench_prefill(args, torch, pkv, wl, pspec)
+                sub, out0 = bench_prefill(args, torch, pkv, wl, pspec)
                 if cpu:
-                    sub["cpu_baseline"] = cpu_baseline_prefill(args, pspec)
+                    sub["cpu_baseline"] = cpu_baseline_prefill(args, pspec, out0)
+                del out0
                 result["prefill"][key] = sub
                 torch.cuda.empty_cache()
             result["mixed"] = bench_mixed(args, torch, pkv, wl)
