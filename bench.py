@@ -1036,8 +1036,8 @@ def main():
         return
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU "
-              "mode in this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library runs each call on "
+              "one GPU and has no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
     import torch
 
